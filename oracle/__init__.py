@@ -1,0 +1,188 @@
+"""fp64 CPU oracle of the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never calls it, and it never calls the product path.
+
+The arithmetic lives in ``ssm_oracle.c`` (plain C, double precision, libm,
+no fast-math), described there with its sources.  This module only builds
+that file with gcc, loads it with ctypes and marshals numpy arrays.
+
+Pins (each checked by a ``-m "not gpu"`` test in tests/test_oracle_pins.py):
+  * brute-force unrolled sum  y_t = sum_k C_t (prod_{s=k+1..t} dA_s) dt_k B_k u_k + D u_t
+    on tiny inputs (page "From FlashAttention to Mamba", §三.2 closed form of
+    the scan; the decay-product form of the Mamba-2/SSD article, §2.2);
+  * geometric closed form for constant delta, B, u (recurrence of the ufo.work
+    article, §1.1);
+  * time-invariant special case == numpy.convolve with kernel
+    K_j = sum_n C_n a_n^j dt B_n (convolution/recurrence duality, SSM
+    engineering essay §1.1);
+  * chunked route (transfer operators, fold and tree combine) == sequential
+    loop (ufo.work article, §3.1);
+  * single-token update applied L times == the scan (ufo.work article, §4.1);
+  * delta = 0 gives y = D u; a decay so strong that exp underflows gives the
+    closed form y_t = dt u_t (C_t . B_t) + D u_t; z = 0 zeroes y; softplus of
+    the inverse-softplus bias returns the drawn step size;
+  * a hand-worked example with exact rational values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+SRC = _HERE / "ssm_oracle.c"
+LIB = _HERE / "libssm_oracle.so"
+
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile the oracle with gcc (no fast-math)."""
+    if not force and LIB.exists() and LIB.stat().st_mtime >= SRC.stat().st_mtime:
+        return LIB
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           str(SRC), "-o", str(tmp), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(str(LIB))
+    i64, dp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [c_int, dp, dp, dp, c_int]
+    lib.oracle_scan_fwd.restype = c_int
+    lib.oracle_scan_chunked.argtypes = ([i64, i64, i64, i64] + [dp] * 8 +
+                                        [c_int, dp, dp, dp, i64, c_int, c_int])
+    lib.oracle_scan_chunked.restype = c_int
+    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_state_update.restype = c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(x, shape=None):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _scan_args(u, delta, A, B, C, D, z, delta_bias, initial_state):
+    u = _f64(u)
+    if u.ndim != 3:
+        raise ValueError("u must be (batch, d_inner, L)")
+    batch, d_inner, L = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    return (batch, d_inner, N, L, u, _f64(delta, u.shape), _f64(A, (d_inner, N)),
+            _f64(B, (batch, N, L)), _f64(C, (batch, N, L)), _f64(D, (d_inner,)),
+            _f64(z, u.shape), _f64(delta_bias, (d_inner,)),
+            _f64(initial_state, (batch, d_inner, N)))
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+             initial_state=None, threads: int | None = None):
+    """Sequential fp64 scan.  Returns (y, last_state), both float64."""
+    lib = _load()
+    (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
+        u, delta, A, B, C, D, z, delta_bias, initial_state)
+    y = np.zeros((batch, d_inner, L))
+    last = np.zeros((batch, d_inner, N))
+    rc = lib.oracle_scan_fwd(batch, d_inner, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                             _ptr(C), _ptr(D), _ptr(z), _ptr(bias), int(bool(softplus)),
+                             _ptr(h0), _ptr(y), _ptr(last), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_fwd failed ({rc})")
+    return y, last
+
+
+def scan_chunked(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+                 initial_state=None, chunk: int = 256, tree: bool = True,
+                 threads: int | None = None):
+    """Chunked fp64 route (transfer operators + combine).  Returns (y, last_state)."""
+    lib = _load()
+    (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
+        u, delta, A, B, C, D, z, delta_bias, initial_state)
+    y = np.zeros((batch, d_inner, L))
+    last = np.zeros((batch, d_inner, N))
+    rc = lib.oracle_scan_chunked(batch, d_inner, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(bias), int(bool(softplus)),
+                                 _ptr(h0), _ptr(y), _ptr(last), int(chunk), int(bool(tree)),
+                                 threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_chunked failed ({rc})")
+    return y, last
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None):
+    """One fp64 single-token update.  Returns (new_state, y); inputs untouched."""
+    lib = _load()
+    s = np.array(state, dtype=np.float64, copy=True, order="C")
+    batch, d_inner, N = s.shape
+    u = _f64(u, (batch, d_inner))
+    delta = _f64(delta, (batch, d_inner))
+    A = _f64(A, (d_inner, N))
+    B = _f64(B, (batch, N))
+    C = _f64(C, (batch, N))
+    D = _f64(D, (d_inner,))
+    z = _f64(z, (batch, d_inner))
+    y = np.zeros((batch, d_inner))
+    rc = lib.oracle_state_update(batch, d_inner, N, _ptr(s), _ptr(u), _ptr(delta), _ptr(A),
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_state_update failed ({rc})")
+    return s, y
+
+
+def scan_rows(inputs_f64: dict, rows, threads: int | None = None):
+    """Oracle on a subset of (b, d) rows of one workload.
+
+    ``inputs_f64`` holds decoded float64 arrays (keys u, delta, A, B, C, D, z,
+    delta_bias, softplus, optional initial_state).  Returns (y_rows, state_rows) with
+    shapes (len(rows), L) and (len(rows), N), in the order of ``rows``.
+    """
+    u = inputs_f64["u"]
+    L = u.shape[2]
+    N = inputs_f64["A"].shape[1]
+    ys = np.zeros((len(rows), L))
+    hs = np.zeros((len(rows), N))
+    by_batch: dict[int, list[int]] = {}
+    for i, (b, d) in enumerate(rows):
+        by_batch.setdefault(int(b), []).append(i)
+    for b, idx in by_batch.items():
+        ds = np.array([rows[i][1] for i in idx])
+        sel = lambda key: None if inputs_f64.get(key) is None else inputs_f64[key][b:b + 1, ds]
+        vec = lambda key: None if inputs_f64.get(key) is None else inputs_f64[key][ds]
+        h0 = inputs_f64.get("initial_state")
+        y, h = scan_fwd(sel("u"), sel("delta"), inputs_f64["A"][ds], inputs_f64["B"][b:b + 1],
+                        inputs_f64["C"][b:b + 1], vec("D"), sel("z"), vec("delta_bias"),
+                        softplus=bool(inputs_f64.get("softplus", 1)),
+                        initial_state=None if h0 is None else h0[b:b + 1, ds],
+                        threads=threads)
+        ys[idx] = y[0]
+        hs[idx] = h[0]
+    return ys, hs

@@ -1,0 +1,325 @@
+/*
+ * ssm_oracle.c -- plain, slow, fp64 CPU reference of the selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the two meet only through
+ * the seeded inputs.
+ *
+ * Every value is evaluated in double precision with libm exp/log1p, compiled
+ * without fast-math.  Inputs arrive already decoded to double (after the
+ * rounding to the I/O dtype that the GPU path also sees).
+ *
+ * Sources (web pages on the Mamba selective scan):
+ *   [P1] "Mamba hardware-aware operator fusion and selective-scan
+ *        parallelisation for long meeting sequences" (ufo.work, first article)
+ *   [P2] "From FlashAttention to Mamba: inference optimisation" (kj168168)
+ *   [P5] SSM engineering essay (discosf.com)
+ *
+ * What is computed, per batch row b and channel d, independently:
+ *   delta_t = softplus(delta_raw + bias[d]) if the flag is set, else the sum
+ *                                  -- [P5] §1.3 (input-dependent step size,
+ *                                     through softplus); [P1] §2.1 (dt_proj
+ *                                     then softplus); bias added before it.
+ *   dA      = exp(delta_t * A[d,n])                   -- [P1] §1.1, [P2] §三.1
+ *   dBu     = delta_t * B[b,n,t] * u[b,d,t]           -- [P1] §1.1 (B-bar =
+ *                                     Delta*B, applied to the input x_t)
+ *   h_t[n]  = dA * h_{t-1}[n] + dBu,  h_{-1} = 0      -- [P1] §1.1, [P5] §1.2
+ *   y_t     = sum_n C[b,n,t] h_t[n] + D[d] u[b,d,t]   -- [P1] §1.1 (y = C h),
+ *                                     [P5] §1.1 (skip term D x)
+ *   y_t    *= z / (1 + exp(-z))   when a gate z is given (silu gate)
+ *   last_state[b,d,n] = h_{L-1}[n]
+ * Single-token update ([P1] §4.1, persistent state, h_new = A h_old + B x):
+ *   state[b,d,n] <- exp(delta A[d,n]) state + delta B[b,n] u[b,d]
+ *   y[b,d]        = (sum_n C[b,n] state[b,d,n] + D[d] u[b,d]) * silu(z)
+ *
+ * Layouts (row-major, last index fastest):
+ *   u, delta, z, y: (batch, d_inner, L)   B, C: (batch, N, L)
+ *   A: (d_inner, N)   D, delta_bias: (d_inner)   states: (batch, d_inner, N)
+ *
+ * The second entry point, oracle_scan_chunked, reaches the same result by
+ * the chunked route of [P1] §3.1: each chunk's transfer operator
+ * (A_chunk, B_chunk) with h_end = A_chunk h_start + B_chunk, an exclusive
+ * combine of the operators across chunks (left fold, or a balanced tree of
+ * the associative composition), then a re-run of every chunk from its
+ * h_start.  It exists only so that tests can check that chunking is an exact
+ * re-association of the sequential loop.
+ *
+ * Parity pins: see the header of oracle/__init__.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------ scalar steps */
+
+/* softplus(x) = log(1 + e^x), written as max(x,0) + log1p(e^{-|x|}) so that
+ * it neither overflows for large x nor loses digits for very negative x. */
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* ------------------------------------------------------------ arguments */
+
+typedef struct {
+    int64_t batch, d_inner, d_state, seqlen;
+    const double *u, *delta, *A, *B, *C, *D, *z, *delta_bias, *h0;
+    int softplus_flag;
+    double *y, *last_state;
+    int64_t chunk;      /* chunked path only */
+    int tree;           /* chunked path only: 1 = balanced tree, 0 = left fold */
+} scan_args;
+
+typedef struct {
+    const scan_args *a;
+    int worker, n_workers;
+    int chunked;
+    int status;
+} worker_args;
+
+static double step_size(const scan_args *a, int64_t d, double raw) {
+    double x = raw + (a->delta_bias ? a->delta_bias[d] : 0.0);
+    return a->softplus_flag ? softplus(x) : x;
+}
+
+/* Run tokens [t0, t1) of row (b, d) starting from state h (updated in
+ * place).  Writes y for those tokens when y_row is not NULL. */
+static void run_tokens(const scan_args *a, int64_t b, int64_t d, int64_t t0, int64_t t1,
+                       double *h, double *y_row) {
+    const int64_t N = a->d_state, L = a->seqlen;
+    const int64_t row = (b * a->d_inner + d) * L;
+    for (int64_t t = t0; t < t1; ++t) {
+        const double u = a->u[row + t];
+        const double dt = step_size(a, d, a->delta[row + t]);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double dA = exp(dt * a->A[d * N + n]);
+            const double dBu = dt * a->B[(b * N + n) * L + t] * u;
+            h[n] = dA * h[n] + dBu;
+            acc += a->C[(b * N + n) * L + t] * h[n];
+        }
+        if (!y_row) continue;
+        if (a->D) acc += a->D[d] * u;
+        if (a->z) acc *= silu(a->z[row + t]);
+        y_row[t] = acc;
+    }
+}
+
+static void init_state(const scan_args *a, int64_t b, int64_t d, double *h) {
+    const int64_t N = a->d_state;
+    for (int64_t n = 0; n < N; ++n)
+        h[n] = a->h0 ? a->h0[(b * a->d_inner + d) * N + n] : 0.0;
+}
+
+static void store_state(const scan_args *a, int64_t b, int64_t d, const double *h) {
+    if (!a->last_state) return;
+    const int64_t N = a->d_state;
+    memcpy(a->last_state + (b * a->d_inner + d) * N, h, (size_t)N * sizeof(double));
+}
+
+/* ------------------------------------------------------------ sequential */
+
+static int scan_row_sequential(const scan_args *a, int64_t b, int64_t d, double *h) {
+    init_state(a, b, d, h);
+    run_tokens(a, b, d, 0, a->seqlen, h, a->y + (b * a->d_inner + d) * a->seqlen);
+    store_state(a, b, d, h);
+    return 0;
+}
+
+/* ------------------------------------------------------------ chunked */
+
+/* Transfer operator of a token range: h_end = op.a (elementwise) h_start + op.b.
+ * compose(first, second) applies `first`, then `second`:
+ *   (a2, b2) o (a1, b1) = (a1 a2, a2 b1 + b2)                                */
+static void compose(const double *a1, const double *b1, const double *a2, const double *b2,
+                    double *ao, double *bo, int64_t N) {
+    for (int64_t n = 0; n < N; ++n) {
+        const double a = a1[n] * a2[n];
+        const double bb = a2[n] * b1[n] + b2[n];
+        ao[n] = a;
+        bo[n] = bb;
+    }
+}
+
+static int scan_row_chunked(const scan_args *a, int64_t b, int64_t d, double *h) {
+    const int64_t N = a->d_state, L = a->seqlen, K = a->chunk;
+    const int64_t nc = (L + K - 1) / K;
+    int64_t P = 1;
+    while (P < nc) P <<= 1;
+    /* opa/opb: per-chunk operators, padded to a power of two with identity. */
+    double *opa = malloc(sizeof(double) * (size_t)(P * N));
+    double *opb = malloc(sizeof(double) * (size_t)(P * N));
+    double *ta = malloc(sizeof(double) * (size_t)N);
+    double *tb = malloc(sizeof(double) * (size_t)N);
+    if (!opa || !opb || !ta || !tb) {
+        free(opa); free(opb); free(ta); free(tb);
+        return -1;
+    }
+    const int64_t row = (b * a->d_inner + d) * L;
+
+    /* 1. Local scan of each chunk from a zero state: B_chunk is the state it
+     *    ends in, A_chunk is the product of its decays. */
+    for (int64_t k = 0; k < P; ++k) {
+        double *ka = opa + k * N, *kb = opb + k * N;
+        for (int64_t n = 0; n < N; ++n) { ka[n] = 1.0; kb[n] = 0.0; }
+        if (k >= nc) continue;
+        const int64_t t1 = (k + 1) * K < L ? (k + 1) * K : L;
+        for (int64_t t = k * K; t < t1; ++t) {
+            const double u = a->u[row + t];
+            const double dt = step_size(a, d, a->delta[row + t]);
+            for (int64_t n = 0; n < N; ++n) {
+                const double dA = exp(dt * a->A[d * N + n]);
+                ka[n] *= dA;
+                kb[n] = dA * kb[n] + dt * a->B[(b * N + n) * L + t] * u;
+            }
+        }
+    }
+
+    /* 2. Exclusive prefix of the operators: slot k receives the composition
+     *    of chunks 0..k-1 (identity for chunk 0). */
+    if (a->tree) {
+        /* Balanced tree: up-sweep builds subtree totals, down-sweep hands
+         * every left subtree the prefix of its parent and every right subtree
+         * that prefix followed by its left sibling's total. */
+        for (int64_t s = 1; s < P; s <<= 1)
+            for (int64_t i = 0; i + 2 * s - 1 < P; i += 2 * s) {
+                const int64_t l = i + s - 1, r = i + 2 * s - 1;
+                compose(opa + l * N, opb + l * N, opa + r * N, opb + r * N,
+                        opa + r * N, opb + r * N, N);
+            }
+        for (int64_t n = 0; n < N; ++n) { opa[(P - 1) * N + n] = 1.0; opb[(P - 1) * N + n] = 0.0; }
+        for (int64_t s = P >> 1; s >= 1; s >>= 1)
+            for (int64_t i = 0; i + 2 * s - 1 < P; i += 2 * s) {
+                const int64_t l = i + s - 1, r = i + 2 * s - 1;
+                memcpy(ta, opa + l * N, sizeof(double) * (size_t)N);
+                memcpy(tb, opb + l * N, sizeof(double) * (size_t)N);
+                memcpy(opa + l * N, opa + r * N, sizeof(double) * (size_t)N);
+                memcpy(opb + l * N, opb + r * N, sizeof(double) * (size_t)N);
+                compose(opa + r * N, opb + r * N, ta, tb, opa + r * N, opb + r * N, N);
+            }
+    } else {
+        /* Left fold. */
+        double *ra = ta, *rb = tb;
+        for (int64_t n = 0; n < N; ++n) { ra[n] = 1.0; rb[n] = 0.0; }
+        for (int64_t k = 0; k < nc; ++k) {
+            double *ka = opa + k * N, *kb = opb + k * N;
+            for (int64_t n = 0; n < N; ++n) {
+                const double na = ra[n] * ka[n];
+                const double nb = ka[n] * rb[n] + kb[n];
+                ka[n] = ra[n]; kb[n] = rb[n];   /* exclusive prefix */
+                ra[n] = na; rb[n] = nb;
+            }
+        }
+    }
+
+    /* 3. Broadcast h_start = prefix applied to the initial state and re-run
+     *    every chunk from it, producing y. */
+    double *y_row = a->y + row;
+    init_state(a, b, d, ta);   /* ta now holds the initial state */
+    for (int64_t k = 0; k < nc; ++k) {
+        for (int64_t n = 0; n < N; ++n) h[n] = opa[k * N + n] * ta[n] + opb[k * N + n];
+        const int64_t t1 = (k + 1) * K < L ? (k + 1) * K : L;
+        run_tokens(a, b, d, k * K, t1, h, y_row);
+    }
+    store_state(a, b, d, h);
+    free(opa); free(opb); free(ta); free(tb);
+    return 0;
+}
+
+/* ------------------------------------------------------------ threading */
+
+static void *worker_main(void *p) {
+    worker_args *w = (worker_args *)p;
+    const scan_args *a = w->a;
+    double *h = malloc(sizeof(double) * (size_t)(a->d_state > 0 ? a->d_state : 1));
+    if (!h) { w->status = -1; return NULL; }
+    const int64_t rows = a->batch * a->d_inner;
+    for (int64_t r = w->worker; r < rows; r += w->n_workers) {
+        const int64_t b = r / a->d_inner, d = r % a->d_inner;
+        const int s = w->chunked ? scan_row_chunked(a, b, d, h) : scan_row_sequential(a, b, d, h);
+        if (s) { w->status = s; break; }
+    }
+    free(h);
+    return NULL;
+}
+
+static int run_rows(const scan_args *a, int chunked, int n_threads) {
+    const int64_t rows = a->batch * a->d_inner;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > rows) n_threads = (int)(rows > 0 ? rows : 1);
+    pthread_t *tid = malloc(sizeof(pthread_t) * (size_t)n_threads);
+    worker_args *wa = malloc(sizeof(worker_args) * (size_t)n_threads);
+    if (!tid || !wa) { free(tid); free(wa); return -1; }
+    int started = 0, status = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        wa[i] = (worker_args){a, i, n_threads, chunked, 0};
+        if (i == 0) continue;
+        if (pthread_create(&tid[i], NULL, worker_main, &wa[i]) != 0) { status = -1; break; }
+        started = i;
+    }
+    if (status == 0) {
+        worker_main(&wa[0]);
+    }
+    for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+    for (int i = 0; i < n_threads && status == 0; ++i) status = wa[i].status;
+    free(tid); free(wa);
+    return status;
+}
+
+static int check_dims(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seqlen) {
+    return batch >= 0 && d_inner >= 0 && d_state >= 1 && seqlen >= 0;
+}
+
+/* ------------------------------------------------------------ exports */
+
+int oracle_scan_fwd(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seqlen,
+                    const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *delta_bias,
+                    int softplus_flag, const double *initial_state, double *y,
+                    double *last_state, int n_threads) {
+    if (!check_dims(batch, d_inner, d_state, seqlen)) return -1;
+    if (batch * d_inner == 0) return 0;
+    if (!u || !delta || !A || !B || !C || !y) return -1;
+    scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
+                   initial_state, softplus_flag, y, last_state, 0, 0};
+    return run_rows(&a, 0, n_threads);
+}
+
+int oracle_scan_chunked(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seqlen,
+                        const double *u, const double *delta, const double *A, const double *B,
+                        const double *C, const double *D, const double *z,
+                        const double *delta_bias, int softplus_flag,
+                        const double *initial_state, double *y, double *last_state,
+                        int64_t chunk, int tree_combine, int n_threads) {
+    if (!check_dims(batch, d_inner, d_state, seqlen) || chunk < 1) return -1;
+    if (batch * d_inner == 0) return 0;
+    if (!u || !delta || !A || !B || !C || !y) return -1;
+    scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
+                   initial_state, softplus_flag, y, last_state, chunk, tree_combine ? 1 : 0};
+    return run_rows(&a, 1, n_threads);
+}
+
+int oracle_state_update(int64_t batch, int64_t d_inner, int64_t d_state, double *state,
+                        const double *u, const double *delta, const double *A, const double *B,
+                        const double *C, const double *D, const double *z, double *y) {
+    if (batch < 0 || d_inner < 0 || d_state < 1) return -1;
+    if (batch * d_inner == 0) return 0;
+    if (!state || !u || !delta || !A || !B || !C || !y) return -1;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < d_inner; ++d) {
+            const int64_t i = b * d_inner + d;
+            const double dt = delta[i], x = u[i];
+            double *s = state + i * d_state;
+            double acc = 0.0;
+            for (int64_t n = 0; n < d_state; ++n) {
+                s[n] = exp(dt * A[d * d_state + n]) * s[n] + dt * B[b * d_state + n] * x;
+                acc += C[b * d_state + n] * s[n];
+            }
+            if (D) acc += D[d] * x;
+            if (z) acc *= silu(z[i]);
+            y[i] = acc;
+        }
+    return 0;
+}

@@ -1,0 +1,253 @@
+"""Benchmark of the MI355X selective scan (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the fused prefill scan of the workload (softplus step size, discretisation,
+recurrence, chunk carry, output with skip term and gate, last_state), then
+one single-token state update of every channel continuing from that
+last_state.  Inputs are resident in HBM before timing starts; the step cycles
+through several independent input sets whose total size exceeds the 256 MB
+last-level cache, so every step reads from HBM.
+
+Prints one JSON line.  ``value`` is channel-tokens per second over the timed
+steps (batch * d_inner * (L + 1) per step).  ``roofline`` covers the dominant
+kernel, the pass that writes y, timed with HIP events recorded around it on
+its stream inside the timed region.  ``cpu_baseline`` is the fp64 oracle on
+the host cores (rank 0, one GPU only) on a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ssm_inputs  # noqa: E402
+
+METRIC = "selective-scan channel-tokens/sec"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DEFAULT_CONFIG = "c1_mamba130m_f32"
+CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
+
+
+def algorithmic_bytes(batch, d_inner, N, L, io, gate, last_state=True):
+    """Bytes the scan must move once: u, delta, (z) read and y written per
+    channel-token; B and C read once per (batch, token); A, D, bias per
+    channel; last_state written per channel."""
+    e = 2 if io == "bf16" else 4
+    per_chtok = (3 + (1 if gate else 0)) * e
+    return (batch * d_inner * L * per_chtok + 2 * batch * N * L * e +
+            d_inner * (N + 2) * 4 + (batch * d_inner * N * 4 if last_state else 0))
+
+
+class HipEvents:
+    """Raw hipEvent_t handles via the HIP runtime (the library records them on
+    its own stream around the pass that writes y)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the HIP runtime torch uses)
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def upload(arr, dev):
+    import torch
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the workload
+    (whole channels, every token), scaled to channel-tokens/s."""
+    import oracle
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    threads = oracle.default_threads()
+    # sample: the first rows of batch row 0, all L tokens; grow until the
+    # budget is used
+    inp = ssm_inputs.make_scan_inputs(1, min(d_inner, 4096), N, L, io_dtype=cfg["io_dtype"],
+                                      gate=cfg["gate"], seed=0)
+    f = {k: ssm_inputs.to_f64(inp.get(k)) for k in ("u", "delta", "B", "C", "z")}
+    total_rows = f["u"].shape[1]
+    rows = min(threads, total_rows)
+    done_chtok, spent, passes = 0, 0.0, 0
+    while spent < budget_s:
+        sl = slice(0, rows)
+        t0 = time.perf_counter()
+        oracle.scan_fwd(f["u"][:, sl], f["delta"][:, sl], inp["A"][sl], f["B"], f["C"],
+                        inp["D"][sl], None if f["z"] is None else f["z"][:, sl],
+                        inp["delta_bias"][sl], softplus=True, threads=threads)
+        dt = time.perf_counter() - t0
+        done_chtok += rows * L
+        spent += dt
+        passes += 1
+        if rows < total_rows and dt < budget_s / 8:
+            rows = min(total_rows, rows * 2)
+    return {"value": done_chtok / spent, "unit": "channel-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} passes over up to {rows} whole channels of batch row 0 "
+                      f"({done_chtok // L} channel rows x {L} tokens, N={N}, "
+                      f"{cfg['io_dtype']} inputs), {spent:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(ssm_inputs.CONFIGS))
+    ap.add_argument("--chunk", type=int, default=0, help="chunk size (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, "
+                 f"WORLD_SIZE={world}); this build has no multi-GPU path.")
+
+    import torch
+    import selective_state_space_fwd_amd as ssm
+
+    ssm.load_library()
+    dev = torch.device("cuda:0")
+    cfg = dict(ssm_inputs.CONFIGS[args.config])
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    io, gate = cfg["io_dtype"], cfg["gate"]
+    set_bytes = algorithmic_bytes(batch, d_inner, N, L, io, gate)
+    n_sets = max(2, min(8, -(-3 * CACHE_BYTES // set_bytes)))
+
+    # ---- inputs, resident in HBM
+    sets = []
+    for s in range(n_sets):
+        inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=s)
+        dec = ssm_inputs.make_update_inputs(batch, d_inner, N, io_dtype=io, gate=gate,
+                                            seed=1000 + s)
+        t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z")}
+        t.update({k: upload(inp[k], dev) for k in ("A", "D", "delta_bias")})
+        t["y"] = torch.empty_like(t["u"])
+        t["last"] = torch.empty((batch, d_inner, N), dtype=torch.float32, device=dev)
+        t.update({"dec_" + k: upload(dec[k], dev) for k in ("u", "delta", "B", "C", "z")})
+        t["dec_y"] = torch.empty_like(t["dec_u"])
+        sets.append(t)
+        del inp, dec
+    K = ssm.ssm_scan_chunk_size(batch, d_inner, N, L, 1 if io == "bf16" else 0, args.chunk)
+    ws = torch.empty(max(1, ssm.ssm_scan_workspace_bytes(batch, d_inner, N, L,
+                                                         1 if io == "bf16" else 0, args.chunk)),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    ev = hip.create(2 * (args.steps + args.warmup))
+
+    def step(i, evs):
+        t = sets[i % n_sets]
+        ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                         t["delta_bias"], softplus=True, chunk_size=args.chunk, y=t["y"],
+                         last_state=t["last"], workspace=ws, profile_events=evs)
+        ssm.ssm_state_update(t["last"], t["dec_u"], t["dec_delta"], t["A"], t["dec_B"],
+                             t["dec_C"], t["D"], t["dec_z"], y=t["dec_y"])
+
+    for i in range(args.warmup):
+        step(i, (ev[2 * i], ev[2 * i + 1]))
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    base = 2 * args.warmup
+    start.record()
+    for i in range(args.steps):
+        step(i, (ev[base + 2 * i], ev[base + 2 * i + 1]))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kern_ms = [hip.elapsed_ms(ev[base + 2 * i], ev[base + 2 * i + 1]) for i in range(args.steps)]
+    hip.destroy(ev)
+
+    ms_per_step = total_ms / args.steps
+    chtok = batch * d_inner * (L + 1)
+    value = chtok / (ms_per_step * 1e-3)
+    kavg = float(np.mean(kern_ms))
+    achieved = set_bytes / (kavg * 1e-3) / 1e9
+
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get(args.config)
+        if tj and tj.get("bytes_per_launch"):
+            traffic = tj["bytes_per_launch"]
+    except (OSError, ValueError):
+        traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: selective scan batch={batch} d_inner={d_inner} "
+                        f"N={N} L={L} {io} I/O{' + silu gate' if gate else ''}, then one "
+                        f"decode token per channel",
+            "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L, "io_dtype": io,
+            "gate": gate, "chunk": K, "input_sets": n_sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "chunk_kernel (pass writing y)",
+            "kernel_ms": kavg,
+            "algorithmic_bytes": set_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * ssm.h -- C ABI of libssm, the MI355X (gfx950) selective state-space scan.
+ *
+ * Two operations, both from the Mamba selective-scan pages:
+ *
+ *   ssm_scan_fwd      the fused prefill scan.  Per token it forms the step
+ *                     size delta_t = softplus(delta + delta_bias) (SSM
+ *                     engineering essay, discosf.com, §1.3; ufo.work article
+ *                     "Mamba hardware-aware operator fusion and selective-scan
+ *                     parallelisation", §2.1), discretises dA = exp(delta_t A),
+ *                     dBu = delta_t B_t u_t (ufo.work article §1.1; "From
+ *                     FlashAttention to Mamba", kj168168, §三.1), runs the
+ *                     diagonal recurrence h_t = dA h_{t-1} + dBu (ufo.work
+ *                     article §1.1) and emits y_t = C_t . h_t + D u_t (essay
+ *                     §1.1, skip term D), optionally multiplied by silu(z_t).
+ *                     Long sequences are cut into chunks joined by transfer
+ *                     operators (ufo.work article §3.1).
+ *
+ *   ssm_state_update  the single-token update of a persistent state
+ *                     h_new = exp(delta A) h_old + delta B u (ufo.work article
+ *                     §4.1), with the same output rule.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc'd or from an
+ *     allocator built on it); the descriptor itself is host memory.  The
+ *     caller owns every buffer; the library never allocates device memory
+ *     and keeps no pointer after the call returns.
+ *   - Layouts are dense, row-major, last index fastest:
+ *       u, delta, z, y       (batch, d_inner, seqlen)     [scan]
+ *       B, C                 (batch, d_state, seqlen)     [scan]
+ *       u, delta, z, y       (batch, d_inner)             [update]
+ *       B, C                 (batch, d_state)             [update]
+ *       A                    (d_inner, d_state)  float32
+ *       D, delta_bias        (d_inner)           float32
+ *       state, last_state    (batch, d_inner, d_state) float32
+ *     B and C are shared by all channels of a batch row.
+ *   - io_dtype selects the element type of u, delta, z, B, C and y
+ *     (float32 or bfloat16).  A, D, delta_bias and the states are always
+ *     float32; all arithmetic is float32.  bf16 results are rounded to
+ *     nearest, ties to even.
+ *   - All work is enqueued on `stream` (NULL = the default stream).  Calls
+ *     are asynchronous: they return once the kernels are queued, never
+ *     synchronise, and a device fault surfaces at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated before anything is launched; on an error
+ *     nothing is launched and no buffer is touched.  Input values are not
+ *     inspected: NaN and Inf propagate.
+ *   - No buffer may overlap another, except where stated.
+ *   - Thread safety: calls are reentrant; concurrent calls must not share a
+ *     workspace or an output.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t, so a hipStream_t can be passed unchanged. */
+typedef struct ihipStream_t *ssm_stream_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL_ARG = 1,     /* a required pointer (or the descriptor) is NULL        */
+    SSM_ERR_BAD_SHAPE = 2,    /* a negative dimension, or a bad chunk_size            */
+    SSM_ERR_UNSUPPORTED = 3,  /* d_state outside 1..256, or an unknown io_dtype       */
+    SSM_ERR_MISALIGNED = 4,   /* a pointer not aligned to its element size            */
+    SSM_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than ssm_scan_workspace_bytes */
+    SSM_ERR_HIP = 6           /* a HIP launch error (hipGetLastError after launching) */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+#define SSM_MAX_D_STATE 256
+
+typedef struct ssm_desc {
+    int64_t batch;            /* >= 0 */
+    int64_t d_inner;          /* >= 0, channels */
+    int64_t d_state;          /* N, 1..256 */
+    int64_t seqlen;           /* L >= 0; ignored by ssm_state_update */
+    int32_t io_dtype;         /* ssm_dtype */
+    int32_t chunk_size;       /* scan only: tokens per chunk; 0 = chosen by the
+                                 library, else a positive multiple of 16.  A chunk
+                                 covers tokens [kK, min((k+1)K, L)). */
+    void *workspace;          /* scan only: device scratch, >= workspace_bytes */
+    size_t workspace_bytes;   /* scan only */
+    void *profile_begin;      /* scan only, optional hipEvent_t: when both are set, */
+    void *profile_end;        /* recorded on `stream` right before and right after
+                                 the pass that writes y (measurement hook) */
+} ssm_desc;
+
+/* Bytes of device workspace that ssm_scan_fwd needs for this descriptor
+ * (its shapes, io_dtype and chunk_size; the workspace fields are ignored).
+ * Returns 0 for an invalid descriptor.  Host-only, never touches the GPU. */
+size_t ssm_scan_workspace_bytes(const ssm_desc *desc);
+
+/* Chunk length that ssm_scan_fwd uses for this descriptor (chunk_size, or
+ * the library's choice when it is 0); seqlen means a single chunk.  Returns
+ * -1 for an invalid descriptor.  Host-only. */
+int64_t ssm_scan_chunk_size(const ssm_desc *desc);
+
+/* Fused selective-scan forward pass.
+ *   u, delta       (batch, d_inner, L) io_dtype; delta is the raw step size
+ *   A              (d_inner, N) float32
+ *   B, C           (batch, N, L) io_dtype
+ *   D              (d_inner) float32 or NULL (no skip term)
+ *   z              (batch, d_inner, L) io_dtype or NULL (no gate)
+ *   delta_bias     (d_inner) float32 or NULL (zero); added before softplus
+ *   softplus_flag  nonzero: delta_t = softplus(delta + bias); zero: delta + bias
+ *   y              (batch, d_inner, L) io_dtype, written
+ *   last_state     (batch, d_inner, N) float32, written with h_{L-1}
+ *                  (zeros when L == 0), or NULL
+ * The state starts at zero.  Needs desc->workspace of at least
+ * ssm_scan_workspace_bytes(desc) bytes (may be NULL when that is 0); its
+ * contents on entry do not matter and are garbage afterwards. */
+ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, void *y, float *last_state,
+                        ssm_stream_t stream);
+
+/* Single-token update of a persistent state, in place.
+ *   state  (batch, d_inner, N) float32, read and overwritten with
+ *          exp(delta A) state + delta B u
+ *   u, delta (batch, d_inner) io_dtype; delta is the FINAL step size
+ *          (no bias, no softplus)
+ *   A (d_inner, N) float32;  B, C (batch, N) io_dtype
+ *   D (d_inner) float32 or NULL;  z (batch, d_inner) io_dtype or NULL
+ *   y (batch, d_inner) io_dtype, written: (C . state_new + D u) silu(z)
+ * desc->seqlen, chunk_size and the workspace fields are ignored. */
+ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, const void *delta,
+                            const float *A, const void *B, const void *C, const float *D,
+                            const void *z, void *y, ssm_stream_t stream);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char *ssm_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

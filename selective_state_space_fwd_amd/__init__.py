@@ -1,0 +1,220 @@
+"""MI355X (gfx950) selective state-space scan: Python binding of libssm.
+
+The library (``libssm.so``, built from ``csrc/`` by ``build.py``) exports the
+C ABI declared in ``include/ssm.h``.  This module only marshals arguments:
+it checks tensor shapes and dtypes, allocates the outputs and the workspace
+with PyTorch (device memory and streams are the only things torch provides),
+and passes raw pointers plus the current HIP stream to the library.  Every
+step of the computation runs in the HIP kernels; there is no fallback.
+
+    y, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias,
+                                 softplus=True, return_last_state=True)
+    y = ssm_state_update(state, u, delta, A, B, C, D, z)   # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "ssm_scan_workspace_bytes",
+           "ssm_scan_chunk_size", "ssm_status_string", "SsmError", "load_library",
+           "LIB_PATH"]
+
+LIB_PATH = Path(__file__).resolve().parent / "libssm.so"
+
+SSM_F32, SSM_BF16 = 0, 1
+
+
+class SsmError(RuntimeError):
+    """A libssm call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class SsmDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("d_inner", ctypes.c_int64),
+        ("d_state", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("profile_begin", ctypes.c_void_p),
+        ("profile_end", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
+    """Load libssm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(
+            f"{p} is missing: build the HIP library first "
+            "(python -m selective_state_space_fwd_amd.build)")
+    lib = ctypes.CDLL(str(p))
+    vp, dp = ctypes.c_void_p, ctypes.POINTER(SsmDesc)
+    lib.ssm_scan_workspace_bytes.argtypes = [dp]
+    lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_chunk_size.argtypes = [dp]
+    lib.ssm_scan_chunk_size.restype = ctypes.c_int64
+    lib.ssm_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_status_string.argtypes = [ctypes.c_int]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_version.argtypes = []
+    lib.ssm_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def ssm_status_string(status: int) -> str:
+    return load_library().ssm_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise SsmError(status, ssm_status_string(status))
+
+
+# ---------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return SSM_F32
+    if dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _expect(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> SsmDesc:
+    return SsmDesc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size, None, 0, None, None)
+
+
+def ssm_scan_workspace_bytes(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> int:
+    d = make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size)
+    return int(load_library().ssm_scan_workspace_bytes(ctypes.byref(d)))
+
+
+def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> int:
+    d = make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size)
+    return int(load_library().ssm_scan_chunk_size(ctypes.byref(d)))
+
+
+# ---------------------------------------------------------------- entry points
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+                 return_last_state=True, chunk_size=0, y=None, last_state=None,
+                 workspace=None, profile_events=None):
+    """Fused selective-scan forward pass on the GPU.
+
+    u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
+    bfloat16.  A: (d_inner, N), D and delta_bias: (d_inner,), float32.
+    Returns (y, last_state); last_state is None unless requested.
+    profile_events: optional pair of raw hipEvent_t handles recorded around
+    the pass that writes y.
+    """
+    torch = _torch()
+    lib = load_library()
+    batch, d_inner, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev, io = u.device, u.dtype
+    code = _io_code(io)
+    _expect(u, "u", (batch, d_inner, L), io, dev)
+    _expect(delta, "delta", (batch, d_inner, L), io, dev)
+    _expect(A, "A", (d_inner, N), torch.float32, dev)
+    _expect(B, "B", (batch, N, L), io, dev)
+    _expect(C, "C", (batch, N, L), io, dev)
+    _expect(D, "D", (d_inner,), torch.float32, dev)
+    _expect(z, "z", (batch, d_inner, L), io, dev)
+    _expect(delta_bias, "delta_bias", (d_inner,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, d_inner, L), dtype=io, device=dev)
+    _expect(y, "y", (batch, d_inner, L), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, d_inner, N), dtype=torch.float32, device=dev)
+    _expect(last_state, "last_state", (batch, d_inner, N), torch.float32, dev)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    if profile_events is not None:
+        desc.profile_begin, desc.profile_end = profile_events
+    st = lib.ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
+                          _ptr(last_state), _stream(dev))
+    _check(st)
+    return y, last_state
+
+
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None):
+    """One single-token update of ``state`` (batch, d_inner, N) float32, in place.
+
+    u, delta, z: (batch, d_inner); B, C: (batch, N); float32 or bfloat16.
+    delta is the final step size.  Returns y (batch, d_inner).
+    """
+    torch = _torch()
+    lib = load_library()
+    batch, d_inner, N = state.shape
+    dev, io = u.device, u.dtype
+    code = _io_code(io)
+    _expect(state, "state", (batch, d_inner, N), torch.float32, dev)
+    _expect(u, "u", (batch, d_inner), io, dev)
+    _expect(delta, "delta", (batch, d_inner), io, dev)
+    _expect(A, "A", (d_inner, N), torch.float32, dev)
+    _expect(B, "B", (batch, N), io, dev)
+    _expect(C, "C", (batch, N), io, dev)
+    _expect(D, "D", (d_inner,), torch.float32, dev)
+    _expect(z, "z", (batch, d_inner), io, dev)
+    if y is None:
+        y = torch.empty((batch, d_inner), dtype=io, device=dev)
+    _expect(y, "y", (batch, d_inner), io, dev)
+    desc = make_desc(batch, d_inner, N, 0, code)
+    st = lib.ssm_state_update(ctypes.byref(desc), _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
+                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(dev))
+    _check(st)
+    return y

@@ -1,0 +1,205 @@
+// ssm_api.hip -- the C ABI of libssm: validation, planning, workspace layout
+// and launch.  Declarations and the contract of every entry point are in
+// include/ssm.h.
+#include "ssm.h"
+
+#include <hip/hip_runtime.h>
+#include <limits.h>
+
+#include "ssm_launch.h"
+
+namespace {
+
+using ssm::ScanArgs;
+
+constexpr int64_t kMaxGridY = 65535;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Dense-shape sanity: every product we index with must fit in int64 and the
+// grid sizes in 32 bits.
+bool dims_ok(int64_t a, int64_t b, int64_t c) {
+    if (a < 0 || b < 0 || c < 0) return false;
+    const double p = static_cast<double>(a) * static_cast<double>(b) * static_cast<double>(c);
+    return p < 9.0e18;
+}
+
+struct Plan {
+    int G = 1;            // state groups of 16 per channel, padded to a power of two
+    int64_t K = 0;        // chunk length
+    int64_t J = 1;        // chunks
+    int64_t n_cblk = 0;   // 64-channel blocks per batch row
+    size_t off_bc = 0, off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
+};
+
+ssm_status check_desc(const ssm_desc *d) {
+    if (!d) return SSM_ERR_NULL_ARG;
+    if (d->batch < 0 || d->d_inner < 0 || d->seqlen < 0) return SSM_ERR_BAD_SHAPE;
+    if (d->d_state < 1 || d->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
+    if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if (!dims_ok(d->batch, d->d_inner, d->seqlen > 0 ? d->seqlen : 1)) return SSM_ERR_BAD_SHAPE;
+    if (!dims_ok(d->batch, d->d_inner, d->d_state)) return SSM_ERR_BAD_SHAPE;
+    return SSM_OK;
+}
+
+// Waves wanted in flight: two per SIMD on 256 CUs x 4 SIMDs.
+constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kEnoughWaves = 1024;
+constexpr int64_t kMinAutoChunk = 64;
+
+ssm_status make_plan(const ssm_desc *d, Plan *p) {
+    const ssm_status st = check_desc(d);
+    if (st != SSM_OK) return st;
+    if (d->chunk_size < 0 || (d->chunk_size > 0 && d->chunk_size % 16 != 0))
+        return SSM_ERR_BAD_SHAPE;
+    const int64_t L = d->seqlen;
+    int groups = static_cast<int>((d->d_state + 15) / 16);
+    int G = 1;
+    while (G < groups) G <<= 1;
+    p->G = G;
+    p->n_cblk = (d->d_inner + 63) / 64;
+    if (L == 0 || d->batch * d->d_inner == 0) {
+        p->K = L; p->J = L > 0 ? 1 : 0; p->bytes = 0;
+        return SSM_OK;
+    }
+    int64_t K;
+    if (d->chunk_size > 0) {
+        K = d->chunk_size;
+    } else {
+        const int64_t waves = d->batch * p->n_cblk * G;
+        K = L;
+        if (waves < kEnoughWaves) {
+            const int64_t J = (kTargetWaves + waves - 1) / waves;
+            int64_t k = (L + J - 1) / J;
+            k = (k + 15) / 16 * 16;
+            if (k < kMinAutoChunk) k = kMinAutoChunk;
+            if (k < L) K = k;
+        }
+    }
+    if (K >= L) K = L;
+    p->K = K;
+    p->J = (L + K - 1) / K;
+    if (p->J > kMaxGridY) return SSM_ERR_UNSUPPORTED;
+    if (p->n_cblk * d->batch > static_cast<int64_t>(UINT_MAX)) return SSM_ERR_UNSUPPORTED;
+    // workspace layout
+    size_t off = 0;
+    p->off_bc = off;
+    off += align_up(static_cast<size_t>(d->batch) * L * G * 32 * sizeof(float));
+    if (p->J > 1) {
+        const size_t cj = static_cast<size_t>(d->batch) * d->d_inner * p->J;
+        p->off_hend = off;
+        off += align_up(cj * G * 16 * sizeof(float));
+        p->off_hstart = off;
+        off += align_up(cj * G * 16 * sizeof(float));
+        p->off_dtsum = off;
+        off += align_up(cj * sizeof(float));
+    }
+    p->bytes = off;
+    return SSM_OK;
+}
+
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
+    Plan p;
+    return make_plan(desc, &p) == SSM_OK ? p.bytes : 0;
+}
+
+int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
+    Plan p;
+    return make_plan(desc, &p) == SSM_OK ? p.K : -1;
+}
+
+ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, void *y, float *last_state,
+                        ssm_stream_t stream) {
+    Plan p;
+    ssm_status st = make_plan(desc, &p);
+    if (st != SSM_OK) return st;
+    const hipStream_t s = stream;
+    const int64_t rows = desc->batch * desc->d_inner;
+    if (rows == 0) return SSM_OK;
+    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
+    if (!A) return SSM_ERR_NULL_ARG;
+    if (!aligned(A, 4) || !aligned(D, 4) || !aligned(delta_bias, 4) || !aligned(last_state, 4))
+        return SSM_ERR_MISALIGNED;
+    if (desc->seqlen == 0) {
+        // h_{-1} = 0 is the final state of an empty sequence.
+        if (last_state &&
+            ssm::launch_fill_zero(last_state, static_cast<size_t>(rows) * desc->d_state, s) !=
+                hipSuccess)
+            return SSM_ERR_HIP;
+        return SSM_OK;
+    }
+    if (!u || !delta || !B || !C || !y) return SSM_ERR_NULL_ARG;
+    if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+        !aligned(y, esz) || !aligned(z, esz))
+        return SSM_ERR_MISALIGNED;
+    if (p.bytes > 0) {
+        if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
+        if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
+    }
+    char *ws = static_cast<char *>(desc->workspace);
+    ScanArgs a{};
+    a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state; a.L = desc->seqlen;
+    a.G = p.G; a.K = p.K; a.J = p.J; a.n_cblk = p.n_cblk;
+    a.bf16 = desc->io_dtype == SSM_BF16;
+    a.softplus = softplus_flag != 0;
+    a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
+    a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
+    a.bc = reinterpret_cast<float *>(ws + p.off_bc);
+    if (p.J > 1) {
+        a.hend = reinterpret_cast<float *>(ws + p.off_hend);
+        a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
+        a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
+    }
+    a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
+    a.ev_end = static_cast<hipEvent_t>(desc->profile_end);
+    return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, const void *delta,
+                            const float *A, const void *B, const void *C, const float *D,
+                            const void *z, void *y, ssm_stream_t stream) {
+    if (!desc) return SSM_ERR_NULL_ARG;
+    if (desc->batch < 0 || desc->d_inner < 0) return SSM_ERR_BAD_SHAPE;
+    if (desc->d_state < 1 || desc->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
+    if (desc->io_dtype != SSM_F32 && desc->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if (!dims_ok(desc->batch, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
+    if (desc->batch * desc->d_inner == 0) return SSM_OK;
+    if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
+    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
+    if (!aligned(state, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(u, esz) ||
+        !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) || !aligned(z, esz) ||
+        !aligned(y, esz))
+        return SSM_ERR_MISALIGNED;
+    ssm::UpdateArgs a{};
+    a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state;
+    a.bf16 = desc->io_dtype == SSM_BF16;
+    a.state = state; a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
+    a.A = A; a.Dskip = D;
+    return ssm::launch_update(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+const char *ssm_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_NULL_ARG: return "SSM_ERR_NULL_ARG: a required pointer is NULL";
+        case SSM_ERR_BAD_SHAPE: return "SSM_ERR_BAD_SHAPE: invalid dimension or chunk_size";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: d_state or io_dtype not supported";
+        case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED: pointer not aligned to its element";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP: kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ssm_version(void) { return 100; }
+
+}  // extern "C"

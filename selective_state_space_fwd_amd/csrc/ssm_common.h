@@ -1,0 +1,64 @@
+// ssm_common.h -- device helpers shared by the libssm kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;       // CDNA wavefront
+constexpr int kGroup = 16;      // states held per lane (one state group)
+
+// ---------------------------------------------------------------- I/O types
+// float32 or bfloat16 (raw bits); arithmetic is always float32.
+struct F32 {
+    using T = float;
+    static __device__ __forceinline__ float load(const T *p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(T *p, size_t i, float v) { p[i] = v; }
+};
+struct BF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T *p, size_t i) {
+        return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+    }
+    // Round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32).
+    static __device__ __forceinline__ void store(T *p, size_t i, float v) {
+        __hip_bfloat16 b = __float2bfloat16(v);
+        p[i] = *reinterpret_cast<uint16_t *>(&b);
+    }
+};
+
+// ---------------------------------------------------------------- constant view
+// Read-only view of global memory in the constant address space: loads whose
+// address is uniform across the wavefront become scalar (s_load) loads.  Only
+// for buffers that no kernel writes while the reading kernel runs.
+using cfloat = __attribute__((address_space(4))) const float;
+__device__ __forceinline__ cfloat *as_constant(const float *p) {
+    return (cfloat *)(p);
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
+// log1p(e) is taken as log(1 + e) plus the exact rounding error of 1 + e,
+// c = (1 - fl(1 + e)) + e: log1p(e) = log(fl(1+e)) + log(1 + c / fl(1+e)),
+// and |c| <= 2^-24 makes the last term equal to c within 2^-24 relative.
+__device__ __forceinline__ float softplus_f32(float x) {
+    const float e = exp2_hw(-fabsf(x) * kLog2e);
+    const float s = 1.0f + e;
+    const float c = (1.0f - s) + e;
+    return fmaxf(x, 0.0f) + __builtin_fmaf(log2_hw(s), kLn2, c);
+}
+
+// silu(z) = z / (1 + e^{-z}); e^{-z} = inf for very negative z gives -0.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+}
+
+}  // namespace ssm

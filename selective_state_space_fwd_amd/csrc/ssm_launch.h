@@ -1,0 +1,42 @@
+// ssm_launch.h -- host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Everything a prefill scan launch needs; built and validated by ssm_api.
+struct ScanArgs {
+    int64_t Bsz, D, N, L;       // batch, d_inner, d_state, seqlen
+    int G;                      // state groups of 16 per channel (power of two)
+    int64_t K, J, n_cblk;       // chunk length, chunk count, 64-channel blocks
+    int bf16;                   // io dtype
+    int softplus;
+    const void *u, *delta, *z, *B, *C;
+    void *y;
+    const float *A, *Dskip, *delta_bias;
+    float *last_state;
+    // workspace views
+    float *bc;                  // (batch, L, G, 32) packed B/C rows
+    float *hend;                // (batch, d_inner, J, G*16) chunk end states from zero
+    float *dtsum;               // (batch, d_inner, J) sum of step sizes per chunk
+    float *hstart;              // (batch, d_inner, J, G*16) chunk start states
+    hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
+};
+
+struct UpdateArgs {
+    int64_t Bsz, D, N;
+    int bf16;
+    float *state;
+    const void *u, *delta, *z, *B, *C;
+    void *y;
+    const float *A, *Dskip;
+};
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+hipError_t launch_update(const UpdateArgs &a, hipStream_t s);
+hipError_t launch_fill_zero(float *p, size_t n, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,135 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/ssm.h declares, and validates arguments on the host before any launch.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_fwd_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssm.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("ssm_scan_fwd", "ssm_state_update", "ssm_scan_workspace_bytes",
+              "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert ssm.ssm_status_string(0) == "SSM_OK"
+    for s in range(1, 7):
+        assert ssm.ssm_status_string(s).startswith("SSM_ERR_")
+    assert ssm.ssm_status_string(99) == "unknown status"
+    assert lib.ssm_version() >= 100
+
+
+def desc(**kw):
+    base = dict(batch=2, d_inner=64, d_state=16, seqlen=2048, io_dtype=0, chunk_size=0)
+    base.update(kw)
+    return ssm.make_desc(**base)
+
+
+def test_workspace_and_chunk_plan(lib):
+    d = desc()
+    K = lib.ssm_scan_chunk_size(ctypes.byref(d))
+    assert 16 <= K <= 2048 and (K % 16 == 0 or K == 2048)
+    J = -(-2048 // K)
+    need = lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+    packed = 2 * 2048 * 1 * 32 * 4
+    assert need >= packed
+    if J > 1:
+        assert need >= packed + 2 * (2 * 64 * J * 16 * 4) + 2 * 64 * J * 4
+    for k in (16, 256, 1024):
+        d = desc(chunk_size=k)
+        assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == k
+    d = desc(chunk_size=4096)
+    assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048     # one chunk
+    d = desc(batch=8, d_inner=5120 * 4)                         # enough channels
+    assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048
+    # state groups are padded to a power of two of 16-state groups
+    for N, G in ((1, 1), (16, 1), (17, 2), (33, 4), (100, 8), (256, 16)):
+        d = desc(d_state=N, chunk_size=2048)
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 2 * 2048 * G * 32 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(d_inner=-1), 2),
+    (dict(d_state=0), 3), (dict(d_state=257), 3), (dict(io_dtype=7), 3),
+    (dict(chunk_size=10), 2), (dict(chunk_size=-16), 2),
+])
+def test_invalid_descriptors(lib, kw, status):
+    d = desc(**kw)
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == -1
+    # validation fails before any pointer is looked at or anything is launched
+    st = lib.ssm_scan_fwd(ctypes.byref(d), 16, 16, 16, 16, 16, None, None, None, 1, 16, None, None)
+    assert st == status
+
+
+def test_null_and_misaligned_arguments(lib):
+    d = desc(chunk_size=2048)
+    d.workspace, d.workspace_bytes = 4096, 1 << 30
+    ok = 4096
+    args = [ok, ok, ok, ok, ok, None, None, None, 1, ok, None, None]
+    assert lib.ssm_scan_fwd(None, *args) == 1
+    for i in (0, 1, 2, 3, 4, 9):          # u, delta, A, B, C, y
+        bad = list(args)
+        bad[i] = None
+        assert lib.ssm_scan_fwd(ctypes.byref(d), *bad) == 1
+    bad = list(args)
+    bad[0] = 4098                           # u misaligned for float32
+    assert lib.ssm_scan_fwd(ctypes.byref(d), *bad) == 4
+    d.workspace, d.workspace_bytes = None, 0
+    assert lib.ssm_scan_fwd(ctypes.byref(d), *args) == 5
+    d.workspace, d.workspace_bytes = 4096, 16
+    assert lib.ssm_scan_fwd(ctypes.byref(d), *args) == 5
+
+
+def test_update_validation(lib):
+    d = ssm.make_desc(4, 8, 16, 0, 0)
+    ok = 4096
+    assert lib.ssm_state_update(None, ok, ok, ok, ok, ok, ok, None, None, ok, None) == 1
+    assert lib.ssm_state_update(ctypes.byref(d), None, ok, ok, ok, ok, ok, None, None, ok,
+                                None) == 1
+    d2 = ssm.make_desc(4, 8, 300, 0, 0)
+    assert lib.ssm_state_update(ctypes.byref(d2), ok, ok, ok, ok, ok, ok, None, None, ok,
+                                None) == 3
+    d3 = ssm.make_desc(4, 8, 16, 0, 1)
+    assert lib.ssm_state_update(ctypes.byref(d3), ok, 4097, ok, ok, ok, ok, None, None, ok,
+                                None) == 4
+
+
+def test_empty_problems_return_ok_without_launch(lib):
+    d = desc(batch=0)
+    assert lib.ssm_scan_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                            1, None, None, None) == 0
+    d = ssm.make_desc(0, 8, 16, 0, 0)
+    assert lib.ssm_state_update(ctypes.byref(d), None, None, None, None, None, None, None,
+                                None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="build the HIP library"):
+        ssm.load_library(tmp_path / "libssm.so")

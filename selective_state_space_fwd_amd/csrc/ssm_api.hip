@@ -29,7 +29,8 @@ struct Plan {
     int G = 1;            // state groups of 16 per channel, padded to a power of two
     int64_t K = 0;        // chunk length
     int64_t J = 1;        // chunks
-    int64_t n_cblk = 0;   // 64-channel blocks per batch row
+    int64_t n_cblk = 0;   // channel blocks per batch row (16 channels when quad, else 64)
+    int quad = 0;         // d_state <= 16: quad-row kernel
     size_t off_bc = 0, off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
 };
 
@@ -58,7 +59,9 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     int G = 1;
     while (G < groups) G <<= 1;
     p->G = G;
-    p->n_cblk = (d->d_inner + 63) / 64;
+    p->quad = d->d_state <= 16;
+    const int64_t cb = p->quad ? 16 : 64;
+    p->n_cblk = (d->d_inner + cb - 1) / cb;
     if (L == 0 || d->batch * d->d_inner == 0) {
         p->K = L; p->J = L > 0 ? 1 : 0; p->bytes = 0;
         return SSM_OK;
@@ -67,7 +70,7 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     if (d->chunk_size > 0) {
         K = d->chunk_size;
     } else {
-        const int64_t waves = d->batch * p->n_cblk * G;
+        const int64_t waves = d->batch * p->n_cblk * (p->quad ? 1 : G);
         K = L;
         if (waves < kEnoughWaves) {
             const int64_t J = (kTargetWaves + waves - 1) / waves;
@@ -148,7 +151,7 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
     char *ws = static_cast<char *>(desc->workspace);
     ScanArgs a{};
     a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state; a.L = desc->seqlen;
-    a.G = p.G; a.K = p.K; a.J = p.J; a.n_cblk = p.n_cblk;
+    a.G = p.G; a.K = p.K; a.J = p.J; a.n_cblk = p.n_cblk; a.quad = p.quad;
     a.bf16 = desc->io_dtype == SSM_BF16;
     a.softplus = softplus_flag != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;

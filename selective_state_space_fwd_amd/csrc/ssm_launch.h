@@ -11,7 +11,8 @@ namespace ssm {
 struct ScanArgs {
     int64_t Bsz, D, N, L;       // batch, d_inner, d_state, seqlen
     int G;                      // state groups of 16 per channel (power of two)
-    int64_t K, J, n_cblk;       // chunk length, chunk count, 64-channel blocks
+    int64_t K, J, n_cblk;       // chunk length, chunk count, channel blocks per batch row
+    int quad;                   // 1: d_state <= 16 path, 16-channel blocks (quad_kernel)
     int bf16;                   // io dtype
     int softplus;
     const void *u, *delta, *z, *B, *C;

@@ -34,14 +34,18 @@
 // and feeds them to the VALU as SGPR operands: no LDS traffic for B/C.
 // u, delta and z (L-contiguous rows) are staged through LDS with coalesced
 // loads and read back transposed, one row per lane.
+#include <type_traits>
+
 #include "ssm_common.h"
 #include "ssm_launch.h"
 
 namespace ssm {
 
 // ============================================================ B/C repack
-// bc[((b*L + t)*G + g)*32 + k]: k < 16 -> B[b, 16g+k, t], else C[b, 16g+k-16, t];
-// states n >= N are zero.  Grid ceil(L/64) * G * batch (1-D), 256 threads.
+// bc[((b*G + g)*L + t)*32 + k]: k < 16 -> B[b, 16g+k, t], else C[b, 16g+k-16, t];
+// states n >= N are zero.  A group's rows are contiguous along t, so a tile of
+// T tokens is one contiguous 128*T-byte piece.  Grid ceil(L/64) * G * batch
+// (1-D), 256 threads.
 template <class IO>
 __global__ __launch_bounds__(256) void bc_pack_kernel(const typename IO::T *__restrict__ Bm,
                                                       const typename IO::T *__restrict__ Cm,
@@ -68,27 +72,109 @@ __global__ __launch_bounds__(256) void bc_pack_kernel(const typename IO::T *__re
     for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
         const int tt = idx >> 5, k = idx & 31;
         const int64_t t = t0 + tt;
-        if (t < L) bc[((static_cast<size_t>(b) * L + t) * G + g) * 32 + k] = tile[k][tt];
+        if (t < L) bc[((static_cast<size_t>(b) * G + g) * L + t) * 32 + k] = tile[k][tt];
     }
 }
 
 // ============================================================ chunk kernel
-// Grid (n_cblk * batch, J); block 64*G threads (wavefront g = state group g).
+// Grid (n_cblk * batch, chunks); block 64*G threads (wavefront g = state group g).
 // Tokens of chunk j: [j*K, min((j+1)*K, L)).
-template <class IO, int G, int T, bool FULL>
+//
+// The chunk is walked in tiles of T tokens x 64 channels.  Everything the
+// recurrence reads during a tile sits in LDS, so the token loop waits on LDS
+// only (LDS results return in order; a scalar load in flight would force
+// every LDS wait to drain it).  Per tile:
+//  (a) the tile's raw u, delta, z and its packed B/C rows, loaded one tile
+//      ahead with 16-byte vector loads (consecutive lanes on consecutive
+//      16-byte pieces of a row), are turned into dt = softplus(delta + bias),
+//      w = dt u, du = D u, g = silu(z) and written to LDS.  Channel rows are
+//      padded to T + 4 floats: 16-byte aligned, and the 8 rows read by one
+//      ds_read_b128 pass land on distinct banks;
+//  (b) each lane walks its channel's row, 4 tokens per ds_read_b128 of
+//      (dt, w).  B_t is read as one VGPR replicated in every 16-lane row
+//      (lane l holds B_t[l % 16]) and enters w B_t[n] through the DPP operand
+//      row_newbcast:n, folded into v_mul_f32_dpp; C_t comes from four
+//      uniform-address ds_read_b128 broadcasts, read a token ahead.  The
+//      finished y (or the group's partial C.h) goes back to LDS;
+//  (c) y is stored with coalesced 16-byte stores.
+// Tokens past the chunk end carry dt = 0 and w = 0, so they leave h alone.
+
+template <class IO>
+struct Seg;   // one 16-byte piece of a row: VW consecutive tokens
+
+template <>
+struct Seg<F32> {
+    static constexpr int VW = 4;
+    using V = float4;
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[VW]) {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ V pack(const float (&o)[VW]) {
+        return make_float4(o[0], o[1], o[2], o[3]);
+    }
+};
+
+template <>
+struct Seg<BF16> {
+    static constexpr int VW = 8;
+    using V = uint4;
+    static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+    static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[VW]) {
+        o[0] = lo(v.x); o[1] = hi(v.x); o[2] = lo(v.y); o[3] = hi(v.y);
+        o[4] = lo(v.z); o[5] = hi(v.z); o[6] = lo(v.w); o[7] = hi(v.w);
+    }
+    static __device__ __forceinline__ uint32_t pk(float a, float b) {
+        const __hip_bfloat162 h = __float22bfloat162_rn(make_float2(a, b));
+        return *reinterpret_cast<const uint32_t *>(&h);
+    }
+    static __device__ __forceinline__ V pack(const float (&o)[VW]) {
+        return make_uint4(pk(o[0], o[1]), pk(o[2], o[3]), pk(o[4], o[5]), pk(o[6], o[7]));
+    }
+};
+
+// Lane n of each 16-lane row, broadcast to the whole row (gfx90a+ DPP).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, true));
+}
+
+// One token of the recurrence for a lane's 16 states.
+//   h[n] = exp2(dt A2[n]) h[n] + w B[n];  acc[n % 4] += C[n] h[n]
+template <bool FULL, int N>
+__device__ __forceinline__ void token_step(float (&h)[kGroup], const float (&A2)[kGroup],
+                                           float dt, float w, float Bv,
+                                           const float (&Cv)[kGroup], float (&acc)[4]) {
+    if constexpr (N < kGroup) {
+        const float dA = exp2_hw(dt * A2[N]);
+        h[N] = __builtin_fmaf(dA, h[N], row_bcast<N>(Bv) * w);
+        if (FULL) acc[N & 3] = __builtin_fmaf(Cv[N], h[N], acc[N & 3]);
+        token_step<FULL, N + 1>(h, A2, dt, w, Bv, Cv, acc);
+    }
+}
+
+template <class IO, int G, int T, bool FULL, bool VEC>
 __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
     using IT = typename IO::T;
+    using S = Seg<IO>;
+    constexpr int VW = S::VW;
+    static_assert(T % VW == 0 && T % 4 == 0, "tile");
+    constexpr int TP = T + 4;                       // padded LDS row
     constexpr int NT = 64 * G;
-    constexpr int TP = T + 1;                       // padded row: conflict-free column reads
-    __shared__ float s_dt[kWave * TP];              // step size, then (G == 1) y
-    __shared__ float s_w[kWave * TP];               // step size * u
-    __shared__ float s_y[G > 1 ? G * kWave * TP : 1];
+    constexpr int SPR = T / VW;                     // segments per row
+    constexpr int NSEG = kWave * SPR;               // segments per tile and tensor
+    constexpr int SEG = (NSEG + NT - 1) / NT;       // segments per thread
+    constexpr int NARR = FULL ? 4 : 2;
+    constexpr int BCQ = T * 32 / 4 / kWave;         // float4 of B/C rows per lane and tile
+    static_assert(BCQ * 4 * kWave == T * 32, "B/C tile");
+    __shared__ __attribute__((aligned(16))) float s_x[NARR][kWave * TP];  // dt, w, du, g
+    __shared__ __attribute__((aligned(16))) float s_bc[G][T * 32];        // B_t(16) C_t(16)
+    __shared__ __attribute__((aligned(16))) float s_y[G > 1 ? G * kWave * TP : 4];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
     const IT *__restrict__ z = static_cast<const IT *>(a.z);
     IT *__restrict__ y = static_cast<IT *>(a.y);
-    cfloat *bc = as_constant(a.bc);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -102,113 +188,228 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
     const int64_t t_begin = j * a.K;
     const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
     const int Npad = G * kGroup;
+    const bool gate = a.z != nullptr;
+    const float *__restrict__ bcg = a.bc + (static_cast<size_t>(b) * G + g) * L * 32;
 
-    // Per-lane constants: A[d, n] * log2(e) (zero for padded states).
+    // ---- this thread's tile segments: fixed rows, per-row constants.
+    // Loads use addresses clamped into the valid range and are zeroed by
+    // select, so the load path has no divergent branches.
+    int seg_row[SEG], seg_col[SEG];
+    bool seg_rv[SEG];                               // segment exists and its row < d_inner
+    size_t seg_base[SEG];                           // element offset of the row start
+    float seg_bias[SEG], seg_D[SEG];
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) {
+        const int sidx = e * NT + tid;
+        const bool on = sidx < NSEG;
+        seg_row[e] = on ? sidx / SPR : 0;
+        seg_col[e] = on ? (sidx % SPR) * VW : 0;
+        const int64_t dd = d0 + seg_row[e];
+        seg_rv[e] = on && dd < a.D;
+        const int64_t dc = dd < a.D ? dd : a.D - 1;
+        seg_base[e] = (static_cast<size_t>(b) * a.D + dc) * L;
+        seg_bias[e] = (seg_rv[e] && a.delta_bias) ? a.delta_bias[dc] : 0.0f;
+        seg_D[e] = (seg_rv[e] && a.Dskip) ? a.Dskip[dc] : 0.0f;
+    }
+
+    // raw tile registers (prefetched one tile ahead)
+    typename S::V vu[SEG], vd[SEG], vz[SEG];        // VEC path
+    float ru[SEG][VW], rd[SEG][VW], rz[SEG][VW];    // element path
+    float4 vbc[BCQ];                                // this wavefront's B/C rows of the tile
+    auto load_tile = [&](int64_t t0) {
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) {
+            const int64_t t = t0 + seg_col[e];
+            if (VEC) {
+                const int64_t tl = t < t_end ? t : t_end - VW;   // t_end >= VW here
+                const size_t off = seg_base[e] + tl;
+                vu[e] = *reinterpret_cast<const typename S::V *>(u + off);
+                vd[e] = *reinterpret_cast<const typename S::V *>(dl + off);
+                if (FULL && gate) vz[e] = *reinterpret_cast<const typename S::V *>(z + off);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VW; ++i) {
+                    const int64_t tl = t + i < t_end ? t + i : t_end - 1;
+                    const size_t off = seg_base[e] + tl;
+                    ru[e][i] = IO::load(u, off);
+                    rd[e][i] = IO::load(dl, off);
+                    rz[e][i] = (FULL && gate) ? IO::load(z, off) : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < BCQ; ++q) {
+            const int idx = q * kWave + lane;       // float4 index within the tile
+            const int64_t t = t0 + idx / 8;
+            const int64_t tc = t < L ? t : L - 1;   // rows past L are never used
+            vbc[q] = *reinterpret_cast<const float4 *>(bcg + tc * 32 + (idx & 7) * 4);
+        }
+    };
+
+    // ---- per-lane constants and initial state (unconditional loads from
+    //      clamped indices, then select: no per-load branches)
+    const int64_t dcl = lane_ok ? d : a.D - 1;
     float A2[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
         const int n = g * kGroup + i;
-        A2[i] = (lane_ok && n < a.N) ? a.A[d * a.N + n] * kLog2e : 0.0f;
+        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+        A2[i] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
     }
-    // Initial state of this chunk.
     float h[kGroup];
-    const size_t cd = (static_cast<size_t>(b) * a.D + (lane_ok ? d : 0)) * a.J + j;
-    if (FULL && a.J > 1) {
+    const size_t cd = (static_cast<size_t>(b) * a.D + dcl) * a.J + j;
+    if (FULL && a.J > 1 && j > 0) {
         const float *hs = a.hstart + cd * Npad + g * kGroup;
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) h[i] = lane_ok ? hs[i] : 0.0f;
+        for (int i = 0; i < kGroup; ++i) {
+            const float v = hs[i];
+            h[i] = lane_ok ? v : 0.0f;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) h[i] = 0.0f;
     }
     float dt_sum = 0.0f;
+    const float *sbc = &s_bc[g][0];
 
+    load_tile(t_begin);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-        // (a) coalesced load of the tile [64 channels x T tokens]: consecutive
-        //     threads read consecutive tokens of a row.
-        for (int idx = tid; idx < kWave * T; idx += NT) {
-            const int r = idx / T, c = idx % T;
-            const int64_t dd = d0 + r, t = t0 + c;
-            float dt = 0.0f, w = 0.0f;
-            if (dd < a.D && t < t_end) {
-                const size_t off = (static_cast<size_t>(b) * a.D + dd) * L + t;
-                const float uu = IO::load(u, off);
-                float x = IO::load(dl, off);
-                if (a.delta_bias) x += a.delta_bias[dd];
-                dt = a.softplus ? softplus_f32(x) : x;
-                w = dt * uu;
+        // (a) convert the prefetched tile and write it to LDS.  The softplus
+        //     and gate flags are hoisted out of the element loops.
+        auto convert = [&](auto sp_tag, auto gate_tag) {
+            constexpr bool SP = decltype(sp_tag)::value;
+            constexpr bool GT = decltype(gate_tag)::value;
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) {
+                if (e * NT + tid >= NSEG) continue;  // compile-time false when SEG*NT == NSEG
+                float xu[VW], xd[VW], xz[VW];
+                if (VEC) {
+                    S::unpack(vu[e], xu);
+                    S::unpack(vd[e], xd);
+                    if (FULL && GT) S::unpack(vz[e], xz);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VW; ++i) {
+                        xu[i] = ru[e][i];
+                        xd[i] = rd[e][i];
+                        xz[i] = rz[e][i];
+                    }
+                }
+                float xdt[VW], xw[VW], xdu[VW], xg[VW];
+#pragma unroll
+                for (int i = 0; i < VW; ++i) {
+                    // branch-free: evaluate for every lane, zero by a 0/1 factor
+                    const float m = (seg_rv[e] && t0 + seg_col[e] + i < t_end) ? 1.0f : 0.0f;
+                    const bool ok = m != 0.0f;
+                    const float x = xd[i] + seg_bias[e];
+                    const float dt = (SP ? softplus_f32(x) : x) * m;
+                    const float uu = ok ? xu[i] : 0.0f;
+                    xdt[i] = dt;
+                    xw[i] = dt * uu;
+                    if (FULL) {
+                        xdu[i] = seg_D[e] * uu;
+                        xg[i] = GT ? silu_f32(ok ? xz[i] : 0.0f) : 1.0f;
+                    }
+                }
+                const int o = seg_row[e] * TP + seg_col[e];
+#pragma unroll
+                for (int q = 0; q < VW; q += 4) {
+                    *reinterpret_cast<float4 *>(&s_x[0][o + q]) = make_float4(xdt[q], xdt[q + 1], xdt[q + 2], xdt[q + 3]);
+                    *reinterpret_cast<float4 *>(&s_x[1][o + q]) = make_float4(xw[q], xw[q + 1], xw[q + 2], xw[q + 3]);
+                    if (FULL) {
+                        *reinterpret_cast<float4 *>(&s_x[2][o + q]) = make_float4(xdu[q], xdu[q + 1], xdu[q + 2], xdu[q + 3]);
+                        *reinterpret_cast<float4 *>(&s_x[3][o + q]) = make_float4(xg[q], xg[q + 1], xg[q + 2], xg[q + 3]);
+                    }
+                }
             }
-            s_dt[r * TP + c] = dt;
-            s_w[r * TP + c] = w;
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (a.softplus) {
+            if (FULL && gate) convert(T_{}, T_{}); else convert(T_{}, F_{});
+        } else {
+            if (FULL && gate) convert(F_{}, T_{}); else convert(F_{}, F_{});
         }
+#pragma unroll
+        for (int q = 0; q < BCQ; ++q)
+            *reinterpret_cast<float4 *>(&s_bc[g][(q * kWave + lane) * 4]) = vbc[q];
+        // Unconditional prefetch (addresses are clamped into range): the same
+        // number of loads on every path keeps the wait counts exact, so the
+        // next tile's loads are waited on without draining this tile's stores.
+        load_tile(t0 + T);
         __syncthreads();
 
-        // (b) the recurrence, one lane per channel; B/C rows via scalar loads,
-        //     fetched one token ahead.  Padded tokens have dt = 0 and w = 0:
-        //     h is unchanged.
+        // (b) the recurrence: one lane per channel, 4 tokens per LDS read of
+        //     (dt, w); B and C rows of the next token read a token ahead.
         const int tcount = static_cast<int>(t_end - t0 < T ? t_end - t0 : T);
-        cfloat *p = bc + ((static_cast<size_t>(b) * L + t0) * G + g) * 32;
-        float Bc[kGroup], Cc[kGroup];
+        const int row = lane * TP;
+        float Bn = sbc[lane & 15];
+        float Cn[kGroup];
+        if (FULL) {
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-            Bc[i] = p[i];
-            Cc[i] = FULL ? p[kGroup + i] : 0.0f;
-        }
-        float dtc = s_dt[lane * TP], wc = s_w[lane * TP];
-#pragma unroll 2
-        for (int c = 0; c < tcount; ++c) {
-            const int cn = c + 1 < tcount ? c + 1 : c;
-            cfloat *pn = p + (cn - c) * G * 32;
-            float Bn[kGroup], Cn[kGroup];
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                Bn[i] = pn[i];
-                Cn[i] = FULL ? pn[kGroup + i] : 0.0f;
+            for (int q = 0; q < kGroup; q += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&sbc[kGroup + q]);
+                Cn[q] = v.x; Cn[q + 1] = v.y; Cn[q + 2] = v.z; Cn[q + 3] = v.w;
             }
-            const float dtn = s_dt[lane * TP + cn], wn = s_w[lane * TP + cn];
-            float acc = 0.0f;
+        }
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const float dA = exp2_hw(dtc * A2[i]);
-                h[i] = __builtin_fmaf(dA, h[i], wc * Bc[i]);
-                if (FULL) acc = __builtin_fmaf(Cc[i], h[i], acc);
+        for (int c = 0; c < T; c += 4) {
+            if (c >= tcount) break;
+            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_x[0][row + c]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_x[1][row + c]);
+            const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+            const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            float yv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float Bc = Bn;
+                float Cc[kGroup];
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) Cc[i] = Cn[i];
+                const int tn = c + k + 1 < T ? c + k + 1 : c + k;   // stays inside the tile
+                Bn = sbc[tn * 32 + (lane & 15)];
+                if (FULL) {
+#pragma unroll
+                    for (int q = 0; q < kGroup; q += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(&sbc[tn * 32 + kGroup + q]);
+                        Cn[q] = v.x; Cn[q + 1] = v.y; Cn[q + 2] = v.z; Cn[q + 3] = v.w;
+                    }
+                }
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                token_step<FULL, 0>(h, A2, dtv[k], wv[k], Bc, Cc, acc);
+                yv[k] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                if (!FULL) dt_sum += dtv[k];
             }
             if (FULL) {
-                if (G == 1) s_dt[lane * TP + c] = acc;
-                else s_y[(g * kWave + lane) * TP + c] = acc;
-            } else {
-                dt_sum += dtc;
+                float *dst = G == 1 ? &s_x[0][row + c] : &s_y[(g * kWave + lane) * TP + c];
+                *reinterpret_cast<float4 *>(dst) = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                Bc[i] = Bn[i];
-                Cc[i] = Cn[i];
-            }
-            dtc = dtn;
-            wc = wn;
-            p = pn;
         }
 
-        // (c) finalize y for the tile: sum of group partials (fixed order),
-        //     skip term, gate, coalesced store.
+        // (c) store y: sum of group partials in a fixed order, skip term, gate
         if (FULL) {
             __syncthreads();
-            for (int idx = tid; idx < kWave * T; idx += NT) {
-                const int r = idx / T, c = idx % T;
-                const int64_t dd = d0 + r, t = t0 + c;
-                if (dd < a.D && t < t_end) {
-                    float acc;
-                    if (G == 1) {
-                        acc = s_dt[r * TP + c];
-                    } else {
-                        acc = s_y[r * TP + c];
 #pragma unroll
-                        for (int gg = 1; gg < G; ++gg) acc += s_y[(gg * kWave + r) * TP + c];
-                    }
-                    const size_t off = (static_cast<size_t>(b) * a.D + dd) * L + t;
-                    if (a.Dskip) acc = __builtin_fmaf(a.Dskip[dd], IO::load(u, off), acc);
-                    if (a.z) acc *= silu_f32(IO::load(z, off));
-                    IO::store(y, off, acc);
+            for (int e = 0; e < SEG; ++e) {
+                if (e * NT + tid >= NSEG) continue;
+                const int64_t t = t0 + seg_col[e];
+                const int o = seg_row[e] * TP + seg_col[e];
+                float yo[VW];
+#pragma unroll
+                for (int i = 0; i < VW; ++i) {
+                    float acc = G == 1 ? s_x[0][o + i] : s_y[o + i];
+#pragma unroll
+                    for (int gg = 1; gg < G; ++gg) acc += s_y[gg * kWave * TP + o + i];
+                    yo[i] = (acc + s_x[2][o + i]) * s_x[3][o + i];
+                }
+                const size_t off = seg_base[e] + t;
+                if (VEC) {
+                    if (seg_rv[e] && t < t_end)
+                        *reinterpret_cast<typename S::V *>(y + off) = S::pack(yo);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VW; ++i)
+                        if (seg_rv[e] && t + i < t_end) IO::store(y, off + i, yo[i]);
                 }
             }
         }
@@ -228,6 +429,267 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) he[i] = h[i];
         if (g == 0) a.dtsum[cd] = dt_sum;
+    }
+}
+
+// ============================================================ quad-row kernel (N <= 16)
+// The path for d_state <= 16.  A wavefront covers 16 channels in 4 lane-rows:
+// lane l serves channel c = l % 16 and the 4 states 4q..4q+3, q = l / 16.
+// Compared with one lane per channel this streams 16 rows per wavefront
+// instead of 64 (the partially consumed cache lines of all wavefronts in
+// flight then fit in the L2 of their XCD, so each line is fetched once), and
+// it gives 4x as many wavefronts, so fewer sequence chunks are needed to fill
+// the chip.  Per 4 tokens the 4 row-partials of C.h are summed with a
+// transposing butterfly of v_permlane16_swap / v_permlane32_swap (3 swaps and
+// 3 adds): afterwards row q holds the full sum for token q of the group.
+//
+// Tile: 16 channels x T tokens, T = 64 bytes / element size, so each lane
+// loads exactly one 16-byte piece per tensor per tile.  Per tile:
+//  (a) convert the lane's piece (dt = softplus(delta + bias), w = dt u,
+//      du = D u, g = silu(z)) into LDS rows padded to T + 4 floats, and the
+//      tile's B/C rows;
+//  (b) walk the tile 4 tokens per ds_read_b128 of (dt, w): B_t enters
+//      w B_t[4q + k] through DPP row_newbcast:k (lane 16q + k holds
+//      B_t[4q + k]), C_t[4q..4q+3] is one ds_read_b128;
+//  (c) coalesced 16-byte stores of y.
+template <class IO, bool FULL, bool VEC>
+__global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
+    using IT = typename IO::T;
+    using S = Seg<IO>;
+    constexpr int VW = S::VW;
+    constexpr int T = 4 * VW;                       // 64 bytes of a row per tile
+    constexpr int TP = T + 4;
+    constexpr int QC = 16;                          // channels per wavefront
+    constexpr int NARR = FULL ? 4 : 2;
+    constexpr int BCQ = T * 32 / 4 / kWave;         // float4 of B/C rows per lane and tile
+    __shared__ __attribute__((aligned(16))) float s_x[NARR][QC * TP];   // dt(then y), w, du, g
+    __shared__ __attribute__((aligned(16))) float s_bc[T * 32];        // B_t(16) C_t(16)
+
+    const IT *__restrict__ u = static_cast<const IT *>(a.u);
+    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
+    const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    IT *__restrict__ y = static_cast<IT *>(a.y);
+
+    const int lane = threadIdx.x;
+    const int c = lane & 15;                        // channel within the block
+    const int q = lane >> 4;                        // lane-row: states 4q .. 4q+3
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t j = blockIdx.y;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * QC;
+    const int64_t d = d0 + c;
+    const bool lane_ok = d < a.D;
+    const int64_t L = a.L;
+    const int64_t t_begin = j * a.K;
+    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
+    const bool gate = a.z != nullptr;
+    const float *__restrict__ bcb = a.bc + static_cast<size_t>(b) * L * 32;
+
+    // ---- this lane's tile piece: row r, tokens [sc, sc + VW) of the tile
+    const int r = lane >> 2;
+    const int sc = (lane & 3) * VW;
+    const int64_t dr = d0 + r;
+    const bool row_ok = dr < a.D;
+    const int64_t drc = row_ok ? dr : a.D - 1;
+    const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
+    const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
+    const float rD = (row_ok && a.Dskip) ? a.Dskip[drc] : 0.0f;
+
+    // Prefetched tile registers: named scalars and vectors only (no arrays or
+    // aggregates carried around the loop), so that they stay in VGPRs.
+    static_assert(BCQ >= 1 && BCQ <= 4, "B/C pieces per lane");
+    using V = typename S::V;
+    V vu{}, vd{}, vz{};
+    float4 b0{}, b1{}, b2{}, b3{};
+    auto load_bc = [&](int64_t t0, int k) {
+        const int idx = k * kWave + lane;           // float4 index within the tile
+        const int64_t tt = t0 + idx / 8;
+        const int64_t tc = tt < L ? tt : L - 1;     // rows past L are never used
+        return *reinterpret_cast<const float4 *>(bcb + tc * 32 + (idx & 7) * 4);
+    };
+    // element path: VW scalar loads per tensor, packed into the same vector
+    // registers as the 16-byte path
+    auto load_elems = [&](const IT *p, int64_t t) {
+        float e[VW];
+#pragma unroll
+        for (int i = 0; i < VW; ++i) {
+            const int64_t tc = t + i < t_end ? t + i : t_end - 1;
+            e[i] = IO::load(p, rbase + tc);
+        }
+        return S::pack(e);
+    };
+    auto load_tile = [&](int64_t t0) {
+        const int64_t t = t0 + sc;
+        if (VEC) {
+            const int64_t tc = t < t_end ? t : t_end - VW;   // t_end >= VW here
+            vu = *reinterpret_cast<const V *>(u + rbase + tc);
+            vd = *reinterpret_cast<const V *>(dl + rbase + tc);
+            if (FULL && gate) vz = *reinterpret_cast<const V *>(z + rbase + tc);
+        } else {
+            vu = load_elems(u, t);
+            vd = load_elems(dl, t);
+            if (FULL && gate) vz = load_elems(z, t);
+        }
+        b0 = load_bc(t0, 0);
+        if constexpr (BCQ > 1) b1 = load_bc(t0, 1);
+        if constexpr (BCQ > 2) b2 = load_bc(t0, 2);
+        if constexpr (BCQ > 3) b3 = load_bc(t0, 3);
+    };
+
+    // ---- per-lane constants and initial state
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    float A2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+        A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
+    }
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const size_t cd = (static_cast<size_t>(b) * a.D + dcl) * a.J + j;
+    if (FULL && a.J > 1 && j > 0) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.hstart + cd * 16 + 4 * q);
+        h[0] = lane_ok ? v.x : 0.0f; h[1] = lane_ok ? v.y : 0.0f;
+        h[2] = lane_ok ? v.z : 0.0f; h[3] = lane_ok ? v.w : 0.0f;
+    }
+    float dt_sum = 0.0f;
+
+    load_tile(t_begin);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        // (a) convert this lane's piece, write it and the B/C rows to LDS
+        auto convert = [&](auto sp_tag, auto gate_tag) {
+            constexpr bool SP = decltype(sp_tag)::value;
+            constexpr bool GT = decltype(gate_tag)::value;
+            float xu[VW], xd[VW], xz[VW];
+            S::unpack(vu, xu);
+            S::unpack(vd, xd);
+            if (FULL && GT) S::unpack(vz, xz);
+            float xdt[VW], xw[VW], xdu[VW], xg[VW];
+#pragma unroll
+            for (int i = 0; i < VW; ++i) {
+                // branch-free: evaluate for every lane, zero by a 0/1 factor
+                const float m = (row_ok && t0 + sc + i < t_end) ? 1.0f : 0.0f;
+                const bool ok = m != 0.0f;
+                const float x = xd[i] + rbias;
+                const float dt = (SP ? softplus_f32(x) : x) * m;
+                const float uu = ok ? xu[i] : 0.0f;
+                xdt[i] = dt;
+                xw[i] = dt * uu;
+                if (FULL) {
+                    xdu[i] = rD * uu;
+                    xg[i] = GT ? silu_f32(ok ? xz[i] : 0.0f) : 1.0f;
+                }
+            }
+            const int o = r * TP + sc;
+#pragma unroll
+            for (int i = 0; i < VW; i += 4) {
+                *reinterpret_cast<float4 *>(&s_x[0][o + i]) = make_float4(xdt[i], xdt[i + 1], xdt[i + 2], xdt[i + 3]);
+                *reinterpret_cast<float4 *>(&s_x[1][o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
+                if (FULL) {
+                    *reinterpret_cast<float4 *>(&s_x[2][o + i]) = make_float4(xdu[i], xdu[i + 1], xdu[i + 2], xdu[i + 3]);
+                    *reinterpret_cast<float4 *>(&s_x[3][o + i]) = make_float4(xg[i], xg[i + 1], xg[i + 2], xg[i + 3]);
+                }
+            }
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (a.softplus) {
+            if (FULL && gate) convert(T_{}, T_{}); else convert(T_{}, F_{});
+        } else {
+            if (FULL && gate) convert(F_{}, T_{}); else convert(F_{}, F_{});
+        }
+        *reinterpret_cast<float4 *>(&s_bc[(0 * kWave + lane) * 4]) = b0;
+        if constexpr (BCQ > 1) *reinterpret_cast<float4 *>(&s_bc[(1 * kWave + lane) * 4]) = b1;
+        if constexpr (BCQ > 2) *reinterpret_cast<float4 *>(&s_bc[(2 * kWave + lane) * 4]) = b2;
+        if constexpr (BCQ > 3) *reinterpret_cast<float4 *>(&s_bc[(3 * kWave + lane) * 4]) = b3;
+        // Unconditional prefetch (addresses are clamped into range): the same
+        // number of loads on every path keeps the wait counts exact.
+        load_tile(t0 + T);
+        __syncthreads();
+
+        // (b) the recurrence, 4 tokens per group
+        const int tcount = static_cast<int>(t_end - t0 < T ? t_end - t0 : T);
+        const int rowc = c * TP;
+        const int bsel = 4 * q + (lane & 3);       // B row-replication index
+        float Bn = s_bc[bsel];
+        float4 Cn = FULL ? *reinterpret_cast<const float4 *>(&s_bc[16 + 4 * q])
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int c4 = 0; c4 < T; c4 += 4) {
+            if (c4 >= tcount) break;
+            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_x[0][rowc + c4]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_x[1][rowc + c4]);
+            const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+            const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            float accv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float Bc = Bn;
+                const float4 Cc = Cn;
+                const int tn = c4 + k + 1 < T ? c4 + k + 1 : c4 + k;   // stays inside the tile
+                Bn = s_bc[tn * 32 + bsel];
+                if (FULL) Cn = *reinterpret_cast<const float4 *>(&s_bc[tn * 32 + 16 + 4 * q]);
+                const float dt = dtv[k], w = wv[k];
+                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bc) * w);
+                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bc) * w);
+                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bc) * w);
+                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bc) * w);
+                if (FULL)
+                    accv[k] = __builtin_fmaf(Cc.x, h[0], __builtin_fmaf(Cc.y, h[1],
+                              __builtin_fmaf(Cc.z, h[2], Cc.w * h[3])));
+                else
+                    dt_sum += dt;
+            }
+            if (FULL) {
+                // rows (0,1) and (2,3): even rows sum token 0/2, odd rows 1/3
+                const auto s01 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(accv[0]), __float_as_uint(accv[1]), false, false);
+                const auto s23 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(accv[2]), __float_as_uint(accv[3]), false, false);
+                const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+                const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+                // halves: rows 0,1 keep tokens 0,1; rows 2,3 keep tokens 2,3
+                const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01),
+                                                                __float_as_uint(p23), false, false);
+                const float ysum = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // token c4 + q
+                const int o = rowc + c4 + q;
+                s_x[0][o] = (ysum + s_x[2][o]) * s_x[3][o];
+            }
+        }
+
+        // (c) coalesced store of y
+        if (FULL) {
+            __syncthreads();
+            const int64_t t = t0 + sc;
+            const int o = r * TP + sc;
+            float yo[VW];
+#pragma unroll
+            for (int i = 0; i < VW; i += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&s_x[0][o + i]);
+                yo[i] = v.x; yo[i + 1] = v.y; yo[i + 2] = v.z; yo[i + 3] = v.w;
+            }
+            if (VEC) {
+                if (row_ok && t < t_end)
+                    *reinterpret_cast<typename S::V *>(y + rbase + t) = S::pack(yo);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VW; ++i)
+                    if (row_ok && t + i < t_end) IO::store(y, rbase + t + i, yo[i]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!lane_ok) return;
+    if (FULL) {
+        if (a.last_state && j == a.J - 1) {
+            float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (4 * q + k < a.N) ls[4 * q + k] = h[k];
+        }
+    } else {
+        *reinterpret_cast<float4 *>(a.hend + cd * 16 + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+        if (q == 0) a.dtsum[cd] = dt_sum;
     }
 }
 
@@ -268,7 +730,8 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
         const int n = g * kGroup + i;
-        A2[i] = n < a.N ? a.A[d * a.N + n] * kLog2e : 0.0f;
+        const float v = a.A[d * a.N + (n < a.N ? n : a.N - 1)];
+        A2[i] = n < a.N ? v * kLog2e : 0.0f;
         hin[i] = 0.0f;
     }
     for (int64_t j0 = 0; j0 < a.J; j0 += kWave) {
@@ -276,13 +739,19 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs a) {
         const bool ok = jj < a.J;                    // h_start is written for every chunk
         const bool has_op = jj < a.J - 1;            // the last chunk acts as identity
         const size_t cd = static_cast<size_t>(bd) * a.J + (ok ? jj : 0);
-        const float sdt = has_op ? a.dtsum[cd] : 0.0f;
+        // cd is a valid index for every lane; the last chunk's slots hold no
+        // operator, so their (finite or not) contents are replaced by select.
+        const float sdt_raw = a.dtsum[cd];
+        const float sdt = has_op ? sdt_raw : 0.0f;
         const float *he = a.hend + cd * Npad + g * kGroup;
         float *hs = a.hstart + cd * Npad + g * kGroup;
+        float hev[kGroup];
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) hev[i] = he[i];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
             float av = has_op ? exp2_hw(A2[i] * sdt) : 1.0f;
-            float bv = has_op ? he[i] : 0.0f;
+            float bv = has_op ? hev[i] : 0.0f;
             scan_step<0x111, 0xF>(av, bv);   // row_shr:1
             scan_step<0x112, 0xF>(av, bv);   // row_shr:2
             scan_step<0x114, 0xF>(av, bv);   // row_shr:4
@@ -308,20 +777,49 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-template <class IO, int G>
+#ifndef SSM_TILE
+#define SSM_TILE 8
+#endif
+template <class IO, int G, bool VEC>
 static hipError_t launch_chunks(const ScanArgs &a, hipStream_t s) {
-    constexpr int T = G == 1 ? 32 : 16;
+    constexpr int T = SSM_TILE;
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         // the last chunk's operator is never needed
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((chunk_kernel<IO, G, T, false>), agrid, dim3(64 * G), 0, s, a);
+        hipLaunchKernelGGL((chunk_kernel<IO, G, T, false, VEC>), agrid, dim3(64 * G), 0, s, a);
         const int64_t waves = a.Bsz * a.D * a.G;
         const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
         hipLaunchKernelGGL(carry_kernel, dim3(blocks), dim3(256), 0, s, a);
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((chunk_kernel<IO, G, T, true>), grid, dim3(64 * G), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<IO, G, T, true, VEC>), grid, dim3(64 * G), 0, s, a);
+    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
+    return hipGetLastError();
+}
+
+template <class IO, int G>
+static hipError_t launch_chunks_vec(const ScanArgs &a, hipStream_t s) {
+    // 16-byte vector access needs every row start and the base pointers
+    // 16-byte aligned.
+    constexpr int VW = Seg<IO>::VW;
+    auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z));
+    return vec ? launch_chunks<IO, G, true>(a, s) : launch_chunks<IO, G, false>(a, s);
+}
+
+template <class IO, bool VEC>
+static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
+    if (a.J > 1) {
+        const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
+        hipLaunchKernelGGL((quad_kernel<IO, false, VEC>), agrid, dim3(64), 0, s, a);
+        const int64_t waves = a.Bsz * a.D;
+        hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0,
+                           s, a);
+    }
+    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
+    hipLaunchKernelGGL((quad_kernel<IO, true, VEC>), grid, dim3(64), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
@@ -332,12 +830,18 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(bc_pack_kernel<IO>, pgrid, dim3(256), 0, s,
                        static_cast<const typename IO::T *>(a.B),
                        static_cast<const typename IO::T *>(a.C), a.bc, a.L, a.N, a.G);
+    if (a.quad) {
+        constexpr int VW = Seg<IO>::VW;
+        auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+        const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z));
+        return vec ? launch_quad<IO, true>(a, s) : launch_quad<IO, false>(a, s);
+    }
     switch (a.G) {   // the plan pads G to a power of two
-        case 1: return launch_chunks<IO, 1>(a, s);
-        case 2: return launch_chunks<IO, 2>(a, s);
-        case 4: return launch_chunks<IO, 4>(a, s);
-        case 8: return launch_chunks<IO, 8>(a, s);
-        case 16: return launch_chunks<IO, 16>(a, s);
+        case 1: return launch_chunks_vec<IO, 1>(a, s);
+        case 2: return launch_chunks_vec<IO, 2>(a, s);
+        case 4: return launch_chunks_vec<IO, 4>(a, s);
+        case 8: return launch_chunks_vec<IO, 8>(a, s);
+        case 16: return launch_chunks_vec<IO, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -34,8 +34,21 @@ import ssm_inputs  # noqa: E402
 
 METRIC = "selective-scan channel-tokens/sec"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# MI355X fp32 vector peak, published: 157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128
+# FMA lanes per clock.  ALU work below is counted in FMA-equivalent issue
+# slots (2 FLOP each); a transcendental (exp2, log2, rcp) issues at a quarter
+# of the FMA rate and so occupies 4 slots.
+VALU_PEAK_TFLOPS = 157.3
 DEFAULT_CONFIG = "c1_mamba130m_f32"
 CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
+
+# Minimal instruction mix of the method, in FMA-equivalent slots.
+SLOTS_PER_UPDATE = 4 + 4       # dt*A', w*B, state FMA, output FMA; one exp2
+SLOTS_PER_CHTOK = {            # per (batch, channel, token), outside the N loop
+    "softplus": 7 + 2 * 4,     # 7 VALU + exp2 + log2
+    "common": 4,               # bias add, w = dt*u, D*u, (y + Du)
+    "gate": 3 + 2 * 4,         # 3 VALU + exp2 + rcp
+}
 
 
 def algorithmic_bytes(batch, d_inner, N, L, io, gate, last_state=True):
@@ -46,6 +59,26 @@ def algorithmic_bytes(batch, d_inner, N, L, io, gate, last_state=True):
     per_chtok = (3 + (1 if gate else 0)) * e
     return (batch * d_inner * L * per_chtok + 2 * batch * N * L * e +
             d_inner * (N + 2) * 4 + (batch * d_inner * N * 4 if last_state else 0))
+
+
+def algorithmic_slots(batch, d_inner, N, L, gate):
+    """FMA-equivalent VALU issue slots the scan needs at minimum."""
+    chtok = batch * d_inner * L
+    per = SLOTS_PER_CHTOK["softplus"] + SLOTS_PER_CHTOK["common"]
+    if gate:
+        per += SLOTS_PER_CHTOK["gate"]
+    return chtok * (N * SLOTS_PER_UPDATE + per)
+
+
+def versions():
+    import torch
+    out = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            out["rocm"] = f.read().strip()
+    except OSError:
+        out["rocm"] = None
+    return out
 
 
 class HipEvents:
@@ -134,6 +167,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,6 +179,15 @@ def main():
 
     import torch
     import selective_state_space_fwd_amd as ssm
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": src.numel() * 4, "copies": 5}))
+        return
 
     ssm.load_library()
     dev = torch.device("cuda:0")
@@ -201,7 +246,9 @@ def main():
     chtok = batch * d_inner * (L + 1)
     value = chtok / (ms_per_step * 1e-3)
     kavg = float(np.mean(kern_ms))
-    achieved = set_bytes / (kavg * 1e-3) / 1e9
+    hbm_gbs = set_bytes / (kavg * 1e-3) / 1e9
+    slots = algorithmic_slots(batch, d_inner, N, L, gate)
+    alu_tflops = 2.0 * slots / (kavg * 1e-3) / 1e12
 
     traffic = None
     try:
@@ -233,16 +280,20 @@ def main():
             "gate": gate, "chunk": K, "input_sets": n_sets,
         },
         "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            "bound": "alu",
+            "achieved": alu_tflops,
+            "peak": VALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": alu_tflops / VALU_PEAK_TFLOPS,
             "traffic": traffic,
-            "kernel": "chunk_kernel (pass writing y)",
+            "kernel": "scan pass writing y (quad_kernel for N <= 16, chunk_kernel above)",
             "kernel_ms": kavg,
+            "algorithmic_slots": slots,
+            "hbm_achieved_gbs": hbm_gbs,
+            "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": set_bytes,
         },
+        "versions": versions(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

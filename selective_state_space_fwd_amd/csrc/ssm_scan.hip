@@ -10,15 +10,19 @@
 //   SSM engineering essay (discosf.com) -- §1.1 skip term D, §1.3 softplus
 //     step size.
 //
-// Mapping on CDNA4.  One lane owns one channel (b, d) and one group of 16
-// states, held in VGPRs; a wavefront covers 64 consecutive channels of one
-// batch row.  Because A is diagonal, each lane runs the recurrence
-// h = exp(dt A) h + dt B u serially over its tokens: no per-token scan work.
-// Parallelism comes from channels, from state groups (a workgroup holds the
-// G = ceil(N/16) groups of the same 64 channels, one wavefront each, and sums
-// their partial C.h in LDS in a fixed order), and -- when channels are too
-// few to fill 256 CUs -- from sequence chunks of K tokens:
-//   pass 1 (chunk_kernel<AGG>)   every chunk but the last runs from a zero
+// Mapping on CDNA4.  Because A is diagonal, every (channel, state) pair runs
+// the recurrence h = exp(dt A) h + dt B u serially over its tokens, in a VGPR
+// of one lane: no per-token scan work.  Two kernels share that core:
+//   quad_kernel   (d_state <= 16) one wavefront = 16 channels x 4 lane-rows,
+//                 4 states per lane; the row-partials of C.h are summed with
+//                 cross-lane permutes;
+//   chunk_kernel  (d_state > 16) one lane = one channel and one group of 16
+//                 states, a wavefront = 64 channels of one group, a workgroup
+//                 = the G = ceil(N/16) groups of those channels, whose partial
+//                 C.h are summed in LDS in a fixed order.
+// When channels are too few to fill 256 CUs, the sequence is also cut into
+// chunks of K tokens:
+//   pass 1 (<FULL = false>)      every chunk but the last runs from a zero
 //                                state; it publishes its transfer operator
 //                                (sum of dt, h_end): A_chunk = exp(A sum dt),
 //                                B_chunk = h_end;
@@ -26,14 +30,13 @@
 //                                associative composition
 //                                (a2,b2) o (a1,b1) = (a1 a2, a2 b1 + b2),
 //                                lanes along chunks, wave64 DPP steps;
-//   pass 3 (chunk_kernel<FULL>)  every chunk re-runs from its h_start and
+//   pass 3 (<FULL = true>)       every chunk re-runs from its h_start and
 //                                writes y (and the last chunk, last_state).
 // B and C are shared by all channels of a batch row.  A pre-pass repacks them
-// as fp32 rows [B_t(16) C_t(16)] per (b, t, group) so that a wavefront reads
-// the 32 values of token t through scalar loads (one s_load_dwordx16 pair)
-// and feeds them to the VALU as SGPR operands: no LDS traffic for B/C.
-// u, delta and z (L-contiguous rows) are staged through LDS with coalesced
-// loads and read back transposed, one row per lane.
+// as fp32 rows [B_t(16) C_t(16)] per (b, t, group), so a tile's B/C is one
+// contiguous piece that the wavefront stages in LDS; u, delta and z
+// (L-contiguous rows) are loaded with coalesced 16-byte loads, converted and
+// staged through LDS, and read back one row per lane.
 #include <type_traits>
 
 #include "ssm_common.h"

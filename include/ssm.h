@@ -66,7 +66,7 @@ typedef enum {
     SSM_OK = 0,
     SSM_ERR_NULL_ARG = 1,     /* a required pointer (or the descriptor) is NULL        */
     SSM_ERR_BAD_SHAPE = 2,    /* a negative dimension, or a bad chunk_size            */
-    SSM_ERR_UNSUPPORTED = 3,  /* d_state outside 1..256, or an unknown io_dtype       */
+    SSM_ERR_UNSUPPORTED = 3,  /* d_state outside 1..256, seqlen > SSM_MAX_SEQLEN, an unknown io_dtype, or more chunks than a grid holds */
     SSM_ERR_MISALIGNED = 4,   /* a pointer not aligned to its element size            */
     SSM_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than ssm_scan_workspace_bytes */
     SSM_ERR_HIP = 6           /* a HIP launch error (hipGetLastError after launching) */
@@ -75,6 +75,9 @@ typedef enum {
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
 #define SSM_MAX_D_STATE 256
+/* Longest sequence ssm_scan_fwd accepts (token offsets inside one row of the
+ * packed B/C workspace stay within 32 bits). */
+#define SSM_MAX_SEQLEN (1LL << 25)
 
 typedef struct ssm_desc {
     int64_t batch;            /* >= 0 */

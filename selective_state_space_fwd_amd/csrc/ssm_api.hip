@@ -39,6 +39,7 @@ ssm_status check_desc(const ssm_desc *d) {
     if (d->batch < 0 || d->d_inner < 0 || d->seqlen < 0) return SSM_ERR_BAD_SHAPE;
     if (d->d_state < 1 || d->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if (d->seqlen > SSM_MAX_SEQLEN) return SSM_ERR_UNSUPPORTED;
     if (!dims_ok(d->batch, d->d_inner, d->seqlen > 0 ? d->seqlen : 1)) return SSM_ERR_BAD_SHAPE;
     if (!dims_ok(d->batch, d->d_inner, d->d_state)) return SSM_ERR_BAD_SHAPE;
     return SSM_OK;

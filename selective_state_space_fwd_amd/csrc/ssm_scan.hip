@@ -185,6 +185,7 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
     const int64_t b = blockIdx.x / a.n_cblk;
     const int64_t j = blockIdx.y;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * kWave;
+    const bool rows_full = d0 + kWave <= a.D;       // workgroup-uniform
     const int64_t d = d0 + lane;
     const bool lane_ok = d < a.D;
     const int64_t L = a.L;
@@ -279,9 +280,10 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
         // (a) convert the prefetched tile and write it to LDS.  The softplus
         //     and gate flags are hoisted out of the element loops.
-        auto convert = [&](auto sp_tag, auto gate_tag) {
+        auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
             constexpr bool SP = decltype(sp_tag)::value;
             constexpr bool GT = decltype(gate_tag)::value;
+            constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
             for (int e = 0; e < SEG; ++e) {
                 if (e * NT + tid >= NSEG) continue;  // compile-time false when SEG*NT == NSEG
@@ -302,10 +304,11 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
 #pragma unroll
                 for (int i = 0; i < VW; ++i) {
                     // branch-free: evaluate for every lane, zero by a 0/1 factor
-                    const float m = (seg_rv[e] && t0 + seg_col[e] + i < t_end) ? 1.0f : 0.0f;
-                    const bool ok = m != 0.0f;
+                    // (only the last tile of a chunk or block needs the mask)
+                    const float m = !MASK || (seg_rv[e] && t0 + seg_col[e] + i < t_end) ? 1.0f : 0.0f;
+                    const bool ok = !MASK || m != 0.0f;
                     const float x = xd[i] + seg_bias[e];
-                    const float dt = (SP ? softplus_f32(x) : x) * m;
+                    const float dt = MASK ? (SP ? softplus_f32(x) : x) * m : (SP ? softplus_f32(x) : x);
                     const float uu = ok ? xu[i] : 0.0f;
                     xdt[i] = dt;
                     xw[i] = dt * uu;
@@ -328,10 +331,18 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
-        if (a.softplus) {
-            if (FULL && gate) convert(T_{}, T_{}); else convert(T_{}, F_{});
+        if (rows_full && t0 + T <= t_end) {
+            if (a.softplus) {
+                if (FULL && gate) convert(T_{}, T_{}, F_{}); else convert(T_{}, F_{}, F_{});
+            } else {
+                if (FULL && gate) convert(F_{}, T_{}, F_{}); else convert(F_{}, F_{}, F_{});
+            }
         } else {
-            if (FULL && gate) convert(F_{}, T_{}); else convert(F_{}, F_{});
+            if (a.softplus) {
+                if (FULL && gate) convert(T_{}, T_{}, T_{}); else convert(T_{}, F_{}, T_{});
+            } else {
+                if (FULL && gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
+            }
         }
 #pragma unroll
         for (int q = 0; q < BCQ; ++q)
@@ -463,10 +474,15 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     constexpr int T = 4 * VW;                       // 64 bytes of a row per tile
     constexpr int TP = T + 4;
     constexpr int QC = 16;                          // channels per wavefront
-    constexpr int NARR = FULL ? 4 : 2;
     constexpr int BCQ = T * 32 / 4 / kWave;         // float4 of B/C rows per lane and tile
-    __shared__ __attribute__((aligned(16))) float s_x[NARR][QC * TP];   // dt(then y), w, du, g
-    __shared__ __attribute__((aligned(16))) float s_bc[T * 32];        // B_t(16) C_t(16)
+    // Separate LDS objects, so that the compiler sees that the y written by
+    // one token group (into s_du, in place) never aliases the dt, w and B/C
+    // read by the next group, and can issue those reads early.
+    __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
+    __shared__ __attribute__((aligned(16))) float s_w[QC * TP];
+    __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];   // D u, then y
+    __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];    // silu(z)
+    __shared__ __attribute__((aligned(16))) float s_bc[T * 32];              // B_t(16) C_t(16)
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -492,6 +508,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const int sc = (lane & 3) * VW;
     const int64_t dr = d0 + r;
     const bool row_ok = dr < a.D;
+    const bool rows_full = d0 + QC <= a.D;          // wave-uniform
     const int64_t drc = row_ok ? dr : a.D - 1;
     const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
     const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
@@ -503,10 +520,12 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     using V = typename S::V;
     V vu{}, vd{}, vz{};
     float4 b0{}, b1{}, b2{}, b3{};
+    // token offsets inside a row fit in 32 bits (the plan bounds L)
+    const int Lm1 = static_cast<int>(L - 1);
     auto load_bc = [&](int64_t t0, int k) {
         const int idx = k * kWave + lane;           // float4 index within the tile
-        const int64_t tt = t0 + idx / 8;
-        const int64_t tc = tt < L ? tt : L - 1;     // rows past L are never used
+        const int tt = static_cast<int>(t0) + idx / 8;
+        const int tc = tt < Lm1 ? tt : Lm1;         // rows past L are never used
         return *reinterpret_cast<const float4 *>(bcb + tc * 32 + (idx & 7) * 4);
     };
     // element path: VW scalar loads per tensor, packed into the same vector
@@ -559,9 +578,10 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     load_tile(t_begin);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
         // (a) convert this lane's piece, write it and the B/C rows to LDS
-        auto convert = [&](auto sp_tag, auto gate_tag) {
+        auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
             constexpr bool SP = decltype(sp_tag)::value;
             constexpr bool GT = decltype(gate_tag)::value;
+            constexpr bool MASK = decltype(mask_tag)::value;
             float xu[VW], xd[VW], xz[VW];
             S::unpack(vu, xu);
             S::unpack(vd, xd);
@@ -570,10 +590,11 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #pragma unroll
             for (int i = 0; i < VW; ++i) {
                 // branch-free: evaluate for every lane, zero by a 0/1 factor
-                const float m = (row_ok && t0 + sc + i < t_end) ? 1.0f : 0.0f;
-                const bool ok = m != 0.0f;
+                // (only the last tile of a chunk or block needs the mask)
+                const float m = !MASK || (row_ok && t0 + sc + i < t_end) ? 1.0f : 0.0f;
+                const bool ok = !MASK || m != 0.0f;
                 const float x = xd[i] + rbias;
-                const float dt = (SP ? softplus_f32(x) : x) * m;
+                const float dt = MASK ? (SP ? softplus_f32(x) : x) * m : (SP ? softplus_f32(x) : x);
                 const float uu = ok ? xu[i] : 0.0f;
                 xdt[i] = dt;
                 xw[i] = dt * uu;
@@ -585,20 +606,28 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
             const int o = r * TP + sc;
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
-                *reinterpret_cast<float4 *>(&s_x[0][o + i]) = make_float4(xdt[i], xdt[i + 1], xdt[i + 2], xdt[i + 3]);
-                *reinterpret_cast<float4 *>(&s_x[1][o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
+                *reinterpret_cast<float4 *>(&s_dt[o + i]) = make_float4(xdt[i], xdt[i + 1], xdt[i + 2], xdt[i + 3]);
+                *reinterpret_cast<float4 *>(&s_w[o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
                 if (FULL) {
-                    *reinterpret_cast<float4 *>(&s_x[2][o + i]) = make_float4(xdu[i], xdu[i + 1], xdu[i + 2], xdu[i + 3]);
-                    *reinterpret_cast<float4 *>(&s_x[3][o + i]) = make_float4(xg[i], xg[i + 1], xg[i + 2], xg[i + 3]);
+                    *reinterpret_cast<float4 *>(&s_du[o + i]) = make_float4(xdu[i], xdu[i + 1], xdu[i + 2], xdu[i + 3]);
+                    *reinterpret_cast<float4 *>(&s_g[o + i]) = make_float4(xg[i], xg[i + 1], xg[i + 2], xg[i + 3]);
                 }
             }
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
-        if (a.softplus) {
-            if (FULL && gate) convert(T_{}, T_{}); else convert(T_{}, F_{});
+        if (rows_full && t0 + T <= t_end) {
+            if (a.softplus) {
+                if (FULL && gate) convert(T_{}, T_{}, F_{}); else convert(T_{}, F_{}, F_{});
+            } else {
+                if (FULL && gate) convert(F_{}, T_{}, F_{}); else convert(F_{}, F_{}, F_{});
+            }
         } else {
-            if (FULL && gate) convert(F_{}, T_{}); else convert(F_{}, F_{});
+            if (a.softplus) {
+                if (FULL && gate) convert(T_{}, T_{}, T_{}); else convert(T_{}, F_{}, T_{});
+            } else {
+                if (FULL && gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
+            }
         }
         *reinterpret_cast<float4 *>(&s_bc[(0 * kWave + lane) * 4]) = b0;
         if constexpr (BCQ > 1) *reinterpret_cast<float4 *>(&s_bc[(1 * kWave + lane) * 4]) = b1;
@@ -609,8 +638,9 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         load_tile(t0 + T);
         __syncthreads();
 
-        // (b) the recurrence, 4 tokens per group
-        const int tcount = static_cast<int>(t_end - t0 < T ? t_end - t0 : T);
+        // (b) the recurrence, 4 tokens per group.  The whole tile is one
+        // straight-line block (tokens past the chunk end are no-ops), so the
+        // LDS reads of a group can be issued under the previous group's math.
         const int rowc = c * TP;
         const int bsel = 4 * q + (lane & 3);       // B row-replication index
         float Bn = s_bc[bsel];
@@ -618,9 +648,8 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
-            if (c4 >= tcount) break;
-            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_x[0][rowc + c4]);
-            const float4 w4 = *reinterpret_cast<const float4 *>(&s_x[1][rowc + c4]);
+            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[rowc + c4]);
             const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
             const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
             float accv[4];
@@ -655,7 +684,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
                                                                 __float_as_uint(p23), false, false);
                 const float ysum = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // token c4 + q
                 const int o = rowc + c4 + q;
-                s_x[0][o] = (ysum + s_x[2][o]) * s_x[3][o];
+                s_du[o] = (ysum + s_du[o]) * s_g[o];
             }
         }
 
@@ -667,7 +696,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
             float yo[VW];
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(&s_x[0][o + i]);
+                const float4 v = *reinterpret_cast<const float4 *>(&s_du[o + i]);
                 yo[i] = v.x; yo[i + 1] = v.y; yo[i + 2] = v.z; yo[i + 3] = v.w;
             }
             if (VEC) {

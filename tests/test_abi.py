@@ -77,7 +77,7 @@ def test_workspace_and_chunk_plan(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(d_inner=-1), 2),
     (dict(d_state=0), 3), (dict(d_state=257), 3), (dict(io_dtype=7), 3),
-    (dict(chunk_size=10), 2), (dict(chunk_size=-16), 2),
+    (dict(chunk_size=10), 2), (dict(chunk_size=-16), 2), (dict(seqlen=(1 << 25) + 1), 3),
 ])
 def test_invalid_descriptors(lib, kw, status):
     d = desc(**kw)

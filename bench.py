@@ -254,7 +254,7 @@ def main():
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f).get(args.config)
-        if tj and tj.get("bytes_per_launch"):
+        if tj and tj.get("bytes_per_launch") and not tj.get("stale"):
             traffic = tj["bytes_per_launch"]
     except (OSError, ValueError):
         traffic = None

@@ -31,6 +31,7 @@ struct Plan {
     int64_t J = 1;        // chunks
     int64_t n_cblk = 0;   // channel blocks per batch row (16 channels when quad, else 64)
     int quad = 0;         // d_state <= 16: quad-row kernel
+    int fold = 0;         // chunks fold their predecessors' operators (no carry kernel)
     size_t off_bc = 0, off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
 };
 
@@ -49,6 +50,10 @@ ssm_status check_desc(const ssm_desc *d) {
 constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kEnoughWaves = 1024;
 constexpr int64_t kMinAutoChunk = 64;
+// Up to this many chunks, each chunk of the quad path folds the transfer
+// operators of the chunks before it (at most this many exp per state) instead
+// of waiting for a separate carry kernel.
+constexpr int64_t kFoldMaxChunks = 32;
 
 ssm_status make_plan(const ssm_desc *d, Plan *p) {
     const ssm_status st = check_desc(d);
@@ -86,18 +91,22 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     p->J = (L + K - 1) / K;
     if (p->J > kMaxGridY) return SSM_ERR_UNSUPPORTED;
     if (p->n_cblk * d->batch > static_cast<int64_t>(UINT_MAX)) return SSM_ERR_UNSUPPORTED;
-    // workspace layout
+    p->fold = p->quad && p->J <= kFoldMaxChunks;
+    // workspace layout: packed B/C rows (chunk_kernel only), then the chunk
+    // operators and, without folding, the chunk start states
     size_t off = 0;
     p->off_bc = off;
-    off += align_up(static_cast<size_t>(d->batch) * L * G * 32 * sizeof(float));
+    if (!p->quad) off += align_up(static_cast<size_t>(d->batch) * L * G * 32 * sizeof(float));
     if (p->J > 1) {
         const size_t cj = static_cast<size_t>(d->batch) * d->d_inner * p->J;
         p->off_hend = off;
         off += align_up(cj * G * 16 * sizeof(float));
-        p->off_hstart = off;
-        off += align_up(cj * G * 16 * sizeof(float));
         p->off_dtsum = off;
         off += align_up(cj * sizeof(float));
+        if (!p->fold) {
+            p->off_hstart = off;
+            off += align_up(cj * G * 16 * sizeof(float));
+        }
     }
     p->bytes = off;
     return SSM_OK;
@@ -157,11 +166,11 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
     a.softplus = softplus_flag != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
-    a.bc = reinterpret_cast<float *>(ws + p.off_bc);
+    if (!p.quad) a.bc = reinterpret_cast<float *>(ws + p.off_bc);
     if (p.J > 1) {
         a.hend = reinterpret_cast<float *>(ws + p.off_hend);
-        a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
+        if (!p.fold) a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
     }
     a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
     a.ev_end = static_cast<hipEvent_t>(desc->profile_end);

@@ -457,36 +457,47 @@ __global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
 // transposing butterfly of v_permlane16_swap / v_permlane32_swap (3 swaps and
 // 3 adds): afterwards row q holds the full sum for token q of the group.
 //
-// Tile: 16 channels x T tokens, T = 64 bytes / element size, so each lane
-// loads exactly one 16-byte piece per tensor per tile.  Per tile:
-//  (a) convert the lane's piece (dt = softplus(delta + bias), w = dt u,
-//      du = D u, g = silu(z)) into LDS rows padded to T + 4 floats, and the
-//      tile's B/C rows;
-//  (b) walk the tile 4 tokens per ds_read_b128 of (dt, w): B_t enters
-//      w B_t[4q + k] through DPP row_newbcast:k (lane 16q + k holds
-//      B_t[4q + k]), C_t[4q..4q+3] is one ds_read_b128;
+// Tile: 16 channels x T tokens, T = 64 bytes / element size.  B and C keep
+// their (batch, N, L) layout, so the tile's B rows (and C rows) are 16 more
+// rows of the same shape as the channel rows: every lane loads exactly one
+// 16-byte piece of each of u, delta, z, B and C per tile, one tile ahead.
+// Per tile:
+//  (a) convert the lane's pieces (dt = softplus(delta + bias), w = dt u,
+//      du = D u, g = silu(z); B and C widened to fp32, states n >= N zeroed)
+//      into LDS rows padded to T + 4 floats;
+//  (b) walk the tile 4 tokens at a time.  ds_read_b128 gives 4 tokens of
+//      dt, of w and of B[4q + (lane % 4)]; B_t[4q + k] enters w B through
+//      the DPP operand row_newbcast:k (lane 16q + k holds state 4q + k), and
+//      C[4q + k] for 4 tokens is one more ds_read_b128 per state;
 //  (c) coalesced 16-byte stores of y.
+// A FULL pass that starts inside the sequence takes its start state either
+// from the carry kernel (h_start) or, when the chunks before it are few, by
+// folding their transfer operators itself: h = exp(A sum dt) h + h_end, in
+// chunk order.
 template <class IO, bool FULL, bool VEC>
 __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using S = Seg<IO>;
+    using V = typename S::V;
     constexpr int VW = S::VW;
     constexpr int T = 4 * VW;                       // 64 bytes of a row per tile
     constexpr int TP = T + 4;
     constexpr int QC = 16;                          // channels per wavefront
-    constexpr int BCQ = T * 32 / 4 / kWave;         // float4 of B/C rows per lane and tile
     // Separate LDS objects, so that the compiler sees that the y written by
-    // one token group (into s_du, in place) never aliases the dt, w and B/C
+    // one token group (into s_du, in place) never aliases the dt, w, B and C
     // read by the next group, and can issue those reads early.
     __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
     __shared__ __attribute__((aligned(16))) float s_w[QC * TP];
     __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];   // D u, then y
     __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];    // silu(z)
-    __shared__ __attribute__((aligned(16))) float s_bc[T * 32];              // B_t(16) C_t(16)
+    __shared__ __attribute__((aligned(16))) float s_B[16 * TP];              // state-major
+    __shared__ __attribute__((aligned(16))) float s_C[FULL ? 16 * TP : 4];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
     const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    const IT *__restrict__ Bm = static_cast<const IT *>(a.B);
+    const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
     IT *__restrict__ y = static_cast<IT *>(a.y);
 
     const int lane = threadIdx.x;
@@ -501,9 +512,9 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const int64_t t_begin = j * a.K;
     const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
     const bool gate = a.z != nullptr;
-    const float *__restrict__ bcb = a.bc + static_cast<size_t>(b) * L * 32;
 
-    // ---- this lane's tile piece: row r, tokens [sc, sc + VW) of the tile
+    // ---- this lane's tile pieces: row r (channel d0 + r, and state r of B
+    // and C), tokens [sc, sc + VW) of the tile
     const int r = lane >> 2;
     const int sc = (lane & 3) * VW;
     const int64_t dr = d0 + r;
@@ -513,29 +524,21 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
     const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
     const float rD = (row_ok && a.Dskip) ? a.Dskip[drc] : 0.0f;
+    const bool st_ok = r < a.N;
+    const size_t sbase = (static_cast<size_t>(b) * a.N + (st_ok ? r : a.N - 1)) * L;
 
-    // Prefetched tile registers: named scalars and vectors only (no arrays or
-    // aggregates carried around the loop), so that they stay in VGPRs.
-    static_assert(BCQ >= 1 && BCQ <= 4, "B/C pieces per lane");
-    using V = typename S::V;
-    V vu{}, vd{}, vz{};
-    float4 b0{}, b1{}, b2{}, b3{};
-    // token offsets inside a row fit in 32 bits (the plan bounds L)
-    const int Lm1 = static_cast<int>(L - 1);
-    auto load_bc = [&](int64_t t0, int k) {
-        const int idx = k * kWave + lane;           // float4 index within the tile
-        const int tt = static_cast<int>(t0) + idx / 8;
-        const int tc = tt < Lm1 ? tt : Lm1;         // rows past L are never used
-        return *reinterpret_cast<const float4 *>(bcb + tc * 32 + (idx & 7) * 4);
-    };
+    // Prefetched tile registers: named vectors only (no arrays or aggregates
+    // carried around the loop), so that they stay in VGPRs.
+    V vu{}, vd{}, vz{}, vb{}, vc{};
     // element path: VW scalar loads per tensor, packed into the same vector
-    // registers as the 16-byte path
-    auto load_elems = [&](const IT *p, int64_t t) {
+    // registers as the 16-byte path; tokens past the chunk are clamped to its
+    // last token (their values are never used)
+    auto load_elems = [&](const IT *p, size_t base, int64_t t) {
         float e[VW];
 #pragma unroll
         for (int i = 0; i < VW; ++i) {
             const int64_t tc = t + i < t_end ? t + i : t_end - 1;
-            e[i] = IO::load(p, rbase + tc);
+            e[i] = IO::load(p, base + tc);
         }
         return S::pack(e);
     };
@@ -546,15 +549,15 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
             vu = *reinterpret_cast<const V *>(u + rbase + tc);
             vd = *reinterpret_cast<const V *>(dl + rbase + tc);
             if (FULL && gate) vz = *reinterpret_cast<const V *>(z + rbase + tc);
+            vb = *reinterpret_cast<const V *>(Bm + sbase + tc);
+            if (FULL) vc = *reinterpret_cast<const V *>(Cm + sbase + tc);
         } else {
-            vu = load_elems(u, t);
-            vd = load_elems(dl, t);
-            if (FULL && gate) vz = load_elems(z, t);
+            vu = load_elems(u, rbase, t);
+            vd = load_elems(dl, rbase, t);
+            if (FULL && gate) vz = load_elems(z, rbase, t);
+            vb = load_elems(Bm, sbase, t);
+            if (FULL) vc = load_elems(Cm, sbase, t);
         }
-        b0 = load_bc(t0, 0);
-        if constexpr (BCQ > 1) b1 = load_bc(t0, 1);
-        if constexpr (BCQ > 2) b2 = load_bc(t0, 2);
-        if constexpr (BCQ > 3) b3 = load_bc(t0, 3);
     };
 
     // ---- per-lane constants and initial state
@@ -567,17 +570,31 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
     }
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const size_t cd = (static_cast<size_t>(b) * a.D + dcl) * a.J + j;
-    if (FULL && a.J > 1 && j > 0) {
-        const float4 v = *reinterpret_cast<const float4 *>(a.hstart + cd * 16 + 4 * q);
-        h[0] = lane_ok ? v.x : 0.0f; h[1] = lane_ok ? v.y : 0.0f;
-        h[2] = lane_ok ? v.z : 0.0f; h[3] = lane_ok ? v.w : 0.0f;
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;   // chunk 0 of this channel
+    const size_t cd = cd0 + j;
+    load_tile(t_begin);
+    if (FULL && j > 0) {
+        if (a.hstart) {
+            const float4 v = *reinterpret_cast<const float4 *>(a.hstart + cd * 16 + 4 * q);
+            h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+        } else {
+            // fold the transfer operators of chunks 0 .. j-1 in order
+            for (int64_t i = 0; i < j; ++i) {
+                const float sdt = a.dtsum[cd0 + i];
+                const float4 v = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * 16 + 4 * q);
+                h[0] = __builtin_fmaf(exp2_hw(A2[0] * sdt), h[0], v.x);
+                h[1] = __builtin_fmaf(exp2_hw(A2[1] * sdt), h[1], v.y);
+                h[2] = __builtin_fmaf(exp2_hw(A2[2] * sdt), h[2], v.z);
+                h[3] = __builtin_fmaf(exp2_hw(A2[3] * sdt), h[3], v.w);
+            }
+        }
+        // padded channels carry no state (their A is zeroed, B is not)
+        if (!lane_ok) h[0] = h[1] = h[2] = h[3] = 0.0f;
     }
     float dt_sum = 0.0f;
 
-    load_tile(t_begin);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-        // (a) convert this lane's piece, write it and the B/C rows to LDS
+        // (a) convert this lane's pieces and write them to LDS
         auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
             constexpr bool SP = decltype(sp_tag)::value;
             constexpr bool GT = decltype(gate_tag)::value;
@@ -629,45 +646,65 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
                 if (FULL && gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
             }
         }
-        *reinterpret_cast<float4 *>(&s_bc[(0 * kWave + lane) * 4]) = b0;
-        if constexpr (BCQ > 1) *reinterpret_cast<float4 *>(&s_bc[(1 * kWave + lane) * 4]) = b1;
-        if constexpr (BCQ > 2) *reinterpret_cast<float4 *>(&s_bc[(2 * kWave + lane) * 4]) = b2;
-        if constexpr (BCQ > 3) *reinterpret_cast<float4 *>(&s_bc[(3 * kWave + lane) * 4]) = b3;
+        {
+            // B and C rows: state r; states n >= N are zero
+            float xb[VW], xc[VW];
+            S::unpack(vb, xb);
+            if (FULL) S::unpack(vc, xc);
+            const int o = r * TP + sc;
+#pragma unroll
+            for (int i = 0; i < VW; i += 4) {
+                *reinterpret_cast<float4 *>(&s_B[o + i]) =
+                    st_ok ? make_float4(xb[i], xb[i + 1], xb[i + 2], xb[i + 3])
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (FULL)
+                    *reinterpret_cast<float4 *>(&s_C[o + i]) =
+                        st_ok ? make_float4(xc[i], xc[i + 1], xc[i + 2], xc[i + 3])
+                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
         // Unconditional prefetch (addresses are clamped into range): the same
         // number of loads on every path keeps the wait counts exact.
         load_tile(t0 + T);
         __syncthreads();
 
         // (b) the recurrence, 4 tokens per group.  The whole tile is one
-        // straight-line block (tokens past the chunk end are no-ops), so the
-        // LDS reads of a group can be issued under the previous group's math.
+        // straight-line block (tokens past the chunk end are no-ops: dt = 0,
+        // w = 0), so the LDS reads of a group can be issued under the
+        // previous group's math.
         const int rowc = c * TP;
-        const int bsel = 4 * q + (lane & 3);       // B row-replication index
-        float Bn = s_bc[bsel];
-        float4 Cn = FULL ? *reinterpret_cast<const float4 *>(&s_bc[16 + 4 * q])
-                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const int brow = (4 * q + (lane & 3)) * TP;   // B row-replication source
+        const int crow = 4 * q * TP;
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
             const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
             const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[rowc + c4]);
+            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[brow + c4]);
+            float4 C0{}, C1{}, C2{}, C3{};
+            if (FULL) {
+                C0 = *reinterpret_cast<const float4 *>(&s_C[crow + c4]);
+                C1 = *reinterpret_cast<const float4 *>(&s_C[crow + TP + c4]);
+                C2 = *reinterpret_cast<const float4 *>(&s_C[crow + 2 * TP + c4]);
+                C3 = *reinterpret_cast<const float4 *>(&s_C[crow + 3 * TP + c4]);
+            }
             const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
             const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+            const float c0[4] = {C0.x, C0.y, C0.z, C0.w};
+            const float c1[4] = {C1.x, C1.y, C1.z, C1.w};
+            const float c2[4] = {C2.x, C2.y, C2.z, C2.w};
+            const float c3[4] = {C3.x, C3.y, C3.z, C3.w};
             float accv[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float Bc = Bn;
-                const float4 Cc = Cn;
-                const int tn = c4 + k + 1 < T ? c4 + k + 1 : c4 + k;   // stays inside the tile
-                Bn = s_bc[tn * 32 + bsel];
-                if (FULL) Cn = *reinterpret_cast<const float4 *>(&s_bc[tn * 32 + 16 + 4 * q]);
-                const float dt = dtv[k], w = wv[k];
-                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bc) * w);
-                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bc) * w);
-                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bc) * w);
-                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bc) * w);
+                const float dt = dtv[k], w = wv[k], Bk = bv[k];
+                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
+                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
+                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
+                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
                 if (FULL)
-                    accv[k] = __builtin_fmaf(Cc.x, h[0], __builtin_fmaf(Cc.y, h[1],
-                              __builtin_fmaf(Cc.z, h[2], Cc.w * h[3])));
+                    accv[k] = __builtin_fmaf(c0[k], h[0], __builtin_fmaf(c1[k], h[1],
+                              __builtin_fmaf(c2[k], h[2], c3[k] * h[3])));
                 else
                     dt_sum += dt;
             }
@@ -846,9 +883,11 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
         hipLaunchKernelGGL((quad_kernel<IO, false, VEC>), agrid, dim3(64), 0, s, a);
-        const int64_t waves = a.Bsz * a.D;
-        hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0,
-                           s, a);
+        if (a.hstart) {   // otherwise every chunk folds its predecessors itself
+            const int64_t waves = a.Bsz * a.D;
+            hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
+                               dim3(256), 0, s, a);
+        }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
     hipLaunchKernelGGL((quad_kernel<IO, true, VEC>), grid, dim3(64), 0, s, a);
@@ -858,16 +897,17 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
 
 template <class IO>
 static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
+    if (a.quad) {
+        constexpr int VW = Seg<IO>::VW;
+        auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+        const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) &&
+                         (!a.z || al(a.z)) && al(a.B) && al(a.C);
+        return vec ? launch_quad<IO, true>(a, s) : launch_quad<IO, false>(a, s);
+    }
     const dim3 pgrid(static_cast<unsigned>((a.L + 63) / 64 * a.G * a.Bsz));
     hipLaunchKernelGGL(bc_pack_kernel<IO>, pgrid, dim3(256), 0, s,
                        static_cast<const typename IO::T *>(a.B),
                        static_cast<const typename IO::T *>(a.C), a.bc, a.L, a.N, a.G);
-    if (a.quad) {
-        constexpr int VW = Seg<IO>::VW;
-        auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-        const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z));
-        return vec ? launch_quad<IO, true>(a, s) : launch_quad<IO, false>(a, s);
-    }
     switch (a.G) {   // the plan pads G to a power of two
         case 1: return launch_chunks_vec<IO, 1>(a, s);
         case 2: return launch_chunks_vec<IO, 2>(a, s);

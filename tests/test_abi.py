@@ -51,27 +51,41 @@ def desc(**kw):
     return ssm.make_desc(**base)
 
 
+def _al(x):
+    return -(-x // 256) * 256
+
+
 def test_workspace_and_chunk_plan(lib):
+    # desc(): batch 2, d_inner 64, N 16, L 2048 -> the d_state <= 16 path,
+    # which reads B and C in place (no packed copy) and, with at most 32
+    # chunks, folds the chunk operators in the scan pass (no start states)
     d = desc()
     K = lib.ssm_scan_chunk_size(ctypes.byref(d))
     assert 16 <= K <= 2048 and (K % 16 == 0 or K == 2048)
     J = -(-2048 // K)
     need = lib.ssm_scan_workspace_bytes(ctypes.byref(d))
-    packed = 2 * 2048 * 1 * 32 * 4
-    assert need >= packed
-    if J > 1:
-        assert need >= packed + 2 * (2 * 64 * J * 16 * 4) + 2 * 64 * J * 4
+    ops = _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4)
+    assert need == (ops if J > 1 else 0)
     for k in (16, 256, 1024):
         d = desc(chunk_size=k)
         assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == k
+    # more than 32 chunks: start states come from the carry kernel
+    d = desc(chunk_size=16)
+    J = 2048 // 16
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == (
+        2 * _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4))
     d = desc(chunk_size=4096)
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048     # one chunk
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
     d = desc(batch=8, d_inner=5120 * 4)                         # enough channels
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048
-    # state groups are padded to a power of two of 16-state groups
-    for N, G in ((1, 1), (16, 1), (17, 2), (33, 4), (100, 8), (256, 16)):
+    # d_state > 16: packed B/C rows, state groups padded to a power of two
+    for N, G in ((17, 2), (33, 4), (100, 8), (256, 16)):
         d = desc(d_state=N, chunk_size=2048)
         assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 2 * 2048 * G * 32 * 4
+    for N in (1, 16):
+        d = desc(d_state=N, chunk_size=2048)
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -89,7 +103,7 @@ def test_invalid_descriptors(lib, kw, status):
 
 
 def test_null_and_misaligned_arguments(lib):
-    d = desc(chunk_size=2048)
+    d = desc(chunk_size=256)                # 8 chunks: needs a workspace
     d.workspace, d.workspace_bytes = 4096, 1 << 30
     ok = 4096
     args = [ok, ok, ok, ok, ok, None, None, None, 1, ok, None, None]

@@ -26,13 +26,13 @@ bool dims_ok(int64_t a, int64_t b, int64_t c) {
 }
 
 struct Plan {
-    int G = 1;            // state groups of 16 per channel, padded to a power of two
+    int G = 1;            // groups of 16 states in a padded state row
     int64_t K = 0;        // chunk length
     int64_t J = 1;        // chunks
-    int64_t n_cblk = 0;   // channel blocks per batch row (16 channels when quad, else 64)
+    int64_t n_cblk = 0;   // blocks of 16 channels per batch row
     int quad = 0;         // d_state <= 16: quad-row kernel
     int fold = 0;         // chunks fold their predecessors' operators (no carry kernel)
-    size_t off_bc = 0, off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
+    size_t off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
 };
 
 ssm_status check_desc(const ssm_desc *d) {
@@ -61,13 +61,12 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     if (d->chunk_size < 0 || (d->chunk_size > 0 && d->chunk_size % 16 != 0))
         return SSM_ERR_BAD_SHAPE;
     const int64_t L = d->seqlen;
-    int groups = static_cast<int>((d->d_state + 15) / 16);
-    int G = 1;
-    while (G < groups) G <<= 1;
-    p->G = G;
     p->quad = d->d_state <= 16;
-    const int64_t cb = p->quad ? 16 : 64;
-    p->n_cblk = (d->d_inner + cb - 1) / cb;
+    int GW = 1;   // wavefronts of 32 states (group_kernel), a power of two
+    while (32 * GW < d->d_state) GW <<= 1;
+    const int G = p->quad ? 1 : 2 * GW;
+    p->G = G;
+    p->n_cblk = (d->d_inner + 15) / 16;
     if (L == 0 || d->batch * d->d_inner == 0) {
         p->K = L; p->J = L > 0 ? 1 : 0; p->bytes = 0;
         return SSM_OK;
@@ -76,7 +75,7 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     if (d->chunk_size > 0) {
         K = d->chunk_size;
     } else {
-        const int64_t waves = d->batch * p->n_cblk * (p->quad ? 1 : G);
+        const int64_t waves = d->batch * p->n_cblk * (p->quad ? 1 : GW);
         K = L;
         if (waves < kEnoughWaves) {
             const int64_t J = (kTargetWaves + waves - 1) / waves;
@@ -91,12 +90,10 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     p->J = (L + K - 1) / K;
     if (p->J > kMaxGridY) return SSM_ERR_UNSUPPORTED;
     if (p->n_cblk * d->batch > static_cast<int64_t>(UINT_MAX)) return SSM_ERR_UNSUPPORTED;
-    p->fold = p->quad && p->J <= kFoldMaxChunks;
-    // workspace layout: packed B/C rows (chunk_kernel only), then the chunk
-    // operators and, without folding, the chunk start states
+    p->fold = p->J <= kFoldMaxChunks;
+    // workspace layout: the chunk operators and, without folding, the chunk
+    // start states; rows of G * 16 floats per (batch, channel, chunk)
     size_t off = 0;
-    p->off_bc = off;
-    if (!p->quad) off += align_up(static_cast<size_t>(d->batch) * L * G * 32 * sizeof(float));
     if (p->J > 1) {
         const size_t cj = static_cast<size_t>(d->batch) * d->d_inner * p->J;
         p->off_hend = off;
@@ -166,7 +163,6 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
     a.softplus = softplus_flag != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
-    if (!p.quad) a.bc = reinterpret_cast<float *>(ws + p.off_bc);
     if (p.J > 1) {
         a.hend = reinterpret_cast<float *>(ws + p.off_hend);
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);

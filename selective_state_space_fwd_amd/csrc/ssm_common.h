@@ -10,7 +10,7 @@ namespace ssm {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;       // CDNA wavefront
-constexpr int kGroup = 16;      // states held per lane (one state group)
+constexpr int kGroup = 16;      // states per group in the chunk-operator rows
 
 // ---------------------------------------------------------------- I/O types
 // float32 or bfloat16 (raw bits); arithmetic is always float32.

@@ -10,9 +10,10 @@ namespace ssm {
 // Everything a prefill scan launch needs; built and validated by ssm_api.
 struct ScanArgs {
     int64_t Bsz, D, N, L;       // batch, d_inner, d_state, seqlen
-    int G;                      // state groups of 16 per channel (power of two)
-    int64_t K, J, n_cblk;       // chunk length, chunk count, channel blocks per batch row
-    int quad;                   // 1: d_state <= 16 path, 16-channel blocks (quad_kernel)
+    int G;                      // groups of 16 states in a padded state row (power of two):
+                                // 1 for quad_kernel, 2 x its wavefronts for group_kernel
+    int64_t K, J, n_cblk;       // chunk length, chunk count, 16-channel blocks per batch row
+    int quad;                   // 1: d_state <= 16 path (quad_kernel), else group_kernel
     int bf16;                   // io dtype
     int softplus;
     const void *u, *delta, *z, *B, *C;
@@ -20,7 +21,6 @@ struct ScanArgs {
     const float *A, *Dskip, *delta_bias;
     float *last_state;
     // workspace views
-    float *bc;                  // (batch, L, G, 32) packed B/C rows
     float *hend;                // (batch, d_inner, J, G*16) chunk end states from zero
     float *dtsum;               // (batch, d_inner, J) sum of step sizes per chunk
     float *hstart;              // (batch, d_inner, J, G*16) chunk start states

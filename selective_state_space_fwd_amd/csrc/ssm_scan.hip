@@ -12,16 +12,18 @@
 //
 // Mapping on CDNA4.  Because A is diagonal, every (channel, state) pair runs
 // the recurrence h = exp(dt A) h + dt B u serially over its tokens, in a VGPR
-// of one lane: no per-token scan work.  Two kernels share that core:
-//   quad_kernel   (d_state <= 16) one wavefront = 16 channels x 4 lane-rows,
-//                 4 states per lane; the row-partials of C.h are summed with
-//                 cross-lane permutes;
-//   chunk_kernel  (d_state > 16) one lane = one channel and one group of 16
-//                 states, a wavefront = 64 channels of one group, a workgroup
-//                 = the G = ceil(N/16) groups of those channels, whose partial
-//                 C.h are summed in LDS in a fixed order.
-// When channels are too few to fill 256 CUs, the sequence is also cut into
-// chunks of K tokens:
+// of one lane: no per-token scan work.  Two kernels share that core; both
+// give a wavefront 16 channels in 4 lane-rows of 16 lanes:
+//   quad_kernel   (d_state <= 16) 4 states per lane, one wavefront per block
+//                 of 16 channels;
+//   group_kernel  (16 < d_state <= 256) 8 states per lane, so 32 states per
+//                 wavefront and G = ceil(N/32) wavefronts per workgroup, whose
+//                 partial C.h are summed in LDS in a fixed order.
+// The row-partials of C.h inside a wavefront are summed with cross-lane
+// permutes.  B and C are shared by all channels of a batch row; they are read
+// in place, as 16 (or 32 G) more rows of the tile, and kept state-major in
+// LDS.  When channels are too few to fill 256 CUs, the sequence is also cut
+// into chunks of K tokens:
 //   pass 1 (<FULL = false>)      every chunk but the last runs from a zero
 //                                state; it publishes its transfer operator
 //                                (sum of dt, h_end): A_chunk = exp(A sum dt),
@@ -29,78 +31,17 @@
 //   pass 2 (carry_kernel)        an exclusive scan of the operators with the
 //                                associative composition
 //                                (a2,b2) o (a1,b1) = (a1 a2, a2 b1 + b2),
-//                                lanes along chunks, wave64 DPP steps;
+//                                lanes along chunks, wave64 DPP steps -- or,
+//                                when the chunks are few, each chunk of
+//                                pass 3 folds its predecessors itself;
 //   pass 3 (<FULL = true>)       every chunk re-runs from its h_start and
 //                                writes y (and the last chunk, last_state).
-// B and C are shared by all channels of a batch row.  A pre-pass repacks them
-// as fp32 rows [B_t(16) C_t(16)] per (b, t, group), so a tile's B/C is one
-// contiguous piece that the wavefront stages in LDS; u, delta and z
-// (L-contiguous rows) are loaded with coalesced 16-byte loads, converted and
-// staged through LDS, and read back one row per lane.
 #include <type_traits>
 
 #include "ssm_common.h"
 #include "ssm_launch.h"
 
 namespace ssm {
-
-// ============================================================ B/C repack
-// bc[((b*G + g)*L + t)*32 + k]: k < 16 -> B[b, 16g+k, t], else C[b, 16g+k-16, t];
-// states n >= N are zero.  A group's rows are contiguous along t, so a tile of
-// T tokens is one contiguous 128*T-byte piece.  Grid ceil(L/64) * G * batch
-// (1-D), 256 threads.
-template <class IO>
-__global__ __launch_bounds__(256) void bc_pack_kernel(const typename IO::T *__restrict__ Bm,
-                                                      const typename IO::T *__restrict__ Cm,
-                                                      float *__restrict__ bc, int64_t L, int N,
-                                                      int G) {
-    __shared__ float tile[32][65];
-    const int64_t tiles = (L + 63) / 64;
-    const int64_t blk = blockIdx.x;
-    const int g = static_cast<int>((blk / tiles) % G);
-    const int64_t b = blk / (tiles * G);
-    const int64_t t0 = (blk % tiles) * 64;
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
-        const int k = idx >> 6, tt = idx & 63;
-        const int n = g * kGroup + (k & 15);
-        const int64_t t = t0 + tt;
-        float v = 0.0f;
-        if (n < N && t < L) {
-            const size_t off = (static_cast<size_t>(b) * N + n) * L + t;
-            v = k < 16 ? IO::load(Bm, off) : IO::load(Cm, off);
-        }
-        tile[k][tt] = v;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
-        const int tt = idx >> 5, k = idx & 31;
-        const int64_t t = t0 + tt;
-        if (t < L) bc[((static_cast<size_t>(b) * G + g) * L + t) * 32 + k] = tile[k][tt];
-    }
-}
-
-// ============================================================ chunk kernel
-// Grid (n_cblk * batch, chunks); block 64*G threads (wavefront g = state group g).
-// Tokens of chunk j: [j*K, min((j+1)*K, L)).
-//
-// The chunk is walked in tiles of T tokens x 64 channels.  Everything the
-// recurrence reads during a tile sits in LDS, so the token loop waits on LDS
-// only (LDS results return in order; a scalar load in flight would force
-// every LDS wait to drain it).  Per tile:
-//  (a) the tile's raw u, delta, z and its packed B/C rows, loaded one tile
-//      ahead with 16-byte vector loads (consecutive lanes on consecutive
-//      16-byte pieces of a row), are turned into dt = softplus(delta + bias),
-//      w = dt u, du = D u, g = silu(z) and written to LDS.  Channel rows are
-//      padded to T + 4 floats: 16-byte aligned, and the 8 rows read by one
-//      ds_read_b128 pass land on distinct banks;
-//  (b) each lane walks its channel's row, 4 tokens per ds_read_b128 of
-//      (dt, w).  B_t is read as one VGPR replicated in every 16-lane row
-//      (lane l holds B_t[l % 16]) and enters w B_t[n] through the DPP operand
-//      row_newbcast:n, folded into v_mul_f32_dpp; C_t comes from four
-//      uniform-address ds_read_b128 broadcasts, read a token ahead.  The
-//      finished y (or the group's partial C.h) goes back to LDS;
-//  (c) y is stored with coalesced 16-byte stores.
-// Tokens past the chunk end carry dt = 0 and w = 0, so they leave h alone.
 
 template <class IO>
 struct Seg;   // one 16-byte piece of a row: VW consecutive tokens
@@ -142,309 +83,34 @@ __device__ __forceinline__ float row_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, true));
 }
 
-// One token of the recurrence for a lane's 16 states.
-//   h[n] = exp2(dt A2[n]) h[n] + w B[n];  acc[n % 4] += C[n] h[n]
-template <bool FULL, int N>
-__device__ __forceinline__ void token_step(float (&h)[kGroup], const float (&A2)[kGroup],
-                                           float dt, float w, float Bv,
-                                           const float (&Cv)[kGroup], float (&acc)[4]) {
-    if constexpr (N < kGroup) {
-        const float dA = exp2_hw(dt * A2[N]);
-        h[N] = __builtin_fmaf(dA, h[N], row_bcast<N>(Bv) * w);
-        if (FULL) acc[N & 3] = __builtin_fmaf(Cv[N], h[N], acc[N & 3]);
-        token_step<FULL, N + 1>(h, A2, dt, w, Bv, Cv, acc);
+template <class IO>
+struct Piece4;   // 4 consecutive tokens of a row: 16 bytes (fp32) or 8 bytes (bf16)
+
+template <>
+struct Piece4<F32> {
+    using V = float4;
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[4]) {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
     }
-}
-
-template <class IO, int G, int T, bool FULL, bool VEC>
-__global__ __launch_bounds__(64 * G) void chunk_kernel(ScanArgs a) {
-    using IT = typename IO::T;
-    using S = Seg<IO>;
-    constexpr int VW = S::VW;
-    static_assert(T % VW == 0 && T % 4 == 0, "tile");
-    constexpr int TP = T + 4;                       // padded LDS row
-    constexpr int NT = 64 * G;
-    constexpr int SPR = T / VW;                     // segments per row
-    constexpr int NSEG = kWave * SPR;               // segments per tile and tensor
-    constexpr int SEG = (NSEG + NT - 1) / NT;       // segments per thread
-    constexpr int NARR = FULL ? 4 : 2;
-    constexpr int BCQ = T * 32 / 4 / kWave;         // float4 of B/C rows per lane and tile
-    static_assert(BCQ * 4 * kWave == T * 32, "B/C tile");
-    __shared__ __attribute__((aligned(16))) float s_x[NARR][kWave * TP];  // dt, w, du, g
-    __shared__ __attribute__((aligned(16))) float s_bc[G][T * 32];        // B_t(16) C_t(16)
-    __shared__ __attribute__((aligned(16))) float s_y[G > 1 ? G * kWave * TP : 4];
-
-    const IT *__restrict__ u = static_cast<const IT *>(a.u);
-    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
-    const IT *__restrict__ z = static_cast<const IT *>(a.z);
-    IT *__restrict__ y = static_cast<IT *>(a.y);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t b = blockIdx.x / a.n_cblk;
-    const int64_t j = blockIdx.y;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * kWave;
-    const bool rows_full = d0 + kWave <= a.D;       // workgroup-uniform
-    const int64_t d = d0 + lane;
-    const bool lane_ok = d < a.D;
-    const int64_t L = a.L;
-    const int64_t t_begin = j * a.K;
-    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
-    const int Npad = G * kGroup;
-    const bool gate = a.z != nullptr;
-    const float *__restrict__ bcg = a.bc + (static_cast<size_t>(b) * G + g) * L * 32;
-
-    // ---- this thread's tile segments: fixed rows, per-row constants.
-    // Loads use addresses clamped into the valid range and are zeroed by
-    // select, so the load path has no divergent branches.
-    int seg_row[SEG], seg_col[SEG];
-    bool seg_rv[SEG];                               // segment exists and its row < d_inner
-    size_t seg_base[SEG];                           // element offset of the row start
-    float seg_bias[SEG], seg_D[SEG];
-#pragma unroll
-    for (int e = 0; e < SEG; ++e) {
-        const int sidx = e * NT + tid;
-        const bool on = sidx < NSEG;
-        seg_row[e] = on ? sidx / SPR : 0;
-        seg_col[e] = on ? (sidx % SPR) * VW : 0;
-        const int64_t dd = d0 + seg_row[e];
-        seg_rv[e] = on && dd < a.D;
-        const int64_t dc = dd < a.D ? dd : a.D - 1;
-        seg_base[e] = (static_cast<size_t>(b) * a.D + dc) * L;
-        seg_bias[e] = (seg_rv[e] && a.delta_bias) ? a.delta_bias[dc] : 0.0f;
-        seg_D[e] = (seg_rv[e] && a.Dskip) ? a.Dskip[dc] : 0.0f;
+    static __device__ __forceinline__ V pack(const float (&o)[4]) {
+        return make_float4(o[0], o[1], o[2], o[3]);
     }
+};
 
-    // raw tile registers (prefetched one tile ahead)
-    typename S::V vu[SEG], vd[SEG], vz[SEG];        // VEC path
-    float ru[SEG][VW], rd[SEG][VW], rz[SEG][VW];    // element path
-    float4 vbc[BCQ];                                // this wavefront's B/C rows of the tile
-    auto load_tile = [&](int64_t t0) {
-#pragma unroll
-        for (int e = 0; e < SEG; ++e) {
-            const int64_t t = t0 + seg_col[e];
-            if (VEC) {
-                const int64_t tl = t < t_end ? t : t_end - VW;   // t_end >= VW here
-                const size_t off = seg_base[e] + tl;
-                vu[e] = *reinterpret_cast<const typename S::V *>(u + off);
-                vd[e] = *reinterpret_cast<const typename S::V *>(dl + off);
-                if (FULL && gate) vz[e] = *reinterpret_cast<const typename S::V *>(z + off);
-            } else {
-#pragma unroll
-                for (int i = 0; i < VW; ++i) {
-                    const int64_t tl = t + i < t_end ? t + i : t_end - 1;
-                    const size_t off = seg_base[e] + tl;
-                    ru[e][i] = IO::load(u, off);
-                    rd[e][i] = IO::load(dl, off);
-                    rz[e][i] = (FULL && gate) ? IO::load(z, off) : 0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < BCQ; ++q) {
-            const int idx = q * kWave + lane;       // float4 index within the tile
-            const int64_t t = t0 + idx / 8;
-            const int64_t tc = t < L ? t : L - 1;   // rows past L are never used
-            vbc[q] = *reinterpret_cast<const float4 *>(bcg + tc * 32 + (idx & 7) * 4);
-        }
-    };
-
-    // ---- per-lane constants and initial state (unconditional loads from
-    //      clamped indices, then select: no per-load branches)
-    const int64_t dcl = lane_ok ? d : a.D - 1;
-    float A2[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-        const int n = g * kGroup + i;
-        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
-        A2[i] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
+template <>
+struct Piece4<BF16> {
+    using V = uint2;
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[4]) {
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
     }
-    float h[kGroup];
-    const size_t cd = (static_cast<size_t>(b) * a.D + dcl) * a.J + j;
-    if (FULL && a.J > 1 && j > 0) {
-        const float *hs = a.hstart + cd * Npad + g * kGroup;
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-            const float v = hs[i];
-            h[i] = lane_ok ? v : 0.0f;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) h[i] = 0.0f;
+    static __device__ __forceinline__ V pack(const float (&o)[4]) {
+        // only ever packs values that were read from bf16 storage: exact
+        return make_uint2((__float_as_uint(o[0]) >> 16) | (__float_as_uint(o[1]) & 0xffff0000u),
+                          (__float_as_uint(o[2]) >> 16) | (__float_as_uint(o[3]) & 0xffff0000u));
     }
-    float dt_sum = 0.0f;
-    const float *sbc = &s_bc[g][0];
+};
 
-    load_tile(t_begin);
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-        // (a) convert the prefetched tile and write it to LDS.  The softplus
-        //     and gate flags are hoisted out of the element loops.
-        auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
-            constexpr bool SP = decltype(sp_tag)::value;
-            constexpr bool GT = decltype(gate_tag)::value;
-            constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-            for (int e = 0; e < SEG; ++e) {
-                if (e * NT + tid >= NSEG) continue;  // compile-time false when SEG*NT == NSEG
-                float xu[VW], xd[VW], xz[VW];
-                if (VEC) {
-                    S::unpack(vu[e], xu);
-                    S::unpack(vd[e], xd);
-                    if (FULL && GT) S::unpack(vz[e], xz);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VW; ++i) {
-                        xu[i] = ru[e][i];
-                        xd[i] = rd[e][i];
-                        xz[i] = rz[e][i];
-                    }
-                }
-                float xdt[VW], xw[VW], xdu[VW], xg[VW];
-#pragma unroll
-                for (int i = 0; i < VW; ++i) {
-                    // branch-free: evaluate for every lane, zero by a 0/1 factor
-                    // (only the last tile of a chunk or block needs the mask)
-                    const float m = !MASK || (seg_rv[e] && t0 + seg_col[e] + i < t_end) ? 1.0f : 0.0f;
-                    const bool ok = !MASK || m != 0.0f;
-                    const float x = xd[i] + seg_bias[e];
-                    const float dt = MASK ? (SP ? softplus_f32(x) : x) * m : (SP ? softplus_f32(x) : x);
-                    const float uu = ok ? xu[i] : 0.0f;
-                    xdt[i] = dt;
-                    xw[i] = dt * uu;
-                    if (FULL) {
-                        xdu[i] = seg_D[e] * uu;
-                        xg[i] = GT ? silu_f32(ok ? xz[i] : 0.0f) : 1.0f;
-                    }
-                }
-                const int o = seg_row[e] * TP + seg_col[e];
-#pragma unroll
-                for (int q = 0; q < VW; q += 4) {
-                    *reinterpret_cast<float4 *>(&s_x[0][o + q]) = make_float4(xdt[q], xdt[q + 1], xdt[q + 2], xdt[q + 3]);
-                    *reinterpret_cast<float4 *>(&s_x[1][o + q]) = make_float4(xw[q], xw[q + 1], xw[q + 2], xw[q + 3]);
-                    if (FULL) {
-                        *reinterpret_cast<float4 *>(&s_x[2][o + q]) = make_float4(xdu[q], xdu[q + 1], xdu[q + 2], xdu[q + 3]);
-                        *reinterpret_cast<float4 *>(&s_x[3][o + q]) = make_float4(xg[q], xg[q + 1], xg[q + 2], xg[q + 3]);
-                    }
-                }
-            }
-        };
-        using T_ = std::true_type;
-        using F_ = std::false_type;
-        if (rows_full && t0 + T <= t_end) {
-            if (a.softplus) {
-                if (FULL && gate) convert(T_{}, T_{}, F_{}); else convert(T_{}, F_{}, F_{});
-            } else {
-                if (FULL && gate) convert(F_{}, T_{}, F_{}); else convert(F_{}, F_{}, F_{});
-            }
-        } else {
-            if (a.softplus) {
-                if (FULL && gate) convert(T_{}, T_{}, T_{}); else convert(T_{}, F_{}, T_{});
-            } else {
-                if (FULL && gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < BCQ; ++q)
-            *reinterpret_cast<float4 *>(&s_bc[g][(q * kWave + lane) * 4]) = vbc[q];
-        // Unconditional prefetch (addresses are clamped into range): the same
-        // number of loads on every path keeps the wait counts exact, so the
-        // next tile's loads are waited on without draining this tile's stores.
-        load_tile(t0 + T);
-        __syncthreads();
-
-        // (b) the recurrence: one lane per channel, 4 tokens per LDS read of
-        //     (dt, w); B and C rows of the next token read a token ahead.
-        const int tcount = static_cast<int>(t_end - t0 < T ? t_end - t0 : T);
-        const int row = lane * TP;
-        float Bn = sbc[lane & 15];
-        float Cn[kGroup];
-        if (FULL) {
-#pragma unroll
-            for (int q = 0; q < kGroup; q += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(&sbc[kGroup + q]);
-                Cn[q] = v.x; Cn[q + 1] = v.y; Cn[q + 2] = v.z; Cn[q + 3] = v.w;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < T; c += 4) {
-            if (c >= tcount) break;
-            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_x[0][row + c]);
-            const float4 w4 = *reinterpret_cast<const float4 *>(&s_x[1][row + c]);
-            const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
-            const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-            float yv[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float Bc = Bn;
-                float Cc[kGroup];
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i) Cc[i] = Cn[i];
-                const int tn = c + k + 1 < T ? c + k + 1 : c + k;   // stays inside the tile
-                Bn = sbc[tn * 32 + (lane & 15)];
-                if (FULL) {
-#pragma unroll
-                    for (int q = 0; q < kGroup; q += 4) {
-                        const float4 v = *reinterpret_cast<const float4 *>(&sbc[tn * 32 + kGroup + q]);
-                        Cn[q] = v.x; Cn[q + 1] = v.y; Cn[q + 2] = v.z; Cn[q + 3] = v.w;
-                    }
-                }
-                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                token_step<FULL, 0>(h, A2, dtv[k], wv[k], Bc, Cc, acc);
-                yv[k] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                if (!FULL) dt_sum += dtv[k];
-            }
-            if (FULL) {
-                float *dst = G == 1 ? &s_x[0][row + c] : &s_y[(g * kWave + lane) * TP + c];
-                *reinterpret_cast<float4 *>(dst) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-            }
-        }
-
-        // (c) store y: sum of group partials in a fixed order, skip term, gate
-        if (FULL) {
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < SEG; ++e) {
-                if (e * NT + tid >= NSEG) continue;
-                const int64_t t = t0 + seg_col[e];
-                const int o = seg_row[e] * TP + seg_col[e];
-                float yo[VW];
-#pragma unroll
-                for (int i = 0; i < VW; ++i) {
-                    float acc = G == 1 ? s_x[0][o + i] : s_y[o + i];
-#pragma unroll
-                    for (int gg = 1; gg < G; ++gg) acc += s_y[gg * kWave * TP + o + i];
-                    yo[i] = (acc + s_x[2][o + i]) * s_x[3][o + i];
-                }
-                const size_t off = seg_base[e] + t;
-                if (VEC) {
-                    if (seg_rv[e] && t < t_end)
-                        *reinterpret_cast<typename S::V *>(y + off) = S::pack(yo);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VW; ++i)
-                        if (seg_rv[e] && t + i < t_end) IO::store(y, off + i, yo[i]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    if (!lane_ok) return;
-    if (FULL) {
-        if (a.last_state && j == a.J - 1) {
-            float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                if (g * kGroup + i < a.N) ls[g * kGroup + i] = h[i];
-        }
-    } else {
-        float *he = a.hend + cd * Npad + g * kGroup;
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) he[i] = h[i];
-        if (g == 0) a.dtsum[cd] = dt_sum;
-    }
-}
 
 // ============================================================ quad-row kernel (N <= 16)
 // The path for d_state <= 16.  A wavefront covers 16 channels in 4 lane-rows:
@@ -762,6 +428,316 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     }
 }
 
+// ============================================================ group kernel (N > 16)
+// The path for 16 < d_state <= 256: the state dimension is split into groups
+// of 32 states on G wavefronts of one workgroup (the state-dimension groups
+// of the ufo.work article, §3.2), all serving the same 16 channels.  In
+// wavefront g, lane l serves channel c = l % 16 and the 8 states
+// 32g + 8q .. 32g + 8q + 7, q = l / 16, in VGPRs.
+//
+// Tile: 16 channels x 16 tokens.  Per tile:
+//  (a) the workgroup loads and converts the tile's u, delta, z (one to four
+//      consecutive tokens per thread) into dt, w = dt u, D u and silu(z) rows
+//      in LDS, and the tile's B and C rows (state-major, two 4-token pieces of
+//      each per thread, states n >= N zeroed); the next tile's values are
+//      loaded meanwhile;
+//  (b) every wavefront walks the tile 4 tokens at a time: ds_read_b128 gives
+//      4 tokens of dt, of w and of B[32g + 8q + (lane % 8)], which enters
+//      w B through the DPP operand row_newbcast:k; C for 4 tokens is one
+//      ds_read_b128 per state.  The 4 lane-rows' partial C.h are summed with
+//      the same permlane butterfly as the quad kernel, and each wavefront
+//      writes its group's partial y to LDS;
+//  (c) the partials of the G groups are added in group order (a fixed order:
+//      the result does not depend on timing), then + D u, times silu(z),
+//      and stored.
+#ifndef SSM_GROUP_WAVES_PER_SIMD
+#define SSM_GROUP_WAVES_PER_SIMD 4
+#endif
+template <class IO, int G, bool FULL, bool VEC>
+__global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel(ScanArgs a) {
+    using IT = typename IO::T;
+    using P = Piece4<IO>;
+    constexpr int T = 16;                           // tokens per tile
+    constexpr int TP = T + 4;                       // padded LDS row
+    constexpr int QC = 16;                          // channels per workgroup
+    constexpr int NS = 32 * G;                      // padded states per channel
+    constexpr int NT = 64 * G;                      // threads
+    constexpr int EPT = G >= 4 ? 1 : 4 / G;         // u/delta/z elements per thread
+    constexpr int NACT = QC * T / EPT;              // threads that hold elements
+    static_assert(NACT <= NT, "element mapping");
+    __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
+    __shared__ __attribute__((aligned(16))) float s_w[QC * TP];
+    __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];
+    __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];
+    __shared__ __attribute__((aligned(16))) float s_B[NS * TP];
+    __shared__ __attribute__((aligned(16))) float s_C[FULL ? NS * TP : 4];
+    __shared__ __attribute__((aligned(16))) float s_yp[FULL ? G * QC * TP : 4];
+
+    const IT *__restrict__ u = static_cast<const IT *>(a.u);
+    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
+    const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    const IT *__restrict__ Bm = static_cast<const IT *>(a.B);
+    const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
+    IT *__restrict__ y = static_cast<IT *>(a.y);
+
+    const int tid = threadIdx.x;
+    const int g = tid >> 6;                         // state group of this wavefront
+    const int lane = tid & 63;
+    const int c = lane & 15;
+    const int q = lane >> 4;
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t j = blockIdx.y;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * QC;
+    const int64_t d = d0 + c;
+    const bool lane_ok = d < a.D;
+    const int64_t L = a.L;
+    const int64_t t_begin = j * a.K;
+    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
+    const bool gate = a.z != nullptr;
+
+    // ---- element mapping for u, delta, z, y: row er, tokens [et, et + EPT)
+    const bool act = tid < NACT;
+    const int er = (tid * EPT) >> 4;
+    const int et = (tid * EPT) & 15;
+    const int64_t edr = d0 + (act ? er : 0);
+    const bool erow_ok = act && edr < a.D;
+    const size_t ebase = (static_cast<size_t>(b) * a.D + (edr < a.D ? edr : a.D - 1)) * L;
+    const float ebias = (erow_ok && a.delta_bias) ? a.delta_bias[edr] : 0.0f;
+    const float eD = (erow_ok && a.Dskip) ? a.Dskip[edr] : 0.0f;
+
+    // ---- B/C piece mapping: pieces tid and tid + NT of each tensor;
+    // piece p = row p / 4 (a state), tokens 4 (p % 4) .. + 3
+    const int pr0 = tid >> 2, pr1 = (tid + NT) >> 2;
+    const int ps = (tid & 3) * 4;                   // same column for both (NT % 4 == 0)
+    const bool pok0 = pr0 < a.N, pok1 = pr1 < a.N;
+    const size_t pb0 = (static_cast<size_t>(b) * a.N + (pok0 ? pr0 : a.N - 1)) * L;
+    const size_t pb1 = (static_cast<size_t>(b) * a.N + (pok1 ? pr1 : a.N - 1)) * L;
+
+    // prefetch registers (named; no arrays carried around the loop)
+    float eu0 = 0.f, eu1 = 0.f, eu2 = 0.f, eu3 = 0.f;
+    float ed0 = 0.f, ed1 = 0.f, ed2 = 0.f, ed3 = 0.f;
+    float ez0 = 0.f, ez1 = 0.f, ez2 = 0.f, ez3 = 0.f;
+    typename P::V vb0{}, vb1{}, vc0{}, vc1{};
+    auto eload = [&](const IT *p, int64_t t, int i) {
+        const int64_t tt = t + i < t_end ? t + i : t_end - 1;
+        return IO::load(p, ebase + tt);
+    };
+    auto pload = [&](const IT *p, size_t base, int64_t t) {
+        if (VEC) {
+            const int64_t tc = t < t_end ? t : t_end - 4;   // t_end >= 4 here
+            return *reinterpret_cast<const typename P::V *>(p + base + tc);
+        }
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tt = t + i < t_end ? t + i : t_end - 1;
+            e[i] = IO::load(p, base + tt);
+        }
+        return P::pack(e);
+    };
+    auto load_tile = [&](int64_t t0) {
+        if (act) {
+            const int64_t t = t0 + et;
+            eu0 = eload(u, t, 0); ed0 = eload(dl, t, 0);
+            if (EPT > 1) { eu1 = eload(u, t, 1); ed1 = eload(dl, t, 1); }
+            if (EPT > 2) {
+                eu2 = eload(u, t, 2); ed2 = eload(dl, t, 2);
+                eu3 = eload(u, t, 3); ed3 = eload(dl, t, 3);
+            }
+            if (FULL && gate) {
+                ez0 = eload(z, t, 0);
+                if (EPT > 1) ez1 = eload(z, t, 1);
+                if (EPT > 2) { ez2 = eload(z, t, 2); ez3 = eload(z, t, 3); }
+            }
+        }
+        vb0 = pload(Bm, pb0, t0 + ps);
+        vb1 = pload(Bm, pb1, t0 + ps);
+        if (FULL) {
+            vc0 = pload(Cm, pb0, t0 + ps);
+            vc1 = pload(Cm, pb1, t0 + ps);
+        }
+    };
+
+    // ---- per-lane constants and initial state: states n = 32g + 8q + k
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    const int nb = 32 * g + 8 * q;
+    float A2[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int n = nb + k;
+        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+        A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
+    }
+    float h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = 0.0f;
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
+    const size_t cd = cd0 + j;
+    load_tile(t_begin);
+    if (FULL && j > 0) {
+        if (a.hstart) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(a.hstart + cd * NS + nb);
+            const float4 v1 = *reinterpret_cast<const float4 *>(a.hstart + cd * NS + nb + 4);
+            h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
+            h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
+        } else {
+            for (int64_t i = 0; i < j; ++i) {
+                const float sdt = a.dtsum[cd0 + i];
+                const float4 v0 = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * NS + nb);
+                const float4 v1 = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * NS + nb + 4);
+                const float he[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) h[k] = __builtin_fmaf(exp2_hw(A2[k] * sdt), h[k], he[k]);
+            }
+        }
+        if (!lane_ok) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = 0.0f;
+        }
+    }
+    float dt_sum = 0.0f;
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        // (a) convert and stage the tile
+        if (act) {
+            const float xu[4] = {eu0, eu1, eu2, eu3};
+            const float xd[4] = {ed0, ed1, ed2, ed3};
+            const float xz[4] = {ez0, ez1, ez2, ez3};
+            const int o = er * TP + et;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const bool ok = erow_ok && t0 + et + i < t_end;
+                const float x = xd[i] + ebias;
+                const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
+                const float uu = ok ? xu[i] : 0.0f;
+                s_dt[o + i] = dt;
+                s_w[o + i] = dt * uu;
+                if (FULL) {
+                    s_du[o + i] = eD * uu;
+                    s_g[o + i] = (FULL && gate) ? silu_f32(ok ? xz[i] : 0.0f) : 1.0f;
+                }
+            }
+        }
+        {
+            float e[4];
+            P::unpack(vb0, e);
+            *reinterpret_cast<float4 *>(&s_B[pr0 * TP + ps]) =
+                pok0 ? make_float4(e[0], e[1], e[2], e[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            P::unpack(vb1, e);
+            *reinterpret_cast<float4 *>(&s_B[pr1 * TP + ps]) =
+                pok1 ? make_float4(e[0], e[1], e[2], e[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (FULL) {
+                P::unpack(vc0, e);
+                *reinterpret_cast<float4 *>(&s_C[pr0 * TP + ps]) =
+                    pok0 ? make_float4(e[0], e[1], e[2], e[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+                P::unpack(vc1, e);
+                *reinterpret_cast<float4 *>(&s_C[pr1 * TP + ps]) =
+                    pok1 ? make_float4(e[0], e[1], e[2], e[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        load_tile(t0 + T);
+        __syncthreads();
+
+        // (b) the recurrence of this wavefront's 32 states
+        const int rowc = c * TP;
+        const int brow = (nb + (lane & 7)) * TP;
+        const int crow = nb * TP;
+#pragma unroll
+        for (int c4 = 0; c4 < T; c4 += 4) {
+            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[rowc + c4]);
+            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[brow + c4]);
+            float4 Cq[8];
+            if (FULL) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    Cq[k] = *reinterpret_cast<const float4 *>(&s_C[crow + k * TP + c4]);
+            }
+            const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+            const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+            const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+            float accv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float dt = dtv[k], w = wv[k], Bk = bv[k];
+                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
+                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
+                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
+                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
+                h[4] = __builtin_fmaf(exp2_hw(dt * A2[4]), h[4], row_bcast<4>(Bk) * w);
+                h[5] = __builtin_fmaf(exp2_hw(dt * A2[5]), h[5], row_bcast<5>(Bk) * w);
+                h[6] = __builtin_fmaf(exp2_hw(dt * A2[6]), h[6], row_bcast<6>(Bk) * w);
+                h[7] = __builtin_fmaf(exp2_hw(dt * A2[7]), h[7], row_bcast<7>(Bk) * w);
+                if (FULL) {
+                    const float ck[8] = {
+                        k == 0 ? Cq[0].x : k == 1 ? Cq[0].y : k == 2 ? Cq[0].z : Cq[0].w,
+                        k == 0 ? Cq[1].x : k == 1 ? Cq[1].y : k == 2 ? Cq[1].z : Cq[1].w,
+                        k == 0 ? Cq[2].x : k == 1 ? Cq[2].y : k == 2 ? Cq[2].z : Cq[2].w,
+                        k == 0 ? Cq[3].x : k == 1 ? Cq[3].y : k == 2 ? Cq[3].z : Cq[3].w,
+                        k == 0 ? Cq[4].x : k == 1 ? Cq[4].y : k == 2 ? Cq[4].z : Cq[4].w,
+                        k == 0 ? Cq[5].x : k == 1 ? Cq[5].y : k == 2 ? Cq[5].z : Cq[5].w,
+                        k == 0 ? Cq[6].x : k == 1 ? Cq[6].y : k == 2 ? Cq[6].z : Cq[6].w,
+                        k == 0 ? Cq[7].x : k == 1 ? Cq[7].y : k == 2 ? Cq[7].z : Cq[7].w};
+                    float s0 = ck[0] * h[0];
+                    float s1 = ck[1] * h[1];
+                    s0 = __builtin_fmaf(ck[2], h[2], s0);
+                    s1 = __builtin_fmaf(ck[3], h[3], s1);
+                    s0 = __builtin_fmaf(ck[4], h[4], s0);
+                    s1 = __builtin_fmaf(ck[5], h[5], s1);
+                    s0 = __builtin_fmaf(ck[6], h[6], s0);
+                    s1 = __builtin_fmaf(ck[7], h[7], s1);
+                    accv[k] = s0 + s1;
+                } else {
+                    dt_sum += dt;
+                }
+            }
+            if (FULL) {
+                const auto s01 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(accv[0]), __float_as_uint(accv[1]), false, false);
+                const auto s23 = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(accv[2]), __float_as_uint(accv[3]), false, false);
+                const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+                const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+                const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01),
+                                                                __float_as_uint(p23), false, false);
+                s_yp[g * QC * TP + rowc + c4 + q] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+            }
+        }
+
+        // (c) sum the groups' partials in group order, finish and store y
+        if (FULL) {
+            __syncthreads();
+            if (act) {
+                const int o = er * TP + et;
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    float acc = s_yp[o + i];
+#pragma unroll
+                    for (int gg = 1; gg < G; ++gg) acc += s_yp[gg * QC * TP + o + i];
+                    const float v = (acc + s_du[o + i]) * s_g[o + i];
+                    const int64_t t = t0 + et + i;
+                    if (erow_ok && t < t_end) IO::store(y, ebase + t, v);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!lane_ok) return;
+    if (FULL) {
+        if (a.last_state && j == a.J - 1) {
+            float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (nb + k < a.N) ls[nb + k] = h[k];
+        }
+    } else {
+        float *he = a.hend + cd * NS + nb;
+        *reinterpret_cast<float4 *>(he) = make_float4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<float4 *>(he + 4) = make_float4(h[4], h[5], h[6], h[7]);
+        if (g == 0 && q == 0) a.dtsum[cd] = dt_sum;
+    }
+}
 // ============================================================ carry kernel
 // Exclusive scan of chunk transfer operators along the sequence, one
 // wavefront per (b, d, state group), lanes along chunks (64 chunks per step).
@@ -846,37 +822,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-#ifndef SSM_TILE
-#define SSM_TILE 8
-#endif
-template <class IO, int G, bool VEC>
-static hipError_t launch_chunks(const ScanArgs &a, hipStream_t s) {
-    constexpr int T = SSM_TILE;
-    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
-    if (a.J > 1) {
-        // the last chunk's operator is never needed
-        const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((chunk_kernel<IO, G, T, false, VEC>), agrid, dim3(64 * G), 0, s, a);
-        const int64_t waves = a.Bsz * a.D * a.G;
-        const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
-        hipLaunchKernelGGL(carry_kernel, dim3(blocks), dim3(256), 0, s, a);
-    }
-    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((chunk_kernel<IO, G, T, true, VEC>), grid, dim3(64 * G), 0, s, a);
-    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
-    return hipGetLastError();
-}
-
-template <class IO, int G>
-static hipError_t launch_chunks_vec(const ScanArgs &a, hipStream_t s) {
-    // 16-byte vector access needs every row start and the base pointers
-    // 16-byte aligned.
-    constexpr int VW = Seg<IO>::VW;
-    auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z));
-    return vec ? launch_chunks<IO, G, true>(a, s) : launch_chunks<IO, G, false>(a, s);
-}
-
 template <class IO, bool VEC>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
@@ -884,7 +829,7 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
         hipLaunchKernelGGL((quad_kernel<IO, false, VEC>), agrid, dim3(64), 0, s, a);
         if (a.hstart) {   // otherwise every chunk folds its predecessors itself
-            const int64_t waves = a.Bsz * a.D;
+            const int64_t waves = a.Bsz * a.D * a.G;
             hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
                                dim3(256), 0, s, a);
         }
@@ -893,6 +838,32 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((quad_kernel<IO, true, VEC>), grid, dim3(64), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
+}
+
+template <class IO, int GW, bool VEC>
+static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
+    if (a.J > 1) {
+        const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
+        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC>), agrid, dim3(64 * GW), 0, s, a);
+        if (a.hstart) {
+            const int64_t waves = a.Bsz * a.D * a.G;
+            hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
+                               dim3(256), 0, s, a);
+        }
+    }
+    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
+    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC>), grid, dim3(64 * GW), 0, s, a);
+    if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
+    return hipGetLastError();
+}
+
+template <class IO, int GW>
+static hipError_t launch_group_vec(const ScanArgs &a, hipStream_t s) {
+    // 4-token pieces of B and C need their rows and base pointers aligned
+    auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool vec = a.L % 4 == 0 && al(a.B) && al(a.C);
+    return vec ? launch_group<IO, GW, true>(a, s) : launch_group<IO, GW, false>(a, s);
 }
 
 template <class IO>
@@ -904,16 +875,11 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
                          (!a.z || al(a.z)) && al(a.B) && al(a.C);
         return vec ? launch_quad<IO, true>(a, s) : launch_quad<IO, false>(a, s);
     }
-    const dim3 pgrid(static_cast<unsigned>((a.L + 63) / 64 * a.G * a.Bsz));
-    hipLaunchKernelGGL(bc_pack_kernel<IO>, pgrid, dim3(256), 0, s,
-                       static_cast<const typename IO::T *>(a.B),
-                       static_cast<const typename IO::T *>(a.C), a.bc, a.L, a.N, a.G);
-    switch (a.G) {   // the plan pads G to a power of two
-        case 1: return launch_chunks_vec<IO, 1>(a, s);
-        case 2: return launch_chunks_vec<IO, 2>(a, s);
-        case 4: return launch_chunks_vec<IO, 4>(a, s);
-        case 8: return launch_chunks_vec<IO, 8>(a, s);
-        case 16: return launch_chunks_vec<IO, 16>(a, s);
+    switch (a.G / 2) {   // wavefronts of 32 states; the plan pads to a power of two
+        case 1: return launch_group_vec<IO, 1>(a, s);
+        case 2: return launch_group_vec<IO, 2>(a, s);
+        case 4: return launch_group_vec<IO, 4>(a, s);
+        case 8: return launch_group_vec<IO, 8>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -79,13 +79,16 @@ def test_workspace_and_chunk_plan(lib):
     assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
     d = desc(batch=8, d_inner=5120 * 4)                         # enough channels
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048
-    # d_state > 16: packed B/C rows, state groups padded to a power of two
-    for N, G in ((17, 2), (33, 4), (100, 8), (256, 16)):
-        d = desc(d_state=N, chunk_size=2048)
-        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 2 * 2048 * G * 32 * 4
-    for N in (1, 16):
+    # one chunk needs no workspace for any d_state
+    for N in (1, 16, 17, 33, 100, 256):
         d = desc(d_state=N, chunk_size=2048)
         assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
+    # d_state > 16: operator rows of 32 * 2^k states (wavefronts of 32 states,
+    # padded to a power of two)
+    for N, NS in ((17, 32), (33, 64), (100, 128), (256, 256)):
+        d = desc(d_state=N, chunk_size=256)
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == (
+            _al(2 * 64 * 8 * NS * 4) + _al(2 * 64 * 8 * 4))
 
 
 @pytest.mark.parametrize("kw,status", [

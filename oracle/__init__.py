@@ -23,7 +23,11 @@ Pins (each checked by a ``-m "not gpu"`` test in tests/test_oracle_pins.py):
   * delta = 0 gives y = D u; a decay so strong that exp underflows gives the
     closed form y_t = dt u_t (C_t . B_t) + D u_t; z = 0 zeroes y; softplus of
     the inverse-softplus bias returns the drawn step size;
-  * a hand-worked example with exact rational values.
+  * a hand-worked example with exact rational values;
+  * packed variable-length sequences (``scan_varlen``): the brute-force sum
+    with an initial-state term y_t += sum_n C_t[n] (prod_{s<=t} dA_s[n]) h0[n]
+    per sequence, and a packing of sequences that all start from zero equals
+    scanning each as its own batch row.
 """
 from __future__ import annotations
 
@@ -135,6 +139,46 @@ def scan_chunked(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
                                  threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_scan_chunked failed ({rc})")
+    return y, last
+
+
+def scan_varlen(u, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None, softplus=True,
+                initial_state=None, threads: int | None = None):
+    """Packed variable-length sequences, fp64.  Returns (y, last_state).
+
+    u, delta, z: (1, d_inner, total); B, C: (1, N, total); cu_seqlens:
+    n_seqs + 1 nondecreasing offsets with cu_seqlens[0] = 0 and
+    cu_seqlens[-1] = total.  Sequence s is the token range
+    [cu_seqlens[s], cu_seqlens[s+1]); the state is reset at its first token
+    to initial_state[s] (zeros when None), so each sequence is scanned on its
+    own, exactly as ``scan_fwd`` scans one batch row -- the packed-sequence
+    batching of the ufo.work article, §4.2 (cu_seqlens marks the boundaries,
+    the state is reset there), with the start state of §4.1.  last_state is
+    (n_seqs, d_inner, N); an empty sequence keeps its initial state.
+    """
+    u = _f64(u)
+    if u.ndim != 3 or u.shape[0] != 1:
+        raise ValueError("packed sequences need u of shape (1, d_inner, total)")
+    _, d_inner, total = u.shape
+    N = np.asarray(A).shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = cu.size - 1
+    if n < 1 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to the total length")
+    h0 = None if initial_state is None else _f64(initial_state, (n, d_inner, N))
+    y = np.zeros((1, d_inner, total))
+    last = np.zeros((n, d_inner, N))
+    for s in range(n):
+        a, b = int(cu[s]), int(cu[s + 1])
+        hs = None if h0 is None else h0[s:s + 1]
+        if a == b:
+            last[s] = 0.0 if hs is None else hs[0]
+            continue
+        part = lambda x: None if x is None else np.asarray(x)[:, :, a:b]
+        ys, ls = scan_fwd(part(u), part(delta), A, part(B), part(C), D, part(z), delta_bias,
+                          softplus=softplus, initial_state=hs, threads=threads)
+        y[:, :, a:b] = ys
+        last[s] = ls[0]
     return y, last
 
 

@@ -366,3 +366,60 @@ def test_golden_integer_fixture():
         # independent route: running sums
         h = np.cumsum(B[0] * u[0, d][None, :], axis=1)
         assert np.array_equal(np.sum(C[0] * h, axis=0) + D[d] * u[0, d], stored[f"y{d}"])
+
+
+def brute_force_h0(u, dt, A, B, C, D, h0):
+    """brute_force plus the start-state term: each output gains
+    sum_n C_t[n] exp(A_n sum_{s<=t} dt_s) h0[n]; the final state gains
+    exp(A_n sum_s dt_s) h0[n]."""
+    y, last = brute_force(u, dt, A, B, C, D)
+    batch, d_inner, L = u.shape
+    for b in range(batch):
+        for d in range(d_inner):
+            cs = np.cumsum(dt[b, d])                       # cs[t] = sum_{s<=t} dt_s
+            for t in range(L):
+                y[b, d, t] += np.sum(C[b, :, t] * np.exp(A[d] * cs[t]) * h0[b, d])
+            last[b, d] += np.exp(A[d] * (cs[-1] if L else 0.0)) * h0[b, d]
+    return y, last
+
+
+def test_varlen_brute_force_with_initial_state():
+    """Packed sequences (ufo.work article §4.2): every sequence restarts from its
+    own initial state at its first token; an empty sequence keeps it."""
+    d_inner, N = 3, 4
+    lens = [5, 0, 1, 9, 0, 4]
+    total = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    u, dt, A, B, C, D = tiny_inputs(1, d_inner, N, total, RNG)
+    h0 = RNG.standard_normal((len(lens), d_inner, N))
+    y, last = oracle.scan_varlen(u, dt, A, B, C, cu, D, softplus=False, initial_state=h0)
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        if a == b:
+            assert np.array_equal(last[s], h0[s])
+            continue
+        yb, lb = brute_force_h0(u[:, :, a:b], dt[:, :, a:b], A, B[:, :, a:b], C[:, :, a:b], D,
+                                h0[s:s + 1])
+        assert rel(y[:, :, a:b], yb) < 1e-12
+        assert rel(last[s], lb[0]) < 1e-12
+
+
+def test_varlen_zero_start_equals_batch_rows():
+    """Equal-length sequences packed along time, all from zero, equal the same
+    sequences scanned as separate batch rows."""
+    d_inner, N, n, Ls = 4, 3, 3, 7
+    u, dt, A, B, C, D = tiny_inputs(n, d_inner, N, Ls, RNG)
+    pack = lambda x: np.concatenate(list(x), axis=-1)[None]
+    cu = np.arange(n + 1) * Ls
+    y, last = oracle.scan_varlen(pack(u), pack(dt), A, pack(B), pack(C), cu, D, softplus=False)
+    yb, lb = oracle.scan_fwd(u, dt, A, B, C, D, softplus=False)
+    assert np.array_equal(y[0], np.concatenate(list(yb), axis=-1))
+    assert np.array_equal(last, lb)
+
+
+def test_varlen_rejects_bad_offsets():
+    u = np.zeros((1, 2, 5))
+    A = -np.ones((2, 2))
+    B = np.zeros((1, 2, 5))
+    for cu in ([0, 3], [1, 5], [0, 4, 3, 5], [0]):
+        with pytest.raises(ValueError):
+            oracle.scan_varlen(u, u, A, B, B, cu)

@@ -124,6 +124,36 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
                         const float *delta_bias, int softplus_flag, void *y, float *last_state,
                         ssm_stream_t stream);
 
+/* The same scan with explicit start states and, optionally, several
+ * variable-length sequences packed along the token axis (packed-sequence
+ * batching with a cu_seqlens offset table, the state reset at every sequence
+ * boundary: ufo.work article, §4.2; a persistent start state: §4.1).
+ *   initial_state  float32 or NULL (zeros): the state h_{-1} of every sequence
+ *   cu_seqlens     NULL: every batch row is one sequence; initial_state and
+ *                  last_state are (batch, d_inner, N).
+ *                  Else a DEVICE int32 array of n_seqs + 1 token offsets,
+ *                  cu_seqlens[0] = 0, nondecreasing, cu_seqlens[n_seqs] =
+ *                  seqlen, and desc->batch must be 1: sequence s is the token
+ *                  range [cu_seqlens[s], cu_seqlens[s+1]) of the single row;
+ *                  at its first token the state is reset to initial_state[s]
+ *                  (or 0); initial_state and last_state are (n_seqs, d_inner, N)
+ *                  and last_state[s] is the state after the sequence's last
+ *                  token (initial_state[s] or 0 for an empty sequence).
+ *   n_seqs         number of sequences (>= 1) when cu_seqlens is given;
+ *                  ignored otherwise.
+ * The offsets are read on the device and not validated: a table that breaks
+ * the rules above gives unspecified values of y and last_state, but every
+ * memory access stays inside the buffers described here.  Needs the same
+ * workspace as ssm_scan_fwd for the same descriptor.  Every other argument is
+ * as for ssm_scan_fwd, which is this call with initial_state = NULL and
+ * cu_seqlens = NULL.  Extra errors: SSM_ERR_BAD_SHAPE if cu_seqlens is given
+ * with batch != 1 or n_seqs < 1. */
+ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                           const void *B, const void *C, const float *D, const void *z,
+                           const float *delta_bias, int softplus_flag, const float *initial_state,
+                           const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
+                           ssm_stream_t stream);
+
 /* Single-token update of a persistent state, in place.
  *   state  (batch, d_inner, N) float32, read and overwritten with
  *          exp(delta A) state + delta B u

@@ -8,7 +8,8 @@ and passes raw pointers plus the current HIP stream to the library.  Every
 step of the computation runs in the HIP kernels; there is no fallback.
 
     y, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias,
-                                 softplus=True, return_last_state=True)
+                                 softplus=True, return_last_state=True,
+                                 initial_state=None, cu_seqlens=None)
     y = ssm_state_update(state, u, delta, A, B, C, D, z)   # state updated in place
 """
 from __future__ import annotations
@@ -70,6 +71,9 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_chunk_size.restype = ctypes.c_int64
     lib.ssm_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                    ctypes.c_int64, vp, vp, vp]
+    lib.ssm_scan_fwd_ex.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
@@ -146,11 +150,17 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  return_last_state=True, chunk_size=0, y=None, last_state=None,
-                 workspace=None, profile_events=None):
+                 workspace=None, profile_events=None, initial_state=None, cu_seqlens=None):
     """Fused selective-scan forward pass on the GPU.
 
     u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
     bfloat16.  A: (d_inner, N), D and delta_bias: (d_inner,), float32.
+    initial_state: float32 start states, or None for zeros.
+    cu_seqlens: optional int32 device tensor of n_seqs + 1 token offsets; the
+    sequences are packed along L of a single batch row (batch must be 1) and
+    the state starts over at each of them.  States (initial_state,
+    last_state) have one row per batch row, or per sequence when packed:
+    (rows, d_inner, N).
     Returns (y, last_state); last_state is None unless requested.
     profile_events: optional pair of raw hipEvent_t handles recorded around
     the pass that writes y.
@@ -169,12 +179,21 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     _expect(D, "D", (d_inner,), torch.float32, dev)
     _expect(z, "z", (batch, d_inner, L), io, dev)
     _expect(delta_bias, "delta_bias", (d_inner,), torch.float32, dev)
+    n_seqs = 0
+    rows = batch
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must hold n_seqs + 1 >= 2 offsets")
+        n_seqs = cu_seqlens.numel() - 1
+        _expect(cu_seqlens, "cu_seqlens", (n_seqs + 1,), torch.int32, dev)
+        rows = n_seqs
+    _expect(initial_state, "initial_state", (rows, d_inner, N), torch.float32, dev)
     if y is None:
         y = torch.empty((batch, d_inner, L), dtype=io, device=dev)
     _expect(y, "y", (batch, d_inner, L), io, dev)
     if last_state is None and return_last_state:
-        last_state = torch.empty((batch, d_inner, N), dtype=torch.float32, device=dev)
-    _expect(last_state, "last_state", (batch, d_inner, N), torch.float32, dev)
+        last_state = torch.empty((rows, d_inner, N), dtype=torch.float32, device=dev)
+    _expect(last_state, "last_state", (rows, d_inner, N), torch.float32, dev)
     desc = make_desc(batch, d_inner, N, L, code, chunk_size)
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
@@ -184,9 +203,15 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if profile_events is not None:
         desc.profile_begin, desc.profile_end = profile_events
-    st = lib.ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
-                          _ptr(last_state), _stream(dev))
+    if initial_state is None and cu_seqlens is None:
+        st = lib.ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                              _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                              _ptr(y), _ptr(last_state), _stream(dev))
+    else:
+        st = lib.ssm_scan_fwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                 int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
+                                 n_seqs, _ptr(y), _ptr(last_state), _stream(dev))
     _check(st)
     return y, last_state
 

@@ -32,7 +32,7 @@ struct Plan {
     int64_t n_cblk = 0;   // blocks of 16 channels per batch row
     int quad = 0;         // d_state <= 16: quad-row kernel
     int fold = 0;         // chunks fold their predecessors' operators (no carry kernel)
-    size_t off_hend = 0, off_dtsum = 0, off_hstart = 0, bytes = 0;
+    size_t off_hend = 0, off_dtsum = 0, off_keep = 0, off_hstart = 0, bytes = 0;
 };
 
 ssm_status check_desc(const ssm_desc *d) {
@@ -100,6 +100,8 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
         off += align_up(cj * G * 16 * sizeof(float));
         p->off_dtsum = off;
         off += align_up(cj * sizeof(float));
+        p->off_keep = off;
+        off += align_up(static_cast<size_t>(d->batch) * p->J * sizeof(float));
         if (!p->fold) {
             p->off_hstart = off;
             off += align_up(cj * G * 16 * sizeof(float));
@@ -125,26 +127,35 @@ int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
     return make_plan(desc, &p) == SSM_OK ? p.K : -1;
 }
 
-ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
-                        const void *B, const void *C, const float *D, const void *z,
-                        const float *delta_bias, int softplus_flag, void *y, float *last_state,
-                        ssm_stream_t stream) {
+ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                           const void *B, const void *C, const float *D, const void *z,
+                           const float *delta_bias, int softplus_flag, const float *initial_state,
+                           const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
+                           ssm_stream_t stream) {
     Plan p;
     ssm_status st = make_plan(desc, &p);
     if (st != SSM_OK) return st;
     const hipStream_t s = stream;
+    if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
+    const int64_t state_rows = cu_seqlens ? n_seqs : desc->batch;
+    if (!dims_ok(state_rows, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
     const int64_t rows = desc->batch * desc->d_inner;
     if (rows == 0) return SSM_OK;
     const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
     if (!A) return SSM_ERR_NULL_ARG;
-    if (!aligned(A, 4) || !aligned(D, 4) || !aligned(delta_bias, 4) || !aligned(last_state, 4))
+    if (!aligned(A, 4) || !aligned(D, 4) || !aligned(delta_bias, 4) || !aligned(last_state, 4) ||
+        !aligned(initial_state, 4) || !aligned(cu_seqlens, 4))
         return SSM_ERR_MISALIGNED;
     if (desc->seqlen == 0) {
-        // h_{-1} = 0 is the final state of an empty sequence.
-        if (last_state &&
-            ssm::launch_fill_zero(last_state, static_cast<size_t>(rows) * desc->d_state, s) !=
-                hipSuccess)
-            return SSM_ERR_HIP;
+        // every sequence is empty: its final state is its initial state
+        if (last_state) {
+            const size_t n = static_cast<size_t>(state_rows) * desc->d_inner * desc->d_state;
+            const hipError_t e =
+                initial_state ? hipMemcpyAsync(last_state, initial_state, n * sizeof(float),
+                                               hipMemcpyDeviceToDevice, s)
+                              : ssm::launch_fill_zero(last_state, n, s);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
         return SSM_OK;
     }
     if (!u || !delta || !B || !C || !y) return SSM_ERR_NULL_ARG;
@@ -163,14 +174,24 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
     a.softplus = softplus_flag != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
+    a.h0 = initial_state; a.cu = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : desc->batch;
     if (p.J > 1) {
         a.hend = reinterpret_cast<float *>(ws + p.off_hend);
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
+        a.keep = reinterpret_cast<float *>(ws + p.off_keep);
         if (!p.fold) a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
     }
     a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
     a.ev_end = static_cast<hipEvent_t>(desc->profile_end);
     return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, void *y, float *last_state,
+                        ssm_stream_t stream) {
+    return ssm_scan_fwd_ex(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
+                           nullptr, 0, y, last_state, stream);
 }
 
 ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, const void *delta,
@@ -209,6 +230,6 @@ const char *ssm_status_string(int status) {
     }
 }
 
-int ssm_version(void) { return 100; }
+int ssm_version(void) { return 200; }
 
 }  // extern "C"

@@ -19,10 +19,15 @@ struct ScanArgs {
     const void *u, *delta, *z, *B, *C;
     void *y;
     const float *A, *Dskip, *delta_bias;
-    float *last_state;
+    float *last_state;          // (rows, d_inner, N): rows = batch, or n_seqs when packed
+    const float *h0;            // initial states, same rows as last_state, or null (zeros)
+    const int32_t *cu;          // packed sequences: n_seqs + 1 token offsets (batch == 1), or null
+    int64_t n_seqs;
     // workspace views
     float *hend;                // (batch, d_inner, J, G*16) chunk end states from zero
     float *dtsum;               // (batch, d_inner, J) sum of step sizes per chunk
+    float *keep;                // (batch, J) 1: the chunk keeps its incoming state, 0: it
+                                // starts a sequence somewhere, so its operator's decay is 0
     float *hstart;              // (batch, d_inner, J, G*16) chunk start states
     hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
 };

@@ -112,6 +112,79 @@ struct Piece4<BF16> {
 };
 
 
+// ============================================================ sequences
+// Where the state starts over: at token 0 of every batch row or, with packed
+// sequences (ufo.work article, §4.2), at the first token of every sequence of
+// the cu_seqlens table.  All values here are uniform across a workgroup.
+// Offsets are clamped into [0, L], so any table keeps every access in bounds.
+__device__ __forceinline__ int64_t cu_at(const ScanArgs &a, int64_t i) {
+    const int64_t v = a.cu[i];
+    return v < 0 ? 0 : (v > a.L ? a.L : v);
+}
+
+// The sequence that token t belongs to: the last s with cu[s] <= t (empty
+// sequences that start at t come before it and are skipped).
+__device__ __forceinline__ int64_t seq_of(const ScanArgs &a, int64_t t) {
+    int64_t lo = 0, hi = a.n_seqs - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (cu_at(a, mid) <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+struct SeqPos {
+    int64_t s;        // sequence: the batch row when sequences are not packed
+    int64_t end;      // its end, the next token where the state starts over
+    bool reset;       // token t starts the sequence
+};
+
+template <bool SEQ>
+__device__ __forceinline__ SeqPos seq_pos(const ScanArgs &a, int64_t b, int64_t t) {
+    SeqPos p;
+    if (SEQ) {
+        p.s = seq_of(a, t);
+        p.end = cu_at(a, p.s + 1);
+        p.reset = cu_at(a, p.s) == t;
+    } else {
+        p.s = b;
+        p.end = a.L;
+        p.reset = t == 0;
+    }
+    return p;
+}
+
+// The transfer operator's decay for chunk i of batch row b: exp(A sum dt),
+// or 0 when a sequence starts inside the chunk.
+__device__ __forceinline__ float chunk_decay(const ScanArgs &a, int64_t b, int64_t i, float A2,
+                                             float sdt) {
+    return a.keep[b * a.J + i] != 0.0f ? exp2_hw(A2 * sdt) : 0.0f;
+}
+
+// Start state of sequence s for states n0 .. n0 + S - 1 of channel d (zero
+// when there is no initial state, for states n >= N and for padded channels).
+template <int S>
+__device__ __forceinline__ void load_start_state(const ScanArgs &a, int64_t s, int64_t dcl,
+                                                 bool lane_ok, int n0, float (&h)[S]) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        const int n = n0 + k;
+        const float v = a.h0 ? a.h0[(s * a.D + dcl) * a.N + (n < a.N ? n : a.N - 1)] : 0.0f;
+        h[k] = (lane_ok && n < a.N) ? v : 0.0f;
+    }
+}
+
+// Final state of sequence s: states n0 .. n0 + S - 1 of channel d.
+template <int S>
+__device__ __forceinline__ void store_final_state(const ScanArgs &a, int64_t s, int64_t d,
+                                                  bool lane_ok, int n0, const float (&h)[S]) {
+    if (!a.last_state || !lane_ok) return;
+    float *ls = a.last_state + (s * a.D + d) * a.N;
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+        if (n0 + k < a.N) ls[n0 + k] = h[k];
+}
+
 // ============================================================ quad-row kernel (N <= 16)
 // The path for d_state <= 16.  A wavefront covers 16 channels in 4 lane-rows:
 // lane l serves channel c = l % 16 and the 4 states 4q..4q+3, q = l / 16.
@@ -140,7 +213,7 @@ struct Piece4<BF16> {
 // from the carry kernel (h_start) or, when the chunks before it are few, by
 // folding their transfer operators itself: h = exp(A sum dt) h + h_end, in
 // chunk order.
-template <class IO, bool FULL, bool VEC>
+template <class IO, bool FULL, bool VEC, bool SEQ>
 __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using S = Seg<IO>;
@@ -238,8 +311,14 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;   // chunk 0 of this channel
     const size_t cd = cd0 + j;
+    SeqPos sp = seq_pos<SEQ>(a, b, t_begin);
+    // the chunk's operator ignores its incoming state if a sequence starts in it
+    const float keep = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
     load_tile(t_begin);
-    if (FULL && j > 0) {
+    if (sp.reset) {
+        load_start_state<4>(a, sp.s, dcl, lane_ok, 4 * q, h);
+    } else if (FULL) {
+        // a chunk after the first of its sequence: start from h_start
         if (a.hstart) {
             const float4 v = *reinterpret_cast<const float4 *>(a.hstart + cd * 16 + 4 * q);
             h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
@@ -248,10 +327,10 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
             for (int64_t i = 0; i < j; ++i) {
                 const float sdt = a.dtsum[cd0 + i];
                 const float4 v = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * 16 + 4 * q);
-                h[0] = __builtin_fmaf(exp2_hw(A2[0] * sdt), h[0], v.x);
-                h[1] = __builtin_fmaf(exp2_hw(A2[1] * sdt), h[1], v.y);
-                h[2] = __builtin_fmaf(exp2_hw(A2[2] * sdt), h[2], v.z);
-                h[3] = __builtin_fmaf(exp2_hw(A2[3] * sdt), h[3], v.w);
+                h[0] = __builtin_fmaf(chunk_decay(a, b, i, A2[0], sdt), h[0], v.x);
+                h[1] = __builtin_fmaf(chunk_decay(a, b, i, A2[1], sdt), h[1], v.y);
+                h[2] = __builtin_fmaf(chunk_decay(a, b, i, A2[2], sdt), h[2], v.z);
+                h[3] = __builtin_fmaf(chunk_decay(a, b, i, A2[3], sdt), h[3], v.w);
             }
         }
         // padded channels carry no state (their A is zeroed, B is not)
@@ -341,6 +420,33 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         const int rowc = c * TP;
         const int brow = (4 * q + (lane & 3)) * TP;   // B row-replication source
         const int crow = 4 * q * TP;
+        if (SEQ && sp.end < t0 + T && sp.end < t_end) {
+            // a sequence boundary inside the tile: token by token
+            for (int k = 0; k < T; ++k) {
+                const int64_t t = t0 + k;
+                if (t == sp.end && t < t_end) {
+                    if (FULL) store_final_state<4>(a, sp.s, d, lane_ok, 4 * q, h);
+                    sp = seq_pos<SEQ>(a, b, t);
+                    load_start_state<4>(a, sp.s, dcl, lane_ok, 4 * q, h);
+                }
+                const float dt = s_dt[rowc + k], w = s_w[rowc + k], Bk = s_B[brow + k];
+                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
+                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
+                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
+                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
+                if (FULL) {
+                    float acc = s_C[crow + k] * h[0];
+                    acc = __builtin_fmaf(s_C[crow + TP + k], h[1], acc);
+                    acc = __builtin_fmaf(s_C[crow + 2 * TP + k], h[2], acc);
+                    acc = __builtin_fmaf(s_C[crow + 3 * TP + k], h[3], acc);
+                    acc += __shfl_xor(acc, 16);
+                    acc += __shfl_xor(acc, 32);
+                    if (q == 0) s_du[rowc + k] = (acc + s_du[rowc + k]) * s_g[rowc + k];
+                } else {
+                    dt_sum += dt;
+                }
+            }
+        } else {
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
             const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
@@ -390,6 +496,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
                 s_du[o] = (ysum + s_du[o]) * s_g[o];
             }
         }
+        }
 
         // (c) coalesced store of y
         if (FULL) {
@@ -414,15 +521,20 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         __syncthreads();
     }
 
-    if (!lane_ok) return;
     if (FULL) {
-        if (a.last_state && j == a.J - 1) {
-            float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (4 * q + k < a.N) ls[4 * q + k] = h[k];
+        // the sequence that is current at the chunk end ends with it
+        if (sp.end == t_end) store_final_state<4>(a, sp.s, d, lane_ok, 4 * q, h);
+        // empty packed sequences keep their initial state
+        if (SEQ && a.last_state && j == 0) {
+            for (int64_t s = 0; s < a.n_seqs; ++s) {
+                if (cu_at(a, s) != cu_at(a, s + 1)) continue;
+                load_start_state<4>(a, s, dcl, lane_ok, 4 * q, h);
+                store_final_state<4>(a, s, d, lane_ok, 4 * q, h);
+            }
         }
     } else {
+        if (lane == 0 && blockIdx.x % a.n_cblk == 0) a.keep[b * a.J + j] = keep;
+        if (!lane_ok) return;
         *reinterpret_cast<float4 *>(a.hend + cd * 16 + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
         if (q == 0) a.dtsum[cd] = dt_sum;
     }
@@ -453,7 +565,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #ifndef SSM_GROUP_WAVES_PER_SIMD
 #define SSM_GROUP_WAVES_PER_SIMD 4
 #endif
-template <class IO, int G, bool FULL, bool VEC>
+template <class IO, int G, bool FULL, bool VEC, bool SEQ>
 __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using P = Piece4<IO>;
@@ -573,8 +685,12 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
     for (int k = 0; k < 8; ++k) h[k] = 0.0f;
     const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
     const size_t cd = cd0 + j;
+    SeqPos sp = seq_pos<SEQ>(a, b, t_begin);
+    const float keep = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
     load_tile(t_begin);
-    if (FULL && j > 0) {
+    if (sp.reset) {
+        load_start_state<8>(a, sp.s, dcl, lane_ok, nb, h);
+    } else if (FULL) {
         if (a.hstart) {
             const float4 v0 = *reinterpret_cast<const float4 *>(a.hstart + cd * NS + nb);
             const float4 v1 = *reinterpret_cast<const float4 *>(a.hstart + cd * NS + nb + 4);
@@ -587,7 +703,8 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
                 const float4 v1 = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * NS + nb + 4);
                 const float he[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-                for (int k = 0; k < 8; ++k) h[k] = __builtin_fmaf(exp2_hw(A2[k] * sdt), h[k], he[k]);
+                for (int k = 0; k < 8; ++k)
+                    h[k] = __builtin_fmaf(chunk_decay(a, b, i, A2[k], sdt), h[k], he[k]);
             }
         }
         if (!lane_ok) {
@@ -642,6 +759,36 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
         const int rowc = c * TP;
         const int brow = (nb + (lane & 7)) * TP;
         const int crow = nb * TP;
+        if (SEQ && sp.end < t0 + T && sp.end < t_end) {
+            // a sequence boundary inside the tile: token by token
+            for (int k = 0; k < T; ++k) {
+                const int64_t t = t0 + k;
+                if (t == sp.end && t < t_end) {
+                    if (FULL) store_final_state<8>(a, sp.s, d, lane_ok, nb, h);
+                    sp = seq_pos<SEQ>(a, b, t);
+                    load_start_state<8>(a, sp.s, dcl, lane_ok, nb, h);
+                }
+                const float dt = s_dt[rowc + k], w = s_w[rowc + k], Bk = s_B[brow + k];
+                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
+                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
+                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
+                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
+                h[4] = __builtin_fmaf(exp2_hw(dt * A2[4]), h[4], row_bcast<4>(Bk) * w);
+                h[5] = __builtin_fmaf(exp2_hw(dt * A2[5]), h[5], row_bcast<5>(Bk) * w);
+                h[6] = __builtin_fmaf(exp2_hw(dt * A2[6]), h[6], row_bcast<6>(Bk) * w);
+                h[7] = __builtin_fmaf(exp2_hw(dt * A2[7]), h[7], row_bcast<7>(Bk) * w);
+                if (FULL) {
+                    float acc = s_C[crow + k] * h[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(s_C[crow + i * TP + k], h[i], acc);
+                    acc += __shfl_xor(acc, 16);
+                    acc += __shfl_xor(acc, 32);
+                    if (q == 0) s_yp[g * QC * TP + rowc + k] = acc;
+                } else {
+                    dt_sum += dt;
+                }
+            }
+        } else {
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
             const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
@@ -703,6 +850,7 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
                 s_yp[g * QC * TP + rowc + c4 + q] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
             }
         }
+        }
 
         // (c) sum the groups' partials in group order, finish and store y
         if (FULL) {
@@ -723,15 +871,18 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
         __syncthreads();
     }
 
-    if (!lane_ok) return;
     if (FULL) {
-        if (a.last_state && j == a.J - 1) {
-            float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (nb + k < a.N) ls[nb + k] = h[k];
+        if (sp.end == t_end) store_final_state<8>(a, sp.s, d, lane_ok, nb, h);
+        if (SEQ && a.last_state && j == 0) {
+            for (int64_t s = 0; s < a.n_seqs; ++s) {
+                if (cu_at(a, s) != cu_at(a, s + 1)) continue;
+                load_start_state<8>(a, s, dcl, lane_ok, nb, h);
+                store_final_state<8>(a, s, d, lane_ok, nb, h);
+            }
         }
     } else {
+        if (tid == 0 && blockIdx.x % a.n_cblk == 0) a.keep[b * a.J + j] = keep;
+        if (!lane_ok) return;
         float *he = a.hend + cd * NS + nb;
         *reinterpret_cast<float4 *>(he) = make_float4(h[0], h[1], h[2], h[3]);
         *reinterpret_cast<float4 *>(he + 4) = make_float4(h[4], h[5], h[6], h[7]);
@@ -788,6 +939,8 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs a) {
         // operator, so their (finite or not) contents are replaced by select.
         const float sdt_raw = a.dtsum[cd];
         const float sdt = has_op ? sdt_raw : 0.0f;
+        // a chunk in which a sequence starts forgets its incoming state
+        const bool kept = a.keep[(bd / a.D) * a.J + (ok ? jj : 0)] != 0.0f;
         const float *he = a.hend + cd * Npad + g * kGroup;
         float *hs = a.hstart + cd * Npad + g * kGroup;
         float hev[kGroup];
@@ -795,7 +948,7 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs a) {
         for (int i = 0; i < kGroup; ++i) hev[i] = he[i];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
-            float av = has_op ? exp2_hw(A2[i] * sdt) : 1.0f;
+            float av = has_op ? (kept ? exp2_hw(A2[i] * sdt) : 0.0f) : 1.0f;
             float bv = has_op ? hev[i] : 0.0f;
             scan_step<0x111, 0xF>(av, bv);   // row_shr:1
             scan_step<0x112, 0xF>(av, bv);   // row_shr:2
@@ -822,12 +975,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-template <class IO, bool VEC>
+template <class IO, bool VEC, bool SEQ>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((quad_kernel<IO, false, VEC>), agrid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, SEQ>), agrid, dim3(64), 0, s, a);
         if (a.hstart) {   // otherwise every chunk folds its predecessors itself
             const int64_t waves = a.Bsz * a.D * a.G;
             hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
@@ -835,17 +988,18 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((quad_kernel<IO, true, VEC>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((quad_kernel<IO, true, VEC, SEQ>), grid, dim3(64), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
 
-template <class IO, int GW, bool VEC>
+template <class IO, int GW, bool VEC, bool SEQ>
 static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC>), agrid, dim3(64 * GW), 0, s, a);
+        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, SEQ>), agrid, dim3(64 * GW), 0, s,
+                           a);
         if (a.hstart) {
             const int64_t waves = a.Bsz * a.D * a.G;
             hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
@@ -853,7 +1007,7 @@ static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC>), grid, dim3(64 * GW), 0, s, a);
+    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC, SEQ>), grid, dim3(64 * GW), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
@@ -863,7 +1017,9 @@ static hipError_t launch_group_vec(const ScanArgs &a, hipStream_t s) {
     // 4-token pieces of B and C need their rows and base pointers aligned
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     const bool vec = a.L % 4 == 0 && al(a.B) && al(a.C);
-    return vec ? launch_group<IO, GW, true>(a, s) : launch_group<IO, GW, false>(a, s);
+    if (a.cu)
+        return vec ? launch_group<IO, GW, true, true>(a, s) : launch_group<IO, GW, false, true>(a, s);
+    return vec ? launch_group<IO, GW, true, false>(a, s) : launch_group<IO, GW, false, false>(a, s);
 }
 
 template <class IO>
@@ -873,7 +1029,8 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
         auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
         const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) &&
                          (!a.z || al(a.z)) && al(a.B) && al(a.C);
-        return vec ? launch_quad<IO, true>(a, s) : launch_quad<IO, false>(a, s);
+        if (a.cu) return vec ? launch_quad<IO, true, true>(a, s) : launch_quad<IO, false, true>(a, s);
+        return vec ? launch_quad<IO, true, false>(a, s) : launch_quad<IO, false, false>(a, s);
     }
     switch (a.G / 2) {   // wavefronts of 32 states; the plan pads to a power of two
         case 1: return launch_group_vec<IO, 1>(a, s);

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_state_update", "ssm_scan_workspace_bytes",
+    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_scan_workspace_bytes",
               "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -42,7 +42,7 @@ def test_status_strings(lib):
     for s in range(1, 7):
         assert ssm.ssm_status_string(s).startswith("SSM_ERR_")
     assert ssm.ssm_status_string(99) == "unknown status"
-    assert lib.ssm_version() >= 100
+    assert lib.ssm_version() >= 200
 
 
 def desc(**kw):
@@ -64,7 +64,9 @@ def test_workspace_and_chunk_plan(lib):
     assert 16 <= K <= 2048 and (K % 16 == 0 or K == 2048)
     J = -(-2048 // K)
     need = lib.ssm_scan_workspace_bytes(ctypes.byref(d))
-    ops = _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4)
+    # chunk end states, step-size sums, and one "keeps its incoming state" flag
+    # per (batch row, chunk)
+    ops = _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4) + _al(2 * J * 4)
     assert need == (ops if J > 1 else 0)
     for k in (16, 256, 1024):
         d = desc(chunk_size=k)
@@ -73,7 +75,7 @@ def test_workspace_and_chunk_plan(lib):
     d = desc(chunk_size=16)
     J = 2048 // 16
     assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == (
-        2 * _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4))
+        2 * _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4) + _al(2 * J * 4))
     d = desc(chunk_size=4096)
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048     # one chunk
     assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
@@ -88,7 +90,7 @@ def test_workspace_and_chunk_plan(lib):
     for N, NS in ((17, 32), (33, 64), (100, 128), (256, 256)):
         d = desc(d_state=N, chunk_size=256)
         assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == (
-            _al(2 * 64 * 8 * NS * 4) + _al(2 * 64 * 8 * 4))
+            _al(2 * 64 * 8 * NS * 4) + _al(2 * 64 * 8 * 4) + _al(2 * 8 * 4))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -150,3 +152,23 @@ def test_empty_problems_return_ok_without_launch(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="build the HIP library"):
         ssm.load_library(tmp_path / "libssm.so")
+
+
+def test_packed_sequence_validation(lib):
+    """ssm_scan_fwd_ex: packed sequences need batch == 1 and n_seqs >= 1, and
+    the offset table and initial states must be 4-byte aligned; all checked
+    before anything is launched."""
+    ok = 4096
+    def call(d, h0, cu, n):
+        return lib.ssm_scan_fwd_ex(ctypes.byref(d), ok, ok, ok, ok, ok, None, None, None, 1,
+                                   h0, cu, n, ok, None, None)
+    d = desc(chunk_size=2048)                       # batch 2
+    assert call(d, None, ok, 3) == 2
+    d1 = desc(batch=1, chunk_size=2048)
+    assert call(d1, None, ok, 0) == 2
+    assert call(d1, None, ok + 2, 3) == 4
+    assert call(d1, ok + 1, ok, 3) == 4
+    assert call(d, ok + 1, None, 0) == 4
+    # empty problem: nothing to do, nothing launched
+    d0 = desc(batch=1, d_inner=0)
+    assert call(d0, None, ok, 3) == 0

@@ -27,7 +27,11 @@ Pins (each checked by a ``-m "not gpu"`` test in tests/test_oracle_pins.py):
   * packed variable-length sequences (``scan_varlen``): the brute-force sum
     with an initial-state term y_t += sum_n C_t[n] (prod_{s<=t} dA_s[n]) h0[n]
     per sequence, and a packing of sequences that all start from zero equals
-    scanning each as its own batch row.
+    scanning each as its own batch row;
+  * the causal convolution (``causal_conv1d``): impulse response = the
+    reversed kernel, a constant input through the exponentially decaying
+    kernel of "From FlashAttention to Mamba" §三.3 = its geometric partial
+    sums, and a direct double loop on random data.
 """
 from __future__ import annotations
 
@@ -180,6 +184,46 @@ def scan_varlen(u, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None, 
         y[:, :, a:b] = ys
         last[s] = ls[0]
     return y, last
+
+
+def causal_conv1d(x, weight, bias=None, silu=True, cu_seqlens=None, conv_state=None):
+    """Depthwise causal 1-D convolution along the token axis, fp64.
+
+    x: (batch, d_inner, L); weight: (d_inner, W); bias: (d_inner,) or None.
+    out[b, d, t] = bias[d] + sum_k weight[d, k] x[b, d, t - (W - 1) + k], then
+    silu(out) = out / (1 + exp(-out)) when ``silu`` -- the short convolution
+    that precedes the scan in the Mamba layer ("From FlashAttention to Mamba",
+    §三.3), fused with it per §四.3.  Tokens before a sequence's first token
+    are conv_state[s, d, W - 1 - j] for x_{start - 1 - j} (zeros when
+    conv_state is None).  Sequences are the batch rows, or, with cu_seqlens
+    (batch 1), the packed ranges [cu[s], cu[s+1]).  Each channel of each
+    sequence is one numpy.convolve call.
+    """
+    x = _f64(x)
+    batch, d_inner, L = x.shape
+    w = _f64(weight)
+    W = w.shape[1]
+    bvec = np.zeros(d_inner) if bias is None else _f64(bias, (d_inner,))
+    if cu_seqlens is None:
+        bounds = [(b, 0, L) for b in range(batch)]
+    else:
+        if batch != 1:
+            raise ValueError("packed sequences need batch == 1")
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        bounds = [(0, int(cu[s]), int(cu[s + 1])) for s in range(cu.size - 1)]
+    rows = len(bounds)
+    cs = None if conv_state is None else _f64(conv_state, (rows, d_inner, W - 1))
+    out = np.zeros_like(x)
+    for s, (b, a, e) in enumerate(bounds):
+        if a == e:
+            continue
+        for d in range(d_inner):
+            head = np.zeros(W - 1) if cs is None else cs[s, d]
+            seq = np.concatenate([head, x[b, d, a:e]])
+            out[b, d, a:e] = np.convolve(seq, w[d][::-1], mode="valid") + bvec[d]
+    if silu:
+        out = out / (1.0 + np.exp(-out))
+    return out
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None):

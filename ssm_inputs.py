@@ -169,6 +169,25 @@ def make_update_inputs(batch: int, d_inner: int, d_state: int, io_dtype: str = F
 
 # Named workloads: the shapes of the pages' workloads (d_inner 1.5k-5k,
 # N 16-256, L up to 64k).
+def make_conv_params(d_inner: int, width: int = 4, seed: int = 0, decay_kernel: bool = True):
+    """Weights (d_inner, width) and bias (d_inner) of the short causal
+    convolution ahead of the scan, float32.
+
+    decay_kernel: the initialisation the pages describe for it, taps that decay
+    exponentially away from the current token, e^{-l}, e^{-2l}, ... (weight
+    column width-1 multiplies the current token), with l ~ U(0.1, 1) per
+    channel; otherwise N(0, 1/width) weights.  Bias ~ 0.1 N(0, 1).
+    """
+    rng = np.random.default_rng(seed)
+    if decay_kernel:
+        lam = rng.uniform(0.1, 1.0, size=(d_inner, 1))
+        w = np.exp(-lam * np.arange(width, 0, -1)[None, :])
+    else:
+        w = rng.standard_normal((d_inner, width)) / np.sqrt(width)
+    bias = 0.1 * rng.standard_normal(d_inner)
+    return w.astype(np.float32), bias.astype(np.float32)
+
+
 CONFIGS = {
     "c0_tiny_f32": dict(batch=1, d_inner=64, d_state=16, seqlen=256, io_dtype=F32, gate=False),
     "c1_mamba130m_f32": dict(batch=2, d_inner=1536, d_state=16, seqlen=2048, io_dtype=F32, gate=True),

@@ -423,3 +423,71 @@ def test_varlen_rejects_bad_offsets():
     for cu in ([0, 3], [1, 5], [0, 4, 3, 5], [0]):
         with pytest.raises(ValueError):
             oracle.scan_varlen(u, u, A, B, B, cu)
+
+
+# ------------------------------------------------------------ causal conv1d
+
+def conv_direct(x, w, bias, start_state=None):
+    """Double loop: out_t = bias + sum_k w[k] x_{t-(W-1)+k}, x_{<0} from start_state."""
+    L = x.size
+    W = w.size
+    head = np.zeros(W - 1) if start_state is None else start_state
+    out = np.zeros(L)
+    for t in range(L):
+        acc = bias
+        for k in range(W):
+            src = t - (W - 1) + k
+            acc += w[k] * (x[src] if src >= 0 else head[W - 1 + src])
+        out[t] = acc
+    return out
+
+
+def test_conv_impulse_response():
+    """A unit impulse at t0 leaves the taps, newest first: out_{t0+j} = w[W-1-j]."""
+    W, L, t0 = 4, 12, 3
+    w = RNG.standard_normal((2, W))
+    x = np.zeros((1, 2, L))
+    x[0, :, t0] = 1.0
+    out = oracle.causal_conv1d(x, w, None, silu=False)
+    for d in range(2):
+        expect = np.zeros(L)
+        expect[t0:t0 + W] = w[d][::-1]
+        assert np.array_equal(out[0, d], expect)
+
+
+def test_conv_exponential_kernel_geometric_sums():
+    """The pages' initial kernel K = [e^-l, e^-2l, ..., e^-kl] (nearest token
+    first) on a constant input of ones gives the partial geometric sums
+    sum_{j=1..min(t+1,W)} e^{-j l} plus the bias, then silu."""
+    W, L = 4, 9
+    lam = np.array([0.3, 1.1])
+    w = np.stack([np.exp(-lam[d] * np.arange(W, 0, -1)) for d in range(2)])  # w[W-1] = e^-l
+    bias = np.array([0.25, -0.5])
+    out = oracle.causal_conv1d(np.ones((1, 2, L)), w, bias, silu=True)
+    for d in range(2):
+        for t in range(L):
+            m = min(t + 1, W)
+            r = math.exp(-lam[d])
+            pre = bias[d] + r * (1 - r ** m) / (1 - r)
+            assert abs(out[0, d, t] - pre / (1 + math.exp(-pre))) < 1e-14
+
+
+def test_conv_matches_double_loop_with_state_and_packing():
+    W, d_inner = 3, 3
+    lens = [6, 0, 1, 10]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = RNG.standard_normal((1, d_inner, cu[-1]))
+    w = RNG.standard_normal((d_inner, W))
+    bias = RNG.standard_normal(d_inner)
+    cs = RNG.standard_normal((len(lens), d_inner, W - 1))
+    out = oracle.causal_conv1d(x, w, bias, silu=False, cu_seqlens=cu, conv_state=cs)
+    for s in range(len(lens)):
+        for d in range(d_inner):
+            ref = conv_direct(x[0, d, cu[s]:cu[s + 1]], w[d], bias[d], cs[s, d])
+            assert rel(out[0, d, cu[s]:cu[s + 1]], ref) < 1e-14 if ref.size else True
+    # without a start state the batch rows start from zeros
+    xb = RNG.standard_normal((2, d_inner, 7))
+    outb = oracle.causal_conv1d(xb, w, bias, silu=False)
+    for b in range(2):
+        for d in range(d_inner):
+            assert rel(outb[b, d], conv_direct(xb[b, d], w[d], bias[d])) < 1e-14

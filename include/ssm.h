@@ -75,6 +75,8 @@ typedef enum {
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
 #define SSM_MAX_D_STATE 256
+/* Widest causal convolution ssm_scan_fwd_conv fuses (taps per channel). */
+#define SSM_MAX_CONV_WIDTH 4
 /* Longest sequence ssm_scan_fwd accepts (token offsets inside one row of the
  * packed B/C workspace stay within 32 bits). */
 #define SSM_MAX_SEQLEN (1LL << 25)
@@ -153,6 +155,35 @@ ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delt
                            const float *delta_bias, int softplus_flag, const float *initial_state,
                            const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
                            ssm_stream_t stream);
+
+/* The scan with the short depthwise causal convolution that precedes it in
+ * the Mamba layer fused in front ("From FlashAttention to Mamba": the SSM
+ * layer is a 1-D convolution followed by the scan, §三.3; convolution and scan
+ * merged into one kernel, §四.3).  The scan input is computed on the fly and
+ * is not read from memory:
+ *   u[b,d,t] = act(conv_bias[d] + sum_k conv_weight[d,k] x[b,d,t-(W-1)+k])
+ * with W = conv_width (1..SSM_MAX_CONV_WIDTH) and act = silu when conv_silu
+ * is nonzero, identity otherwise.  It feeds both the recurrence (dt u B) and
+ * the skip term (D u).
+ *   x            (batch, d_inner, L) io_dtype: the convolution's input
+ *   conv_weight  (d_inner, W) float32; column W-1 multiplies the current token
+ *   conv_bias    (d_inner) float32 or NULL (zero)
+ *   conv_state   float32 (rows, d_inner, W-1) or NULL (zeros): the inputs
+ *                before each sequence's first token, conv_state[s,d,W-2] being
+ *                the one just before it; rows as for initial_state
+ *   u_out        (batch, d_inner, L) io_dtype or NULL: written with u
+ * Sequences (batch rows, or cu_seqlens ranges) never see each other's inputs
+ * through the convolution.  All other arguments as for ssm_scan_fwd_ex.
+ * Extra errors: SSM_ERR_UNSUPPORTED for conv_width outside 1..4,
+ * SSM_ERR_NULL_ARG for a NULL conv_weight. */
+ssm_status ssm_scan_fwd_conv(const ssm_desc *desc, const void *x, const float *conv_weight,
+                             const float *conv_bias, int conv_width, int conv_silu,
+                             const float *conv_state, const void *delta, const float *A,
+                             const void *B, const void *C, const float *D, const void *z,
+                             const float *delta_bias, int softplus_flag,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int64_t n_seqs, void *y, float *last_state, void *u_out,
+                             ssm_stream_t stream);
 
 /* Single-token update of a persistent state, in place.
  *   state  (batch, d_inner, N) float32, read and overwritten with

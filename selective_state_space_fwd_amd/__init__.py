@@ -18,7 +18,7 @@ import ctypes
 import os
 from pathlib import Path
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "ssm_scan_workspace_bytes",
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_state_update", "ssm_scan_workspace_bytes",
            "ssm_scan_chunk_size", "ssm_status_string", "SsmError", "load_library",
            "LIB_PATH"]
 
@@ -74,6 +74,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
                                     ctypes.c_int64, vp, vp, vp]
     lib.ssm_scan_fwd_ex.restype = ctypes.c_int
+    lib.ssm_scan_fwd_conv.argtypes = [dp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp,
+                                      vp, vp, vp]
+    lib.ssm_scan_fwd_conv.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +218,74 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
                                  n_seqs, _ptr(y), _ptr(last_state), _stream(dev))
     _check(st)
     return y, last_state
+
+
+def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
+                      delta_bias=None, softplus=True, conv_silu=True, conv_state=None,
+                      initial_state=None, cu_seqlens=None, return_last_state=True,
+                      return_u=False, chunk_size=0, y=None, last_state=None, u_out=None,
+                      workspace=None, profile_events=None):
+    """The scan with the causal depthwise convolution fused in front: the scan
+    input is u = silu(conv(x) + conv_bias) (identity instead of silu when
+    conv_silu is False), computed on the fly.
+
+    x: (batch, d_inner, L) like u of ssm_scan_fwd; conv_weight: (d_inner, W)
+    float32, W <= 4, column W-1 on the current token; conv_bias: (d_inner,) or
+    None; conv_state: (rows, d_inner, W-1) float32 inputs before each
+    sequence, or None for zeros.  Returns (y, last_state, u) with u only when
+    return_u (else None).
+    """
+    torch = _torch()
+    lib = load_library()
+    batch, d_inner, L = x.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev, io = x.device, x.dtype
+    code = _io_code(io)
+    if conv_weight.dim() != 2 or conv_weight.shape[0] != d_inner:
+        raise ValueError(f"conv_weight must be (d_inner, W), got {tuple(conv_weight.shape)}")
+    W = conv_weight.shape[1]
+    for t, name, shape in ((x, "x", (batch, d_inner, L)), (delta, "delta", (batch, d_inner, L)),
+                           (B, "B", (batch, N, L)), (C, "C", (batch, N, L)),
+                           (z, "z", (batch, d_inner, L))):
+        _expect(t, name, shape, io, dev)
+    for t, name, shape in ((A, "A", (d_inner, N)), (D, "D", (d_inner,)),
+                           (delta_bias, "delta_bias", (d_inner,)),
+                           (conv_weight, "conv_weight", (d_inner, W)),
+                           (conv_bias, "conv_bias", (d_inner,))):
+        _expect(t, name, shape, torch.float32, dev)
+    n_seqs, rows = 0, batch
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must hold n_seqs + 1 >= 2 offsets")
+        n_seqs = rows = cu_seqlens.numel() - 1
+        _expect(cu_seqlens, "cu_seqlens", (n_seqs + 1,), torch.int32, dev)
+    _expect(initial_state, "initial_state", (rows, d_inner, N), torch.float32, dev)
+    _expect(conv_state, "conv_state", (rows, d_inner, W - 1), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, d_inner, L), dtype=io, device=dev)
+    _expect(y, "y", (batch, d_inner, L), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((rows, d_inner, N), dtype=torch.float32, device=dev)
+    _expect(last_state, "last_state", (rows, d_inner, N), torch.float32, dev)
+    if u_out is None and return_u:
+        u_out = torch.empty((batch, d_inner, L), dtype=io, device=dev)
+    _expect(u_out, "u_out", (batch, d_inner, L), io, dev)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    if profile_events is not None:
+        desc.profile_begin, desc.profile_end = profile_events
+    st = lib.ssm_scan_fwd_conv(ctypes.byref(desc), _ptr(x), _ptr(conv_weight), _ptr(conv_bias),
+                               int(W), int(bool(conv_silu)), _ptr(conv_state), _ptr(delta),
+                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                               int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
+                               n_seqs, _ptr(y), _ptr(last_state), _ptr(u_out), _stream(dev))
+    _check(st)
+    return y, last_state, u_out
 
 
 def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None):

@@ -115,23 +115,20 @@ bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % 
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
-    Plan p;
-    return make_plan(desc, &p) == SSM_OK ? p.bytes : 0;
-}
+struct ConvSpec {
+    int width = 0;
+    int silu = 0;
+    const float *weight = nullptr, *bias = nullptr, *state = nullptr;
+    void *u_out = nullptr;
+};
 
-int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
-    Plan p;
-    return make_plan(desc, &p) == SSM_OK ? p.K : -1;
-}
-
-ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delta, const float *A,
-                           const void *B, const void *C, const float *D, const void *z,
-                           const float *delta_bias, int softplus_flag, const float *initial_state,
-                           const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
-                           ssm_stream_t stream) {
+ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, const void *delta,
+                     const float *A, const void *B, const void *C, const float *D, const void *z,
+                     const float *delta_bias, int softplus_flag, const float *initial_state,
+                     const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
+                     ssm_stream_t stream) {
     Plan p;
     ssm_status st = make_plan(desc, &p);
     if (st != SSM_OK) return st;
@@ -143,8 +140,12 @@ ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delt
     if (rows == 0) return SSM_OK;
     const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
     if (!A) return SSM_ERR_NULL_ARG;
+    if (cv.width != 0 && (cv.width < 1 || cv.width > SSM_MAX_CONV_WIDTH))
+        return SSM_ERR_UNSUPPORTED;
+    if (cv.width != 0 && !cv.weight) return SSM_ERR_NULL_ARG;
     if (!aligned(A, 4) || !aligned(D, 4) || !aligned(delta_bias, 4) || !aligned(last_state, 4) ||
-        !aligned(initial_state, 4) || !aligned(cu_seqlens, 4))
+        !aligned(initial_state, 4) || !aligned(cu_seqlens, 4) || !aligned(cv.weight, 4) ||
+        !aligned(cv.bias, 4) || !aligned(cv.state, 4) || !aligned(cv.u_out, esz))
         return SSM_ERR_MISALIGNED;
     if (desc->seqlen == 0) {
         // every sequence is empty: its final state is its initial state
@@ -175,6 +176,8 @@ ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delt
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
     a.h0 = initial_state; a.cu = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : desc->batch;
+    a.conv_w = cv.width; a.conv_silu = cv.silu; a.conv_weight = cv.weight;
+    a.conv_bias = cv.bias; a.conv_state = cv.state; a.u_out = cv.u_out;
     if (p.J > 1) {
         a.hend = reinterpret_cast<float *>(ws + p.off_hend);
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
@@ -184,6 +187,48 @@ ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delt
     a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
     a.ev_end = static_cast<hipEvent_t>(desc->profile_end);
     return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
+    Plan p;
+    return make_plan(desc, &p) == SSM_OK ? p.bytes : 0;
+}
+
+int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
+    Plan p;
+    return make_plan(desc, &p) == SSM_OK ? p.K : -1;
+}
+
+ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                           const void *B, const void *C, const float *D, const void *z,
+                           const float *delta_bias, int softplus_flag, const float *initial_state,
+                           const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
+                           ssm_stream_t stream) {
+    return scan_impl(desc, u, ConvSpec{}, delta, A, B, C, D, z, delta_bias, softplus_flag,
+                     initial_state, cu_seqlens, n_seqs, y, last_state, stream);
+}
+
+ssm_status ssm_scan_fwd_conv(const ssm_desc *desc, const void *x, const float *conv_weight,
+                             const float *conv_bias, int conv_width, int conv_silu,
+                             const float *conv_state, const void *delta, const float *A,
+                             const void *B, const void *C, const float *D, const void *z,
+                             const float *delta_bias, int softplus_flag,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int64_t n_seqs, void *y, float *last_state, void *u_out,
+                             ssm_stream_t stream) {
+    if (conv_width < 1 || conv_width > SSM_MAX_CONV_WIDTH) {
+        if (!desc) return SSM_ERR_NULL_ARG;
+        return SSM_ERR_UNSUPPORTED;
+    }
+    ConvSpec cv;
+    cv.width = conv_width; cv.silu = conv_silu != 0; cv.weight = conv_weight;
+    cv.bias = conv_bias; cv.state = conv_state; cv.u_out = u_out;
+    return scan_impl(desc, x, cv, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state,
+                     cu_seqlens, n_seqs, y, last_state, stream);
 }
 
 ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,

@@ -23,6 +23,14 @@ struct ScanArgs {
     const float *h0;            // initial states, same rows as last_state, or null (zeros)
     const int32_t *cu;          // packed sequences: n_seqs + 1 token offsets (batch == 1), or null
     int64_t n_seqs;
+    // optional depthwise causal conv1d ahead of the scan: u then holds its
+    // input x, and the scan input is silu(conv(x) + bias)
+    int conv_w;                 // taps, 0 = no convolution
+    int conv_silu;
+    const float *conv_weight;   // (d_inner, conv_w)
+    const float *conv_bias;     // (d_inner) or null
+    const float *conv_state;    // (rows, d_inner, conv_w - 1): inputs before each sequence, or null
+    void *u_out;                // optional: the scan input (batch, d_inner, L), io dtype
     // workspace views
     float *hend;                // (batch, d_inner, J, G*16) chunk end states from zero
     float *dtsum;               // (batch, d_inner, J) sum of step sizes per chunk

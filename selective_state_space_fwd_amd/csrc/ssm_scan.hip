@@ -139,10 +139,10 @@ struct SeqPos {
     bool reset;       // token t starts the sequence
 };
 
-template <bool SEQ>
+template <bool EXT>
 __device__ __forceinline__ SeqPos seq_pos(const ScanArgs &a, int64_t b, int64_t t) {
     SeqPos p;
-    if (SEQ) {
+    if (EXT && a.cu) {
         p.s = seq_of(a, t);
         p.end = cu_at(a, p.s + 1);
         p.reset = cu_at(a, p.s) == t;
@@ -185,6 +185,61 @@ __device__ __forceinline__ void store_final_state(const ScanArgs &a, int64_t s, 
         if (n0 + k < a.N) ls[n0 + k] = h[k];
 }
 
+// ============================================================ causal convolution
+// The short depthwise convolution ahead of the scan ("From FlashAttention to
+// Mamba", §三.3), for NT consecutive tokens t .. t + NT - 1 of one channel
+// row.  The raw inputs are in LDS at xs[-3 .. NT) (xs[i] = x_{t+i}); cw holds
+// the weights of x_{t-3} .. x_t (zero for taps beyond the width).  Inputs
+// before the sequence start of a token come from conv_state, or are zero.
+template <int NT, bool EXT>
+__device__ __forceinline__ void conv_run(const ScanArgs &a, const float *xs, int64_t t,
+                                         const SeqPos &sp, int64_t st_cur, int64_t drc,
+                                         float4 cw, float cb, float (&u)[NT]) {
+    float xv[NT + 3];
+#pragma unroll
+    for (int m = 0; m < NT + 3; ++m) xv[m] = xs[m - 3];
+    const int W = a.conv_w;
+    const float wk[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t tt = t + i;
+        int64_t s = sp.s, st = st_cur;
+        // a later packed sequence (padding tokens past L belong to the last
+        // one); without packed sequences every token shares the row's start
+        if (EXT && a.cu && tt >= sp.end) {
+            s = seq_of(a, tt);
+            st = cu_at(a, s);
+        }
+        float acc = cb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t src = tt - 3 + k;
+            float v = xv[i + k];
+            if (k < 4 - W) {
+                v = 0.0f;
+            } else if (src < st) {
+                v = a.conv_state
+                        ? a.conv_state[(s * a.D + drc) * (W - 1) + (W - 1) - (st - src)]
+                        : 0.0f;
+            }
+            acc = __builtin_fmaf(wk[k], v, acc);
+        }
+        u[i] = a.conv_silu ? silu_f32(acc) : acc;
+    }
+}
+
+// Weights of one channel as the 4 taps on x_{t-3} .. x_t.
+__device__ __forceinline__ float4 conv_taps(const ScanArgs &a, int64_t drc) {
+    const int W = a.conv_w;
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int kk = k - (4 - W);
+        w[k] = kk >= 0 ? a.conv_weight[drc * W + (kk >= 0 ? kk : 0)] : 0.0f;
+    }
+    return make_float4(w[0], w[1], w[2], w[3]);
+}
+
 // ============================================================ quad-row kernel (N <= 16)
 // The path for d_state <= 16.  A wavefront covers 16 channels in 4 lane-rows:
 // lane l serves channel c = l % 16 and the 4 states 4q..4q+3, q = l / 16.
@@ -213,7 +268,9 @@ __device__ __forceinline__ void store_final_state(const ScanArgs &a, int64_t s, 
 // from the carry kernel (h_start) or, when the chunks before it are few, by
 // folding their transfer operators itself: h = exp(A sum dt) h + h_end, in
 // chunk order.
-template <class IO, bool FULL, bool VEC, bool SEQ>
+// EXT: the instance that also handles packed sequences and the fused
+// convolution; calls with neither use the lean instance.
+template <class IO, bool FULL, bool VEC, bool EXT>
 __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using S = Seg<IO>;
@@ -226,7 +283,10 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     // one token group (into s_du, in place) never aliases the dt, w, B and C
     // read by the next group, and can issue those reads early.
     __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
-    __shared__ __attribute__((aligned(16))) float s_w[QC * TP];
+    // s_w rows start 4 floats in: the 4 floats before a row's tokens (the
+    // previous row's padding) keep the inputs of the 4 tokens before the
+    // tile when the scan input is computed by the causal convolution
+    __shared__ __attribute__((aligned(16))) float s_w[QC * TP + 4];
     __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];   // D u, then y
     __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];    // silu(z)
     __shared__ __attribute__((aligned(16))) float s_B[16 * TP];              // state-major
@@ -265,6 +325,9 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const float rD = (row_ok && a.Dskip) ? a.Dskip[drc] : 0.0f;
     const bool st_ok = r < a.N;
     const size_t sbase = (static_cast<size_t>(b) * a.N + (st_ok ? r : a.N - 1)) * L;
+    const bool conv = EXT && a.conv_w > 0;                 // u holds the convolution's input
+    const float4 cw = conv ? conv_taps(a, drc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float cbias = (conv && a.conv_bias) ? a.conv_bias[drc] : 0.0f;
 
     // Prefetched tile registers: named vectors only (no arrays or aggregates
     // carried around the loop), so that they stay in VGPRs.
@@ -311,7 +374,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;   // chunk 0 of this channel
     const size_t cd = cd0 + j;
-    SeqPos sp = seq_pos<SEQ>(a, b, t_begin);
+    SeqPos sp = seq_pos<EXT>(a, b, t_begin);
     // the chunk's operator ignores its incoming state if a sequence starts in it
     const float keep = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
     load_tile(t_begin);
@@ -337,15 +400,62 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         if (!lane_ok) h[0] = h[1] = h[2] = h[3] = 0.0f;
     }
     float dt_sum = 0.0f;
+    if (conv && (lane & 3) == 0) {
+        // convolution inputs of the 4 tokens before the chunk
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t tt = t_begin - 4 + k;
+            s_w[r * TP + k] = tt >= 0 ? IO::load(u, rbase + tt) : 0.0f;
+        }
+    }
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        if (conv) {
+            // (a0) the scan input u = act(conv(x)) of this lane's piece: stage
+            // the raw inputs, convolve, keep the tile's last 4 inputs for the
+            // next tile, and leave u in s_dt for the conversion below
+            float xr[VW], uc[VW];
+            S::unpack(vu, xr);
+            const int o = r * TP + sc;
+#pragma unroll
+            for (int i = 0; i < VW; i += 4)
+                *reinterpret_cast<float4 *>(&s_w[4 + o + i]) = make_float4(xr[i], xr[i + 1], xr[i + 2], xr[i + 3]);
+            __syncthreads();
+            const int64_t st_cur = (EXT && a.cu) ? cu_at(a, sp.s) : 0;
+            conv_run<VW, EXT>(a, &s_w[4 + o], t0 + sc, sp, st_cur, drc, cw, cbias, uc);
+            __syncthreads();
+            if (sc == T - VW) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) s_w[r * TP + k] = xr[VW - 4 + k];
+            }
+#pragma unroll
+            for (int i = 0; i < VW; i += 4)
+                *reinterpret_cast<float4 *>(&s_dt[o + i]) = make_float4(uc[i], uc[i + 1], uc[i + 2], uc[i + 3]);
+            if (FULL && a.u_out) {
+                IT *uo = static_cast<IT *>(a.u_out);
+                const int64_t t = t0 + sc;
+                if (VEC) {
+                    if (row_ok && t < t_end) *reinterpret_cast<V *>(uo + rbase + t) = S::pack(uc);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VW; ++i)
+                        if (row_ok && t + i < t_end) IO::store(uo, rbase + t + i, uc[i]);
+                }
+            }
+        }
         // (a) convert this lane's pieces and write them to LDS
         auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
             constexpr bool SP = decltype(sp_tag)::value;
             constexpr bool GT = decltype(gate_tag)::value;
             constexpr bool MASK = decltype(mask_tag)::value;
             float xu[VW], xd[VW], xz[VW];
-            S::unpack(vu, xu);
+            if (conv) {
+                // the convolution left u in this lane's own s_dt slots
+#pragma unroll
+                for (int i = 0; i < VW; ++i) xu[i] = s_dt[r * TP + sc + i];
+            } else {
+                S::unpack(vu, xu);
+            }
             S::unpack(vd, xd);
             if (FULL && GT) S::unpack(vz, xz);
             float xdt[VW], xw[VW], xdu[VW], xg[VW];
@@ -369,7 +479,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
                 *reinterpret_cast<float4 *>(&s_dt[o + i]) = make_float4(xdt[i], xdt[i + 1], xdt[i + 2], xdt[i + 3]);
-                *reinterpret_cast<float4 *>(&s_w[o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
+                *reinterpret_cast<float4 *>(&s_w[4 + o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
                 if (FULL) {
                     *reinterpret_cast<float4 *>(&s_du[o + i]) = make_float4(xdu[i], xdu[i + 1], xdu[i + 2], xdu[i + 3]);
                     *reinterpret_cast<float4 *>(&s_g[o + i]) = make_float4(xg[i], xg[i + 1], xg[i + 2], xg[i + 3]);
@@ -420,16 +530,16 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         const int rowc = c * TP;
         const int brow = (4 * q + (lane & 3)) * TP;   // B row-replication source
         const int crow = 4 * q * TP;
-        if (SEQ && sp.end < t0 + T && sp.end < t_end) {
+        if (EXT && sp.end < t0 + T && sp.end < t_end) {
             // a sequence boundary inside the tile: token by token
             for (int k = 0; k < T; ++k) {
                 const int64_t t = t0 + k;
                 if (t == sp.end && t < t_end) {
                     if (FULL) store_final_state<4>(a, sp.s, d, lane_ok, 4 * q, h);
-                    sp = seq_pos<SEQ>(a, b, t);
+                    sp = seq_pos<EXT>(a, b, t);
                     load_start_state<4>(a, sp.s, dcl, lane_ok, 4 * q, h);
                 }
-                const float dt = s_dt[rowc + k], w = s_w[rowc + k], Bk = s_B[brow + k];
+                const float dt = s_dt[rowc + k], w = s_w[4 + rowc + k], Bk = s_B[brow + k];
                 h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
                 h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
                 h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
@@ -450,7 +560,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
             const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
-            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[rowc + c4]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[4 + rowc + c4]);
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[brow + c4]);
             float4 C0{}, C1{}, C2{}, C3{};
             if (FULL) {
@@ -525,7 +635,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         // the sequence that is current at the chunk end ends with it
         if (sp.end == t_end) store_final_state<4>(a, sp.s, d, lane_ok, 4 * q, h);
         // empty packed sequences keep their initial state
-        if (SEQ && a.last_state && j == 0) {
+        if (EXT && a.cu && a.last_state && j == 0) {
             for (int64_t s = 0; s < a.n_seqs; ++s) {
                 if (cu_at(a, s) != cu_at(a, s + 1)) continue;
                 load_start_state<4>(a, s, dcl, lane_ok, 4 * q, h);
@@ -565,7 +675,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #ifndef SSM_GROUP_WAVES_PER_SIMD
 #define SSM_GROUP_WAVES_PER_SIMD 4
 #endif
-template <class IO, int G, bool FULL, bool VEC, bool SEQ>
+template <class IO, int G, bool FULL, bool VEC, bool EXT>
 __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using P = Piece4<IO>;
@@ -578,7 +688,9 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
     constexpr int NACT = QC * T / EPT;              // threads that hold elements
     static_assert(NACT <= NT, "element mapping");
     __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
-    __shared__ __attribute__((aligned(16))) float s_w[QC * TP];
+    // rows start 4 floats in: the 4 floats before a row (the previous row's
+    // padding) keep the convolution inputs of the 4 tokens before the tile
+    __shared__ __attribute__((aligned(16))) float s_w[QC * TP + 4];
     __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];
     __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];
     __shared__ __attribute__((aligned(16))) float s_B[NS * TP];
@@ -616,6 +728,10 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
     const size_t ebase = (static_cast<size_t>(b) * a.D + (edr < a.D ? edr : a.D - 1)) * L;
     const float ebias = (erow_ok && a.delta_bias) ? a.delta_bias[edr] : 0.0f;
     const float eD = (erow_ok && a.Dskip) ? a.Dskip[edr] : 0.0f;
+    const int64_t edrc = edr < a.D ? edr : a.D - 1;
+    const bool conv = EXT && a.conv_w > 0;                 // u holds the convolution's input
+    const float4 cw = (conv && act) ? conv_taps(a, edrc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float cbias = (conv && act && a.conv_bias) ? a.conv_bias[edrc] : 0.0f;
 
     // ---- B/C piece mapping: pieces tid and tid + NT of each tensor;
     // piece p = row p / 4 (a state), tokens 4 (p % 4) .. + 3
@@ -685,7 +801,7 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
     for (int k = 0; k < 8; ++k) h[k] = 0.0f;
     const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
     const size_t cd = cd0 + j;
-    SeqPos sp = seq_pos<SEQ>(a, b, t_begin);
+    SeqPos sp = seq_pos<EXT>(a, b, t_begin);
     const float keep = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
     load_tile(t_begin);
     if (sp.reset) {
@@ -713,11 +829,50 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
         }
     }
     float dt_sum = 0.0f;
+    if (conv && act && et == 0) {
+        // convolution inputs of the 4 tokens before the chunk
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t tt = t_begin - 4 + k;
+            s_w[er * TP + k] = tt >= 0 ? IO::load(u, ebase + tt) : 0.0f;
+        }
+    }
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        float uc[EPT];
+        if (conv) {
+            // (a0) the scan input u = act(conv(x)) of this thread's elements
+            const float xr[4] = {eu0, eu1, eu2, eu3};
+            const int o = er * TP + et;
+            if (act) {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) s_w[4 + o + i] = xr[i];
+            }
+            __syncthreads();
+            if (act) {
+                const int64_t st_cur = (EXT && a.cu) ? cu_at(a, sp.s) : 0;
+                conv_run<EPT, EXT>(a, &s_w[4 + o], t0 + et, sp, st_cur, edrc, cw, cbias, uc);
+            }
+            __syncthreads();
+            if (act) {
+                // keep the tile's last 4 inputs for the next tile
+#pragma unroll
+                for (int i = 0; i < EPT; ++i)
+                    if (et + i >= T - 4) s_w[er * TP + et + i - (T - 4)] = xr[i];
+                if (FULL && a.u_out) {
+#pragma unroll
+                    for (int i = 0; i < EPT; ++i) {
+                        const int64_t t = t0 + et + i;
+                        if (erow_ok && t < t_end) IO::store(static_cast<IT *>(a.u_out), ebase + t, uc[i]);
+                    }
+                }
+            }
+        }
         // (a) convert and stage the tile
         if (act) {
-            const float xu[4] = {eu0, eu1, eu2, eu3};
+            const float xu[4] = {conv ? uc[0] : eu0, conv && EPT > 1 ? uc[EPT > 1 ? 1 : 0] : eu1,
+                                 conv && EPT > 2 ? uc[EPT > 2 ? 2 : 0] : eu2,
+                                 conv && EPT > 3 ? uc[EPT > 3 ? 3 : 0] : eu3};
             const float xd[4] = {ed0, ed1, ed2, ed3};
             const float xz[4] = {ez0, ez1, ez2, ez3};
             const int o = er * TP + et;
@@ -728,7 +883,7 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
                 const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
                 const float uu = ok ? xu[i] : 0.0f;
                 s_dt[o + i] = dt;
-                s_w[o + i] = dt * uu;
+                s_w[4 + o + i] = dt * uu;
                 if (FULL) {
                     s_du[o + i] = eD * uu;
                     s_g[o + i] = (FULL && gate) ? silu_f32(ok ? xz[i] : 0.0f) : 1.0f;
@@ -759,16 +914,16 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
         const int rowc = c * TP;
         const int brow = (nb + (lane & 7)) * TP;
         const int crow = nb * TP;
-        if (SEQ && sp.end < t0 + T && sp.end < t_end) {
+        if (EXT && sp.end < t0 + T && sp.end < t_end) {
             // a sequence boundary inside the tile: token by token
             for (int k = 0; k < T; ++k) {
                 const int64_t t = t0 + k;
                 if (t == sp.end && t < t_end) {
                     if (FULL) store_final_state<8>(a, sp.s, d, lane_ok, nb, h);
-                    sp = seq_pos<SEQ>(a, b, t);
+                    sp = seq_pos<EXT>(a, b, t);
                     load_start_state<8>(a, sp.s, dcl, lane_ok, nb, h);
                 }
-                const float dt = s_dt[rowc + k], w = s_w[rowc + k], Bk = s_B[brow + k];
+                const float dt = s_dt[rowc + k], w = s_w[4 + rowc + k], Bk = s_B[brow + k];
                 h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
                 h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
                 h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
@@ -792,7 +947,7 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
 #pragma unroll
         for (int c4 = 0; c4 < T; c4 += 4) {
             const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
-            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[rowc + c4]);
+            const float4 w4 = *reinterpret_cast<const float4 *>(&s_w[4 + rowc + c4]);
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[brow + c4]);
             float4 Cq[8];
             if (FULL) {
@@ -873,7 +1028,7 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
 
     if (FULL) {
         if (sp.end == t_end) store_final_state<8>(a, sp.s, d, lane_ok, nb, h);
-        if (SEQ && a.last_state && j == 0) {
+        if (EXT && a.cu && a.last_state && j == 0) {
             for (int64_t s = 0; s < a.n_seqs; ++s) {
                 if (cu_at(a, s) != cu_at(a, s + 1)) continue;
                 load_start_state<8>(a, s, dcl, lane_ok, nb, h);
@@ -975,12 +1130,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-template <class IO, bool VEC, bool SEQ>
+template <class IO, bool VEC, bool EXT>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, SEQ>), agrid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, EXT>), agrid, dim3(64), 0, s, a);
         if (a.hstart) {   // otherwise every chunk folds its predecessors itself
             const int64_t waves = a.Bsz * a.D * a.G;
             hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
@@ -988,17 +1143,17 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((quad_kernel<IO, true, VEC, SEQ>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((quad_kernel<IO, true, VEC, EXT>), grid, dim3(64), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
 
-template <class IO, int GW, bool VEC, bool SEQ>
+template <class IO, int GW, bool VEC, bool EXT>
 static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, SEQ>), agrid, dim3(64 * GW), 0, s,
+        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, EXT>), agrid, dim3(64 * GW), 0, s,
                            a);
         if (a.hstart) {
             const int64_t waves = a.Bsz * a.D * a.G;
@@ -1007,7 +1162,7 @@ static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC, SEQ>), grid, dim3(64 * GW), 0, s, a);
+    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC, EXT>), grid, dim3(64 * GW), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
@@ -1017,7 +1172,7 @@ static hipError_t launch_group_vec(const ScanArgs &a, hipStream_t s) {
     // 4-token pieces of B and C need their rows and base pointers aligned
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     const bool vec = a.L % 4 == 0 && al(a.B) && al(a.C);
-    if (a.cu)
+    if (a.cu || a.conv_w > 0)
         return vec ? launch_group<IO, GW, true, true>(a, s) : launch_group<IO, GW, false, true>(a, s);
     return vec ? launch_group<IO, GW, true, false>(a, s) : launch_group<IO, GW, false, false>(a, s);
 }
@@ -1029,7 +1184,8 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
         auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
         const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) &&
                          (!a.z || al(a.z)) && al(a.B) && al(a.C);
-        if (a.cu) return vec ? launch_quad<IO, true, true>(a, s) : launch_quad<IO, false, true>(a, s);
+        if (a.cu || a.conv_w > 0)
+            return vec ? launch_quad<IO, true, true>(a, s) : launch_quad<IO, false, true>(a, s);
         return vec ? launch_quad<IO, true, false>(a, s) : launch_quad<IO, false, false>(a, s);
     }
     switch (a.G / 2) {   // wavefronts of 32 states; the plan pads to a power of two

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_scan_workspace_bytes",
+    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_state_update", "ssm_scan_workspace_bytes",
               "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -172,3 +172,19 @@ def test_packed_sequence_validation(lib):
     # empty problem: nothing to do, nothing launched
     d0 = desc(batch=1, d_inner=0)
     assert call(d0, None, ok, 3) == 0
+
+
+def test_conv_validation(lib):
+    """ssm_scan_fwd_conv: the width must be 1..4 and the weights present."""
+    ok = 4096
+    d = desc(chunk_size=2048)
+    def call(width, weight):
+        return lib.ssm_scan_fwd_conv(ctypes.byref(d), ok, weight, None, width, 1, None, ok, ok,
+                                     ok, ok, None, None, None, 1, None, None, 0, ok, None, None,
+                                     None)
+    assert call(0, ok) == 3
+    assert call(5, ok) == 3
+    assert call(4, None) == 1
+    assert call(3, ok + 2) == 4
+    assert lib.ssm_scan_fwd_conv(None, ok, ok, None, 4, 1, None, ok, ok, ok, ok, None, None,
+                                 None, 1, None, None, 0, ok, None, None, None) == 1

@@ -68,12 +68,13 @@ def _load():
     build(force=False)
     lib = ctypes.CDLL(str(LIB))
     i64, dp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [c_int, dp, dp, dp, c_int]
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [c_int, dp, dp, dp, c_int,
+                                                                        c_int]
     lib.oracle_scan_fwd.restype = c_int
     lib.oracle_scan_chunked.argtypes = ([i64, i64, i64, i64] + [dp] * 8 +
-                                        [c_int, dp, dp, dp, i64, c_int, c_int])
+                                        [c_int, dp, dp, dp, c_int, i64, c_int, c_int])
     lib.oracle_scan_chunked.restype = c_int
-    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [c_int]
     lib.oracle_state_update.restype = c_int
     _lib = lib
     return lib
@@ -113,8 +114,9 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, initial_state):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-             initial_state=None, threads: int | None = None):
-    """Sequential fp64 scan.  Returns (y, last_state), both float64."""
+             initial_state=None, threads: int | None = None, zoh: bool = False):
+    """Sequential fp64 scan.  Returns (y, last_state), both float64.
+    zoh: zero-order-hold input term (exp(dt A) - 1) / A * B u instead of dt B u."""
     lib = _load()
     (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
         u, delta, A, B, C, D, z, delta_bias, initial_state)
@@ -122,7 +124,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
     last = np.zeros((batch, d_inner, N))
     rc = lib.oracle_scan_fwd(batch, d_inner, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                              _ptr(C), _ptr(D), _ptr(z), _ptr(bias), int(bool(softplus)),
-                             _ptr(h0), _ptr(y), _ptr(last), threads or default_threads())
+                             _ptr(h0), _ptr(y), _ptr(last), int(bool(zoh)),
+                             threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_scan_fwd failed ({rc})")
     return y, last
@@ -130,7 +133,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
 
 def scan_chunked(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  initial_state=None, chunk: int = 256, tree: bool = True,
-                 threads: int | None = None):
+                 threads: int | None = None, zoh: bool = False):
     """Chunked fp64 route (transfer operators + combine).  Returns (y, last_state)."""
     lib = _load()
     (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
@@ -139,15 +142,15 @@ def scan_chunked(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     last = np.zeros((batch, d_inner, N))
     rc = lib.oracle_scan_chunked(batch, d_inner, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(z), _ptr(bias), int(bool(softplus)),
-                                 _ptr(h0), _ptr(y), _ptr(last), int(chunk), int(bool(tree)),
-                                 threads or default_threads())
+                                 _ptr(h0), _ptr(y), _ptr(last), int(bool(zoh)), int(chunk),
+                                 int(bool(tree)), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_scan_chunked failed ({rc})")
     return y, last
 
 
 def scan_varlen(u, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None, softplus=True,
-                initial_state=None, threads: int | None = None):
+                initial_state=None, threads: int | None = None, zoh: bool = False):
     """Packed variable-length sequences, fp64.  Returns (y, last_state).
 
     u, delta, z: (1, d_inner, total); B, C: (1, N, total); cu_seqlens:
@@ -180,7 +183,7 @@ def scan_varlen(u, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None, 
             continue
         part = lambda x: None if x is None else np.asarray(x)[:, :, a:b]
         ys, ls = scan_fwd(part(u), part(delta), A, part(B), part(C), D, part(z), delta_bias,
-                          softplus=softplus, initial_state=hs, threads=threads)
+                          softplus=softplus, initial_state=hs, threads=threads, zoh=zoh)
         y[:, :, a:b] = ys
         last[s] = ls[0]
     return y, last
@@ -226,7 +229,7 @@ def causal_conv1d(x, weight, bias=None, silu=True, cu_seqlens=None, conv_state=N
     return out
 
 
-def state_update(state, u, delta, A, B, C, D=None, z=None):
+def state_update(state, u, delta, A, B, C, D=None, z=None, zoh: bool = False):
     """One fp64 single-token update.  Returns (new_state, y); inputs untouched."""
     lib = _load()
     s = np.array(state, dtype=np.float64, copy=True, order="C")
@@ -240,7 +243,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None):
     z = _f64(z, (batch, d_inner))
     y = np.zeros((batch, d_inner))
     rc = lib.oracle_state_update(batch, d_inner, N, _ptr(s), _ptr(u), _ptr(delta), _ptr(A),
-                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), int(bool(zoh)))
     if rc != 0:
         raise RuntimeError(f"oracle_state_update failed ({rc})")
     return s, y

@@ -23,7 +23,9 @@
  *                                     then softplus); bias added before it.
  *   dA      = exp(delta_t * A[d,n])                   -- [P1] §1.1, [P2] §三.1
  *   dBu     = delta_t * B[b,n,t] * u[b,d,t]           -- [P1] §1.1 (B-bar =
- *                                     Delta*B, applied to the input x_t)
+ *                                     Delta*B, applied to the input x_t);
+ *             or, with zero-order hold, (exp(delta_t A) - 1) / A * B u
+ *                                  -- [P5] §1.2 (B-bar of the ZOH rule)
  *   h_t[n]  = dA * h_{t-1}[n] + dBu,  h_{-1} = 0      -- [P1] §1.1, [P5] §1.2
  *   y_t     = sum_n C[b,n,t] h_t[n] + D[d] u[b,d,t]   -- [P1] §1.1 (y = C h),
  *                                     [P5] §1.1 (skip term D x)
@@ -61,6 +63,15 @@ static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Factor of B u in the state update.  Euler (the default): dt.  Zero-order
+ * hold -- the input held constant over the step -- (SSM engineering essay,
+ * §1.2: B_bar = (dt A)^-1 (exp(dt A) - 1) dt B): (exp(dt A) - 1) / A, whose
+ * limit at A = 0 is dt. */
+static double input_coeff(double dt, double A, int zoh) {
+    if (!zoh) return dt;
+    return A != 0.0 ? expm1(dt * A) / A : dt;
+}
+
 /* ------------------------------------------------------------ arguments */
 
 typedef struct {
@@ -68,6 +79,7 @@ typedef struct {
     const double *u, *delta, *A, *B, *C, *D, *z, *delta_bias, *h0;
     int softplus_flag;
     double *y, *last_state;
+    int zoh;            /* zero-order-hold input term instead of Euler */
     int64_t chunk;      /* chunked path only */
     int tree;           /* chunked path only: 1 = balanced tree, 0 = left fold */
 } scan_args;
@@ -96,7 +108,8 @@ static void run_tokens(const scan_args *a, int64_t b, int64_t d, int64_t t0, int
         double acc = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             const double dA = exp(dt * a->A[d * N + n]);
-            const double dBu = dt * a->B[(b * N + n) * L + t] * u;
+            const double dBu = input_coeff(dt, a->A[d * N + n], a->zoh) *
+                               a->B[(b * N + n) * L + t] * u;
             h[n] = dA * h[n] + dBu;
             acc += a->C[(b * N + n) * L + t] * h[n];
         }
@@ -172,7 +185,8 @@ static int scan_row_chunked(const scan_args *a, int64_t b, int64_t d, double *h)
             for (int64_t n = 0; n < N; ++n) {
                 const double dA = exp(dt * a->A[d * N + n]);
                 ka[n] *= dA;
-                kb[n] = dA * kb[n] + dt * a->B[(b * N + n) * L + t] * u;
+                kb[n] = dA * kb[n] + input_coeff(dt, a->A[d * N + n], a->zoh) *
+                                         a->B[(b * N + n) * L + t] * u;
             }
         }
     }
@@ -278,12 +292,12 @@ int oracle_scan_fwd(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seq
                     const double *u, const double *delta, const double *A, const double *B,
                     const double *C, const double *D, const double *z, const double *delta_bias,
                     int softplus_flag, const double *initial_state, double *y,
-                    double *last_state, int n_threads) {
+                    double *last_state, int zoh, int n_threads) {
     if (!check_dims(batch, d_inner, d_state, seqlen)) return -1;
     if (batch * d_inner == 0) return 0;
     if (!u || !delta || !A || !B || !C || !y) return -1;
     scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
-                   initial_state, softplus_flag, y, last_state, 0, 0};
+                   initial_state, softplus_flag, y, last_state, zoh, 0, 0};
     return run_rows(&a, 0, n_threads);
 }
 
@@ -292,18 +306,19 @@ int oracle_scan_chunked(int64_t batch, int64_t d_inner, int64_t d_state, int64_t
                         const double *C, const double *D, const double *z,
                         const double *delta_bias, int softplus_flag,
                         const double *initial_state, double *y, double *last_state,
-                        int64_t chunk, int tree_combine, int n_threads) {
+                        int zoh, int64_t chunk, int tree_combine, int n_threads) {
     if (!check_dims(batch, d_inner, d_state, seqlen) || chunk < 1) return -1;
     if (batch * d_inner == 0) return 0;
     if (!u || !delta || !A || !B || !C || !y) return -1;
     scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
-                   initial_state, softplus_flag, y, last_state, chunk, tree_combine ? 1 : 0};
+                   initial_state, softplus_flag, y, last_state, zoh, chunk,
+                   tree_combine ? 1 : 0};
     return run_rows(&a, 1, n_threads);
 }
 
 int oracle_state_update(int64_t batch, int64_t d_inner, int64_t d_state, double *state,
                         const double *u, const double *delta, const double *A, const double *B,
-                        const double *C, const double *D, const double *z, double *y) {
+                        const double *C, const double *D, const double *z, double *y, int zoh) {
     if (batch < 0 || d_inner < 0 || d_state < 1) return -1;
     if (batch * d_inner == 0) return 0;
     if (!state || !u || !delta || !A || !B || !C || !y) return -1;
@@ -314,7 +329,8 @@ int oracle_state_update(int64_t batch, int64_t d_inner, int64_t d_state, double 
             double *s = state + i * d_state;
             double acc = 0.0;
             for (int64_t n = 0; n < d_state; ++n) {
-                s[n] = exp(dt * A[d * d_state + n]) * s[n] + dt * B[b * d_state + n] * x;
+                const double An = A[d * d_state + n];
+                s[n] = exp(dt * An) * s[n] + input_coeff(dt, An, zoh) * B[b * d_state + n] * x;
                 acc += C[b * d_state + n] * s[n];
             }
             if (D) acc += D[d] * x;

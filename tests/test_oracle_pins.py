@@ -491,3 +491,52 @@ def test_conv_matches_double_loop_with_state_and_packing():
     for b in range(2):
         for d in range(d_inner):
             assert rel(outb[b, d], conv_direct(xb[b, d], w[d], bias[d])) < 1e-14
+
+
+# ------------------------------------------------------------ zero-order hold
+
+def test_zoh_matches_continuous_solution():
+    """Zero-order hold (SSM engineering essay, §1.2) is exact for an input held
+    constant: L steps of size dt reach the continuous solution at T = L dt,
+    h(T) = e^{A T} h0 + (e^{A T} - 1) / A * B u, whatever the step count."""
+    N, dt, u0 = 4, 0.037, 1.3
+    A = -np.array([[0.5, 1.0, 2.0, 7.0]])
+    Bn = np.array([0.3, -1.1, 0.7, 2.0])
+    Cn = np.array([1.0, 0.5, -0.25, 0.125])
+    h0 = np.array([[[0.2, -0.4, 1.5, 0.9]]])
+    for L in (1, 2, 7, 50):
+        u = np.full((1, 1, L), u0)
+        dts = np.full((1, 1, L), dt)
+        B = np.broadcast_to(Bn[None, :, None], (1, N, L)).copy()
+        C = np.broadcast_to(Cn[None, :, None], (1, N, L)).copy()
+        y, last = oracle.scan_fwd(u, dts, A, B, C, softplus=False, initial_state=h0, zoh=True)
+        T = L * dt
+        for t in range(L):
+            Tt = (t + 1) * dt
+            ht = np.exp(A[0] * Tt) * h0[0, 0] + np.expm1(A[0] * Tt) / A[0] * Bn * u0
+            assert abs(y[0, 0, t] - np.sum(Cn * ht)) < 1e-12
+        hT = np.exp(A[0] * T) * h0[0, 0] + np.expm1(A[0] * T) / A[0] * Bn * u0
+        assert rel(last[0, 0], hT) < 1e-12
+
+
+def test_zoh_reduces_to_euler_at_zero_decay():
+    """At A = 0 the hold rule's input factor (e^{dt A} - 1) / A has the limit
+    dt, the Euler factor, so both rules give the same scan."""
+    u, dt, _, B, C, D = tiny_inputs(1, 3, 4, 20, RNG)
+    A = np.zeros((3, 4))
+    y0, h0 = oracle.scan_fwd(u, dt, A, B, C, D, softplus=False)
+    y1, h1 = oracle.scan_fwd(u, dt, A, B, C, D, softplus=False, zoh=True)
+    assert np.array_equal(y0, y1) and np.array_equal(h0, h1)
+
+
+def test_zoh_chunked_and_decode_agree():
+    u, dt, A, B, C, D = tiny_inputs(2, 3, 5, 37, RNG)
+    y, h = oracle.scan_fwd(u, dt, A, B, C, D, softplus=False, zoh=True)
+    yc, hc = oracle.scan_chunked(u, dt, A, B, C, D, softplus=False, chunk=8, zoh=True)
+    assert rel(yc, y) < 1e-13 and rel(hc, h) < 1e-13
+    s = np.zeros((2, 3, 5))
+    for t in range(37):
+        s, yt = oracle.state_update(s, u[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], D,
+                                    zoh=True)
+        assert rel(yt, y[:, :, t]) < 1e-12
+    assert rel(s, h) < 1e-12

@@ -95,7 +95,15 @@ typedef struct ssm_desc {
     void *profile_begin;      /* scan only, optional hipEvent_t: when both are set, */
     void *profile_end;        /* recorded on `stream` right before and right after
                                  the pass that writes y (measurement hook) */
+    uint32_t flags;           /* SSM_FLAG_* bits; unknown bits: SSM_ERR_UNSUPPORTED */
+    uint32_t reserved;        /* must be 0 */
 } ssm_desc;
+
+/* Zero-order-hold discretisation of the input term (SSM engineering essay,
+ * §1.2: the input is held constant over the step): the state update becomes
+ * h = exp(dt A) h + (exp(dt A) - 1) / A * B u, with the A = 0 limit dt B u,
+ * instead of the default Euler term dt B u.  Scan and single-token update. */
+#define SSM_FLAG_ZOH 1u
 
 /* Bytes of device workspace that ssm_scan_fwd needs for this descriptor
  * (its shapes, io_dtype and chunk_size; the workspace fields are ignored).

@@ -47,6 +47,8 @@ class SsmDesc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("profile_begin", ctypes.c_void_p),
         ("profile_end", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -136,8 +138,12 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> SsmDesc:
-    return SsmDesc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size, None, 0, None, None)
+SSM_FLAG_ZOH = 1
+
+
+def make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0, flags=0) -> SsmDesc:
+    return SsmDesc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size, None, 0, None, None,
+                   flags, 0)
 
 
 def ssm_scan_workspace_bytes(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> int:
@@ -154,7 +160,8 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  return_last_state=True, chunk_size=0, y=None, last_state=None,
-                 workspace=None, profile_events=None, initial_state=None, cu_seqlens=None):
+                 workspace=None, profile_events=None, initial_state=None, cu_seqlens=None,
+                 zoh=False):
     """Fused selective-scan forward pass on the GPU.
 
     u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
@@ -165,6 +172,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     the state starts over at each of them.  States (initial_state,
     last_state) have one row per batch row, or per sequence when packed:
     (rows, d_inner, N).
+    zoh: zero-order-hold input term (exp(dt A) - 1) / A * B u instead of dt B u.
     Returns (y, last_state); last_state is None unless requested.
     profile_events: optional pair of raw hipEvent_t handles recorded around
     the pass that writes y.
@@ -198,7 +206,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     if last_state is None and return_last_state:
         last_state = torch.empty((rows, d_inner, N), dtype=torch.float32, device=dev)
     _expect(last_state, "last_state", (rows, d_inner, N), torch.float32, dev)
-    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size, SSM_FLAG_ZOH if zoh else 0)
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -224,7 +232,7 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
                       delta_bias=None, softplus=True, conv_silu=True, conv_state=None,
                       initial_state=None, cu_seqlens=None, return_last_state=True,
                       return_u=False, chunk_size=0, y=None, last_state=None, u_out=None,
-                      workspace=None, profile_events=None):
+                      workspace=None, profile_events=None, zoh=False):
     """The scan with the causal depthwise convolution fused in front: the scan
     input is u = silu(conv(x) + conv_bias) (identity instead of silu when
     conv_silu is False), computed on the fly.
@@ -270,7 +278,7 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
     if u_out is None and return_u:
         u_out = torch.empty((batch, d_inner, L), dtype=io, device=dev)
     _expect(u_out, "u_out", (batch, d_inner, L), io, dev)
-    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size, SSM_FLAG_ZOH if zoh else 0)
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -288,11 +296,12 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
     return y, last_state, u_out
 
 
-def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None):
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None, zoh=False):
     """One single-token update of ``state`` (batch, d_inner, N) float32, in place.
 
     u, delta, z: (batch, d_inner); B, C: (batch, N); float32 or bfloat16.
-    delta is the final step size.  Returns y (batch, d_inner).
+    delta is the final step size; zoh selects the zero-order-hold input term.
+    Returns y (batch, d_inner).
     """
     torch = _torch()
     lib = load_library()
@@ -310,7 +319,7 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None):
     if y is None:
         y = torch.empty((batch, d_inner), dtype=io, device=dev)
     _expect(y, "y", (batch, d_inner), io, dev)
-    desc = make_desc(batch, d_inner, N, 0, code)
+    desc = make_desc(batch, d_inner, N, 0, code, 0, SSM_FLAG_ZOH if zoh else 0)
     st = lib.ssm_state_update(ctypes.byref(desc), _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
                               _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(dev))
     _check(st)

@@ -40,6 +40,7 @@ ssm_status check_desc(const ssm_desc *d) {
     if (d->batch < 0 || d->d_inner < 0 || d->seqlen < 0) return SSM_ERR_BAD_SHAPE;
     if (d->d_state < 1 || d->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if ((d->flags & ~SSM_FLAG_ZOH) != 0 || d->reserved != 0) return SSM_ERR_UNSUPPORTED;
     if (d->seqlen > SSM_MAX_SEQLEN) return SSM_ERR_UNSUPPORTED;
     if (!dims_ok(d->batch, d->d_inner, d->seqlen > 0 ? d->seqlen : 1)) return SSM_ERR_BAD_SHAPE;
     if (!dims_ok(d->batch, d->d_inner, d->d_state)) return SSM_ERR_BAD_SHAPE;
@@ -173,6 +174,7 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     a.G = p.G; a.K = p.K; a.J = p.J; a.n_cblk = p.n_cblk; a.quad = p.quad;
     a.bf16 = desc->io_dtype == SSM_BF16;
     a.softplus = softplus_flag != 0;
+    a.zoh = (desc->flags & SSM_FLAG_ZOH) != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.last_state = last_state;
     a.h0 = initial_state; a.cu = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : desc->batch;
@@ -246,6 +248,7 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
     if (desc->batch < 0 || desc->d_inner < 0) return SSM_ERR_BAD_SHAPE;
     if (desc->d_state < 1 || desc->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     if (desc->io_dtype != SSM_F32 && desc->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+    if ((desc->flags & ~SSM_FLAG_ZOH) != 0 || desc->reserved != 0) return SSM_ERR_UNSUPPORTED;
     if (!dims_ok(desc->batch, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
     if (desc->batch * desc->d_inner == 0) return SSM_OK;
     if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
@@ -257,6 +260,7 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
     ssm::UpdateArgs a{};
     a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state;
     a.bf16 = desc->io_dtype == SSM_BF16;
+    a.zoh = (desc->flags & SSM_FLAG_ZOH) != 0;
     a.state = state; a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D;
     return ssm::launch_update(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
@@ -275,6 +279,6 @@ const char *ssm_status_string(int status) {
     }
 }
 
-int ssm_version(void) { return 200; }
+int ssm_version(void) { return 300; }
 
 }  // extern "C"

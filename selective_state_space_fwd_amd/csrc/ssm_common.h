@@ -61,4 +61,23 @@ __device__ __forceinline__ float silu_f32(float z) {
     return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }
 
+// Zero-order-hold input factor (SSM engineering essay, §1.2: B_bar =
+// (dt A)^-1 (exp(dt A) - 1) dt B), per unit of dt: phi(x) = (e^x - 1) / x at
+// x = dt A, given e = e^x; (exp(dt A) - 1) / A = dt phi(dt A), and phi(0) = 1
+// (the Euler factor).  Below |x| = 1/2 the difference e - 1 would lose up to
+// 2^-24 / |x| relative, so there phi is its Taylor polynomial to x^7
+// (truncation below 1e-8 relative); above, (e - 1) / x.
+__device__ __forceinline__ float zoh_phi(float x, float e) {
+    float p = 1.0f / 40320.0f;
+    p = __builtin_fmaf(p, x, 1.0f / 5040.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 720.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 120.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 24.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 6.0f);
+    p = __builtin_fmaf(p, x, 0.5f);
+    p = __builtin_fmaf(p, x, 1.0f);
+    const float q = (e - 1.0f) * rcp_hw(x);
+    return fabsf(x) < 0.5f ? p : q;
+}
+
 }  // namespace ssm

@@ -16,6 +16,7 @@ struct ScanArgs {
     int quad;                   // 1: d_state <= 16 path (quad_kernel), else group_kernel
     int bf16;                   // io dtype
     int softplus;
+    int zoh;                    // zero-order-hold input term
     const void *u, *delta, *z, *B, *C;
     void *y;
     const float *A, *Dskip, *delta_bias;
@@ -43,6 +44,7 @@ struct ScanArgs {
 struct UpdateArgs {
     int64_t Bsz, D, N;
     int bf16;
+    int zoh;
     float *state;
     const void *u, *delta, *z, *B, *C;
     void *y;

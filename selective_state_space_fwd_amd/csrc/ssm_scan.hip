@@ -240,6 +240,16 @@ __device__ __forceinline__ float4 conv_taps(const ScanArgs &a, int64_t drc) {
     return make_float4(w[0], w[1], w[2], w[3]);
 }
 
+// One token of the recurrence for one state: h = exp(dt A) h + c B u, with
+// w_b = dt u B and c the Euler factor 1 or, under zero-order hold, phi(dt A).
+// A2 = A log2(e), so dt A2 feeds the base-2 exponential directly.
+template <bool ZOH>
+__device__ __forceinline__ float state_step(float dt, float A2, float h, float w_b) {
+    const float xa = dt * A2;
+    const float e = exp2_hw(xa);
+    return __builtin_fmaf(e, h, ZOH ? w_b * zoh_phi(xa * kLn2, e) : w_b);
+}
+
 // ============================================================ quad-row kernel (N <= 16)
 // The path for d_state <= 16.  A wavefront covers 16 channels in 4 lane-rows:
 // lane l serves channel c = l % 16 and the 4 states 4q..4q+3, q = l / 16.
@@ -269,8 +279,9 @@ __device__ __forceinline__ float4 conv_taps(const ScanArgs &a, int64_t drc) {
 // folding their transfer operators itself: h = exp(A sum dt) h + h_end, in
 // chunk order.
 // EXT: the instance that also handles packed sequences and the fused
-// convolution; calls with neither use the lean instance.
-template <class IO, bool FULL, bool VEC, bool EXT>
+// convolution; calls with neither use the lean instance.  ZOH (EXT only):
+// zero-order-hold input term.
+template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH>
 __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using S = Seg<IO>;
@@ -540,10 +551,10 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
                     load_start_state<4>(a, sp.s, dcl, lane_ok, 4 * q, h);
                 }
                 const float dt = s_dt[rowc + k], w = s_w[4 + rowc + k], Bk = s_B[brow + k];
-                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
-                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
-                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
-                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
+                h[0] = state_step<ZOH>(dt, A2[0], h[0], row_bcast<0>(Bk) * w);
+                h[1] = state_step<ZOH>(dt, A2[1], h[1], row_bcast<1>(Bk) * w);
+                h[2] = state_step<ZOH>(dt, A2[2], h[2], row_bcast<2>(Bk) * w);
+                h[3] = state_step<ZOH>(dt, A2[3], h[3], row_bcast<3>(Bk) * w);
                 if (FULL) {
                     float acc = s_C[crow + k] * h[0];
                     acc = __builtin_fmaf(s_C[crow + TP + k], h[1], acc);
@@ -580,10 +591,10 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float dt = dtv[k], w = wv[k], Bk = bv[k];
-                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
-                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
-                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
-                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
+                h[0] = state_step<ZOH>(dt, A2[0], h[0], row_bcast<0>(Bk) * w);
+                h[1] = state_step<ZOH>(dt, A2[1], h[1], row_bcast<1>(Bk) * w);
+                h[2] = state_step<ZOH>(dt, A2[2], h[2], row_bcast<2>(Bk) * w);
+                h[3] = state_step<ZOH>(dt, A2[3], h[3], row_bcast<3>(Bk) * w);
                 if (FULL)
                     accv[k] = __builtin_fmaf(c0[k], h[0], __builtin_fmaf(c1[k], h[1],
                               __builtin_fmaf(c2[k], h[2], c3[k] * h[3])));
@@ -675,7 +686,7 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 #ifndef SSM_GROUP_WAVES_PER_SIMD
 #define SSM_GROUP_WAVES_PER_SIMD 4
 #endif
-template <class IO, int G, bool FULL, bool VEC, bool EXT>
+template <class IO, int G, bool FULL, bool VEC, bool EXT, bool ZOH>
 __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using P = Piece4<IO>;
@@ -924,14 +935,14 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
                     load_start_state<8>(a, sp.s, dcl, lane_ok, nb, h);
                 }
                 const float dt = s_dt[rowc + k], w = s_w[4 + rowc + k], Bk = s_B[brow + k];
-                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
-                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
-                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
-                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
-                h[4] = __builtin_fmaf(exp2_hw(dt * A2[4]), h[4], row_bcast<4>(Bk) * w);
-                h[5] = __builtin_fmaf(exp2_hw(dt * A2[5]), h[5], row_bcast<5>(Bk) * w);
-                h[6] = __builtin_fmaf(exp2_hw(dt * A2[6]), h[6], row_bcast<6>(Bk) * w);
-                h[7] = __builtin_fmaf(exp2_hw(dt * A2[7]), h[7], row_bcast<7>(Bk) * w);
+                h[0] = state_step<ZOH>(dt, A2[0], h[0], row_bcast<0>(Bk) * w);
+                h[1] = state_step<ZOH>(dt, A2[1], h[1], row_bcast<1>(Bk) * w);
+                h[2] = state_step<ZOH>(dt, A2[2], h[2], row_bcast<2>(Bk) * w);
+                h[3] = state_step<ZOH>(dt, A2[3], h[3], row_bcast<3>(Bk) * w);
+                h[4] = state_step<ZOH>(dt, A2[4], h[4], row_bcast<4>(Bk) * w);
+                h[5] = state_step<ZOH>(dt, A2[5], h[5], row_bcast<5>(Bk) * w);
+                h[6] = state_step<ZOH>(dt, A2[6], h[6], row_bcast<6>(Bk) * w);
+                h[7] = state_step<ZOH>(dt, A2[7], h[7], row_bcast<7>(Bk) * w);
                 if (FULL) {
                     float acc = s_C[crow + k] * h[0];
 #pragma unroll
@@ -962,14 +973,14 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float dt = dtv[k], w = wv[k], Bk = bv[k];
-                h[0] = __builtin_fmaf(exp2_hw(dt * A2[0]), h[0], row_bcast<0>(Bk) * w);
-                h[1] = __builtin_fmaf(exp2_hw(dt * A2[1]), h[1], row_bcast<1>(Bk) * w);
-                h[2] = __builtin_fmaf(exp2_hw(dt * A2[2]), h[2], row_bcast<2>(Bk) * w);
-                h[3] = __builtin_fmaf(exp2_hw(dt * A2[3]), h[3], row_bcast<3>(Bk) * w);
-                h[4] = __builtin_fmaf(exp2_hw(dt * A2[4]), h[4], row_bcast<4>(Bk) * w);
-                h[5] = __builtin_fmaf(exp2_hw(dt * A2[5]), h[5], row_bcast<5>(Bk) * w);
-                h[6] = __builtin_fmaf(exp2_hw(dt * A2[6]), h[6], row_bcast<6>(Bk) * w);
-                h[7] = __builtin_fmaf(exp2_hw(dt * A2[7]), h[7], row_bcast<7>(Bk) * w);
+                h[0] = state_step<ZOH>(dt, A2[0], h[0], row_bcast<0>(Bk) * w);
+                h[1] = state_step<ZOH>(dt, A2[1], h[1], row_bcast<1>(Bk) * w);
+                h[2] = state_step<ZOH>(dt, A2[2], h[2], row_bcast<2>(Bk) * w);
+                h[3] = state_step<ZOH>(dt, A2[3], h[3], row_bcast<3>(Bk) * w);
+                h[4] = state_step<ZOH>(dt, A2[4], h[4], row_bcast<4>(Bk) * w);
+                h[5] = state_step<ZOH>(dt, A2[5], h[5], row_bcast<5>(Bk) * w);
+                h[6] = state_step<ZOH>(dt, A2[6], h[6], row_bcast<6>(Bk) * w);
+                h[7] = state_step<ZOH>(dt, A2[7], h[7], row_bcast<7>(Bk) * w);
                 if (FULL) {
                     const float ck[8] = {
                         k == 0 ? Cq[0].x : k == 1 ? Cq[0].y : k == 2 ? Cq[0].z : Cq[0].w,
@@ -1130,12 +1141,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-template <class IO, bool VEC, bool EXT>
+template <class IO, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, EXT>), agrid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, EXT, ZOH>), agrid, dim3(64), 0, s, a);
         if (a.hstart) {   // otherwise every chunk folds its predecessors itself
             const int64_t waves = a.Bsz * a.D * a.G;
             hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
@@ -1143,17 +1154,17 @@ static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((quad_kernel<IO, true, VEC, EXT>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((quad_kernel<IO, true, VEC, EXT, ZOH>), grid, dim3(64), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
 
-template <class IO, int GW, bool VEC, bool EXT>
+template <class IO, int GW, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, EXT>), agrid, dim3(64 * GW), 0, s,
+        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, EXT, ZOH>), agrid, dim3(64 * GW), 0, s,
                            a);
         if (a.hstart) {
             const int64_t waves = a.Bsz * a.D * a.G;
@@ -1162,7 +1173,7 @@ static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
         }
     }
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
-    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC, EXT>), grid, dim3(64 * GW), 0, s, a);
+    hipLaunchKernelGGL((group_kernel<IO, GW, true, VEC, EXT, ZOH>), grid, dim3(64 * GW), 0, s, a);
     if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
     return hipGetLastError();
 }
@@ -1172,9 +1183,14 @@ static hipError_t launch_group_vec(const ScanArgs &a, hipStream_t s) {
     // 4-token pieces of B and C need their rows and base pointers aligned
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     const bool vec = a.L % 4 == 0 && al(a.B) && al(a.C);
+    if (a.zoh)
+        return vec ? launch_group<IO, GW, true, true, true>(a, s)
+                   : launch_group<IO, GW, false, true, true>(a, s);
     if (a.cu || a.conv_w > 0)
-        return vec ? launch_group<IO, GW, true, true>(a, s) : launch_group<IO, GW, false, true>(a, s);
-    return vec ? launch_group<IO, GW, true, false>(a, s) : launch_group<IO, GW, false, false>(a, s);
+        return vec ? launch_group<IO, GW, true, true, false>(a, s)
+                   : launch_group<IO, GW, false, true, false>(a, s);
+    return vec ? launch_group<IO, GW, true, false, false>(a, s)
+               : launch_group<IO, GW, false, false, false>(a, s);
 }
 
 template <class IO>
@@ -1184,9 +1200,14 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
         auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
         const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) &&
                          (!a.z || al(a.z)) && al(a.B) && al(a.C);
+        if (a.zoh)
+            return vec ? launch_quad<IO, true, true, true>(a, s)
+                       : launch_quad<IO, false, true, true>(a, s);
         if (a.cu || a.conv_w > 0)
-            return vec ? launch_quad<IO, true, true>(a, s) : launch_quad<IO, false, true>(a, s);
-        return vec ? launch_quad<IO, true, false>(a, s) : launch_quad<IO, false, false>(a, s);
+            return vec ? launch_quad<IO, true, true, false>(a, s)
+                       : launch_quad<IO, false, true, false>(a, s);
+        return vec ? launch_quad<IO, true, false, false>(a, s)
+                   : launch_quad<IO, false, false, false>(a, s);
     }
     switch (a.G / 2) {   // wavefronts of 32 states; the plan pads to a power of two
         case 1: return launch_group_vec<IO, 1>(a, s);

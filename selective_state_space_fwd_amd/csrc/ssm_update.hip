@@ -2,8 +2,9 @@
 //
 // The persistent per-channel state of the ufo.work article "Mamba
 // hardware-aware operator fusion and selective-scan parallelisation", §4.1:
-// one token advances it in place by h_new = exp(dt A) h_old + dt B u, and the
-// output is y = (C . h_new + D u) silu(z).
+// one token advances it in place by h_new = exp(dt A) h_old + dt B u (or the
+// zero-order-hold term (exp(dt A) - 1) / A B u), and the output is
+// y = (C . h_new + D u) silu(z).
 //
 // The step is a pure stream over the state (read + write of N floats per
 // channel), so the mapping is chosen for coalescing: P lanes per channel,
@@ -50,8 +51,10 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a, int P, int lo
             const float av[4] = {A4.x, A4.y, A4.z, A4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float dA = exp2_hw(dt * (av[i] * kLog2e));
-                sv[i] = __builtin_fmaf(dA, sv[i], w * IO::load(Bm, bo + i));
+                const float xa = dt * (av[i] * kLog2e);
+                const float dA = exp2_hw(xa);
+                const float wi = a.zoh ? w * zoh_phi(xa * kLn2, dA) : w;
+                sv[i] = __builtin_fmaf(dA, sv[i], wi * IO::load(Bm, bo + i));
                 acc = __builtin_fmaf(IO::load(Cm, bo + i), sv[i], acc);
             }
             *reinterpret_cast<float4 *>(st) = make_float4(sv[0], sv[1], sv[2], sv[3]);
@@ -59,8 +62,10 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a, int P, int lo
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (n0 + i < a.N) {
-                    const float dA = exp2_hw(dt * (Ar[i] * kLog2e));
-                    const float sv = __builtin_fmaf(dA, st[i], w * IO::load(Bm, bo + i));
+                    const float xa = dt * (Ar[i] * kLog2e);
+                    const float dA = exp2_hw(xa);
+                    const float wi = a.zoh ? w * zoh_phi(xa * kLn2, dA) : w;
+                    const float sv = __builtin_fmaf(dA, st[i], wi * IO::load(Bm, bo + i));
                     st[i] = sv;
                     acc = __builtin_fmaf(IO::load(Cm, bo + i), sv, acc);
                 }

@@ -188,3 +188,20 @@ def test_conv_validation(lib):
     assert call(3, ok + 2) == 4
     assert lib.ssm_scan_fwd_conv(None, ok, ok, None, 4, 1, None, ok, ok, ok, ok, None, None,
                                  None, 1, None, None, 0, ok, None, None, None) == 1
+
+
+def test_flags_validation(lib):
+    """Unknown flag bits and a nonzero reserved field are rejected."""
+    ok = 4096
+    for flags, reserved, status in ((2, 0, 3), (1 << 31, 0, 3), (1, 1, 3)):
+        d = desc(chunk_size=2048)
+        d.flags, d.reserved = flags, reserved
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
+        assert lib.ssm_scan_fwd(ctypes.byref(d), ok, ok, ok, ok, ok, None, None, None, 1, ok,
+                                None, None) == status
+        du = ssm.make_desc(4, 8, 16, 0, 0, 0, flags)
+        du.reserved = reserved
+        assert lib.ssm_state_update(ctypes.byref(du), ok, ok, ok, ok, ok, ok, None, None, ok,
+                                    None) == status
+    d = desc(chunk_size=2048, flags=ssm.SSM_FLAG_ZOH)
+    assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048

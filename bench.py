@@ -39,6 +39,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 # slots (2 FLOP each); a transcendental (exp2, log2, rcp) issues at a quarter
 # of the FMA rate and so occupies 4 slots.
 VALU_PEAK_TFLOPS = 157.3
+# That published figure counts packed FP32 (v_pk_fma_f32: two FMAs per lane per
+# clock).  These kernels are compiled with packed FP32 disabled, so the vector
+# ceiling they can reach is one FMA per lane per clock:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s.
+VALU_PEAK_NONPACKED_TFLOPS = 78.6
 DEFAULT_CONFIG = "c1_mamba130m_f32"
 CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 
@@ -157,6 +162,72 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"{cfg['io_dtype']} inputs), {spent:.1f} s of oracle time"}
 
 
+def bench_decode(args, torch, ssm, dev):
+    """The decode step alone: every channel of 256 sequences advances its
+    persistent state by one token.  An HBM-bound stream: the state is read and
+    written once; per channel also u, dt, z, y, and B, C per sequence."""
+    cfg = dict(ssm_inputs.DECODE_CONFIG)
+    batch, d_inner, N = cfg["batch"], cfg["d_inner"], cfg["d_state"]
+    sets = []
+    per_set = batch * d_inner * N * 8
+    n_sets = max(2, min(8, -(-3 * CACHE_BYTES // per_set)))
+    for s in range(n_sets):
+        inp = ssm_inputs.make_update_inputs(batch, d_inner, N, io_dtype="f32", gate=True,
+                                            seed=2000 + s)
+        t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z", "A", "D", "state")}
+        t["y"] = torch.empty_like(t["u"])
+        sets.append(t)
+    torch.cuda.synchronize()
+
+    # The step is ~30 us of GPU work, close to the binding's own Python cost, so
+    # the arguments are marshalled once and the C ABI is called directly.
+    lib = ssm.load_library()
+    desc = ssm.make_desc(batch, d_inner, N, 0, 0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    argv = [[t[k].data_ptr() for k in ("state", "u", "delta", "A", "B", "C", "D", "z", "y")]
+            for t in sets]
+
+    def step(i):
+        st = lib.ssm_state_update(ctypes.byref(desc), *argv[i % n_sets], stream)
+        if st != 0:
+            raise RuntimeError(ssm.ssm_status_string(st))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = (batch * d_inner * (N * 8 + 4 * 4) + 2 * batch * N * 4 + d_inner * (N + 1) * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get("decode")
+        if tj and tj.get("bytes_per_launch") and not tj.get("stale"):
+            traffic = tj["bytes_per_launch"]
+    except (OSError, ValueError):
+        traffic = None
+    return {
+        "metric": "single-token state update, channels/sec",
+        "value": batch * d_inner / (ms * 1e-3), "unit": "channels/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode: {batch} sequences x {d_inner} channels x N={N}, "
+                               "fp32 state, gate", "batch": batch, "d_inner": d_inner,
+                   "d_state": N, "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "kernel_ms": ms},
+        "versions": versions(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +238,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--decode", action="store_true",
+                    help="time only the single-token state update of 256 sequences x 5120 "
+                         "channels x N=16 (fp32 state, gate) and report it against HBM")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -191,6 +265,9 @@ def main():
 
     ssm.load_library()
     dev = torch.device("cuda:0")
+    if args.decode:
+        print(json.dumps(bench_decode(args, torch, ssm, dev)), flush=True)
+        return
     cfg = dict(ssm_inputs.CONFIGS[args.config])
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
     io, gate = cfg["io_dtype"], cfg["gate"]
@@ -286,7 +363,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": alu_tflops / VALU_PEAK_TFLOPS,
             "traffic": traffic,
-            "kernel": "scan pass writing y (quad_kernel for N <= 16, chunk_kernel above)",
+            "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
+            "frac_nonpacked": alu_tflops / VALU_PEAK_NONPACKED_TFLOPS,
+            "kernel": "scan pass writing y (quad_kernel for N <= 16, group_kernel above)",
             "kernel_ms": kavg,
             "algorithmic_slots": slots,
             "hbm_achieved_gbs": hbm_gbs,

@@ -358,7 +358,7 @@ def test_decode_repeated_equals_scan(dev):
     assert floored_err(to_f64(state), to_f64(h)) < 1e-5
 
 
-@pytest.mark.parametrize("N", [1, 3, 4, 16, 17, 64, 256])
+@pytest.mark.parametrize("N", [1, 3, 4, 12, 16, 17, 20, 36, 64, 256])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_decode_shapes(dev, N, io):
     import torch

@@ -28,6 +28,8 @@ Pins (each checked by a ``-m "not gpu"`` test in tests/test_oracle_pins.py):
     with an initial-state term y_t += sum_n C_t[n] (prod_{s<=t} dA_s[n]) h0[n]
     per sequence, and a packing of sequences that all start from zero equals
     scanning each as its own batch row;
+  * the backward pass (``scan_bwd``): every gradient against central finite
+    differences of the forward oracle's loss on tiny inputs;
   * the causal convolution (``causal_conv1d``): impulse response = the
     reversed kernel, a constant input through the exponentially decaying
     kernel of "From FlashAttention to Mamba" §三.3 = its geometric partial
@@ -75,6 +77,9 @@ def _load():
                                         [c_int, dp, dp, dp, c_int, i64, c_int, c_int])
     lib.oracle_scan_chunked.restype = c_int
     lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [c_int]
+    lib.oracle_scan_bwd.argtypes = ([i64, i64, i64, i64] + [dp] * 8 + [c_int] + [dp] * 3 +
+                                    [dp] * 9 + [c_int])
+    lib.oracle_scan_bwd.restype = c_int
     lib.oracle_state_update.restype = c_int
     _lib = lib
     return lib
@@ -226,6 +231,37 @@ def causal_conv1d(x, weight, bias=None, silu=True, cu_seqlens=None, conv_state=N
             out[b, d, a:e] = np.convolve(seq, w[d][::-1], mode="valid") + bvec[d]
     if silu:
         out = out / (1.0 + np.exp(-out))
+    return out
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
+             initial_state=None, dlast=None, threads: int | None = None):
+    """Gradients of sum(dy * y) + sum(dlast * last_state) for the Euler scan,
+    fp64 (the reverse walk is written out in ssm_oracle.c).  Returns a dict
+    with du, ddelta (w.r.t. the raw step before bias and softplus), dz (None
+    without a gate), dA, dB, dC, dD, ddelta_bias, dh0 (w.r.t. initial_state)."""
+    lib = _load()
+    (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
+        u, delta, A, B, C, D, z, delta_bias, initial_state)
+    dy = _f64(dy, (batch, d_inner, L))
+    dlast = _f64(dlast, (batch, d_inner, N))
+    out = {k: np.zeros((batch, d_inner, L)) for k in ("du", "ddelta")}
+    out["dz"] = np.zeros((batch, d_inner, L)) if z is not None else None
+    out["dA"] = np.zeros((d_inner, N))
+    out["dB"] = np.zeros((batch, N, L))
+    out["dC"] = np.zeros((batch, N, L))
+    out["dD"] = np.zeros(d_inner)
+    out["ddelta_bias"] = np.zeros(d_inner)
+    out["dh0"] = np.zeros((batch, d_inner, N))
+    rc = lib.oracle_scan_bwd(batch, d_inner, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                             _ptr(C), _ptr(D), _ptr(z), _ptr(bias), int(bool(softplus)),
+                             _ptr(h0), _ptr(dy), _ptr(dlast), _ptr(out["du"]),
+                             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                             _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                             _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+                             threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_bwd failed ({rc})")
     return out
 
 

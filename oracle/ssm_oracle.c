@@ -286,6 +286,164 @@ static int check_dims(int64_t batch, int64_t d_inner, int64_t d_state, int64_t s
     return batch >= 0 && d_inner >= 0 && d_state >= 1 && seqlen >= 0;
 }
 
+/* ------------------------------------------------------------ backward */
+
+/* Gradients of the loss  sum_t dy_t y_t + sum_n dlast_n h_{L-1,n}  (dy and
+ * dlast are the upstream gradients of y and last_state) with respect to every
+ * input of the Euler scan, by reverse-mode differentiation of the recurrence
+ * written out by hand -- the backward step the ufo.work article, §2.2, pairs
+ * with the fused forward (recompute the states, then walk back).  For one
+ * row (b, d), with x_t = delta_raw_t + bias, dt_t = softplus(x_t) (or x_t),
+ * a_t = exp(dt_t A), w_t = dt_t u_t, o_t = C_t . h_t + D u_t and
+ * g_t = silu(z_t) (or 1), walking t = L-1 .. 0 with G = dlast:
+ *   do_t   = dy_t g_t                      dz_t  = dy_t o_t silu'(z_t)
+ *   dh_t   = G + do_t C_t                  dC_t += do_t h_t,  dB_t += w_t dh_t
+ *   dw_t   = dh_t . B_t                    da_t  = dh_t h_{t-1}   (h_{-1} = h0)
+ *   ddt_t  = dw_t u_t + sum_n da_t A a_t   du_t  = do_t D + dw_t dt_t
+ *   dA    += da_t a_t dt_t                 dD   += do_t u_t
+ *   G      = dh_t a_t                      ddelta_t = ddt_t softplus'(x_t)
+ *   dbias += ddelta_t;    finally dh0 = G.
+ * dB and dC sum over the channels of a batch row, dA, dD and dbias over the
+ * batch rows (and tokens): per-thread partial buffers added in a fixed order. */
+typedef struct {
+    const scan_args *a;
+    const double *dy, *dlast;
+    double *du, *ddelta, *dz, *dh0;
+    double *dA_rows, *dD_rows, *dbias_rows;   /* (batch, d_inner, N) / (batch, d_inner) */
+    double *dB_part, *dC_part;                /* per worker: (batch, N, L) */
+    int worker, n_workers, status;
+} bwd_worker;
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void *bwd_main(void *p) {
+    bwd_worker *w = (bwd_worker *)p;
+    const scan_args *a = w->a;
+    const int64_t N = a->d_state, L = a->seqlen, Dn = a->d_inner;
+    double *hs = malloc(sizeof(double) * (size_t)((L + 1) * N));   /* h_{-1} .. h_{L-1} */
+    double *G = malloc(sizeof(double) * (size_t)N);
+    double *dh = malloc(sizeof(double) * (size_t)N);
+    double *dBp = w->dB_part + (size_t)w->worker * (size_t)(a->batch * N * L);
+    double *dCp = w->dC_part + (size_t)w->worker * (size_t)(a->batch * N * L);
+    if (!hs || !G || !dh) { free(hs); free(G); free(dh); w->status = -1; return NULL; }
+    for (int64_t r = w->worker; r < a->batch * Dn; r += w->n_workers) {
+        const int64_t b = r / Dn, d = r % Dn;
+        const int64_t row = (b * Dn + d) * L;
+        /* forward, keeping every state */
+        for (int64_t n = 0; n < N; ++n) hs[n] = a->h0 ? a->h0[(b * Dn + d) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double dt = step_size(a, d, a->delta[row + t]), u = a->u[row + t];
+            for (int64_t n = 0; n < N; ++n)
+                hs[(t + 1) * N + n] = exp(dt * a->A[d * N + n]) * hs[t * N + n] +
+                                      dt * a->B[(b * N + n) * L + t] * u;
+        }
+        /* backward */
+        for (int64_t n = 0; n < N; ++n) G[n] = w->dlast ? w->dlast[(b * Dn + d) * N + n] : 0.0;
+        double dD_acc = 0.0, dbias_acc = 0.0;
+        double *dA_row = w->dA_rows + (b * Dn + d) * N;
+        for (int64_t n = 0; n < N; ++n) dA_row[n] = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const double x = a->delta[row + t] + (a->delta_bias ? a->delta_bias[d] : 0.0);
+            const double dt = a->softplus_flag ? softplus(x) : x;
+            const double u = a->u[row + t];
+            const double *ht = hs + (t + 1) * N, *hp = hs + t * N;
+            double o = 0.0;
+            for (int64_t n = 0; n < N; ++n) o += a->C[(b * N + n) * L + t] * ht[n];
+            if (a->D) o += a->D[d] * u;
+            double g = 1.0;
+            if (a->z) {
+                const double zt = a->z[row + t], sg = sigmoid(zt);
+                g = zt * sg;
+                w->dz[row + t] = w->dy[row + t] * o * sg * (1.0 + zt * (1.0 - sg));
+            }
+            const double dO = w->dy[row + t] * g;
+            dD_acc += dO * u;
+            double dw = 0.0, ddt = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double Bn = a->B[(b * N + n) * L + t], Cn = a->C[(b * N + n) * L + t];
+                const double An = a->A[d * N + n], at = exp(dt * An);
+                dh[n] = G[n] + dO * Cn;
+                dCp[(b * N + n) * L + t] += dO * ht[n];
+                dBp[(b * N + n) * L + t] += dt * u * dh[n];
+                dw += dh[n] * Bn;
+                const double da = dh[n] * hp[n];
+                ddt += da * An * at;
+                dA_row[n] += da * at * dt;
+                G[n] = dh[n] * at;
+            }
+            ddt += dw * u;
+            w->du[row + t] = dO * (a->D ? a->D[d] : 0.0) + dw * dt;
+            const double dx = a->softplus_flag ? ddt * sigmoid(x) : ddt;
+            w->ddelta[row + t] = dx;
+            dbias_acc += dx;
+        }
+        for (int64_t n = 0; n < N; ++n) w->dh0[(b * Dn + d) * N + n] = G[n];
+        w->dD_rows[b * Dn + d] = dD_acc;
+        w->dbias_rows[b * Dn + d] = dbias_acc;
+    }
+    free(hs); free(G); free(dh);
+    return NULL;
+}
+
+int oracle_scan_bwd(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seqlen,
+                    const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *delta_bias,
+                    int softplus_flag, const double *initial_state, const double *dy,
+                    const double *dlast, double *du, double *ddelta, double *dA, double *dB,
+                    double *dC, double *dD, double *dz, double *ddelta_bias, double *dh0,
+                    int n_threads) {
+    if (!check_dims(batch, d_inner, d_state, seqlen)) return -1;
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC || !dD ||
+        !ddelta_bias || !dh0 || (z && !dz))
+        return -1;
+    const int64_t N = d_state, L = seqlen, rows = batch * d_inner;
+    scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
+                   initial_state, softplus_flag, NULL, NULL, 0, 0, 0};
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > rows) n_threads = (int)(rows > 0 ? rows : 1);
+    const size_t part = (size_t)(batch * N * L);
+    double *dBp = calloc((size_t)n_threads * part + 1, sizeof(double));
+    double *dCp = calloc((size_t)n_threads * part + 1, sizeof(double));
+    double *dA_rows = calloc((size_t)(rows * N) + 1, sizeof(double));
+    double *dD_rows = calloc((size_t)rows + 1, sizeof(double));
+    double *db_rows = calloc((size_t)rows + 1, sizeof(double));
+    pthread_t *tid = malloc(sizeof(pthread_t) * (size_t)n_threads);
+    bwd_worker *wk = malloc(sizeof(bwd_worker) * (size_t)n_threads);
+    int status = 0;
+    if (!dBp || !dCp || !dA_rows || !dD_rows || !db_rows || !tid || !wk) status = -1;
+    int started = 0;
+    for (int i = 0; i < n_threads && status == 0; ++i) {
+        wk[i] = (bwd_worker){&a, dy, dlast, du, ddelta, dz, dh0, dA_rows, dD_rows, db_rows,
+                             dBp, dCp, i, n_threads, 0};
+        if (i == 0) continue;
+        if (pthread_create(&tid[i], NULL, bwd_main, &wk[i]) != 0) { status = -1; break; }
+        started = i;
+    }
+    if (status == 0) bwd_main(&wk[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+    for (int i = 0; i < n_threads && status == 0; ++i) status = wk[i].status;
+    if (status == 0) {
+        /* fixed-order reductions */
+        for (size_t k = 0; k < part; ++k) {
+            double sb = 0.0, sc = 0.0;
+            for (int i = 0; i < n_threads; ++i) { sb += dBp[(size_t)i * part + k]; sc += dCp[(size_t)i * part + k]; }
+            dB[k] = sb; dC[k] = sc;
+        }
+        for (int64_t d = 0; d < d_inner; ++d) {
+            double sD = 0.0, sb = 0.0;
+            for (int64_t b = 0; b < batch; ++b) { sD += dD_rows[b * d_inner + d]; sb += db_rows[b * d_inner + d]; }
+            dD[d] = sD; ddelta_bias[d] = sb;
+            for (int64_t n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int64_t b = 0; b < batch; ++b) s += dA_rows[(b * d_inner + d) * N + n];
+                dA[d * N + n] = s;
+            }
+        }
+    }
+    free(dBp); free(dCp); free(dA_rows); free(dD_rows); free(db_rows); free(tid); free(wk);
+    return status;
+}
+
 /* ------------------------------------------------------------ exports */
 
 int oracle_scan_fwd(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seqlen,

@@ -206,6 +206,42 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
                             const float *A, const void *B, const void *C, const float *D,
                             const void *z, void *y, ssm_stream_t stream);
 
+/* Bytes of device workspace that ssm_scan_bwd needs for this descriptor;
+ * 0 for an invalid or unsupported descriptor.  Host-only. */
+size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
+
+/* Backward pass of the scan: the gradients of the loss
+ *   sum(dy * y) + sum(dlast * last_state)
+ * with respect to every input, for upstream gradients dy (of y) and dlast
+ * (of last_state).  It keeps states only at 8-token boundaries and recomputes
+ * the rest while walking back (ufo.work article, §2.2: fine-grained
+ * checkpoints, recompute inside the chunk); the reverse recurrence of the
+ * state gradient is joined across chunks by transfer operators like the
+ * forward one (§3.1).
+ * Supported: d_state <= 16, Euler discretisation (flags == 0), one sequence
+ * per batch row (no packing), no fused convolution; otherwise
+ * SSM_ERR_UNSUPPORTED.
+ * Inputs: as ssm_scan_fwd_ex (initial_state may be NULL), plus
+ *   dy             (batch, d_inner, L) io_dtype
+ *   dlast          (batch, d_inner, N) float32 or NULL (zero)
+ * Outputs, all float32, all overwritten (none is accumulated into):
+ *   du, ddelta     (batch, d_inner, L); ddelta is the gradient of the raw
+ *                  delta (before delta_bias and softplus)
+ *   dA             (d_inner, N)
+ *   dB, dC         (batch, N, L)
+ *   dD             (d_inner) or NULL (not written)
+ *   dz             (batch, d_inner, L); required when z is given
+ *   ddelta_bias    (d_inner) or NULL (not written)
+ *   dh0            (batch, d_inner, N) or NULL: gradient of initial_state
+ * Needs desc->workspace of ssm_scan_bwd_workspace_bytes(desc) bytes.  All
+ * sums run in a fixed order: results are identical from run to run. */
+ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, const float *initial_state,
+                        const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                        float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                        float *dh0, ssm_stream_t stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssm_status_string(int status);
 

@@ -18,7 +18,7 @@ import ctypes
 import os
 from pathlib import Path
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_state_update", "ssm_scan_workspace_bytes",
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_state_update", "ssm_scan_workspace_bytes",
            "ssm_scan_chunk_size", "ssm_status_string", "SsmError", "load_library",
            "LIB_PATH"]
 
@@ -82,6 +82,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_fwd_conv.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [dp]
+    lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd.argtypes = [dp] + [vp] * 8 + [ctypes.c_int] + [vp] * 12 + [vp]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_version.argtypes = []
@@ -294,6 +298,52 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
                                n_seqs, _ptr(y), _ptr(last_state), _ptr(u_out), _stream(dev))
     _check(st)
     return y, last_state, u_out
+
+
+def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
+                 initial_state=None, dlast=None, chunk_size=0, workspace=None):
+    """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
+    respect to all its inputs (d_state <= 16, Euler).  Returns a dict of
+    float32 tensors: du, ddelta (of the raw delta), dA, dB, dC, dD (None
+    without D), dz (None without z), ddelta_bias, dh0 (None without
+    initial_state)."""
+    torch = _torch()
+    lib = load_library()
+    batch, d_inner, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev, io = u.device, u.dtype
+    code = _io_code(io)
+    for t, name, shape in ((u, "u", (batch, d_inner, L)), (delta, "delta", (batch, d_inner, L)),
+                           (B, "B", (batch, N, L)), (C, "C", (batch, N, L)),
+                           (z, "z", (batch, d_inner, L)), (dy, "dy", (batch, d_inner, L))):
+        _expect(t, name, shape, io, dev)
+    for t, name, shape in ((A, "A", (d_inner, N)), (D, "D", (d_inner,)),
+                           (delta_bias, "delta_bias", (d_inner,)),
+                           (initial_state, "initial_state", (batch, d_inner, N)),
+                           (dlast, "dlast", (batch, d_inner, N))):
+        _expect(t, name, shape, torch.float32, dev)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    out = {"du": f32(batch, d_inner, L), "ddelta": f32(batch, d_inner, L), "dA": f32(d_inner, N),
+           "dB": f32(batch, N, L), "dC": f32(batch, N, L),
+           "dD": f32(d_inner) if D is not None else None,
+           "dz": f32(batch, d_inner, L) if z is not None else None,
+           "ddelta_bias": f32(d_inner),
+           "dh0": f32(batch, d_inner, N) if initial_state is not None else None}
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                          _ptr(initial_state), _ptr(dy), _ptr(dlast), _ptr(out["du"]),
+                          _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                          _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                          _ptr(out["dh0"]), _stream(dev))
+    _check(st)
+    return out
 
 
 def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None, zoh=False):

@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD = ROOT / "_build"
 LIB = PKG / "libssm.so"
-SOURCES = ["ssm_api.hip", "ssm_scan.hip", "ssm_update.hip"]
+SOURCES = ["ssm_api.hip", "ssm_scan.hip", "ssm_update.hip", "ssm_bwd.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -114,6 +114,53 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
 
 bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// Backward plan: the forward plan's chunks, at most 32 of them (each chunk
+// folds its neighbours' operators itself), and the workspace of the backward.
+constexpr int64_t kBwdTile = 8;
+
+struct BwdPlan {
+    Plan f;
+    int64_t n_tiles = 0;
+    size_t off_gend = 0, off_bdtsum = 0, off_ckpt = 0, off_dBp = 0, off_dCp = 0, off_dAp = 0,
+           off_dDp = 0, off_dbp = 0, bytes = 0;
+};
+
+ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
+    const ssm_status st = make_plan(d, &p->f);
+    if (st != SSM_OK) return st;
+    if (d->d_state > 16 || d->flags != 0) return SSM_ERR_UNSUPPORTED;
+    Plan &f = p->f;
+    const int64_t L = d->seqlen;
+    if (L == 0 || d->batch * d->d_inner == 0) { p->bytes = 0; return SSM_OK; }
+    if (f.J > kFoldMaxChunks) {
+        int64_t k = (L + kFoldMaxChunks - 1) / kFoldMaxChunks;
+        k = (k + 15) / 16 * 16;
+        f.K = k < L ? k : L;
+        f.J = (L + f.K - 1) / f.K;
+    }
+    f.fold = 1;
+    const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
+    const size_t J = static_cast<size_t>(f.J);
+    p->n_tiles = (L + kBwdTile - 1) / kBwdTile;
+    size_t off = 0;
+    if (f.J > 1) {
+        f.off_hend = off; off += align_up(B * D * J * 16 * sizeof(float));
+        f.off_dtsum = off; off += align_up(B * D * J * sizeof(float));
+        f.off_keep = off; off += align_up(B * J * sizeof(float));
+        p->off_gend = off; off += align_up(B * D * J * 16 * sizeof(float));
+        p->off_bdtsum = off; off += align_up(B * D * J * sizeof(float));
+    }
+    p->off_ckpt = off; off += align_up(B * D * static_cast<size_t>(p->n_tiles) * 16 * sizeof(float));
+    const size_t part = B * static_cast<size_t>(f.n_cblk) * 16 * static_cast<size_t>(L);
+    p->off_dBp = off; off += align_up(part * sizeof(float));
+    p->off_dCp = off; off += align_up(part * sizeof(float));
+    p->off_dAp = off; off += align_up(B * D * J * 16 * sizeof(float));
+    p->off_dDp = off; off += align_up(B * D * J * sizeof(float));
+    p->off_dbp = off; off += align_up(B * D * J * sizeof(float));
+    p->bytes = off;
+    return SSM_OK;
+}
+
 }  // namespace
 
 namespace {
@@ -266,6 +313,81 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
     return ssm::launch_update(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc) {
+    BwdPlan p;
+    return make_bwd_plan(desc, &p) == SSM_OK ? p.bytes : 0;
+}
+
+ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, const float *initial_state,
+                        const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                        float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                        float *dh0, ssm_stream_t stream) {
+    BwdPlan p;
+    ssm_status st = make_bwd_plan(desc, &p);
+    if (st != SSM_OK) return st;
+    const int64_t rows = desc->batch * desc->d_inner;
+    if (rows == 0 || desc->seqlen == 0) {
+        // no tokens: every gradient of a token is empty; those of the
+        // parameters are zero and dh0 = dlast
+        const hipStream_t s = stream;
+        auto zero = [&](float *ptr, size_t n) {
+            return ptr ? ssm::launch_fill_zero(ptr, n, s) : hipSuccess;
+        };
+        const size_t N = static_cast<size_t>(desc->d_state), Dn = static_cast<size_t>(desc->d_inner);
+        hipError_t e = zero(dA, Dn * N);
+        if (e == hipSuccess) e = zero(dD, Dn);
+        if (e == hipSuccess) e = zero(ddelta_bias, Dn);
+        if (e == hipSuccess && dh0) {
+            const size_t n = static_cast<size_t>(rows) * N;
+            e = dlast ? hipMemcpyAsync(dh0, dlast, n * sizeof(float), hipMemcpyDeviceToDevice, s)
+                      : ssm::launch_fill_zero(dh0, n, s);
+        }
+        return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+        return SSM_ERR_NULL_ARG;
+    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
+    if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+        !aligned(z, esz) || !aligned(dy, esz) || !aligned(A, 4) || !aligned(D, 4) ||
+        !aligned(delta_bias, 4) || !aligned(initial_state, 4) || !aligned(dlast, 4) ||
+        !aligned(du, 4) || !aligned(ddelta, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dz, 4) || !aligned(ddelta_bias, 4) ||
+        !aligned(dh0, 4))
+        return SSM_ERR_MISALIGNED;
+    if (z && !dz) return SSM_ERR_NULL_ARG;
+    if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
+    if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
+    char *ws = static_cast<char *>(desc->workspace);
+    const Plan &f = p.f;
+    ScanArgs a{};
+    a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state; a.L = desc->seqlen;
+    a.G = f.G; a.K = f.K; a.J = f.J; a.n_cblk = f.n_cblk; a.quad = f.quad;
+    a.bf16 = desc->io_dtype == SSM_BF16;
+    a.softplus = softplus_flag != 0;
+    a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.h0 = initial_state;
+    a.n_seqs = desc->batch;
+    ssm::BwdArgs g{};
+    g.dy = dy; g.dlast = dlast; g.du = du; g.ddelta = ddelta; g.dz = dz; g.dA = dA; g.dB = dB;
+    g.dC = dC; g.dD = dD; g.dbias = ddelta_bias; g.dh0 = dh0; g.n_tiles = p.n_tiles;
+    if (f.J > 1) {
+        a.hend = reinterpret_cast<float *>(ws + f.off_hend);
+        a.dtsum = reinterpret_cast<float *>(ws + f.off_dtsum);
+        a.keep = reinterpret_cast<float *>(ws + f.off_keep);
+        g.gend = reinterpret_cast<float *>(ws + p.off_gend);
+        g.bdtsum = reinterpret_cast<float *>(ws + p.off_bdtsum);
+    }
+    g.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
+    g.dBp = reinterpret_cast<float *>(ws + p.off_dBp);
+    g.dCp = reinterpret_cast<float *>(ws + p.off_dCp);
+    g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
+    g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
+    g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
+    return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 const char *ssm_status_string(int status) {
     switch (status) {
         case SSM_OK: return "SSM_OK";
@@ -279,6 +401,6 @@ const char *ssm_status_string(int status) {
     }
 }
 
-int ssm_version(void) { return 300; }
+int ssm_version(void) { return 400; }
 
 }  // extern "C"

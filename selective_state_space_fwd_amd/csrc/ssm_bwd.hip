@@ -1,0 +1,527 @@
+// ssm_bwd.hip -- backward pass of the selective scan (d_state <= 16) for gfx950.
+//
+// The ufo.work article "Mamba hardware-aware operator fusion and
+// selective-scan parallelisation", §2.2, pairs the fused forward kernel with a
+// backward that keeps only states at chunk boundaries and recomputes the rest
+// inside the chunk while walking back.  For one channel, with
+// a_t = exp(dt_t A), w_t = dt_t u_t and the upstream gradients dy and dlast,
+// the reverse walk is
+//   dh_t = G + do_t C_t            (G: gradient arriving from token t + 1)
+//   dC_t += do_t h_t,  dB_t += w_t dh_t,  dA += dh_t h_{t-1} a_t dt_t
+//   ddt_t = (dh_t . B_t) u_t + sum_n dh_t h_{t-1} A a_t,   du_t = do_t D + (dh_t . B_t) dt_t
+//   G = dh_t a_t
+// where do_t = dy_t silu(z_t) and dz_t = dy_t o_t silu'(z_t), o_t = C_t . h_t + D u_t.
+// Like the forward, G obeys a linear recurrence, now running backwards, with
+// the same per-chunk decay exp(A sum dt): chunks are joined by transfer
+// operators in the reverse direction.
+//
+// Passes (J chunks of K tokens, J <= 32):
+//   1. the forward aggregate pass (quad_kernel<FULL = false>): chunk end
+//      states from zero;
+//   2. bwd_agg_kernel: per chunk 1 .. J-1, the gradient that leaves the chunk
+//      to its left when none arrives from its right, and its sum of dt;
+//   3. bwd_kernel: per chunk, the start state (fold of pass 1) and the
+//      arriving gradient (fold of pass 2 from the right, starting at dlast);
+//      a forward sweep stores the state entering every 8-token tile; then the
+//      tiles are walked in reverse: each recomputes its 8 states per lane from
+//      its checkpoint (in registers) and walks them back.  dB and dC sum over
+//      the 16 channels of the wavefront through LDS, and over channel blocks
+//      in pass 4;
+//   4. bwd_reduce_kernel: the fixed-order sums of the per-block partials of
+//      dB, dC and the per-chunk partials of dA, dD and dbias.
+// Lane mapping as the forward quad kernel: lane l serves channel l % 16 and
+// states 4q .. 4q+3, q = l / 16; tile pieces: row l / 4 (a channel, or a state
+// of B and C), tokens 2 (l % 4) and 2 (l % 4) + 1.
+#include "ssm_common.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kT = 8;        // tokens per backward tile
+constexpr int kQC = 16;      // channels per wavefront
+
+template <class IO>
+__device__ __forceinline__ float ld_clamped(const typename IO::T *p, size_t base, int64_t t,
+                                           int64_t t_end) {
+    return IO::load(p, base + (t < t_end ? t : t_end - 1));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) {
+    return rcp_hw(1.0f + exp2_hw(-x * kLog2e));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ pass 2
+// Grid (n_cblk * batch, J - 1): chunk j = blockIdx.y + 1.
+template <class IO>
+__global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
+    using IT = typename IO::T;
+    __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_do[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_C[kT * 16];
+    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
+    const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
+    const IT *__restrict__ dy = static_cast<const IT *>(g.dy);
+
+    const int lane = threadIdx.x;
+    const int c = lane & 15, q = lane >> 4;
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t j = static_cast<int64_t>(blockIdx.y) + 1;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * kQC;
+    const int64_t d = d0 + c;
+    const bool lane_ok = d < a.D;
+    const int64_t L = a.L;
+    const int64_t t_begin = j * a.K;
+    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
+    const bool gate = a.z != nullptr;
+
+    const int r = lane >> 2, sc = (lane & 3) * 2;
+    const int64_t dr = d0 + r;
+    const bool row_ok = dr < a.D;
+    const int64_t drc = row_ok ? dr : a.D - 1;
+    const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
+    const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
+    const bool st_ok = r < a.N;
+    const size_t sbase = (static_cast<size_t>(b) * a.N + (st_ok ? r : a.N - 1)) * L;
+
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    float A2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+        A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
+    }
+    float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dts = 0.0f;
+    const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
+    for (int64_t ti = ntile - 1; ti >= 0; --ti) {
+        const int64_t t0 = t_begin + ti * kT;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = t0 + sc + i;
+            const bool ok = row_ok && t < t_end;
+            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
+            const float gg = gate ? silu_f32(ld_clamped<IO>(z, rbase, t, t_end)) : 1.0f;
+            const float dO = ok ? ld_clamped<IO>(dy, rbase, t, t_end) * gg : 0.0f;
+            s_dt[r * kT + sc + i] = dt;
+            s_do[r * kT + sc + i] = dO;
+            const float cv = ld_clamped<IO>(Cm, sbase, t, t_end);
+            s_C[(sc + i) * 16 + r] = st_ok ? cv : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = kT - 1; t >= 0; --t) {
+            const float dt = s_dt[c * kT + t], dO = s_do[c * kT + t];
+            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) G[k] = __builtin_fmaf(dO, cv[k], G[k]) * exp2_hw(dt * A2[k]);
+            dts += dt;
+        }
+        __syncthreads();
+    }
+    if (!lane_ok) return;
+    const size_t cd = (static_cast<size_t>(b) * a.D + d) * a.J + j;
+    *reinterpret_cast<float4 *>(g.gend + cd * 16 + 4 * q) = make_float4(G[0], G[1], G[2], G[3]);
+    if (q == 0) g.bdtsum[cd] = dts;
+}
+
+// ------------------------------------------------------------ pass 3
+// Grid (n_cblk * batch, J).
+template <class IO>
+__global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
+    using IT = typename IO::T;
+    // per (channel, token) values of the tile: [c][t]
+    __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_w[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_do[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_sig[kQC * kT];   // softplus'(x)
+    __shared__ __attribute__((aligned(16))) float s_u[kQC * kT];
+    __shared__ __attribute__((aligned(16))) float s_ds[kQC * kT];    // dy silu'(z)
+    __shared__ __attribute__((aligned(16))) float s_o[kQC * kT];     // C.h + D u
+    // B and C of the tile, token-major: [t][n]
+    __shared__ __attribute__((aligned(16))) float s_B[kT * 16];
+    __shared__ __attribute__((aligned(16))) float s_C[kT * 16];
+    // row partials of dh.B and of sum_n dh h_prev A a: [t][q][c]
+    __shared__ __attribute__((aligned(16))) float s_rw[kT * 64];
+    __shared__ __attribute__((aligned(16))) float s_rd[kT * 64];
+    // per-channel contributions to dB and dC: [t][c][n]
+    __shared__ __attribute__((aligned(16))) float s_gB[kT * kQC * 16];
+    __shared__ __attribute__((aligned(16))) float s_gC[kT * kQC * 16];
+
+    const IT *__restrict__ u = static_cast<const IT *>(a.u);
+    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
+    const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    const IT *__restrict__ Bm = static_cast<const IT *>(a.B);
+    const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
+    const IT *__restrict__ dy = static_cast<const IT *>(g.dy);
+
+    const int lane = threadIdx.x;
+    const int c = lane & 15, q = lane >> 4;
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t cblk = blockIdx.x % a.n_cblk;
+    const int64_t j = blockIdx.y;
+    const int64_t d0 = cblk * kQC;
+    const int64_t d = d0 + c;
+    const bool lane_ok = d < a.D;
+    const int64_t L = a.L;
+    const int64_t t_begin = j * a.K;
+    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
+    const bool gate = a.z != nullptr;
+
+    // tile pieces
+    const int r = lane >> 2, sc = (lane & 3) * 2;
+    const int64_t dr = d0 + r;
+    const bool row_ok = dr < a.D;
+    const int64_t drc = row_ok ? dr : a.D - 1;
+    const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
+    const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
+    const bool st_ok = r < a.N;
+    const size_t sbase = (static_cast<size_t>(b) * a.N + (st_ok ? r : a.N - 1)) * L;
+
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    float A2[4], An[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+        An[k] = (lane_ok && n < a.N) ? v : 0.0f;
+        A2[k] = An[k] * kLog2e;
+    }
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
+    const size_t cd = cd0 + j;
+
+    // ---- start state of the chunk (forward) and the gradient arriving at its
+    // last token (backward)
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (j == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = 4 * q + k;
+            const float v = a.h0 ? a.h0[(static_cast<size_t>(b) * a.D + dcl) * a.N +
+                                        (n < a.N ? n : a.N - 1)] : 0.0f;
+            h[k] = (lane_ok && n < a.N) ? v : 0.0f;
+        }
+    } else {
+        for (int64_t i = 0; i < j; ++i) {
+            const float sdt = a.dtsum[cd0 + i];
+            const bool kept = a.keep[b * a.J + i] != 0.0f;
+            const float4 v = *reinterpret_cast<const float4 *>(a.hend + (cd0 + i) * 16 + 4 * q);
+            const float he[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                h[k] = __builtin_fmaf(kept ? exp2_hw(A2[k] * sdt) : 0.0f, h[k], he[k]);
+        }
+        if (!lane_ok) h[0] = h[1] = h[2] = h[3] = 0.0f;
+    }
+    float G[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        const float v = g.dlast ? g.dlast[(static_cast<size_t>(b) * a.D + dcl) * a.N +
+                                          (n < a.N ? n : a.N - 1)] : 0.0f;
+        G[k] = (lane_ok && n < a.N) ? v : 0.0f;
+    }
+    for (int64_t i = a.J - 1; i > j; --i) {
+        const float sdt = g.bdtsum[cd0 + i];
+        const float4 v = *reinterpret_cast<const float4 *>(g.gend + (cd0 + i) * 16 + 4 * q);
+        const float ge[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) G[k] = __builtin_fmaf(exp2_hw(A2[k] * sdt), G[k], ge[k]);
+    }
+    if (!lane_ok) G[0] = G[1] = G[2] = G[3] = 0.0f;
+
+    const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
+    float *ck = g.ckpt + (static_cast<size_t>(b) * a.D + dcl) * g.n_tiles * 16 + 4 * q;
+
+    // ---- forward sweep: the state entering every tile
+    for (int64_t ti = 0; ti < ntile; ++ti) {
+        const int64_t t0 = t_begin + ti * kT;
+        if (lane_ok)
+            *reinterpret_cast<float4 *>(ck + (t0 / kT) * 16) = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = t0 + sc + i;
+            const bool ok = row_ok && t < t_end;
+            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
+            const float uu = ok ? ld_clamped<IO>(u, rbase, t, t_end) : 0.0f;
+            s_dt[r * kT + sc + i] = dt;
+            s_w[r * kT + sc + i] = dt * uu;
+            const float bv = ld_clamped<IO>(Bm, sbase, t, t_end);
+            s_B[(sc + i) * 16 + r] = st_ok ? bv : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
+            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
+            const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) h[k] = __builtin_fmaf(exp2_hw(dt * A2[k]), h[k], w * bv[k]);
+        }
+        __syncthreads();
+    }
+
+    // ---- reverse sweep
+    float dA_acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dD_acc[2] = {0.0f, 0.0f}, db_acc[2] = {0.0f, 0.0f};
+    const float Dv_lane = (lane_ok && a.Dskip) ? a.Dskip[dcl] : 0.0f;
+    for (int64_t ti = ntile - 1; ti >= 0; --ti) {
+        const int64_t t0 = t_begin + ti * kT;
+        // (a) the tile's inputs
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = t0 + sc + i;
+            const bool ok = row_ok && t < t_end;
+            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
+            const float sig = a.softplus ? sigmoid_f32(x) : 1.0f;
+            const float uu = ok ? ld_clamped<IO>(u, rbase, t, t_end) : 0.0f;
+            const float dyv = ok ? ld_clamped<IO>(dy, rbase, t, t_end) : 0.0f;
+            float gg = 1.0f, dsl = 0.0f;
+            if (gate) {
+                const float zz = ld_clamped<IO>(z, rbase, t, t_end);
+                const float sz = sigmoid_f32(zz);
+                gg = zz * sz;
+                dsl = sz * __builtin_fmaf(zz, 1.0f - sz, 1.0f);
+            }
+            const int o = r * kT + sc + i;
+            s_dt[o] = dt;
+            s_w[o] = dt * uu;
+            s_do[o] = dyv * gg;
+            s_sig[o] = sig;
+            s_u[o] = uu;
+            s_ds[o] = dyv * dsl;
+            const float bv = ld_clamped<IO>(Bm, sbase, t, t_end);
+            const float cv = ld_clamped<IO>(Cm, sbase, t, t_end);
+            s_B[(sc + i) * 16 + r] = st_ok ? bv : 0.0f;
+            s_C[(sc + i) * 16 + r] = st_ok ? cv : 0.0f;
+        }
+        __syncthreads();
+
+        // (b) recompute the tile's states from its checkpoint
+        float hs[4];
+        {
+            const float4 v = *reinterpret_cast<const float4 *>(ck + (t0 / kT) * 16);
+            hs[0] = lane_ok ? v.x : 0.0f; hs[1] = lane_ok ? v.y : 0.0f;
+            hs[2] = lane_ok ? v.z : 0.0f; hs[3] = lane_ok ? v.w : 0.0f;
+        }
+        float hh[kT][4];
+        float part[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
+            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
+            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+            const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
+            float p = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float prev = t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
+                hh[t][k] = __builtin_fmaf(exp2_hw(dt * A2[k]), prev, w * bv[k]);
+                p = __builtin_fmaf(cv[k], hh[t][k], p);
+            }
+            part[t] = p;
+        }
+        // o_t = C_t . h_t + D u_t: the 4 row partials meet in a transposing
+        // butterfly (as in the forward kernel); row q ends with token g4 + q
+#pragma unroll
+        for (int g4 = 0; g4 < kT; g4 += 4) {
+            const auto s01 = __builtin_amdgcn_permlane16_swap(
+                __float_as_uint(part[g4]), __float_as_uint(part[g4 + 1]), false, false);
+            const auto s23 = __builtin_amdgcn_permlane16_swap(
+                __float_as_uint(part[g4 + 2]), __float_as_uint(part[g4 + 3]), false, false);
+            const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+            const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+            const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01),
+                                                            __float_as_uint(p23), false, false);
+            const int o = c * kT + g4 + q;
+            s_o[o] = __builtin_fmaf(Dv_lane, s_u[o], __uint_as_float(s[0]) + __uint_as_float(s[1]));
+        }
+
+        // (c) walk the tile back
+#pragma unroll
+        for (int t = kT - 1; t >= 0; --t) {
+            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t], dO = s_do[c * kT + t];
+            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
+            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+            const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
+            float gb[4], gc[4];
+            float dw = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float prev = t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
+                const float dh = __builtin_fmaf(dO, cv[k], G[k]);
+                const float at = exp2_hw(dt * A2[k]);
+                gc[k] = dO * hh[t][k];
+                gb[k] = w * dh;
+                dw = __builtin_fmaf(dh, bv[k], dw);
+                const float da = dh * prev;
+                dd = __builtin_fmaf(da * An[k], at, dd);
+                dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
+                G[k] = dh * at;
+            }
+            *reinterpret_cast<float4 *>(&s_gB[(t * kQC + c) * 16 + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
+            *reinterpret_cast<float4 *>(&s_gC[(t * kQC + c) * 16 + 4 * q]) = make_float4(gc[0], gc[1], gc[2], gc[3]);
+            s_rw[(t * 4 + q) * kQC + c] = dw;
+            s_rd[(t * 4 + q) * kQC + c] = dd;
+        }
+        __syncthreads();
+
+        // (d) per (channel, token): du, ddelta, dz; lane -> token lane % 8,
+        // channels lane / 8 and lane / 8 + 8
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int ch = (lane >> 3) + 8 * e;
+            const int t = lane & 7;
+            const int64_t tok = t0 + t;
+            const int o = ch * kT + t;
+            float dw = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                dw += s_rw[(t * 4 + qq) * kQC + ch];
+                dd += s_rd[(t * 4 + qq) * kQC + ch];
+            }
+            const int64_t dch = d0 + ch;
+            const bool ok = dch < a.D && tok < t_end;
+            const float dt = s_dt[o], uu = s_u[o], dO = s_do[o];
+            const float Dv = (ok && a.Dskip) ? a.Dskip[dch] : 0.0f;
+            const float du = __builtin_fmaf(dO, Dv, dw * dt);
+            const float ddl = __builtin_fmaf(dw, uu, dd) * s_sig[o];
+            if (ok) {
+                const size_t off = (static_cast<size_t>(b) * a.D + dch) * L + tok;
+                g.du[off] = du;
+                g.ddelta[off] = ddl;
+                if (gate) g.dz[off] = s_ds[o] * s_o[o];
+                dD_acc[e] = __builtin_fmaf(dO, uu, dD_acc[e]);
+                db_acc[e] += ddl;
+            }
+        }
+        // (e) dB, dC: sum over the 16 channels; lane -> tensor lane / 32,
+        // states 4 ((lane / 8) % 4) .. +3, token lane % 8
+        {
+            const int which = lane >> 5;
+            const int n4 = (lane >> 3) & 3;
+            const int t = lane & 7;
+            const float *src = which ? s_gC : s_gB;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ch = 0; ch < kQC; ++ch) {
+                const float4 v = *reinterpret_cast<const float4 *>(&src[(t * kQC + ch) * 16 + 4 * n4]);
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            const int64_t tok = t0 + t;
+            if (tok < t_end) {
+                float *dst = (which ? g.dCp : g.dBp) +
+                             ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
+                dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- chunk results
+    // dD, dbias: the 8 lanes of a channel pair meet in a butterfly
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        for (int off = 1; off < 8; off <<= 1) {
+            dD_acc[e] += __shfl_xor(dD_acc[e], off, 64);
+            db_acc[e] += __shfl_xor(db_acc[e], off, 64);
+        }
+    }
+    if ((lane & 7) == 0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t dch = d0 + (lane >> 3) + 8 * e;
+            if (dch < a.D) {
+                const size_t o = (static_cast<size_t>(b) * a.D + dch) * a.J + j;
+                g.dDp[o] = dD_acc[e];
+                g.dbp[o] = db_acc[e];
+            }
+        }
+    }
+    if (!lane_ok) return;
+    *reinterpret_cast<float4 *>(g.dAp + cd * 16 + 4 * q) =
+        make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
+    if (j == 0 && g.dh0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * q + k < a.N) g.dh0[(static_cast<size_t>(b) * a.D + d) * a.N + 4 * q + k] = G[k];
+    }
+}
+
+// ------------------------------------------------------------ pass 4
+// One thread per output element; every sum runs in a fixed order.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nbc = a.Bsz * a.N * a.L;            // dB and dC elements
+    const int64_t nA = a.D * a.N;
+    if (i < nbc) {
+        const int64_t t = i % a.L;
+        const int64_t n = (i / a.L) % a.N;
+        const int64_t b = i / (a.L * a.N);
+        float sb = 0.0f, sc = 0.0f;
+        for (int64_t k = 0; k < a.n_cblk; ++k) {
+            const size_t o = ((static_cast<size_t>(b) * a.n_cblk + k) * 16 + n) * a.L + t;
+            sb += g.dBp[o];
+            sc += g.dCp[o];
+        }
+        g.dB[i] = sb;
+        g.dC[i] = sc;
+        return;
+    }
+    const int64_t ia = i - nbc;
+    if (ia < nA) {
+        const int64_t dd = ia / a.N, n = ia % a.N;
+        float s = 0.0f;
+        for (int64_t b = 0; b < a.Bsz; ++b)
+            for (int64_t j = 0; j < a.J; ++j)
+                s += g.dAp[((static_cast<size_t>(b) * a.D + dd) * a.J + j) * 16 + n];
+        g.dA[ia] = s;
+        return;
+    }
+    const int64_t id = ia - nA;
+    if (id < a.D) {
+        float sD = 0.0f, sb = 0.0f;
+        for (int64_t b = 0; b < a.Bsz; ++b)
+            for (int64_t j = 0; j < a.J; ++j) {
+                const size_t o = (static_cast<size_t>(b) * a.D + id) * a.J + j;
+                sD += g.dDp[o];
+                sb += g.dbp[o];
+            }
+        if (g.dD) g.dD[id] = sD;
+        if (g.dbias) g.dbias[id] = sb;
+    }
+}
+
+// ------------------------------------------------------------ launch
+template <class IO>
+static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
+    const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
+    if (a.J > 1) {
+        const hipError_t e = launch_scan_agg(a, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_agg_kernel<IO>, dim3(gx, static_cast<unsigned>(a.J - 1)), dim3(64),
+                           0, s, a, g);
+    }
+    hipLaunchKernelGGL(bwd_kernel<IO>, dim3(gx, static_cast<unsigned>(a.J)), dim3(64), 0, s, a, g);
+    const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                       dim3(256), 0, s, a, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
+    return a.bf16 ? launch_bwd_io<BF16>(a, g, s) : launch_bwd_io<F32>(a, g, s);
+}
+
+}  // namespace ssm

@@ -41,6 +41,28 @@ struct ScanArgs {
     hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
 };
 
+// Backward pass (d_state <= 16): upstream gradients, outputs and its own
+// workspace views; the forward quantities come from a ScanArgs.
+struct BwdArgs {
+    const void *dy;             // (batch, d_inner, L) io dtype
+    const float *dlast;         // (batch, d_inner, N) or null
+    float *du, *ddelta, *dz;    // (batch, d_inner, L); dz only with a gate
+    float *dA;                  // (d_inner, N)
+    float *dB, *dC;             // (batch, N, L)
+    float *dD, *dbias;          // (d_inner) or null
+    float *dh0;                 // (batch, d_inner, N) or null
+    int64_t n_tiles;            // 8-token tiles per row (checkpoints)
+    // workspace views
+    float *ckpt;                // (batch, d_inner, n_tiles, 16) state entering each tile
+    float *gend;                // (batch, d_inner, J, 16) gradient leaving each chunk to its left, from zero
+    float *bdtsum;              // (batch, d_inner, J) sum of step sizes (reverse order)
+    float *dBp, *dCp;           // (batch, n_cblk, 16, L) per 16-channel block
+    float *dAp;                 // (batch, d_inner, J, 16)
+    float *dDp, *dbp;           // (batch, d_inner, J)
+};
+
+hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);
+
 struct UpdateArgs {
     int64_t Bsz, D, N;
     int bf16;
@@ -52,6 +74,8 @@ struct UpdateArgs {
 };
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// Only the forward chunk-aggregate pass (chunks 0 .. J-2), d_state <= 16.
+hipError_t launch_scan_agg(const ScanArgs &a, hipStream_t s);
 hipError_t launch_update(const UpdateArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(float *p, size_t n, hipStream_t s);
 

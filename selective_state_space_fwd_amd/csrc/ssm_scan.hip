@@ -1218,6 +1218,24 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
     }
 }
 
+template <class IO>
+static hipError_t launch_agg_io(const ScanArgs &a, hipStream_t s) {
+    constexpr int VW = Seg<IO>::VW;
+    auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.B) && al(a.C);
+    const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
+    if (vec)
+        hipLaunchKernelGGL((quad_kernel<IO, false, true, false, false>), agrid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((quad_kernel<IO, false, false, false, false>), agrid, dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_agg(const ScanArgs &a, hipStream_t s) {
+    if (!a.quad || a.J < 2) return hipErrorInvalidValue;
+    return a.bf16 ? launch_agg_io<BF16>(a, s) : launch_agg_io<F32>(a, s);
+}
+
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
     return a.bf16 ? launch_scan_io<BF16>(a, s) : launch_scan_io<F32>(a, s);
 }

@@ -26,7 +26,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_state_update", "ssm_scan_workspace_bytes",
+    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd",
+              "ssm_scan_bwd_workspace_bytes", "ssm_state_update", "ssm_scan_workspace_bytes",
               "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -42,7 +43,7 @@ def test_status_strings(lib):
     for s in range(1, 7):
         assert ssm.ssm_status_string(s).startswith("SSM_ERR_")
     assert ssm.ssm_status_string(99) == "unknown status"
-    assert lib.ssm_version() >= 200
+    assert lib.ssm_version() >= 400
 
 
 def desc(**kw):
@@ -205,3 +206,32 @@ def test_flags_validation(lib):
                                     None) == status
     d = desc(chunk_size=2048, flags=ssm.SSM_FLAG_ZOH)
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048
+
+
+def test_backward_plan_and_validation(lib):
+    """ssm_scan_bwd: d_state <= 16 and Euler only; workspace sized for at most
+    32 chunks; null and misaligned arguments rejected before any launch."""
+    for kw in (dict(d_state=17), dict(flags=ssm.SSM_FLAG_ZOH)):
+        d = desc(**kw)
+        assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) == 0
+        assert lib.ssm_scan_bwd(ctypes.byref(d), *([4096] * 5), None, None, None, 1, None, 4096,
+                                None, *([4096] * 5), None, None, None, None, None) == 3
+    d = desc(chunk_size=16)              # 128 chunks asked: the backward uses at most 32
+    need16 = lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
+    d64 = desc(chunk_size=64)            # exactly 32 chunks
+    assert need16 == lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d64)) > 0
+    ok = 4096
+    d.workspace, d.workspace_bytes = ok, 1 << 40
+    args = [ok, ok, ok, ok, ok, None, None, None, 1, None, ok, None] + [ok] * 5 + [None] * 4
+    for i in (0, 1, 2, 3, 4, 10, 12, 13, 14, 15, 16):
+        bad = list(args)
+        bad[i] = None
+        assert lib.ssm_scan_bwd(ctypes.byref(d), *bad, None) == 1, i
+    bad = list(args)
+    bad[7] = ok + 2                      # delta_bias misaligned
+    assert lib.ssm_scan_bwd(ctypes.byref(d), *bad, None) == 4
+    bad = list(args)
+    bad[6] = ok                          # z without dz
+    assert lib.ssm_scan_bwd(ctypes.byref(d), *bad, None) == 1
+    d.workspace, d.workspace_bytes = ok, 16
+    assert lib.ssm_scan_bwd(ctypes.byref(d), *args, None) == 5

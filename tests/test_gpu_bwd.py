@@ -1,0 +1,119 @@
+"""GPU parity of the backward pass (ssm_scan_bwd) against the fp64 oracle's
+reverse walk (oracle.scan_bwd, itself pinned to finite differences).
+
+Every gradient is compared: du, ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0.
+Cases: one chunk and many (chunk edges inside and on tile edges, ragged
+tails), gate on and off, start state and upstream last-state gradient on and
+off, d_state 1..16, fp32 and bf16 inputs; exact-integer inputs bit for bit;
+run-to-run identity.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_fwd_amd as ssm
+import ssm_inputs
+from ssm_testutil import TOL, decoded, floored_err, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ssm.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(dev, batch, d_inner, N, L, io, gate, with_state, K, seed):
+    import torch
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    dy = ssm_inputs.encode(rng.standard_normal((batch, d_inner, L)).astype(np.float32), io)
+    h0 = rng.standard_normal((batch, d_inner, N)).astype(np.float32) if with_state else None
+    dlast = rng.standard_normal((batch, d_inner, N)).astype(np.float32) if with_state else None
+    t = {k: to_device(inp.get(k), dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                  "delta_bias")}
+    g = lambda a: None if a is None else torch.from_numpy(a).to(dev)
+    out = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], to_device(dy, dev),
+                           t["D"], t["z"], t["delta_bias"], softplus=True, initial_state=g(h0),
+                           dlast=g(dlast), chunk_size=K)
+    torch.cuda.synchronize()
+    f = decoded(inp)
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], ssm_inputs.to_f64(dy, io),
+                          f["D"], f["z"], f["delta_bias"], softplus=True,
+                          initial_state=None if h0 is None else h0.astype(np.float64),
+                          dlast=None if dlast is None else dlast.astype(np.float64))
+    errs = {}
+    for k in NAMES:
+        if out[k] is None or ref.get(k) is None:
+            continue
+        if k == "dh0" and h0 is None:
+            continue
+        errs[k] = floored_err(to_f64(out[k]), ref[k])
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return out, errs
+
+
+# The gradients are computed in fp32 from the same (rounded) inputs as the
+# oracle, so both I/O types meet the fp32 bar; bf16 keeps its own wider bar.
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,K", [((2, 40, 16, 300), 0), ((2, 40, 16, 300), 16),
+                                     ((1, 33, 5, 77), 32), ((3, 16, 1, 9), 0),
+                                     ((2, 24, 16, 513), 64)])
+@pytest.mark.parametrize("gate,with_state", [(True, True), (False, False)])
+def test_backward_parity(dev, io, shape, K, gate, with_state):
+    say(f"bwd io={io} shape={shape} K={K} gate={gate} state={with_state}")
+    _, errs = run_case(dev, *shape, io, gate, with_state, K, seed=sum(shape) + K)
+    for k, e in errs.items():
+        assert e <= TOL[io], (k, e)
+
+
+def test_backward_mamba130m_layer(dev):
+    """The Mamba-130M-shaped layer (2 x 1536 channels, N = 16, L = 2048,
+    fp32, gate) with the library's own chunking, every gradient compared."""
+    say("bwd mamba130m layer")
+    _, errs = run_case(dev, 2, 1536, 16, 2048, "f32", True, True, 0, seed=5)
+    for k, e in errs.items():
+        assert e <= TOL["f32"], (k, e)
+
+
+def test_backward_integer_bit_exact_and_deterministic(dev):
+    """Exact-integer inputs (unit decay, integer u, B, C, D, dy, start state
+    and last-state gradient, dt = 1): every gradient is an exact integer sum,
+    so all must equal the oracle bit for bit whatever the chunking, and two
+    runs must agree bit for bit."""
+    import torch
+    batch, d_inner, N, L = 2, 40, 16, 40
+    rng = np.random.default_rng(17)
+    ri = lambda *s: rng.integers(-2, 3, size=s).astype(np.float32)
+    u, B, C, dy = ri(batch, d_inner, L), ri(batch, N, L), ri(batch, N, L), ri(batch, d_inner, L)
+    D, h0, dlast = ri(d_inner), ri(batch, d_inner, N), ri(batch, d_inner, N)
+    dt = np.ones((batch, d_inner, L), np.float32)
+    A = np.zeros((d_inner, N), np.float32)
+    ref = oracle.scan_bwd(u, dt, A, B, C, dy, D, softplus=False, initial_state=h0, dlast=dlast)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    first = None
+    for K in (16, 32, 0):
+        out = ssm.ssm_scan_bwd(g(u), g(dt), g(A), g(B), g(C), g(dy), g(D), softplus=False,
+                               initial_state=g(h0), dlast=g(dlast), chunk_size=K)
+        torch.cuda.synchronize()
+        for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+            assert np.array_equal(to_f64(out[k]), ref[k]), (K, k)
+        if first is None:
+            first = out
+    again = ssm.ssm_scan_bwd(g(u), g(dt), g(A), g(B), g(C), g(dy), g(D), softplus=False,
+                             initial_state=g(h0), dlast=g(dlast), chunk_size=16)
+    torch.cuda.synchronize()
+    for k in ("du", "dA", "dB", "dC"):
+        assert torch.equal(again[k], first[k])

@@ -228,6 +228,59 @@ def bench_decode(args, torch, ssm, dev):
     }
 
 
+def bench_backward(args, torch, ssm, dev):
+    """The backward pass alone on the workload: every gradient of
+    sum(dy * y) + sum(dlast * last_state).  Algorithmic bytes: the forward
+    inputs read once, dy read, and du, ddelta, dz (fp32) and dB, dC written."""
+    cfg = dict(ssm_inputs.CONFIGS[args.config])
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    io, gate = cfg["io_dtype"], cfg["gate"]
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=0)
+    t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z", "A", "D", "delta_bias")}
+    rng = np.random.default_rng(1)
+    dy = upload(ssm_inputs.encode(rng.standard_normal((batch, d_inner, L)).astype(np.float32),
+                                  io), dev)
+    dlast = upload(rng.standard_normal((batch, d_inner, N)).astype(np.float32), dev)
+    code = 1 if io == "bf16" else 0
+    desc = ssm.make_desc(batch, d_inner, N, L, code, args.chunk)
+    lib = ssm.load_library()
+    ws = torch.empty(max(1, int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                         t["delta_bias"], softplus=True, dlast=dlast, chunk_size=args.chunk,
+                         workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    e = 2 if io == "bf16" else 4
+    chtok = batch * d_inner * L
+    nbytes = (chtok * ((4 if gate else 3) * e + (3 if gate else 2) * 4) +
+              2 * batch * N * L * (e + 4) + d_inner * (N + 2) * 4)
+    return {
+        "metric": "selective-scan backward channel-tokens/sec", "value": chtok / (ms * 1e-3),
+        "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config}: backward of the scan, batch={batch} "
+                               f"d_inner={d_inner} N={N} L={L} {io} I/O"
+                               f"{' + gate' if gate else ''}",
+                   "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
+                   "io_dtype": io, "gate": gate},
+        "hbm_achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes,
+        "versions": versions(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +294,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time only the single-token state update of 256 sequences x 5120 "
                          "channels x N=16 (fp32 state, gate) and report it against HBM")
+    ap.add_argument("--backward", action="store_true",
+                    help="time only the backward pass (ssm_scan_bwd) of the workload, with "
+                         "upstream gradients of y and last_state")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -267,6 +323,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.decode:
         print(json.dumps(bench_decode(args, torch, ssm, dev)), flush=True)
+        return
+    if args.backward:
+        print(json.dumps(bench_backward(args, torch, ssm, dev)), flush=True)
         return
     cfg = dict(ssm_inputs.CONFIGS[args.config])
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]

@@ -116,7 +116,6 @@ bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % 
 
 // Backward plan: the forward plan's chunks, at most 32 of them (each chunk
 // folds its neighbours' operators itself), and the workspace of the backward.
-constexpr int64_t kBwdTile = 8;
 
 struct BwdPlan {
     Plan f;
@@ -141,7 +140,7 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     f.fold = 1;
     const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
     const size_t J = static_cast<size_t>(f.J);
-    p->n_tiles = (L + kBwdTile - 1) / kBwdTile;
+    p->n_tiles = (L + ssm::kBwdTile - 1) / ssm::kBwdTile;
     size_t off = 0;
     if (f.J > 1) {
         f.off_hend = off; off += align_up(B * D * J * 16 * sizeof(float));

@@ -22,16 +22,16 @@
 //      to its left when none arrives from its right, and its sum of dt;
 //   3. bwd_kernel: per chunk, the start state (fold of pass 1) and the
 //      arriving gradient (fold of pass 2 from the right, starting at dlast);
-//      a forward sweep stores the state entering every 8-token tile; then the
-//      tiles are walked in reverse: each recomputes its 8 states per lane from
-//      its checkpoint (in registers) and walks them back.  dB and dC sum over
+//      a forward sweep stores the state entering every tile of kBwdTile
+//      tokens; then the tiles are walked in reverse: each recomputes its
+//      states from its checkpoint (in registers) and walks them back.  dB and dC sum over
 //      the 16 channels of the wavefront through LDS, and over channel blocks
 //      in pass 4;
 //   4. bwd_reduce_kernel: the fixed-order sums of the per-block partials of
 //      dB, dC and the per-chunk partials of dA, dD and dbias.
 // Lane mapping as the forward quad kernel: lane l serves channel l % 16 and
 // states 4q .. 4q+3, q = l / 16; tile pieces: row l / 4 (a channel, or a state
-// of B and C), tokens 2 (l % 4) and 2 (l % 4) + 1.
+// of B and C), kBwdTile / 4 consecutive tokens.
 #include "ssm_common.h"
 #include "ssm_launch.h"
 
@@ -39,8 +39,9 @@ namespace ssm {
 
 namespace {
 
-constexpr int kT = 8;        // tokens per backward tile
-constexpr int kQC = 16;      // channels per wavefront
+constexpr int kT = kBwdTile;   // tokens per backward tile
+constexpr int kEPL = kT / 4;   // tokens per lane in a tile piece (16 rows x kT tokens)
+constexpr int kQC = 16;        // channels per wavefront
 
 template <class IO>
 __device__ __forceinline__ float ld_clamped(const typename IO::T *p, size_t base, int64_t t,
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
     const bool gate = a.z != nullptr;
 
-    const int r = lane >> 2, sc = (lane & 3) * 2;
+    const int r = lane >> 2, sc = (lane & 3) * kEPL;
     const int64_t dr = d0 + r;
     const bool row_ok = dr < a.D;
     const int64_t drc = row_ok ? dr : a.D - 1;
@@ -99,21 +100,38 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dts = 0.0f;
     const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
+    // the next tile's raw values, loaded one tile ahead (named registers)
+    float px0 = 0.f, px1 = 0.f, pz0 = 0.f, pz1 = 0.f, py0 = 0.f, py1 = 0.f, pc0 = 0.f, pc1 = 0.f;
+    auto prefetch = [&](int64_t t0) {
+        const int64_t t = t0 + sc;
+        px0 = ld_clamped<IO>(dl, rbase, t, t_end);
+        if (gate) pz0 = ld_clamped<IO>(z, rbase, t, t_end);
+        py0 = ld_clamped<IO>(dy, rbase, t, t_end);
+        pc0 = ld_clamped<IO>(Cm, sbase, t, t_end);
+        if (kEPL > 1) {
+            px1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
+            if (gate) pz1 = ld_clamped<IO>(z, rbase, t + 1, t_end);
+            py1 = ld_clamped<IO>(dy, rbase, t + 1, t_end);
+            pc1 = ld_clamped<IO>(Cm, sbase, t + 1, t_end);
+        }
+    };
+    prefetch(t_begin + (ntile - 1) * kT);
     for (int64_t ti = ntile - 1; ti >= 0; --ti) {
         const int64_t t0 = t_begin + ti * kT;
+        const float rx[2] = {px0, px1}, rz[2] = {pz0, pz1}, ry[2] = {py0, py1}, rc[2] = {pc0, pc1};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kEPL; ++i) {
             const int64_t t = t0 + sc + i;
             const bool ok = row_ok && t < t_end;
-            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float x = rx[i] + rbias;
             const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
-            const float gg = gate ? silu_f32(ld_clamped<IO>(z, rbase, t, t_end)) : 1.0f;
-            const float dO = ok ? ld_clamped<IO>(dy, rbase, t, t_end) * gg : 0.0f;
+            const float gg = gate ? silu_f32(rz[i]) : 1.0f;
+            const float dO = ok ? ry[i] * gg : 0.0f;
             s_dt[r * kT + sc + i] = dt;
             s_do[r * kT + sc + i] = dO;
-            const float cv = ld_clamped<IO>(Cm, sbase, t, t_end);
-            s_C[(sc + i) * 16 + r] = st_ok ? cv : 0.0f;
+            s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
         }
+        if (ti > 0) prefetch(t0 - kT);
         __syncthreads();
 #pragma unroll
         for (int t = kT - 1; t >= 0; --t) {
@@ -176,7 +194,7 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
     const bool gate = a.z != nullptr;
 
     // tile pieces
-    const int r = lane >> 2, sc = (lane & 3) * 2;
+    const int r = lane >> 2, sc = (lane & 3) * kEPL;
     const int64_t dr = d0 + r;
     const bool row_ok = dr < a.D;
     const int64_t drc = row_ok ? dr : a.D - 1;
@@ -240,23 +258,37 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
     const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
     float *ck = g.ckpt + (static_cast<size_t>(b) * a.D + dcl) * g.n_tiles * 16 + 4 * q;
 
-    // ---- forward sweep: the state entering every tile
+    // ---- forward sweep: the state entering every tile (inputs one tile ahead)
+    float fx0 = 0.f, fx1 = 0.f, fu0 = 0.f, fu1 = 0.f, fb0 = 0.f, fb1 = 0.f;
+    auto prefetch_fwd = [&](int64_t t0) {
+        const int64_t t = t0 + sc;
+        fx0 = ld_clamped<IO>(dl, rbase, t, t_end);
+        fu0 = ld_clamped<IO>(u, rbase, t, t_end);
+        fb0 = ld_clamped<IO>(Bm, sbase, t, t_end);
+        if (kEPL > 1) {
+            fx1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
+            fu1 = ld_clamped<IO>(u, rbase, t + 1, t_end);
+            fb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
+        }
+    };
+    prefetch_fwd(t_begin);
     for (int64_t ti = 0; ti < ntile; ++ti) {
         const int64_t t0 = t_begin + ti * kT;
         if (lane_ok)
             *reinterpret_cast<float4 *>(ck + (t0 / kT) * 16) = make_float4(h[0], h[1], h[2], h[3]);
+        const float rx[2] = {fx0, fx1}, ru[2] = {fu0, fu1}, rb[2] = {fb0, fb1};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kEPL; ++i) {
             const int64_t t = t0 + sc + i;
             const bool ok = row_ok && t < t_end;
-            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float x = rx[i] + rbias;
             const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
-            const float uu = ok ? ld_clamped<IO>(u, rbase, t, t_end) : 0.0f;
+            const float uu = ok ? ru[i] : 0.0f;
             s_dt[r * kT + sc + i] = dt;
             s_w[r * kT + sc + i] = dt * uu;
-            const float bv = ld_clamped<IO>(Bm, sbase, t, t_end);
-            s_B[(sc + i) * 16 + r] = st_ok ? bv : 0.0f;
+            s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
         }
+        if (ti + 1 < ntile) prefetch_fwd(t0 + kT);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
@@ -271,23 +303,49 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
 
     // ---- reverse sweep
     float dA_acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float dD_acc[2] = {0.0f, 0.0f}, db_acc[2] = {0.0f, 0.0f};
+    float dD_acc[kT / 4] = {}, db_acc[kT / 4] = {};
     const float Dv_lane = (lane_ok && a.Dskip) ? a.Dskip[dcl] : 0.0f;
+    float qx0 = 0.f, qx1 = 0.f, qu0 = 0.f, qu1 = 0.f, qy0 = 0.f, qy1 = 0.f, qz0 = 0.f, qz1 = 0.f;
+    float qb0 = 0.f, qb1 = 0.f, qc0 = 0.f, qc1 = 0.f;
+    float4 qh = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto prefetch_rev = [&](int64_t t0) {
+        const int64_t t = t0 + sc;
+        qx0 = ld_clamped<IO>(dl, rbase, t, t_end);
+        qu0 = ld_clamped<IO>(u, rbase, t, t_end);
+        qy0 = ld_clamped<IO>(dy, rbase, t, t_end);
+        if (gate) qz0 = ld_clamped<IO>(z, rbase, t, t_end);
+        qb0 = ld_clamped<IO>(Bm, sbase, t, t_end);
+        qc0 = ld_clamped<IO>(Cm, sbase, t, t_end);
+        if (kEPL > 1) {
+            qx1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
+            qu1 = ld_clamped<IO>(u, rbase, t + 1, t_end);
+            qy1 = ld_clamped<IO>(dy, rbase, t + 1, t_end);
+            if (gate) qz1 = ld_clamped<IO>(z, rbase, t + 1, t_end);
+            qb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
+            qc1 = ld_clamped<IO>(Cm, sbase, t + 1, t_end);
+        }
+        qh = *reinterpret_cast<const float4 *>(ck + (t0 / kT) * 16);
+    };
+    prefetch_rev(t_begin + (ntile - 1) * kT);
     for (int64_t ti = ntile - 1; ti >= 0; --ti) {
         const int64_t t0 = t_begin + ti * kT;
         // (a) the tile's inputs
+        const float rx[2] = {qx0, qx1}, ru[2] = {qu0, qu1}, ry[2] = {qy0, qy1},
+                    rz[2] = {qz0, qz1}, rb[2] = {qb0, qb1}, rc[2] = {qc0, qc1};
+        float hs[4] = {lane_ok ? qh.x : 0.0f, lane_ok ? qh.y : 0.0f, lane_ok ? qh.z : 0.0f,
+                       lane_ok ? qh.w : 0.0f};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kEPL; ++i) {
             const int64_t t = t0 + sc + i;
             const bool ok = row_ok && t < t_end;
-            const float x = ld_clamped<IO>(dl, rbase, t, t_end) + rbias;
+            const float x = rx[i] + rbias;
             const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
             const float sig = a.softplus ? sigmoid_f32(x) : 1.0f;
-            const float uu = ok ? ld_clamped<IO>(u, rbase, t, t_end) : 0.0f;
-            const float dyv = ok ? ld_clamped<IO>(dy, rbase, t, t_end) : 0.0f;
+            const float uu = ok ? ru[i] : 0.0f;
+            const float dyv = ok ? ry[i] : 0.0f;
             float gg = 1.0f, dsl = 0.0f;
             if (gate) {
-                const float zz = ld_clamped<IO>(z, rbase, t, t_end);
+                const float zz = rz[i];
                 const float sz = sigmoid_f32(zz);
                 gg = zz * sz;
                 dsl = sz * __builtin_fmaf(zz, 1.0f - sz, 1.0f);
@@ -299,20 +357,13 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
             s_sig[o] = sig;
             s_u[o] = uu;
             s_ds[o] = dyv * dsl;
-            const float bv = ld_clamped<IO>(Bm, sbase, t, t_end);
-            const float cv = ld_clamped<IO>(Cm, sbase, t, t_end);
-            s_B[(sc + i) * 16 + r] = st_ok ? bv : 0.0f;
-            s_C[(sc + i) * 16 + r] = st_ok ? cv : 0.0f;
+            s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
+            s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
         }
+        if (ti > 0) prefetch_rev(t0 - kT);
         __syncthreads();
 
         // (b) recompute the tile's states from its checkpoint
-        float hs[4];
-        {
-            const float4 v = *reinterpret_cast<const float4 *>(ck + (t0 / kT) * 16);
-            hs[0] = lane_ok ? v.x : 0.0f; hs[1] = lane_ok ? v.y : 0.0f;
-            hs[2] = lane_ok ? v.z : 0.0f; hs[3] = lane_ok ? v.w : 0.0f;
-        }
         float hh[kT][4];
         float part[kT];
 #pragma unroll
@@ -377,12 +428,12 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
         }
         __syncthreads();
 
-        // (d) per (channel, token): du, ddelta, dz; lane -> token lane % 8,
-        // channels lane / 8 and lane / 8 + 8
+        // (d) per (channel, token): du, ddelta, dz; lane -> token lane % kT,
+        // channels lane / kT + (64 / kT) e
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int ch = (lane >> 3) + 8 * e;
-            const int t = lane & 7;
+        for (int e = 0; e < kT / 4; ++e) {
+            const int ch = lane / kT + (64 / kT) * e;
+            const int t = lane % kT;
             const int64_t tok = t0 + t;
             const int o = ch * kT + t;
             float dw = 0.0f, dd = 0.0f;
@@ -406,12 +457,12 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
                 db_acc[e] += ddl;
             }
         }
-        // (e) dB, dC: sum over the 16 channels; lane -> tensor lane / 32,
-        // states 4 ((lane / 8) % 4) .. +3, token lane % 8
-        {
-            const int which = lane >> 5;
-            const int n4 = (lane >> 3) & 3;
-            const int t = lane & 7;
+        // (e) dB, dC: sum over the 16 channels; job = lane (2 x 4 x kT jobs):
+        // tensor job / (4 kT), states 4 ((job / kT) % 4) .. +3, token job % kT
+        if (lane < 8 * kT) {
+            const int which = lane / (4 * kT);
+            const int n4 = (lane / kT) & 3;
+            const int t = lane % kT;
             const float *src = which ? s_gC : s_gB;
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -430,18 +481,18 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
     }
 
     // ---- chunk results
-    // dD, dbias: the 8 lanes of a channel pair meet in a butterfly
+    // dD, dbias: the kT lanes of a channel meet in a butterfly
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        for (int off = 1; off < 8; off <<= 1) {
+    for (int e = 0; e < kT / 4; ++e) {
+        for (int off = 1; off < kT; off <<= 1) {
             dD_acc[e] += __shfl_xor(dD_acc[e], off, 64);
             db_acc[e] += __shfl_xor(db_acc[e], off, 64);
         }
     }
-    if ((lane & 7) == 0) {
+    if (lane % kT == 0) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int64_t dch = d0 + (lane >> 3) + 8 * e;
+        for (int e = 0; e < kT / 4; ++e) {
+            const int64_t dch = d0 + lane / kT + (64 / kT) * e;
             if (dch < a.D) {
                 const size_t o = (static_cast<size_t>(b) * a.D + dch) * a.J + j;
                 g.dDp[o] = dD_acc[e];

@@ -41,6 +41,13 @@ struct ScanArgs {
     hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
 };
 
+// Tokens per backward tile: the spacing of the state checkpoints.
+#ifndef SSM_BWD_TILE
+#define SSM_BWD_TILE 8
+#endif
+constexpr int kBwdTile = SSM_BWD_TILE;
+static_assert(kBwdTile == 4 || kBwdTile == 8, "backward tile of 4 or 8 tokens");
+
 // Backward pass (d_state <= 16): upstream gradients, outputs and its own
 // workspace views; the forward quantities come from a ScanArgs.
 struct BwdArgs {
@@ -51,7 +58,7 @@ struct BwdArgs {
     float *dB, *dC;             // (batch, N, L)
     float *dD, *dbias;          // (d_inner) or null
     float *dh0;                 // (batch, d_inner, N) or null
-    int64_t n_tiles;            // 8-token tiles per row (checkpoints)
+    int64_t n_tiles;            // backward tiles per row (checkpoints)
     // workspace views
     float *ckpt;                // (batch, d_inner, n_tiles, 16) state entering each tile
     float *gend;                // (batch, d_inner, J, 16) gradient leaving each chunk to its left, from zero

@@ -105,6 +105,19 @@ typedef struct ssm_desc {
  * instead of the default Euler term dt B u.  Scan and single-token update. */
 #define SSM_FLAG_ZOH 1u
 
+/* Scheduling flag of ssm_scan_fwd / _ex / _conv, no effect on the result
+ * bits.  With d_state <= 16, 2..32 chunks and chunks of 1024 tokens or more,
+ * one launch runs the whole chunked scan: each chunk publishes its transfer
+ * operator (ufo.work article
+ * "Accelerating state-space models ...", §3.1) in the workspace, waits for
+ * those of the chunks before it for a bounded time, and computes any that
+ * have not arrived by then itself.  With this flag no chunk waits: each
+ * computes the operators of all chunks before it itself (work grows with
+ * the square of the chunk count).  Meant for testing that path, and for
+ * callers whose other work on the GPU could keep a chunk's predecessors
+ * from running for long.  Accepted and ignored by the other entry points. */
+#define SSM_FLAG_INDEPENDENT_CHUNKS 2u
+
 /* Bytes of device workspace that ssm_scan_fwd needs for this descriptor
  * (its shapes, io_dtype and chunk_size; the workspace fields are ignored).
  * Returns 0 for an invalid descriptor.  Host-only, never touches the GPU. */

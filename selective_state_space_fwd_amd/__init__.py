@@ -143,6 +143,11 @@ def _stream(device) -> int:
 
 
 SSM_FLAG_ZOH = 1
+SSM_FLAG_INDEPENDENT_CHUNKS = 2
+
+
+def _flags(zoh, independent_chunks):
+    return (SSM_FLAG_ZOH if zoh else 0) | (SSM_FLAG_INDEPENDENT_CHUNKS if independent_chunks else 0)
 
 
 def make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0, flags=0) -> SsmDesc:
@@ -165,7 +170,7 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  return_last_state=True, chunk_size=0, y=None, last_state=None,
                  workspace=None, profile_events=None, initial_state=None, cu_seqlens=None,
-                 zoh=False):
+                 zoh=False, independent_chunks=False):
     """Fused selective-scan forward pass on the GPU.
 
     u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
@@ -177,6 +182,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     last_state) have one row per batch row, or per sequence when packed:
     (rows, d_inner, N).
     zoh: zero-order-hold input term (exp(dt A) - 1) / A * B u instead of dt B u.
+    independent_chunks: no chunk waits for the operators of the chunks before
+    it; each computes them itself (same result bits, more work).
     Returns (y, last_state); last_state is None unless requested.
     profile_events: optional pair of raw hipEvent_t handles recorded around
     the pass that writes y.
@@ -210,7 +217,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     if last_state is None and return_last_state:
         last_state = torch.empty((rows, d_inner, N), dtype=torch.float32, device=dev)
     _expect(last_state, "last_state", (rows, d_inner, N), torch.float32, dev)
-    desc = make_desc(batch, d_inner, N, L, code, chunk_size, SSM_FLAG_ZOH if zoh else 0)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size, _flags(zoh, independent_chunks))
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -236,7 +243,8 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
                       delta_bias=None, softplus=True, conv_silu=True, conv_state=None,
                       initial_state=None, cu_seqlens=None, return_last_state=True,
                       return_u=False, chunk_size=0, y=None, last_state=None, u_out=None,
-                      workspace=None, profile_events=None, zoh=False):
+                      workspace=None, profile_events=None, zoh=False,
+                      independent_chunks=False):
     """The scan with the causal depthwise convolution fused in front: the scan
     input is u = silu(conv(x) + conv_bias) (identity instead of silu when
     conv_silu is False), computed on the fly.
@@ -282,7 +290,7 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
     if u_out is None and return_u:
         u_out = torch.empty((batch, d_inner, L), dtype=io, device=dev)
     _expect(u_out, "u_out", (batch, d_inner, L), io, dev)
-    desc = make_desc(batch, d_inner, N, L, code, chunk_size, SSM_FLAG_ZOH if zoh else 0)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size, _flags(zoh, independent_chunks))
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:

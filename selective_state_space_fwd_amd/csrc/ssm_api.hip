@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <limits.h>
 
+#include <atomic>
+#include <chrono>
+
 #include "ssm_launch.h"
 
 namespace {
@@ -32,15 +35,18 @@ struct Plan {
     int64_t n_cblk = 0;   // blocks of 16 channels per batch row
     int quad = 0;         // d_state <= 16: quad-row kernel
     int fold = 0;         // chunks fold their predecessors' operators (no carry kernel)
-    size_t off_hend = 0, off_dtsum = 0, off_keep = 0, off_hstart = 0, bytes = 0;
+    int fused = 0;        // one launch: chunks publish operators and wait for each other
+    size_t off_hend = 0, off_dtsum = 0, off_keep = 0, off_hstart = 0, off_flags = 0, bytes = 0;
 };
+
+constexpr uint32_t kKnownFlags = SSM_FLAG_ZOH | SSM_FLAG_INDEPENDENT_CHUNKS;
 
 ssm_status check_desc(const ssm_desc *d) {
     if (!d) return SSM_ERR_NULL_ARG;
     if (d->batch < 0 || d->d_inner < 0 || d->seqlen < 0) return SSM_ERR_BAD_SHAPE;
     if (d->d_state < 1 || d->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
-    if ((d->flags & ~SSM_FLAG_ZOH) != 0 || d->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if ((d->flags & ~kKnownFlags) != 0 || d->reserved != 0) return SSM_ERR_UNSUPPORTED;
     if (d->seqlen > SSM_MAX_SEQLEN) return SSM_ERR_UNSUPPORTED;
     if (!dims_ok(d->batch, d->d_inner, d->seqlen > 0 ? d->seqlen : 1)) return SSM_ERR_BAD_SHAPE;
     if (!dims_ok(d->batch, d->d_inner, d->d_state)) return SSM_ERR_BAD_SHAPE;
@@ -50,13 +56,28 @@ ssm_status check_desc(const ssm_desc *d) {
 // Waves wanted in flight: two per SIMD on 256 CUs x 4 SIMDs.
 constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kEnoughWaves = 1024;
+// The quad path runs its chunks in one launch (each chunk publishes its
+// operator and waits for its predecessors') from this chunk length on.
+// Measured on MI355X: at 4096-token chunks (1 x 2048 channels x 64 Ki tokens,
+// bf16) one launch takes 934 us against 974-1029 us for the two passes; at
+// 128-208 token chunks (2 x 1536 channels x 2048 tokens, fp32) it is no
+// faster (68-75 us against 70 us): a SIMD serves its oldest wavefront first,
+// and with short chunks the waits of the younger chunks cost what the
+// saved kernel boundary gains.
+constexpr int64_t kFusedMinChunk = 1024;
 constexpr int64_t kMinAutoChunk = 64;
 // Up to this many chunks, each chunk of the quad path folds the transfer
 // operators of the chunks before it (at most this many exp per state) instead
 // of waiting for a separate carry kernel.
 constexpr int64_t kFoldMaxChunks = 32;
+// Longest wait of a chunk for its predecessors' operators: 20 ms of the
+// 100 MHz real-time clock.
+constexpr uint64_t kMaxSpinTicks = 2000000;
 
-ssm_status make_plan(const ssm_desc *d, Plan *p) {
+// fused_ok: the quad path may run as one launch (the forward scan, long
+// chunks); the backward, which reuses the chunk-aggregate pass on its own,
+// passes false.
+ssm_status make_plan(const ssm_desc *d, Plan *p, bool fused_ok = true) {
     const ssm_status st = check_desc(d);
     if (st != SSM_OK) return st;
     if (d->chunk_size < 0 || (d->chunk_size > 0 && d->chunk_size % 16 != 0))
@@ -92,6 +113,7 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
     if (p->J > kMaxGridY) return SSM_ERR_UNSUPPORTED;
     if (p->n_cblk * d->batch > static_cast<int64_t>(UINT_MAX)) return SSM_ERR_UNSUPPORTED;
     p->fold = p->J <= kFoldMaxChunks;
+    p->fused = fused_ok && p->quad && p->fold && p->J > 1 && K >= kFusedMinChunk;
     // workspace layout: the chunk operators and, without folding, the chunk
     // start states; rows of G * 16 floats per (batch, channel, chunk)
     size_t off = 0;
@@ -107,12 +129,28 @@ ssm_status make_plan(const ssm_desc *d, Plan *p) {
             p->off_hstart = off;
             off += align_up(cj * G * 16 * sizeof(float));
         }
+        if (p->fused) {
+            p->off_flags = off;
+            off += align_up(static_cast<size_t>(d->batch) * p->n_cblk * p->J * sizeof(uint64_t));
+        }
     }
     p->bytes = off;
     return SSM_OK;
 }
 
 bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Epochs of one-launch scans: unique per launch within the process, and
+// seeded from the clock and this object's address so that flags left in
+// reused memory by another process or library instance do not match either.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{
+        (static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) *
+         0x9E3779B97F4A7C15ull) ^
+        reinterpret_cast<uintptr_t>(&counter)};
+    uint64_t e = counter.fetch_add(1, std::memory_order_relaxed);
+    return e != 0 ? e : counter.fetch_add(1, std::memory_order_relaxed);
+}
 
 // Backward plan: the forward plan's chunks, at most 32 of them (each chunk
 // folds its neighbours' operators itself), and the workspace of the backward.
@@ -125,9 +163,9 @@ struct BwdPlan {
 };
 
 ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
-    const ssm_status st = make_plan(d, &p->f);
+    const ssm_status st = make_plan(d, &p->f, false);
     if (st != SSM_OK) return st;
-    if (d->d_state > 16 || d->flags != 0) return SSM_ERR_UNSUPPORTED;
+    if (d->d_state > 16 || (d->flags & SSM_FLAG_ZOH) != 0) return SSM_ERR_UNSUPPORTED;
     Plan &f = p->f;
     const int64_t L = d->seqlen;
     if (L == 0 || d->batch * d->d_inner == 0) { p->bytes = 0; return SSM_OK; }
@@ -231,6 +269,27 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
         a.keep = reinterpret_cast<float *>(ws + p.off_keep);
         if (!p.fold) a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
+        if (p.fused) {
+            a.flags = reinterpret_cast<uint64_t *>(ws + p.off_flags);
+            a.epoch = next_epoch();
+            // a chunk's aggregate pass takes ~0.1 us per token; wait up to
+            // 50 us + 0.3 us per token (100 MHz ticks) before computing a
+            // missing predecessor operator locally
+            const uint64_t ticks = 5000u + 30u * static_cast<uint64_t>(p.K);
+            a.spin_ticks = (desc->flags & SSM_FLAG_INDEPENDENT_CHUNKS) ? 0
+                           : ticks < kMaxSpinTicks                   ? ticks
+                                                                     : kMaxSpinTicks;
+            // A captured graph replays this launch with the same epoch: clear
+            // the flags ahead of it (a kernel node, not a memset node), so that
+            // a replay never reads the operators of the replay before it.
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SSM_ERR_HIP;
+            if (cs != hipStreamCaptureStatusNone) {
+                const size_t n = static_cast<size_t>(desc->batch) * p.n_cblk * p.J * 2;
+                if (ssm::launch_fill_zero(reinterpret_cast<float *>(a.flags), n, s) != hipSuccess)
+                    return SSM_ERR_HIP;
+            }
+        }
     }
     a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
     a.ev_end = static_cast<hipEvent_t>(desc->profile_end);
@@ -294,7 +353,7 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
     if (desc->batch < 0 || desc->d_inner < 0) return SSM_ERR_BAD_SHAPE;
     if (desc->d_state < 1 || desc->d_state > SSM_MAX_D_STATE) return SSM_ERR_UNSUPPORTED;
     if (desc->io_dtype != SSM_F32 && desc->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
-    if ((desc->flags & ~SSM_FLAG_ZOH) != 0 || desc->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if ((desc->flags & ~kKnownFlags) != 0 || desc->reserved != 0) return SSM_ERR_UNSUPPORTED;
     if (!dims_ok(desc->batch, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
     if (desc->batch * desc->d_inner == 0) return SSM_OK;
     if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL_ARG;
@@ -400,6 +459,6 @@ const char *ssm_status_string(int status) {
     }
 }
 
-int ssm_version(void) { return 400; }
+int ssm_version(void) { return 500; }
 
 }  // extern "C"

@@ -38,6 +38,13 @@ struct ScanArgs {
     float *keep;                // (batch, J) 1: the chunk keeps its incoming state, 0: it
                                 // starts a sequence somewhere, so its operator's decay is 0
     float *hstart;              // (batch, d_inner, J, G*16) chunk start states
+    // one-launch chunked scan (quad path, 1 < J <= 32): per (batch, channel
+    // block, chunk) publication flags, this launch's epoch, and how long (in
+    // ticks of the 100 MHz real-time clock) a chunk waits for the chunks
+    // before it before computing their operators itself; null flags: two passes
+    uint64_t *flags;
+    uint64_t epoch;
+    uint64_t spin_ticks;
     hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
 };
 

@@ -281,8 +281,41 @@ __device__ __forceinline__ float state_step(float dt, float A2, float h, float w
 // EXT: the instance that also handles packed sequences and the fused
 // convolution; calls with neither use the lean instance.  ZOH (EXT only):
 // zero-order-hold input term.
-template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH>
-__global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
+//
+// quad_pass runs one chunk j of one 16-channel block; the kernels below
+// call it.  FULL = false: the chunk-aggregate pass, which leaves the chunk's
+// end state (from zero, or from the start state of a sequence that begins
+// in it) in h, its sum of dt in dt_sum and its keep flag in keep.  FULL =
+// true: the pass that writes y and final states; with GIVEN it starts from
+// the state the caller leaves in h (unless a sequence starts at its first
+// token), else from h_start or the fold of the workspace operators.
+// The LDS tiles are the caller's, as distinct restrict-qualified arrays, so
+// that the compiler sees that the y written by one token group (into s_du,
+// in place) never aliases the dt, w, B and C read by the next group, and
+// can issue those reads early.
+template <class IO, bool FULL>
+struct QuadTile {
+    static constexpr int VW = Seg<IO>::VW;
+    static constexpr int T = 4 * VW;                // 64 bytes of a row per tile
+    static constexpr int TP = T + 4;
+    static constexpr int QC = 16;                   // channels per wavefront
+    static constexpr int n_dt = QC * TP;
+    // s_w rows start 4 floats in: the 4 floats before a row's tokens (the
+    // previous row's padding) keep the inputs of the 4 tokens before the
+    // tile when the scan input is computed by the causal convolution
+    static constexpr int n_w = QC * TP + 4;
+    static constexpr int n_du = FULL ? QC * TP : 4;   // D u, then y
+    static constexpr int n_g = FULL ? QC * TP : 4;    // silu(z)
+    static constexpr int n_B = 16 * TP;               // state-major
+    static constexpr int n_C = FULL ? 16 * TP : 4;
+};
+
+template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH, bool GIVEN>
+__device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&h)[4],
+                                          float &dt_sum_out, float &keep_out,
+                                          float *__restrict__ s_dt, float *__restrict__ s_w,
+                                          float *__restrict__ s_du, float *__restrict__ s_g,
+                                          float *__restrict__ s_B, float *__restrict__ s_C) {
     using IT = typename IO::T;
     using S = Seg<IO>;
     using V = typename S::V;
@@ -290,18 +323,6 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     constexpr int T = 4 * VW;                       // 64 bytes of a row per tile
     constexpr int TP = T + 4;
     constexpr int QC = 16;                          // channels per wavefront
-    // Separate LDS objects, so that the compiler sees that the y written by
-    // one token group (into s_du, in place) never aliases the dt, w, B and C
-    // read by the next group, and can issue those reads early.
-    __shared__ __attribute__((aligned(16))) float s_dt[QC * TP];
-    // s_w rows start 4 floats in: the 4 floats before a row's tokens (the
-    // previous row's padding) keep the inputs of the 4 tokens before the
-    // tile when the scan input is computed by the causal convolution
-    __shared__ __attribute__((aligned(16))) float s_w[QC * TP + 4];
-    __shared__ __attribute__((aligned(16))) float s_du[FULL ? QC * TP : 4];   // D u, then y
-    __shared__ __attribute__((aligned(16))) float s_g[FULL ? QC * TP : 4];    // silu(z)
-    __shared__ __attribute__((aligned(16))) float s_B[16 * TP];              // state-major
-    __shared__ __attribute__((aligned(16))) float s_C[FULL ? 16 * TP : 4];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -314,7 +335,6 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const int c = lane & 15;                        // channel within the block
     const int q = lane >> 4;                        // lane-row: states 4q .. 4q+3
     const int64_t b = blockIdx.x / a.n_cblk;
-    const int64_t j = blockIdx.y;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * QC;
     const int64_t d = d0 + c;
     const bool lane_ok = d < a.D;
@@ -382,16 +402,20 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
         const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
         A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
     }
-    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;   // chunk 0 of this channel
     const size_t cd = cd0 + j;
     SeqPos sp = seq_pos<EXT>(a, b, t_begin);
     // the chunk's operator ignores its incoming state if a sequence starts in it
-    const float keep = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
+    keep_out = (!sp.reset && sp.end >= t_end) ? 1.0f : 0.0f;
     load_tile(t_begin);
     if (sp.reset) {
         load_start_state<4>(a, sp.s, dcl, lane_ok, 4 * q, h);
-    } else if (FULL) {
+    } else if (!FULL) {
+        h[0] = h[1] = h[2] = h[3] = 0.0f;
+    } else if (GIVEN) {
+        if (!lane_ok) h[0] = h[1] = h[2] = h[3] = 0.0f;
+    } else {
+        h[0] = h[1] = h[2] = h[3] = 0.0f;
         // a chunk after the first of its sequence: start from h_start
         if (a.hstart) {
             const float4 v = *reinterpret_cast<const float4 *>(a.hstart + cd * 16 + 4 * q);
@@ -654,11 +678,183 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
             }
         }
     } else {
+        dt_sum_out = dt_sum;
+    }
+}
+
+// One chunk per wavefront: the aggregate pass (FULL = false, chunks
+// 0 .. J-2, into the workspace) or the pass that writes y, of the two-pass
+// schedule (the chunk start states come from h_start or the fold).
+template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH>
+__global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
+    using Q = QuadTile<IO, FULL>;
+    __shared__ __attribute__((aligned(16))) float s_dt[Q::n_dt];
+    __shared__ __attribute__((aligned(16))) float s_w[Q::n_w];
+    __shared__ __attribute__((aligned(16))) float s_du[Q::n_du];
+    __shared__ __attribute__((aligned(16))) float s_g[Q::n_g];
+    __shared__ __attribute__((aligned(16))) float s_B[Q::n_B];
+    __shared__ __attribute__((aligned(16))) float s_C[Q::n_C];
+    const int64_t j = blockIdx.y;
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dt_sum = 0.0f, keep = 0.0f;
+    quad_pass<IO, FULL, VEC, EXT, ZOH, false>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g, s_B,
+                                              s_C);
+    if (!FULL) {
+        const int lane = threadIdx.x;
+        const int q = lane >> 4;
+        const int64_t b = blockIdx.x / a.n_cblk;
+        const int64_t d = static_cast<int64_t>(blockIdx.x % a.n_cblk) * 16 + (lane & 15);
         if (lane == 0 && blockIdx.x % a.n_cblk == 0) a.keep[b * a.J + j] = keep;
-        if (!lane_ok) return;
+        if (d >= a.D) return;
+        const size_t cd = (static_cast<size_t>(b) * a.D + d) * a.J + j;
         *reinterpret_cast<float4 *>(a.hend + cd * 16 + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
         if (q == 0) a.dtsum[cd] = dt_sum;
     }
+}
+
+// The whole chunked scan in one launch (up to kFoldMaxChunks chunks): the
+// wavefront of chunk j
+//  1. runs the aggregate pass of its own chunk (unless it is the last) and
+//     publishes the result: the end state and sum of dt in the workspace,
+//     then this launch's epoch in its flag;
+//  2. waits until the chunks 0 .. j-1 of its 16-channel block have
+//     published, and folds their transfer operators, in chunk order, into
+//     its start state [ufo.work, "Accelerating state-space models ...",
+//     §3.1: chunk operators combined, start states broadcast];
+//  3. runs the pass that writes y from that state.
+// Scheduling: a SIMD issues from its oldest wavefront first, so without
+// help the first chunk on each SIMD would run its y pass while the later
+// chunks' aggregate passes and folds, which the y passes wait for, starve.
+// Steps 1 and 2 therefore run at raised wave priority (s_setprio), step 3 at
+// the default.
+// Bounded waiting: the wait ends at a real-time deadline (a.spin_ticks of
+// the 100 MHz clock); after it the wavefront computes each missing
+// aggregate itself, with the same code and so the same bits, and never
+// depends on another wavefront being scheduled.  spin_ticks = 0 makes every
+// chunk independent: nothing is published or awaited, each chunk computes
+// all operators before it.
+// Memory ordering across the XCDs' separate L2 caches: the operators and
+// the flag are written with agent-scope atomic stores (sc1: written through
+// to the device-coherent level) and the flag only after s_waitcnt has seen
+// the operator stores complete; readers load flag and operators with
+// agent-scope atomic loads (sc1: read from the coherent level, never a
+// stale L2 line), the operators only after the flag load has returned.  A
+// release/acquire fence pair would instead write back and invalidate whole
+// L2 caches per wavefront (measured: 2.7x slower on the Mamba-130M layer).
+// Flags hold a 64-bit epoch that is new for every launch, so the workspace
+// needs no clearing between launches (graph capture clears it, see the
+// launch).
+template <class IO, bool VEC, bool EXT, bool ZOH>
+__global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
+    using Q = QuadTile<IO, true>;
+    __shared__ __attribute__((aligned(16))) float s_dt[Q::n_dt];
+    __shared__ __attribute__((aligned(16))) float s_w[Q::n_w];
+    __shared__ __attribute__((aligned(16))) float s_du[Q::n_du];
+    __shared__ __attribute__((aligned(16))) float s_g[Q::n_g];
+    __shared__ __attribute__((aligned(16))) float s_B[Q::n_B];
+    __shared__ __attribute__((aligned(16))) float s_C[Q::n_C];
+    const int lane = threadIdx.x;
+    const int q = lane >> 4;
+    const int64_t j = blockIdx.y;
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t d = static_cast<int64_t>(blockIdx.x % a.n_cblk) * 16 + (lane & 15);
+    const bool lane_ok = d < a.D;
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
+    uint64_t *flags = a.flags + static_cast<size_t>(blockIdx.x) * a.J;
+    float h[4], dt_sum = 0.0f, keep = 0.0f;
+    constexpr int kAgent = __HIP_MEMORY_SCOPE_AGENT;
+
+    // 1. this chunk's operator, for the chunks after it (no one reads it
+    // when chunks do not wait)
+    __builtin_amdgcn_s_setprio(3);
+    if (j + 1 < a.J && a.spin_ticks != 0) {
+        quad_pass<IO, false, VEC, EXT, ZOH, false>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g,
+                                                   s_B, s_C);
+        if (lane_ok) {
+            float *he = a.hend + (cd0 + j) * 16 + 4 * q;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) __hip_atomic_store(he + k, h[k], __ATOMIC_RELAXED, kAgent);
+            if (q == 0) __hip_atomic_store(a.dtsum + cd0 + j, dt_sum, __ATOMIC_RELAXED, kAgent);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the operator stores are complete
+        if (lane == 0) __hip_atomic_store(flags + j, a.epoch, __ATOMIC_RELAXED, kAgent);
+    }
+
+    // 2. the start state: fold the operators of chunks 0 .. j-1 (a chunk at
+    // which a sequence starts loads its own start state in the pass)
+    h[0] = h[1] = h[2] = h[3] = 0.0f;
+    if (j > 0 && !seq_pos<EXT>(a, b, j * a.K).reset) {
+        // lane i < j watches chunk i's flag
+        uint64_t ready = 0;
+        const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + a.spin_ticks;
+        while (a.spin_ticks != 0) {
+            const bool mine =
+                lane >= j || __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, kAgent) == a.epoch;
+            ready = __ballot(mine);
+            if (ready == ~0ull || __builtin_amdgcn_s_memrealtime() >= deadline) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        float A2[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = 4 * q + k;
+            const float v = a.A[dcl * a.N + (n < a.N ? n : a.N - 1)];
+            A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
+        }
+        if (ready != ~0ull) {
+            // operators not published in time: compute them here and write
+            // them to their slots (the same bits their owner writes, if it
+            // ever does)
+            for (int64_t i = 0; i < j; ++i) {
+                if ((ready >> i) & 1) continue;
+                float e[4], sdt, kp;
+                quad_pass<IO, false, VEC, EXT, ZOH, false>(a, i, e, sdt, kp, s_dt, s_w, s_du, s_g,
+                                                           s_B, s_C);
+                if (lane_ok) {
+                    float *he = a.hend + (cd0 + i) * 16 + 4 * q;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        __hip_atomic_store(he + k, e[k], __ATOMIC_RELAXED, kAgent);
+                    if (q == 0) __hip_atomic_store(a.dtsum + cd0 + i, sdt, __ATOMIC_RELAXED, kAgent);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        // 8 operators at a time: their loads are issued together
+        constexpr int kBatch = 8;
+        for (int64_t i0 = 0; i0 < j; i0 += kBatch) {
+            float e[kBatch][4], sdt[kBatch];
+#pragma unroll
+            for (int m = 0; m < kBatch; ++m) {
+                const int64_t i = i0 + m < j ? i0 + m : j - 1;
+                const float *he = a.hend + (cd0 + i) * 16 + 4 * q;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    e[m][k] = __hip_atomic_load(he + k, __ATOMIC_RELAXED, kAgent);
+                sdt[m] = __hip_atomic_load(a.dtsum + cd0 + i, __ATOMIC_RELAXED, kAgent);
+            }
+#pragma unroll
+            for (int m = 0; m < kBatch; ++m) {
+                const int64_t i = i0 + m;
+                if (i < j) {
+                    const int64_t tb = i * a.K;
+                    const int64_t te = tb + a.K < a.L ? tb + a.K : a.L;
+                    const SeqPos sp = seq_pos<EXT>(a, b, tb);
+                    const bool kept = !sp.reset && sp.end >= te;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        h[k] = __builtin_fmaf(kept ? exp2_hw(A2[k] * sdt[m]) : 0.0f, h[k],
+                                              e[m][k]);
+                }
+            }
+        }
+    }
+
+    // 3. y and the final states
+    __builtin_amdgcn_s_setprio(0);
+    quad_pass<IO, true, VEC, EXT, ZOH, true>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g, s_B,
+                                             s_C);
 }
 
 // ============================================================ group kernel (N > 16)
@@ -1144,6 +1340,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 template <class IO, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
+    if (a.flags) {
+        if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_begin, s);
+        hipLaunchKernelGGL((quad_fused_kernel<IO, VEC, EXT, ZOH>), grid, dim3(64), 0, s, a);
+        if (a.ev_begin && a.ev_end) (void)hipEventRecord(a.ev_end, s);
+        return hipGetLastError();
+    }
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
         hipLaunchKernelGGL((quad_kernel<IO, false, VEC, EXT, ZOH>), agrid, dim3(64), 0, s, a);

@@ -59,16 +59,29 @@ def _al(x):
 def test_workspace_and_chunk_plan(lib):
     # desc(): batch 2, d_inner 64, N 16, L 2048 -> the d_state <= 16 path,
     # which reads B and C in place (no packed copy) and, with at most 32
-    # chunks, folds the chunk operators in the scan pass (no start states)
+    # chunks, folds the chunk operators in the scan pass (no start states):
+    # 2 x 4 channel blocks are 8 wavefronts per chunk, so the library cuts the
+    # most chunks its minimum length allows (K = 64)
     d = desc()
     K = lib.ssm_scan_chunk_size(ctypes.byref(d))
-    assert 16 <= K <= 2048 and (K % 16 == 0 or K == 2048)
-    J = -(-2048 // K)
+    assert K == 64
+    J = 2048 // K
     need = lib.ssm_scan_workspace_bytes(ctypes.byref(d))
     # chunk end states, step-size sums, and one "keeps its incoming state" flag
     # per (batch row, chunk)
     ops = _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4) + _al(2 * J * 4)
-    assert need == (ops if J > 1 else 0)
+    assert need == ops
+    # chunks of 1024 tokens or more run in one launch, with one 8-byte
+    # publication flag per (batch row, channel block, chunk) in addition
+    d = desc(seqlen=8192, chunk_size=1024)
+    J = 8
+    ops = _al(2 * 64 * J * 16 * 4) + _al(2 * 64 * J * 4) + _al(2 * J * 4)
+    need = lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+    assert need == ops + _al(2 * 4 * J * 8)
+    # the scheduling flag changes neither the plan nor the workspace
+    d = desc(seqlen=8192, chunk_size=1024, flags=ssm.SSM_FLAG_INDEPENDENT_CHUNKS)
+    assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 1024
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == need
     for k in (16, 256, 1024):
         d = desc(chunk_size=k)
         assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == k
@@ -194,7 +207,7 @@ def test_conv_validation(lib):
 def test_flags_validation(lib):
     """Unknown flag bits and a nonzero reserved field are rejected."""
     ok = 4096
-    for flags, reserved, status in ((2, 0, 3), (1 << 31, 0, 3), (1, 1, 3)):
+    for flags, reserved, status in ((4, 0, 3), (1 << 31, 0, 3), (1, 1, 3)):
         d = desc(chunk_size=2048)
         d.flags, d.reserved = flags, reserved
         assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0

@@ -36,8 +36,10 @@ METRIC = "selective-scan channel-tokens/sec"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 # MI355X fp32 vector peak, published: 157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128
 # FMA lanes per clock.  ALU work below is counted in FMA-equivalent issue
-# slots (2 FLOP each); a transcendental (exp2, log2, rcp) issues at a quarter
-# of the FMA rate and so occupies 4 slots.
+# slots (2 FLOP each).  A transcendental (exp2, log2, rcp) occupies the VALU
+# about twice as long as an FMA -- measured on MI355X with independent chains
+# of wave64 instructions: 9.3 SIMD-cycles per v_exp_f32 against 4.5 per
+# v_fma_f32 -- and so counts as 2 slots.
 VALU_PEAK_TFLOPS = 157.3
 # That published figure counts packed FP32 (v_pk_fma_f32: two FMAs per lane per
 # clock).  These kernels are compiled with packed FP32 disabled, so the vector
@@ -48,12 +50,17 @@ DEFAULT_CONFIG = "c1_mamba130m_f32"
 CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 
 # Minimal instruction mix of the method, in FMA-equivalent slots.
-SLOTS_PER_UPDATE = 4 + 4       # dt*A', w*B, state FMA, output FMA; one exp2
-SLOTS_PER_CHTOK = {            # per (batch, channel, token), outside the N loop
-    "softplus": 7 + 2 * 4,     # 7 VALU + exp2 + log2
-    "common": 4,               # bias add, w = dt*u, D*u, (y + Du)
-    "gate": 3 + 2 * 4,         # 3 VALU + exp2 + rcp
+TRANS_SLOTS = 2
+SLOTS_PER_UPDATE = 4 + TRANS_SLOTS      # dt*A', w*B, state FMA, output FMA; one exp2
+SLOTS_PER_CHTOK = {                     # per (batch, channel, token), outside the N loop
+    "softplus": 7 + 2 * TRANS_SLOTS,    # 7 VALU + exp2 + log2
+    "common": 4,                        # bias add, w = dt*u, D*u, (y + Du)
+    "gate": 3 + 2 * TRANS_SLOTS,        # 3 VALU + exp2 + rcp
 }
+# The library's plan (mirrored here only to name the timed kernel): with
+# d_state <= 16 and 2..32 chunks of at least this many tokens the whole
+# chunked scan is one launch.
+FUSED_MIN_CHUNK = 1024
 
 
 def algorithmic_bytes(batch, d_inner, N, L, io, gate, last_state=True):
@@ -385,6 +392,15 @@ def main():
     hbm_gbs = set_bytes / (kavg * 1e-3) / 1e9
     slots = algorithmic_slots(batch, d_inner, N, L, gate)
     alu_tflops = 2.0 * slots / (kavg * 1e-3) / 1e12
+    J = -(-L // K)
+    if N <= 16 and 1 < J <= 32 and K >= FUSED_MIN_CHUNK:
+        kernel_name = ("quad_fused_kernel: the whole chunked scan (chunk aggregates, fold, "
+                       "y) in one launch")
+    elif N <= 16:
+        kernel_name = "quad_kernel pass writing y (after the chunk-aggregate pass)" if J > 1 \
+            else "quad_kernel pass writing y (one chunk)"
+    else:
+        kernel_name = "group_kernel pass writing y"
 
     traffic = None
     try:
@@ -424,7 +440,7 @@ def main():
             "traffic": traffic,
             "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
             "frac_nonpacked": alu_tflops / VALU_PEAK_NONPACKED_TFLOPS,
-            "kernel": "scan pass writing y (quad_kernel for N <= 16, group_kernel above)",
+            "kernel": kernel_name,
             "kernel_ms": kavg,
             "algorithmic_slots": slots,
             "hbm_achieved_gbs": hbm_gbs,

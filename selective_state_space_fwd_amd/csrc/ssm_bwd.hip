@@ -42,6 +42,12 @@ namespace {
 constexpr int kT = kBwdTile;   // tokens per backward tile
 constexpr int kEPL = kT / 4;   // tokens per lane in a tile piece (16 rows x kT tokens)
 constexpr int kQC = 16;        // channels per wavefront
+// Padded LDS strides (floats) of the per-channel partials, chosen so that
+// both their writes (one token, all lanes) and their transposed reads (one
+// channel, lanes over tokens) spread over the banks:
+constexpr int kGC = 20;             // dB / dC partials: channel stride (16 states + 4)
+constexpr int kGT = kQC * kGC + 4;  //   token stride, 81 four-float groups (odd)
+constexpr int kRT = 4 * kQC + 4;    // dw / dd row partials [t][q][c]: token stride
 
 template <class IO>
 __device__ __forceinline__ float ld_clamped(const typename IO::T *p, size_t base, int64_t t,
@@ -167,11 +173,11 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
     __shared__ __attribute__((aligned(16))) float s_B[kT * 16];
     __shared__ __attribute__((aligned(16))) float s_C[kT * 16];
     // row partials of dh.B and of sum_n dh h_prev A a: [t][q][c]
-    __shared__ __attribute__((aligned(16))) float s_rw[kT * 64];
-    __shared__ __attribute__((aligned(16))) float s_rd[kT * 64];
+    __shared__ __attribute__((aligned(16))) float s_rw[kT * kRT];
+    __shared__ __attribute__((aligned(16))) float s_rd[kT * kRT];
     // per-channel contributions to dB and dC: [t][c][n]
-    __shared__ __attribute__((aligned(16))) float s_gB[kT * kQC * 16];
-    __shared__ __attribute__((aligned(16))) float s_gC[kT * kQC * 16];
+    __shared__ __attribute__((aligned(16))) float s_gB[kT * kGT];
+    __shared__ __attribute__((aligned(16))) float s_gC[kT * kGT];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
             for (int k = 0; k < 4; ++k) {
                 const float prev = t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float dh = __builtin_fmaf(dO, cv[k], G[k]);
-                const float at = exp2_hw(dt * A2[k]);
+                const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
                 gc[k] = dO * hh[t][k];
                 gb[k] = w * dh;
                 dw = __builtin_fmaf(dh, bv[k], dw);
@@ -421,10 +427,10 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
                 dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
                 G[k] = dh * at;
             }
-            *reinterpret_cast<float4 *>(&s_gB[(t * kQC + c) * 16 + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
-            *reinterpret_cast<float4 *>(&s_gC[(t * kQC + c) * 16 + 4 * q]) = make_float4(gc[0], gc[1], gc[2], gc[3]);
-            s_rw[(t * 4 + q) * kQC + c] = dw;
-            s_rd[(t * 4 + q) * kQC + c] = dd;
+            *reinterpret_cast<float4 *>(&s_gB[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
+            *reinterpret_cast<float4 *>(&s_gC[t * kGT + c * kGC + 4 * q]) = make_float4(gc[0], gc[1], gc[2], gc[3]);
+            s_rw[t * kRT + q * kQC + c] = dw;
+            s_rd[t * kRT + q * kQC + c] = dd;
         }
         __syncthreads();
 
@@ -439,8 +445,8 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
             float dw = 0.0f, dd = 0.0f;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                dw += s_rw[(t * 4 + qq) * kQC + ch];
-                dd += s_rd[(t * 4 + qq) * kQC + ch];
+                dw += s_rw[t * kRT + qq * kQC + ch];
+                dd += s_rd[t * kRT + qq * kQC + ch];
             }
             const int64_t dch = d0 + ch;
             const bool ok = dch < a.D && tok < t_end;
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int ch = 0; ch < kQC; ++ch) {
-                const float4 v = *reinterpret_cast<const float4 *>(&src[(t * kQC + ch) * 16 + 4 * n4]);
+                const float4 v = *reinterpret_cast<const float4 *>(&src[t * kGT + ch * kGC + 4 * n4]);
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             const int64_t tok = t0 + t;
@@ -521,10 +527,24 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
         const int64_t n = (i / a.L) % a.N;
         const int64_t b = i / (a.L * a.N);
         float sb = 0.0f, sc = 0.0f;
-        for (int64_t k = 0; k < a.n_cblk; ++k) {
-            const size_t o = ((static_cast<size_t>(b) * a.n_cblk + k) * 16 + n) * a.L + t;
-            sb += g.dBp[o];
-            sc += g.dCp[o];
+        const size_t o0 = (static_cast<size_t>(b) * a.n_cblk * 16 + n) * a.L + t;
+        const size_t step = 16 * static_cast<size_t>(a.L);
+        // 8 blocks' partials loaded at a time, added in block order
+        for (int64_t k0 = 0; k0 < a.n_cblk; k0 += 8) {
+            float vb[8], vc[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int64_t k = k0 + m < a.n_cblk ? k0 + m : a.n_cblk - 1;
+                vb[m] = g.dBp[o0 + k * step];
+                vc[m] = g.dCp[o0 + k * step];
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                if (k0 + m < a.n_cblk) {
+                    sb += vb[m];
+                    sc += vc[m];
+                }
+            }
         }
         g.dB[i] = sb;
         g.dC[i] = sc;

@@ -159,7 +159,10 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 // ------------------------------------------------------------ pass 3
 // Grid (n_cblk * batch, J).
 template <class IO>
-__global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
+#ifndef SSM_BWD_WAVES_PER_SIMD
+#define SSM_BWD_WAVES_PER_SIMD 1
+#endif
+__global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
     // per (channel, token) values of the tile: [c][t]
     __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
@@ -311,6 +314,14 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
     float dA_acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dD_acc[kT / 4] = {}, db_acc[kT / 4] = {};
     const float Dv_lane = (lane_ok && a.Dskip) ? a.Dskip[dcl] : 0.0f;
+    // D of the channels this lane serves in step (d), loaded once: a global
+    // load inside the tile loop would wait for the next tile's prefetch too
+    float Dv_d[kT / 4];
+#pragma unroll
+    for (int e = 0; e < kT / 4; ++e) {
+        const int64_t dch = d0 + lane / kT + (64 / kT) * e;
+        Dv_d[e] = (dch < a.D && a.Dskip) ? a.Dskip[dch] : 0.0f;
+    }
     float qx0 = 0.f, qx1 = 0.f, qu0 = 0.f, qu1 = 0.f, qy0 = 0.f, qy1 = 0.f, qz0 = 0.f, qz1 = 0.f;
     float qb0 = 0.f, qb1 = 0.f, qc0 = 0.f, qc1 = 0.f;
     float4 qh = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(64) void bwd_kernel(ScanArgs a, BwdArgs g) {
             const int64_t dch = d0 + ch;
             const bool ok = dch < a.D && tok < t_end;
             const float dt = s_dt[o], uu = s_u[o], dO = s_do[o];
-            const float Dv = (ok && a.Dskip) ? a.Dskip[dch] : 0.0f;
+            const float Dv = ok ? Dv_d[e] : 0.0f;
             const float du = __builtin_fmaf(dO, Dv, dw * dt);
             const float ddl = __builtin_fmaf(dw, uu, dd) * s_sig[o];
             if (ok) {

@@ -231,9 +231,9 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
  * checkpoints, recompute inside the chunk); the reverse recurrence of the
  * state gradient is joined across chunks by transfer operators like the
  * forward one (§3.1).
- * Supported: d_state <= 16, Euler discretisation (flags == 0), one sequence
- * per batch row (no packing), no fused convolution; otherwise
- * SSM_ERR_UNSUPPORTED.
+ * Supported: d_state <= 16, Euler discretisation (no SSM_FLAG_ZOH), no
+ * fused convolution; otherwise SSM_ERR_UNSUPPORTED.  Packed sequences: see
+ * ssm_scan_bwd_ex.
  * Inputs: as ssm_scan_fwd_ex (initial_state may be NULL), plus
  *   dy             (batch, d_inner, L) io_dtype
  *   dlast          (batch, d_inner, N) float32 or NULL (zero)
@@ -254,6 +254,24 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
                         const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
                         float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
                         float *dh0, ssm_stream_t stream);
+
+/* ssm_scan_bwd for sequences packed along L (ufo.work article, §4.2), the
+ * backward of ssm_scan_fwd_ex: batch must be 1 and cu_seqlens holds n_seqs + 1
+ * device int32 token offsets (as in ssm_scan_fwd_ex).  The state gradient
+ * starts over at each sequence's last token from that sequence's row of
+ * dlast, and stops at its first token, where it gives that sequence's row of
+ * dh0.  initial_state, dlast and dh0 are (n_seqs, d_inner, N); an empty
+ * sequence's dh0 is its dlast.  With cu_seqlens NULL this is ssm_scan_bwd.
+ * Errors as ssm_scan_bwd, and SSM_ERR_BAD_SHAPE for packing with batch != 1
+ * or n_seqs < 1.  A malformed offset table gives unspecified gradients but
+ * no access out of bounds. */
+ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delta,
+                           const float *A, const void *B, const void *C, const float *D,
+                           const void *z, const float *delta_bias, int softplus_flag,
+                           const float *initial_state, const int32_t *cu_seqlens, int64_t n_seqs,
+                           const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                           float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                           float *dh0, ssm_stream_t stream);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssm_status_string(int status);

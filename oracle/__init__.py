@@ -265,6 +265,56 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
     return out
 
 
+def scan_bwd_varlen(u, delta, A, B, C, cu_seqlens, dy, D=None, z=None, delta_bias=None,
+                    softplus=True, initial_state=None, dlast=None, threads: int | None = None):
+    """Backward pass of ``scan_varlen`` (packed sequences), fp64: the gradients
+    of sum(dy * y) + sum(dlast * last_state).  Each sequence is its own scan
+    (``scan_varlen``), so its gradients are those of ``scan_bwd`` on its token
+    range with its own initial state and last-state gradient; the token
+    gradients (du, ddelta, dz, dB, dC) of the ranges are placed side by side
+    and the parameter gradients (dA, dD, ddelta_bias) summed over the
+    sequences in order.  An empty sequence passes its initial state straight
+    to its last state, so its dh0 is its dlast.  States are (n_seqs, d_inner,
+    N)."""
+    u = _f64(u)
+    if u.ndim != 3 or u.shape[0] != 1:
+        raise ValueError("packed sequences need u of shape (1, d_inner, total)")
+    _, d_inner, total = u.shape
+    N = np.asarray(A).shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = cu.size - 1
+    if n < 1 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to the total length")
+    h0 = None if initial_state is None else _f64(initial_state, (n, d_inner, N))
+    dl = None if dlast is None else _f64(dlast, (n, d_inner, N))
+    out = {k: np.zeros((1, d_inner, total)) for k in ("du", "ddelta")}
+    out["dz"] = np.zeros((1, d_inner, total)) if z is not None else None
+    out["dA"] = np.zeros((d_inner, N))
+    out["dB"] = np.zeros((1, N, total))
+    out["dC"] = np.zeros((1, N, total))
+    out["dD"] = np.zeros(d_inner)
+    out["ddelta_bias"] = np.zeros(d_inner)
+    out["dh0"] = np.zeros((n, d_inner, N))
+    for s in range(n):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            if dl is not None:
+                out["dh0"][s] = dl[s]
+            continue
+        part = lambda x: None if x is None else np.asarray(x)[:, :, a:b]
+        g = scan_bwd(part(u), part(delta), A, part(B), part(C), part(dy), D, part(z), delta_bias,
+                     softplus=softplus, initial_state=None if h0 is None else h0[s:s + 1],
+                     dlast=None if dl is None else dl[s:s + 1], threads=threads)
+        for k in ("du", "ddelta", "dB", "dC"):
+            out[k][:, :, a:b] = g[k]
+        if z is not None:
+            out["dz"][:, :, a:b] = g["dz"]
+        for k in ("dA", "dD", "ddelta_bias"):
+            out[k] += g[k]
+        out["dh0"][s] = g["dh0"][0]
+    return out
+
+
 def state_update(state, u, delta, A, B, C, D=None, z=None, zoh: bool = False):
     """One fp64 single-token update.  Returns (new_state, y); inputs untouched."""
     lib = _load()

@@ -86,6 +86,9 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_bwd.argtypes = [dp] + [vp] * 8 + [ctypes.c_int] + [vp] * 12 + [vp]
     lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd_ex.argtypes = ([dp] + [vp] * 8 + [ctypes.c_int] + [vp, vp, ctypes.c_int64] +
+                                    [vp] * 11 + [vp])
+    lib.ssm_scan_bwd_ex.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_version.argtypes = []
@@ -309,12 +312,13 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-                 initial_state=None, dlast=None, chunk_size=0, workspace=None):
+                 initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None):
     """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
     respect to all its inputs (d_state <= 16, Euler).  Returns a dict of
     float32 tensors: du, ddelta (of the raw delta), dA, dB, dC, dD (None
     without D), dz (None without z), ddelta_bias, dh0 (None without
-    initial_state)."""
+    initial_state).  cu_seqlens: packed sequences as in ssm_scan_fwd; the
+    states (initial_state, dlast, dh0) then have one row per sequence."""
     torch = _torch()
     lib = load_library()
     batch, d_inner, L = u.shape
@@ -325,10 +329,16 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
                            (B, "B", (batch, N, L)), (C, "C", (batch, N, L)),
                            (z, "z", (batch, d_inner, L)), (dy, "dy", (batch, d_inner, L))):
         _expect(t, name, shape, io, dev)
+    n_seqs, rows = 0, batch
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must hold n_seqs + 1 >= 2 offsets")
+        n_seqs = rows = cu_seqlens.numel() - 1
+        _expect(cu_seqlens, "cu_seqlens", (n_seqs + 1,), torch.int32, dev)
     for t, name, shape in ((A, "A", (d_inner, N)), (D, "D", (d_inner,)),
                            (delta_bias, "delta_bias", (d_inner,)),
-                           (initial_state, "initial_state", (batch, d_inner, N)),
-                           (dlast, "dlast", (batch, d_inner, N))):
+                           (initial_state, "initial_state", (rows, d_inner, N)),
+                           (dlast, "dlast", (rows, d_inner, N))):
         _expect(t, name, shape, torch.float32, dev)
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     out = {"du": f32(batch, d_inner, L), "ddelta": f32(batch, d_inner, L), "dA": f32(d_inner, N),
@@ -336,7 +346,7 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
            "dD": f32(d_inner) if D is not None else None,
            "dz": f32(batch, d_inner, L) if z is not None else None,
            "ddelta_bias": f32(d_inner),
-           "dh0": f32(batch, d_inner, N) if initial_state is not None else None}
+           "dh0": f32(rows, d_inner, N) if initial_state is not None else None}
     desc = make_desc(batch, d_inner, N, L, code, chunk_size)
     need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
@@ -344,12 +354,12 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         desc.workspace = workspace.data_ptr()
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = lib.ssm_scan_bwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                          _ptr(initial_state), _ptr(dy), _ptr(dlast), _ptr(out["du"]),
-                          _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
-                          _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
-                          _ptr(out["dh0"]), _stream(dev))
+    st = lib.ssm_scan_bwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                             _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                             _ptr(initial_state), _ptr(cu_seqlens), n_seqs, _ptr(dy), _ptr(dlast),
+                             _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                             _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _stream(dev))
     _check(st)
     return out
 

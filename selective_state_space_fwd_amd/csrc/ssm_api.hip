@@ -376,15 +376,20 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc) {
     return make_bwd_plan(desc, &p) == SSM_OK ? p.bytes : 0;
 }
 
-ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
-                        const void *B, const void *C, const float *D, const void *z,
-                        const float *delta_bias, int softplus_flag, const float *initial_state,
-                        const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
-                        float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
-                        float *dh0, ssm_stream_t stream) {
+ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delta,
+                           const float *A, const void *B, const void *C, const float *D,
+                           const void *z, const float *delta_bias, int softplus_flag,
+                           const float *initial_state, const int32_t *cu_seqlens, int64_t n_seqs,
+                           const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                           float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                           float *dh0, ssm_stream_t stream) {
     BwdPlan p;
     ssm_status st = make_bwd_plan(desc, &p);
     if (st != SSM_OK) return st;
+    if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
+    const int64_t state_rows = cu_seqlens ? n_seqs : desc->batch;
+    if (!dims_ok(state_rows, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
+    if (!aligned(cu_seqlens, 4)) return SSM_ERR_MISALIGNED;
     const int64_t rows = desc->batch * desc->d_inner;
     if (rows == 0 || desc->seqlen == 0) {
         // no tokens: every gradient of a token is empty; those of the
@@ -398,7 +403,7 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
         if (e == hipSuccess) e = zero(dD, Dn);
         if (e == hipSuccess) e = zero(ddelta_bias, Dn);
         if (e == hipSuccess && dh0) {
-            const size_t n = static_cast<size_t>(rows) * N;
+            const size_t n = static_cast<size_t>(state_rows) * Dn * N;
             e = dlast ? hipMemcpyAsync(dh0, dlast, n * sizeof(float), hipMemcpyDeviceToDevice, s)
                       : ssm::launch_fill_zero(dh0, n, s);
         }
@@ -426,7 +431,8 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
     a.softplus = softplus_flag != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.h0 = initial_state;
-    a.n_seqs = desc->batch;
+    a.cu = cu_seqlens;
+    a.n_seqs = state_rows;
     ssm::BwdArgs g{};
     g.dy = dy; g.dlast = dlast; g.du = du; g.ddelta = ddelta; g.dz = dz; g.dA = dA; g.dB = dB;
     g.dC = dC; g.dD = dD; g.dbias = ddelta_bias; g.dh0 = dh0; g.n_tiles = p.n_tiles;
@@ -444,6 +450,17 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
     g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
     g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
     return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int softplus_flag, const float *initial_state,
+                        const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                        float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
+                        float *dh0, ssm_stream_t stream) {
+    return ssm_scan_bwd_ex(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag,
+                           initial_state, nullptr, 0, dy, dlast, du, ddelta, dA, dB, dC, dD, dz,
+                           ddelta_bias, dh0, stream);
 }
 
 const char *ssm_status_string(int status) {

@@ -34,6 +34,7 @@
 // of B and C), kBwdTile / 4 consecutive tokens.
 #include "ssm_common.h"
 #include "ssm_launch.h"
+#include "ssm_seq.h"
 
 namespace ssm {
 
@@ -61,9 +62,30 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
 
 }  // namespace
 
+// Token marks of a backward tile [t0, t0 + kT) cut at the chunk end: starts
+// (bit i: token t0 + i starts a sequence) and last tokens (*last).  Without
+// packed sequences the tiles need none: the row's start and end are handled
+// at the chunk level.
+template <bool EXT>
+__device__ __forceinline__ uint32_t tile_marks(const ScanArgs &a, int64_t t0, int64_t t_end,
+                                               uint32_t *last) {
+    *last = 0;
+    if (!EXT || !a.cu) return 0;
+    const int64_t n = t_end - t0 < kT ? t_end - t0 : kT;
+    const uint32_t valid = (1u << n) - 1u;
+    uint32_t ls;
+    const uint32_t st = seq_marks(a, t0, kT, &ls);
+    *last = ls & valid;
+    return st & valid;
+}
+
 // ------------------------------------------------------------ pass 2
-// Grid (n_cblk * batch, J - 1): chunk j = blockIdx.y + 1.
-template <class IO>
+// Grid (n_cblk * batch, J - 1): chunk j = blockIdx.y + 1.  The gradient that
+// leaves chunk j to its left when none arrives from its right: the upstream
+// last-state gradient enters at the last token of every sequence, and
+// nothing leaves a sequence's first token (EXT: packed sequences; otherwise
+// the row's last token is in chunk J - 1).
+template <class IO, bool EXT>
 __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
     __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
@@ -104,6 +126,7 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
         A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
     }
     float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!EXT && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
     float dts = 0.0f;
     const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
     // the next tile's raw values, loaded one tile ahead (named registers)
@@ -138,14 +161,19 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
             s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
         }
         if (ti > 0) prefetch(t0 - kT);
+        uint32_t lmask;
+        const uint32_t smask = tile_marks<EXT>(a, t0, t_end, &lmask);
         __syncthreads();
 #pragma unroll
         for (int t = kT - 1; t >= 0; --t) {
             const float dt = s_dt[c * kT + t], dO = s_do[c * kT + t];
             const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
+            if (EXT && ((lmask >> t) & 1u))   // a sequence ends here: its dlast
+                load_state_row<4>(g.dlast, a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, G);
 #pragma unroll
             for (int k = 0; k < 4; ++k) G[k] = __builtin_fmaf(dO, cv[k], G[k]) * exp2_hw(dt * A2[k]);
+            if (EXT && ((smask >> t) & 1u)) G[0] = G[1] = G[2] = G[3] = 0.0f;   // starts here
             dts += dt;
         }
         __syncthreads();
@@ -157,11 +185,12 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 }
 
 // ------------------------------------------------------------ pass 3
-// Grid (n_cblk * batch, J).
-template <class IO>
+// Grid (n_cblk * batch, J).  EXT: packed sequences (the state starts over at
+// every sequence start, the gradient at every sequence end).
 #ifndef SSM_BWD_WAVES_PER_SIMD
 #define SSM_BWD_WAVES_PER_SIMD 1
 #endif
+template <class IO, bool EXT>
 __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
     // per (channel, token) values of the tile: [c][t]
@@ -227,14 +256,9 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     // ---- start state of the chunk (forward) and the gradient arriving at its
     // last token (backward)
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (j == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int n = 4 * q + k;
-            const float v = a.h0 ? a.h0[(static_cast<size_t>(b) * a.D + dcl) * a.N +
-                                        (n < a.N ? n : a.N - 1)] : 0.0f;
-            h[k] = (lane_ok && n < a.N) ? v : 0.0f;
-        }
+    const SeqPos sp0 = seq_pos<EXT>(a, b, t_begin);
+    if (sp0.reset) {
+        load_start_state<4>(a, sp0.s, dcl, lane_ok, 4 * q, h);
     } else {
         for (int64_t i = 0; i < j; ++i) {
             const float sdt = a.dtsum[cd0 + i];
@@ -247,20 +271,25 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
         }
         if (!lane_ok) h[0] = h[1] = h[2] = h[3] = 0.0f;
     }
-    float G[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int n = 4 * q + k;
-        const float v = g.dlast ? g.dlast[(static_cast<size_t>(b) * a.D + dcl) * a.N +
-                                          (n < a.N ? n : a.N - 1)] : 0.0f;
-        G[k] = (lane_ok && n < a.N) ? v : 0.0f;
-    }
+    // the gradient arriving at the chunk's last token from the right: the
+    // reverse operators of chunks J-1 .. j+1 (a chunk in which a sequence
+    // starts passes nothing on from its right); the row's own dlast enters
+    // at its last token, in chunk J-1
+    float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!EXT && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
     for (int64_t i = a.J - 1; i > j; --i) {
         const float sdt = g.bdtsum[cd0 + i];
         const float4 v = *reinterpret_cast<const float4 *>(g.gend + (cd0 + i) * 16 + 4 * q);
         const float ge[4] = {v.x, v.y, v.z, v.w};
+        bool kept = true;
+        if (EXT) {
+            const int64_t tb = i * a.K, te = tb + a.K < L ? tb + a.K : L;
+            const SeqPos sp = seq_pos<EXT>(a, b, tb);
+            kept = !sp.reset && sp.end >= te;
+        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) G[k] = __builtin_fmaf(exp2_hw(A2[k] * sdt), G[k], ge[k]);
+        for (int k = 0; k < 4; ++k)
+            G[k] = __builtin_fmaf(kept ? exp2_hw(A2[k] * sdt) : 0.0f, G[k], ge[k]);
     }
     if (!lane_ok) G[0] = G[1] = G[2] = G[3] = 0.0f;
 
@@ -298,12 +327,16 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
         }
         if (ti + 1 < ntile) prefetch_fwd(t0 + kT);
+        uint32_t fl;
+        const uint32_t fs = tile_marks<EXT>(a, t0, t_end, &fl);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
             const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
+            if (EXT && ((fs >> t) & 1u))   // a sequence starts: its start state
+                load_start_state<4>(a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, h);
 #pragma unroll
             for (int k = 0; k < 4; ++k) h[k] = __builtin_fmaf(exp2_hw(dt * A2[k]), h[k], w * bv[k]);
         }
@@ -378,9 +411,12 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
         }
         if (ti > 0) prefetch_rev(t0 - kT);
+        uint32_t lmask;
+        const uint32_t smask = tile_marks<EXT>(a, t0, t_end, &lmask);
         __syncthreads();
 
-        // (b) recompute the tile's states from its checkpoint
+        // (b) recompute the tile's states from its checkpoint (a token that
+        // starts a sequence continues from that sequence's start state)
         float hh[kT][4];
         float part[kT];
 #pragma unroll
@@ -391,9 +427,12 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
             float p = 0.0f;
+            float h0v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const bool st = EXT && ((smask >> t) & 1u);
+            if (st) load_start_state<4>(a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, h0v);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float prev = t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
+                const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 hh[t][k] = __builtin_fmaf(exp2_hw(dt * A2[k]), prev, w * bv[k]);
                 p = __builtin_fmaf(cv[k], hh[t][k], p);
             }
@@ -415,7 +454,8 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             s_o[o] = __builtin_fmaf(Dv_lane, s_u[o], __uint_as_float(s[0]) + __uint_as_float(s[1]));
         }
 
-        // (c) walk the tile back
+        // (c) walk the tile back (EXT: the gradient starts over from dlast at
+        // a sequence's last token; at its first token it leaves as dh0)
 #pragma unroll
         for (int t = kT - 1; t >= 0; --t) {
             const float dt = s_dt[c * kT + t], w = s_w[c * kT + t], dO = s_do[c * kT + t];
@@ -425,9 +465,15 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
             float gb[4], gc[4];
             float dw = 0.0f, dd = 0.0f;
+            if (EXT && ((lmask >> t) & 1u))
+                load_state_row<4>(g.dlast, a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, G);
+            float h0v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const bool st = EXT && ((smask >> t) & 1u);
+            const int64_t s_st = st ? seq_of(a, t0 + t) : 0;
+            if (st) load_start_state<4>(a, s_st, dcl, lane_ok, 4 * q, h0v);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float prev = t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
+                const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float dh = __builtin_fmaf(dO, cv[k], G[k]);
                 const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
                 gc[k] = dO * hh[t][k];
@@ -437,6 +483,10 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 dd = __builtin_fmaf(da * An[k], at, dd);
                 dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
                 G[k] = dh * at;
+            }
+            if (st) {
+                store_state_row<4>(g.dh0, a, s_st, d, lane_ok, 4 * q, G);
+                G[0] = G[1] = G[2] = G[3] = 0.0f;
             }
             *reinterpret_cast<float4 *>(&s_gB[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
             *reinterpret_cast<float4 *>(&s_gC[t * kGT + c * kGC + 4 * q]) = make_float4(gc[0], gc[1], gc[2], gc[3]);
@@ -520,10 +570,19 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     if (!lane_ok) return;
     *reinterpret_cast<float4 *>(g.dAp + cd * 16 + 4 * q) =
         make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
-    if (j == 0 && g.dh0) {
+    if (!EXT && j == 0 && g.dh0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (4 * q + k < a.N) g.dh0[(static_cast<size_t>(b) * a.D + d) * a.N + 4 * q + k] = G[k];
+    }
+    if (EXT && a.cu && j == 0 && g.dh0) {
+        // an empty sequence passes its start state straight to its last state
+        for (int64_t s = 0; s < a.n_seqs; ++s) {
+            if (cu_at(a, s) != cu_at(a, s + 1)) continue;
+            float e[4];
+            load_state_row<4>(g.dlast, a, s, dcl, lane_ok, 4 * q, e);
+            store_state_row<4>(g.dh0, a, s, d, lane_ok, 4 * q, e);
+        }
     }
 }
 
@@ -586,16 +645,17 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
 }
 
 // ------------------------------------------------------------ launch
-template <class IO>
+template <class IO, bool EXT>
 static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
     if (a.J > 1) {
         const hipError_t e = launch_scan_agg(a, s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_agg_kernel<IO>, dim3(gx, static_cast<unsigned>(a.J - 1)), dim3(64),
-                           0, s, a, g);
+        hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT>), dim3(gx, static_cast<unsigned>(a.J - 1)),
+                           dim3(64), 0, s, a, g);
     }
-    hipLaunchKernelGGL(bwd_kernel<IO>, dim3(gx, static_cast<unsigned>(a.J)), dim3(64), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_kernel<IO, EXT>), dim3(gx, static_cast<unsigned>(a.J)), dim3(64), 0, s,
+                       a, g);
     const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
                        dim3(256), 0, s, a, g);
@@ -603,7 +663,8 @@ static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t
 }
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
-    return a.bf16 ? launch_bwd_io<BF16>(a, g, s) : launch_bwd_io<F32>(a, g, s);
+    if (a.cu) return a.bf16 ? launch_bwd_io<BF16, true>(a, g, s) : launch_bwd_io<F32, true>(a, g, s);
+    return a.bf16 ? launch_bwd_io<BF16, false>(a, g, s) : launch_bwd_io<F32, false>(a, g, s);
 }
 
 }  // namespace ssm

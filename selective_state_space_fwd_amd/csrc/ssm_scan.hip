@@ -40,6 +40,7 @@
 
 #include "ssm_common.h"
 #include "ssm_launch.h"
+#include "ssm_seq.h"
 
 namespace ssm {
 
@@ -112,66 +113,11 @@ struct Piece4<BF16> {
 };
 
 
-// ============================================================ sequences
-// Where the state starts over: at token 0 of every batch row or, with packed
-// sequences (ufo.work article, §4.2), at the first token of every sequence of
-// the cu_seqlens table.  All values here are uniform across a workgroup.
-// Offsets are clamped into [0, L], so any table keeps every access in bounds.
-__device__ __forceinline__ int64_t cu_at(const ScanArgs &a, int64_t i) {
-    const int64_t v = a.cu[i];
-    return v < 0 ? 0 : (v > a.L ? a.L : v);
-}
-
-// The sequence that token t belongs to: the last s with cu[s] <= t (empty
-// sequences that start at t come before it and are skipped).
-__device__ __forceinline__ int64_t seq_of(const ScanArgs &a, int64_t t) {
-    int64_t lo = 0, hi = a.n_seqs - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (cu_at(a, mid) <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-struct SeqPos {
-    int64_t s;        // sequence: the batch row when sequences are not packed
-    int64_t end;      // its end, the next token where the state starts over
-    bool reset;       // token t starts the sequence
-};
-
-template <bool EXT>
-__device__ __forceinline__ SeqPos seq_pos(const ScanArgs &a, int64_t b, int64_t t) {
-    SeqPos p;
-    if (EXT && a.cu) {
-        p.s = seq_of(a, t);
-        p.end = cu_at(a, p.s + 1);
-        p.reset = cu_at(a, p.s) == t;
-    } else {
-        p.s = b;
-        p.end = a.L;
-        p.reset = t == 0;
-    }
-    return p;
-}
-
 // The transfer operator's decay for chunk i of batch row b: exp(A sum dt),
 // or 0 when a sequence starts inside the chunk.
 __device__ __forceinline__ float chunk_decay(const ScanArgs &a, int64_t b, int64_t i, float A2,
                                              float sdt) {
     return a.keep[b * a.J + i] != 0.0f ? exp2_hw(A2 * sdt) : 0.0f;
-}
-
-// Start state of sequence s for states n0 .. n0 + S - 1 of channel d (zero
-// when there is no initial state, for states n >= N and for padded channels).
-template <int S>
-__device__ __forceinline__ void load_start_state(const ScanArgs &a, int64_t s, int64_t dcl,
-                                                 bool lane_ok, int n0, float (&h)[S]) {
-#pragma unroll
-    for (int k = 0; k < S; ++k) {
-        const int n = n0 + k;
-        const float v = a.h0 ? a.h0[(s * a.D + dcl) * a.N + (n < a.N ? n : a.N - 1)] : 0.0f;
-        h[k] = (lane_ok && n < a.N) ? v : 0.0f;
-    }
 }
 
 // Final state of sequence s: states n0 .. n0 + S - 1 of channel d.
@@ -1426,10 +1372,16 @@ static hipError_t launch_agg_io(const ScanArgs &a, hipStream_t s) {
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.B) && al(a.C);
     const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-    if (vec)
+    if (a.cu) {   // packed sequences: the extended instance
+        if (vec)
+            hipLaunchKernelGGL((quad_kernel<IO, false, true, true, false>), agrid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL((quad_kernel<IO, false, false, true, false>), agrid, dim3(64), 0, s, a);
+    } else if (vec) {
         hipLaunchKernelGGL((quad_kernel<IO, false, true, false, false>), agrid, dim3(64), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((quad_kernel<IO, false, false, false, false>), agrid, dim3(64), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd",
+    for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_ex",
               "ssm_scan_bwd_workspace_bytes", "ssm_state_update", "ssm_scan_workspace_bytes",
               "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
         assert n in names
@@ -248,3 +248,17 @@ def test_backward_plan_and_validation(lib):
     assert lib.ssm_scan_bwd(ctypes.byref(d), *bad, None) == 1
     d.workspace, d.workspace_bytes = ok, 16
     assert lib.ssm_scan_bwd(ctypes.byref(d), *args, None) == 5
+    # packed sequences: batch 1 and at least one sequence, an aligned table
+    d.workspace, d.workspace_bytes = ok, 1 << 40
+    # (..., softplus, initial_state, cu_seqlens, n_seqs, dy, dlast, ...)
+    ex = args[:10] + [ok, 3] + args[10:]
+    assert len(ex) == 23
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d), *ex, None) == 2          # batch 2
+    d1 = desc(batch=1, chunk_size=16)
+    d1.workspace, d1.workspace_bytes = ok, 1 << 40
+    bad = list(ex)
+    bad[11] = 0
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d1), *bad, None) == 2        # no sequences
+    bad = list(ex)
+    bad[10] = ok + 2
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d1), *bad, None) == 4        # misaligned table

@@ -598,3 +598,51 @@ def test_backward_threads_do_not_change_result():
         assert np.array_equal(g1[k], g4[k]), k
     for k in ("dB", "dC"):
         assert rel(g1[k], g4[k]) < 1e-14
+
+
+def _loss_varlen(u, dt, A, B, C, D, z, bias, h0, cu, dy, dlast):
+    y, last = oracle.scan_varlen(u, dt, A, B, C, cu, D, z, bias, softplus=True, initial_state=h0)
+    return float(np.sum(dy * y) + np.sum(dlast * last))
+
+
+def test_backward_packed_sequences_against_finite_differences():
+    """Packed sequences (one empty, one of a single token): every gradient of
+    sum(dy*y) + sum(dlast*last_state) from ``scan_bwd_varlen`` equals the
+    central difference of the packed forward oracle's loss.  This pins where
+    the state gradient starts (each sequence's dlast at its last token), where
+    it stops (dh0 at its first token, dlast for the empty one) and that no
+    gradient crosses a boundary."""
+    rng = np.random.default_rng(11)
+    lens = [3, 0, 1, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    d, N, L, n = 2, 3, int(cu[-1]), len(lens)
+    u = rng.standard_normal((1, d, L))
+    raw = 0.5 * rng.standard_normal((1, d, L))
+    A = -np.exp(rng.standard_normal((d, N)))
+    B = rng.standard_normal((1, N, L))
+    C = rng.standard_normal((1, N, L))
+    D = rng.standard_normal(d)
+    z = rng.standard_normal((1, d, L))
+    bias = rng.uniform(-3, -1, d)
+    h0 = rng.standard_normal((n, d, N))
+    dy = rng.standard_normal((1, d, L))
+    dlast = rng.standard_normal((n, d, N))
+    g = oracle.scan_bwd_varlen(u, raw, A, B, C, cu, dy, D, z, bias, softplus=True,
+                               initial_state=h0, dlast=dlast)
+    args = dict(u=u, dt=raw, A=A, B=B, C=C, D=D, z=z, bias=bias, h0=h0)
+    names = {"u": "du", "dt": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+             "z": "dz", "bias": "ddelta_bias", "h0": "dh0"}
+    eps = 1e-6
+    for key, gname in names.items():
+        arr = args[key]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus = {k: v.copy() for k, v in args.items()}
+            minus = {k: v.copy() for k, v in args.items()}
+            plus[key][idx] += eps
+            minus[key][idx] -= eps
+            num[idx] = (_loss_varlen(**plus, cu=cu, dy=dy, dlast=dlast) -
+                        _loss_varlen(**minus, cu=cu, dy=dy, dlast=dlast)) / (2 * eps)
+        assert rel(g[gname], num) < 1e-7, (gname, rel(g[gname], num))
+    # the empty sequence: its initial state goes straight to its last state
+    assert np.array_equal(g["dh0"][1], dlast[1])

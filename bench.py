@@ -63,6 +63,18 @@ SLOTS_PER_CHTOK = {                     # per (batch, channel, token), outside t
 FUSED_MIN_CHUNK = 1024
 
 
+# Backward pass, minimal work of the method (states are not stored by the
+# forward pass, so one recompute of the recurrence is part of it):
+# per (channel-token, state): recompute dt*A', exp2, w*B, state FMA (5);
+# reverse walk dh = G + dO*C, dO*h and w*dh with their channel sums (5),
+# dh.B, dh*h_prev, the dA and ddelta terms (2 + 2), G = dh*a (1): 17 in all.
+# Per channel-token: softplus (11), its derivative (sigmoid: 1 + exp2 + rcp),
+# silu and its derivative (exp2 + rcp + 4), w, dO, the output o and the five
+# token gradients and two sums (9): 35.
+BWD_SLOTS_PER_UPDATE = 5 + 12
+BWD_SLOTS_PER_CHTOK = 35
+
+
 def algorithmic_bytes(batch, d_inner, N, L, io, gate, last_state=True):
     """Bytes the scan must move once: u, delta, (z) read and y written per
     channel-token; B and C read once per (batch, token); A, D, bias per
@@ -273,6 +285,8 @@ def bench_backward(args, torch, ssm, dev):
     chtok = batch * d_inner * L
     nbytes = (chtok * ((4 if gate else 3) * e + (3 if gate else 2) * 4) +
               2 * batch * N * L * (e + 4) + d_inner * (N + 2) * 4)
+    slots = chtok * (N * BWD_SLOTS_PER_UPDATE + BWD_SLOTS_PER_CHTOK)
+    tflops = 2.0 * slots / (ms * 1e-3) / 1e12
     return {
         "metric": "selective-scan backward channel-tokens/sec", "value": chtok / (ms * 1e-3),
         "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -283,6 +297,16 @@ def bench_backward(args, torch, ssm, dev):
                                f"{' + gate' if gate else ''}",
                    "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
                    "io_dtype": io, "gate": gate},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
+                     "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
+                     "frac_nonpacked": tflops / VALU_PEAK_NONPACKED_TFLOPS,
+                     "kernel": "the whole backward call (forward chunk aggregates, reverse "
+                               "chunk aggregates, bwd_kernel, bwd_reduce_kernel)",
+                     "kernel_ms": ms, "algorithmic_slots": slots,
+                     "hbm_achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": nbytes},
         "hbm_achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes,
         "versions": versions(),
     }

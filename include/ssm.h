@@ -231,9 +231,10 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
  * checkpoints, recompute inside the chunk); the reverse recurrence of the
  * state gradient is joined across chunks by transfer operators like the
  * forward one (§3.1).
- * Supported: d_state <= 16, Euler discretisation (no SSM_FLAG_ZOH), no
- * fused convolution; otherwise SSM_ERR_UNSUPPORTED.  Packed sequences: see
- * ssm_scan_bwd_ex.
+ * Supported: d_state <= 16 (otherwise SSM_ERR_UNSUPPORTED), Euler or, with
+ * SSM_FLAG_ZOH in desc->flags, the zero-order-hold input term; the fused
+ * convolution has no backward here (its input u is an input of this call).
+ * Packed sequences: see ssm_scan_bwd_ex.
  * Inputs: as ssm_scan_fwd_ex (initial_state may be NULL), plus
  *   dy             (batch, d_inner, L) io_dtype
  *   dlast          (batch, d_inner, N) float32 or NULL (zero)

@@ -78,7 +78,7 @@ def _load():
     lib.oracle_scan_chunked.restype = c_int
     lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [c_int]
     lib.oracle_scan_bwd.argtypes = ([i64, i64, i64, i64] + [dp] * 8 + [c_int] + [dp] * 3 +
-                                    [dp] * 9 + [c_int])
+                                    [dp] * 9 + [c_int, c_int])
     lib.oracle_scan_bwd.restype = c_int
     lib.oracle_state_update.restype = c_int
     _lib = lib
@@ -235,11 +235,12 @@ def causal_conv1d(x, weight, bias=None, silu=True, cu_seqlens=None, conv_state=N
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-             initial_state=None, dlast=None, threads: int | None = None):
-    """Gradients of sum(dy * y) + sum(dlast * last_state) for the Euler scan,
-    fp64 (the reverse walk is written out in ssm_oracle.c).  Returns a dict
-    with du, ddelta (w.r.t. the raw step before bias and softplus), dz (None
-    without a gate), dA, dB, dC, dD, ddelta_bias, dh0 (w.r.t. initial_state)."""
+             initial_state=None, dlast=None, threads: int | None = None, zoh: bool = False):
+    """Gradients of sum(dy * y) + sum(dlast * last_state) for the scan, fp64
+    (the reverse walk is written out in ssm_oracle.c; zoh: the zero-order-hold
+    input term).  Returns a dict with du, ddelta (w.r.t. the raw step before
+    bias and softplus), dz (None without a gate), dA, dB, dC, dD, ddelta_bias,
+    dh0 (w.r.t. initial_state)."""
     lib = _load()
     (batch, d_inner, N, L, u, delta, A, B, C, D, z, bias, h0) = _scan_args(
         u, delta, A, B, C, D, z, delta_bias, initial_state)
@@ -259,14 +260,15 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
                              _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
                              _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
-                             threads or default_threads())
+                             threads or default_threads(), int(bool(zoh)))
     if rc != 0:
         raise RuntimeError(f"oracle_scan_bwd failed ({rc})")
     return out
 
 
 def scan_bwd_varlen(u, delta, A, B, C, cu_seqlens, dy, D=None, z=None, delta_bias=None,
-                    softplus=True, initial_state=None, dlast=None, threads: int | None = None):
+                    softplus=True, initial_state=None, dlast=None, threads: int | None = None,
+                    zoh: bool = False):
     """Backward pass of ``scan_varlen`` (packed sequences), fp64: the gradients
     of sum(dy * y) + sum(dlast * last_state).  Each sequence is its own scan
     (``scan_varlen``), so its gradients are those of ``scan_bwd`` on its token
@@ -304,7 +306,7 @@ def scan_bwd_varlen(u, delta, A, B, C, cu_seqlens, dy, D=None, z=None, delta_bia
         part = lambda x: None if x is None else np.asarray(x)[:, :, a:b]
         g = scan_bwd(part(u), part(delta), A, part(B), part(C), part(dy), D, part(z), delta_bias,
                      softplus=softplus, initial_state=None if h0 is None else h0[s:s + 1],
-                     dlast=None if dl is None else dl[s:s + 1], threads=threads)
+                     dlast=None if dl is None else dl[s:s + 1], threads=threads, zoh=zoh)
         for k in ("du", "ddelta", "dB", "dC"):
             out[k][:, :, a:b] = g[k]
         if z is not None:

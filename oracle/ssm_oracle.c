@@ -72,6 +72,31 @@ static double input_coeff(double dt, double A, int zoh) {
     return A != 0.0 ? expm1(dt * A) / A : dt;
 }
 
+/* Derivatives of that factor, for the backward pass.  Euler: d/ddt = 1,
+ * d/dA = 0.  Zero-order hold, c = (exp(dt A) - 1) / A: dc/ddt = exp(dt A);
+ * dc/dA = (dt A exp(dt A) - (exp(dt A) - 1)) / A^2 = dt^2 psi(dt A) with
+ * psi(x) = (x e^x - e^x + 1) / x^2 = sum_{m >= 2} (m - 1) x^(m-2) / m!
+ * (the power series of x e^x - e^x + 1 divided by x^2), summed term by term
+ * for |x| < 1 and taken in closed form otherwise. */
+static double zoh_psi(double x) {
+    if (fabs(x) >= 1.0) return (x * exp(x) - expm1(x)) / (x * x);
+    double s = 0.0, fact = 2.0, xp = 1.0;   /* m! and x^(m-2) for m = 2 */
+    for (int m = 2; m < 30; ++m) {
+        s += (double)(m - 1) * xp / fact;
+        xp *= x;
+        fact *= (double)(m + 1);
+    }
+    return s;
+}
+
+static double input_coeff_ddt(double dt, double A, int zoh) {
+    return zoh ? exp(dt * A) : 1.0;
+}
+
+static double input_coeff_dA(double dt, double A, int zoh) {
+    return zoh ? dt * dt * zoh_psi(dt * A) : 0.0;
+}
+
 /* ------------------------------------------------------------ arguments */
 
 typedef struct {
@@ -294,15 +319,18 @@ static int check_dims(int64_t batch, int64_t d_inner, int64_t d_state, int64_t s
  * written out by hand -- the backward step the ufo.work article, §2.2, pairs
  * with the fused forward (recompute the states, then walk back).  For one
  * row (b, d), with x_t = delta_raw_t + bias, dt_t = softplus(x_t) (or x_t),
- * a_t = exp(dt_t A), w_t = dt_t u_t, o_t = C_t . h_t + D u_t and
- * g_t = silu(z_t) (or 1), walking t = L-1 .. 0 with G = dlast:
+ * a_t = exp(dt_t A), c_t the input factor (dt_t, or (a_t - 1) / A with
+ * zero-order hold) with derivatives c' (by dt) and c^A (by A),
+ * o_t = C_t . h_t + D u_t and g_t = silu(z_t) (or 1), walking
+ * t = L-1 .. 0 with G = dlast:
  *   do_t   = dy_t g_t                      dz_t  = dy_t o_t silu'(z_t)
- *   dh_t   = G + do_t C_t                  dC_t += do_t h_t,  dB_t += w_t dh_t
- *   dw_t   = dh_t . B_t                    da_t  = dh_t h_{t-1}   (h_{-1} = h0)
- *   ddt_t  = dw_t u_t + sum_n da_t A a_t   du_t  = do_t D + dw_t dt_t
- *   dA    += da_t a_t dt_t                 dD   += do_t u_t
+ *   dh_t   = G + do_t C_t                  dC_t += do_t h_t,  dB_t += c_t u_t dh_t
+ *   da_t   = dh_t h_{t-1}   (h_{-1} = h0)  du_t  = do_t D + sum_n dh_t B_t c_t
+ *   ddt_t  = sum_n (da_t A a_t + dh_t B_t u_t c'_t)
+ *   dA    += da_t a_t dt_t + dh_t B_t u_t c^A_t          dD += do_t u_t
  *   G      = dh_t a_t                      ddelta_t = ddt_t softplus'(x_t)
  *   dbias += ddelta_t;    finally dh0 = G.
+ * (Euler: c = dt, c' = 1, c^A = 0.)
  * dB and dC sum over the channels of a batch row, dA, dD and dbias over the
  * batch rows (and tokens): per-thread partial buffers added in a fixed order. */
 typedef struct {
@@ -335,7 +363,8 @@ static void *bwd_main(void *p) {
             const double dt = step_size(a, d, a->delta[row + t]), u = a->u[row + t];
             for (int64_t n = 0; n < N; ++n)
                 hs[(t + 1) * N + n] = exp(dt * a->A[d * N + n]) * hs[t * N + n] +
-                                      dt * a->B[(b * N + n) * L + t] * u;
+                                      input_coeff(dt, a->A[d * N + n], a->zoh) *
+                                          a->B[(b * N + n) * L + t] * u;
         }
         /* backward */
         for (int64_t n = 0; n < N; ++n) G[n] = w->dlast ? w->dlast[(b * Dn + d) * N + n] : 0.0;
@@ -358,21 +387,21 @@ static void *bwd_main(void *p) {
             }
             const double dO = w->dy[row + t] * g;
             dD_acc += dO * u;
-            double dw = 0.0, ddt = 0.0;
+            double dux = 0.0, ddt = 0.0;
             for (int64_t n = 0; n < N; ++n) {
                 const double Bn = a->B[(b * N + n) * L + t], Cn = a->C[(b * N + n) * L + t];
                 const double An = a->A[d * N + n], at = exp(dt * An);
+                const double c = input_coeff(dt, An, a->zoh);
                 dh[n] = G[n] + dO * Cn;
                 dCp[(b * N + n) * L + t] += dO * ht[n];
-                dBp[(b * N + n) * L + t] += dt * u * dh[n];
-                dw += dh[n] * Bn;
+                dBp[(b * N + n) * L + t] += c * u * dh[n];
+                dux += dh[n] * Bn * c;
                 const double da = dh[n] * hp[n];
-                ddt += da * An * at;
-                dA_row[n] += da * at * dt;
+                ddt += da * An * at + dh[n] * Bn * u * input_coeff_ddt(dt, An, a->zoh);
+                dA_row[n] += da * at * dt + dh[n] * Bn * u * input_coeff_dA(dt, An, a->zoh);
                 G[n] = dh[n] * at;
             }
-            ddt += dw * u;
-            w->du[row + t] = dO * (a->D ? a->D[d] : 0.0) + dw * dt;
+            w->du[row + t] = dO * (a->D ? a->D[d] : 0.0) + dux;
             const double dx = a->softplus_flag ? ddt * sigmoid(x) : ddt;
             w->ddelta[row + t] = dx;
             dbias_acc += dx;
@@ -391,14 +420,14 @@ int oracle_scan_bwd(int64_t batch, int64_t d_inner, int64_t d_state, int64_t seq
                     int softplus_flag, const double *initial_state, const double *dy,
                     const double *dlast, double *du, double *ddelta, double *dA, double *dB,
                     double *dC, double *dD, double *dz, double *ddelta_bias, double *dh0,
-                    int n_threads) {
+                    int n_threads, int zoh) {
     if (!check_dims(batch, d_inner, d_state, seqlen)) return -1;
     if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC || !dD ||
         !ddelta_bias || !dh0 || (z && !dz))
         return -1;
     const int64_t N = d_state, L = seqlen, rows = batch * d_inner;
     scan_args a = {batch, d_inner, d_state, seqlen, u, delta, A, B, C, D, z, delta_bias,
-                   initial_state, softplus_flag, NULL, NULL, 0, 0, 0};
+                   initial_state, softplus_flag, NULL, NULL, zoh != 0, 0, 0};
     if (n_threads < 1) n_threads = 1;
     if (n_threads > rows) n_threads = (int)(rows > 0 ? rows : 1);
     const size_t part = (size_t)(batch * N * L);

@@ -312,9 +312,11 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
-                 initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None):
+                 initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None,
+                 zoh=False):
     """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
-    respect to all its inputs (d_state <= 16, Euler).  Returns a dict of
+    respect to all its inputs (d_state <= 16; zoh: the zero-order-hold input
+    term, as in ssm_scan_fwd).  Returns a dict of
     float32 tensors: du, ddelta (of the raw delta), dA, dB, dC, dD (None
     without D), dz (None without z), ddelta_bias, dh0 (None without
     initial_state).  cu_seqlens: packed sequences as in ssm_scan_fwd; the
@@ -347,7 +349,7 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
            "dz": f32(batch, d_inner, L) if z is not None else None,
            "ddelta_bias": f32(d_inner),
            "dh0": f32(rows, d_inner, N) if initial_state is not None else None}
-    desc = make_desc(batch, d_inner, N, L, code, chunk_size)
+    desc = make_desc(batch, d_inner, N, L, code, chunk_size, _flags(zoh, False))
     need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:

@@ -165,7 +165,7 @@ struct BwdPlan {
 ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     const ssm_status st = make_plan(d, &p->f, false);
     if (st != SSM_OK) return st;
-    if (d->d_state > 16 || (d->flags & SSM_FLAG_ZOH) != 0) return SSM_ERR_UNSUPPORTED;
+    if (d->d_state > 16) return SSM_ERR_UNSUPPORTED;
     Plan &f = p->f;
     const int64_t L = d->seqlen;
     if (L == 0 || d->batch * d->d_inner == 0) { p->bytes = 0; return SSM_OK; }
@@ -429,6 +429,7 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
     a.G = f.G; a.K = f.K; a.J = f.J; a.n_cblk = f.n_cblk; a.quad = f.quad;
     a.bf16 = desc->io_dtype == SSM_BF16;
     a.softplus = softplus_flag != 0;
+    a.zoh = (desc->flags & SSM_FLAG_ZOH) != 0;
     a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
     a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.h0 = initial_state;
     a.cu = cu_seqlens;

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
         A2[k] = (lane_ok && n < a.N) ? v * kLog2e : 0.0f;
     }
     float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (!EXT && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
+    const bool packed = EXT && a.cu != nullptr;
+    if (!packed && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
     float dts = 0.0f;
     const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
     // the next tile's raw values, loaded one tile ahead (named registers)
@@ -185,12 +186,15 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 }
 
 // ------------------------------------------------------------ pass 3
-// Grid (n_cblk * batch, J).  EXT: packed sequences (the state starts over at
-// every sequence start, the gradient at every sequence end).
+// Grid (n_cblk * batch, J).  EXT: the instance that handles packed sequences
+// (the state starts over at every sequence start, the gradient at every
+// sequence end) and, with ZOH, the zero-order-hold input term: its factor
+// c = (e^{dt A} - 1) / A = phi(dt A) dt scales B u, enters dB and du, adds
+// dh.B u e^{dt A} to ddt (dc/ddt = e^{dt A}) and dh.B u dt^2 psi(dt A) to dA.
 #ifndef SSM_BWD_WAVES_PER_SIMD
 #define SSM_BWD_WAVES_PER_SIMD 1
 #endif
-template <class IO, bool EXT>
+template <class IO, bool EXT, bool ZOH>
 __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
     // per (channel, token) values of the tile: [c][t]
@@ -276,13 +280,14 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     // starts passes nothing on from its right); the row's own dlast enters
     // at its last token, in chunk J-1
     float G[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (!EXT && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
+    const bool packed = EXT && a.cu != nullptr;
+    if (!packed && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
     for (int64_t i = a.J - 1; i > j; --i) {
         const float sdt = g.bdtsum[cd0 + i];
         const float4 v = *reinterpret_cast<const float4 *>(g.gend + (cd0 + i) * 16 + 4 * q);
         const float ge[4] = {v.x, v.y, v.z, v.w};
         bool kept = true;
-        if (EXT) {
+        if (packed) {
             const int64_t tb = i * a.K, te = tb + a.K < L ? tb + a.K : L;
             const SeqPos sp = seq_pos<EXT>(a, b, tb);
             kept = !sp.reset && sp.end >= te;
@@ -338,7 +343,11 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             if (EXT && ((fs >> t) & 1u))   // a sequence starts: its start state
                 load_start_state<4>(a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, h);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) h[k] = __builtin_fmaf(exp2_hw(dt * A2[k]), h[k], w * bv[k]);
+            for (int k = 0; k < 4; ++k) {
+                const float e = exp2_hw(dt * A2[k]);
+                const float wb = ZOH ? zoh_phi(dt * An[k], e) * (w * bv[k]) : w * bv[k];
+                h[k] = __builtin_fmaf(e, h[k], wb);
+            }
         }
         __syncthreads();
     }
@@ -433,7 +442,9 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
-                hh[t][k] = __builtin_fmaf(exp2_hw(dt * A2[k]), prev, w * bv[k]);
+                const float e = exp2_hw(dt * A2[k]);
+                const float wb = ZOH ? zoh_phi(dt * An[k], e) * (w * bv[k]) : w * bv[k];
+                hh[t][k] = __builtin_fmaf(e, prev, wb);
                 p = __builtin_fmaf(cv[k], hh[t][k], p);
             }
             part[t] = p;
@@ -471,17 +482,30 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const bool st = EXT && ((smask >> t) & 1u);
             const int64_t s_st = st ? seq_of(a, t0 + t) : 0;
             if (st) load_start_state<4>(a, s_st, dcl, lane_ok, 4 * q, h0v);
+            const float uc = ZOH ? s_u[c * kT + t] : 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float dh = __builtin_fmaf(dO, cv[k], G[k]);
                 const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
                 gc[k] = dO * hh[t][k];
-                gb[k] = w * dh;
-                dw = __builtin_fmaf(dh, bv[k], dw);
                 const float da = dh * prev;
-                dd = __builtin_fmaf(da * An[k], at, dd);
-                dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
+                if (ZOH) {
+                    const float x = dt * An[k];
+                    const float phi = zoh_phi(x, at);
+                    const float dhb = dh * bv[k];
+                    gb[k] = (w * phi) * dh;
+                    dw = __builtin_fmaf(dhb, phi, dw);               // du: dh.B c / dt
+                    dd = __builtin_fmaf(da * An[k], at, dd);
+                    dd = __builtin_fmaf(dhb * uc, at, dd);           // dc/ddt = e^{dt A}
+                    dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
+                    dA_acc[k] = __builtin_fmaf(dhb * uc, (dt * dt) * zoh_psi(x, at), dA_acc[k]);
+                } else {
+                    gb[k] = w * dh;
+                    dw = __builtin_fmaf(dh, bv[k], dw);
+                    dd = __builtin_fmaf(da * An[k], at, dd);
+                    dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
+                }
                 G[k] = dh * at;
             }
             if (st) {
@@ -514,7 +538,8 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const float dt = s_dt[o], uu = s_u[o], dO = s_do[o];
             const float Dv = ok ? Dv_d[e] : 0.0f;
             const float du = __builtin_fmaf(dO, Dv, dw * dt);
-            const float ddl = __builtin_fmaf(dw, uu, dd) * s_sig[o];
+            // (with ZOH the u term of ddt is already in dd)
+            const float ddl = (ZOH ? dd : __builtin_fmaf(dw, uu, dd)) * s_sig[o];
             if (ok) {
                 const size_t off = (static_cast<size_t>(b) * a.D + dch) * L + tok;
                 g.du[off] = du;
@@ -570,7 +595,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     if (!lane_ok) return;
     *reinterpret_cast<float4 *>(g.dAp + cd * 16 + 4 * q) =
         make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
-    if (!EXT && j == 0 && g.dh0) {
+    if (!packed && j == 0 && g.dh0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (4 * q + k < a.N) g.dh0[(static_cast<size_t>(b) * a.D + d) * a.N + 4 * q + k] = G[k];
@@ -645,7 +670,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
 }
 
 // ------------------------------------------------------------ launch
-template <class IO, bool EXT>
+// Instances: lean; EXT (packed sequences); EXT + ZOH (either, with the
+// zero-order-hold input term).
+template <class IO, bool EXT, bool ZOH>
 static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
     if (a.J > 1) {
@@ -654,17 +681,23 @@ static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t
         hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT>), dim3(gx, static_cast<unsigned>(a.J - 1)),
                            dim3(64), 0, s, a, g);
     }
-    hipLaunchKernelGGL((bwd_kernel<IO, EXT>), dim3(gx, static_cast<unsigned>(a.J)), dim3(64), 0, s,
-                       a, g);
+    hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH>), dim3(gx, static_cast<unsigned>(a.J)), dim3(64),
+                       0, s, a, g);
     const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
                        dim3(256), 0, s, a, g);
     return hipGetLastError();
 }
 
+template <class IO>
+static hipError_t launch_bwd_sel(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
+    if (a.zoh) return launch_bwd_io<IO, true, true>(a, g, s);
+    if (a.cu) return launch_bwd_io<IO, true, false>(a, g, s);
+    return launch_bwd_io<IO, false, false>(a, g, s);
+}
+
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
-    if (a.cu) return a.bf16 ? launch_bwd_io<BF16, true>(a, g, s) : launch_bwd_io<F32, true>(a, g, s);
-    return a.bf16 ? launch_bwd_io<BF16, false>(a, g, s) : launch_bwd_io<F32, false>(a, g, s);
+    return a.bf16 ? launch_bwd_sel<BF16>(a, g, s) : launch_bwd_sel<F32>(a, g, s);
 }
 
 }  // namespace ssm

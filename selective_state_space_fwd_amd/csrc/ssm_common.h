@@ -80,4 +80,22 @@ __device__ __forceinline__ float zoh_phi(float x, float e) {
     return fabsf(x) < 0.5f ? p : q;
 }
 
+// psi(x) = (x e^x - e^x + 1) / x^2, x = dt A, e = e^x: the derivative of the
+// zero-order-hold factor (e^{dt A} - 1) / A with respect to A is dt^2 psi(dt A)
+// (backward pass).  Its power series is sum_{m >= 2} (m - 1) x^(m-2) / m!;
+// below |x| = 1/2 the closed form loses digits to cancellation, so there it is
+// that series to x^7 (truncation below 1e-8 relative); above, the closed form.
+__device__ __forceinline__ float zoh_psi(float x, float e) {
+    float p = 1.0f / 45360.0f;
+    p = __builtin_fmaf(p, x, 1.0f / 5760.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 840.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 144.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 30.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 8.0f);
+    p = __builtin_fmaf(p, x, 1.0f / 3.0f);
+    p = __builtin_fmaf(p, x, 0.5f);
+    const float q = __builtin_fmaf(x, e, -(e - 1.0f)) * rcp_hw(x * x);
+    return fabsf(x) < 0.5f ? p : q;
+}
+
 }  // namespace ssm

@@ -1372,7 +1372,12 @@ static hipError_t launch_agg_io(const ScanArgs &a, hipStream_t s) {
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.B) && al(a.C);
     const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-    if (a.cu) {   // packed sequences: the extended instance
+    if (a.zoh) {   // zero-order hold: the extended ZOH instance
+        if (vec)
+            hipLaunchKernelGGL((quad_kernel<IO, false, true, true, true>), agrid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL((quad_kernel<IO, false, false, true, true>), agrid, dim3(64), 0, s, a);
+    } else if (a.cu) {   // packed sequences: the extended instance
         if (vec)
             hipLaunchKernelGGL((quad_kernel<IO, false, true, true, false>), agrid, dim3(64), 0, s, a);
         else

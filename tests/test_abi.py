@@ -222,13 +222,15 @@ def test_flags_validation(lib):
 
 
 def test_backward_plan_and_validation(lib):
-    """ssm_scan_bwd: d_state <= 16 and Euler only; workspace sized for at most
-    32 chunks; null and misaligned arguments rejected before any launch."""
-    for kw in (dict(d_state=17), dict(flags=ssm.SSM_FLAG_ZOH)):
-        d = desc(**kw)
-        assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) == 0
-        assert lib.ssm_scan_bwd(ctypes.byref(d), *([4096] * 5), None, None, None, 1, None, 4096,
-                                None, *([4096] * 5), None, None, None, None, None) == 3
+    """ssm_scan_bwd: d_state <= 16 only (Euler or ZOH, same workspace);
+    workspace sized for at most 32 chunks; null and misaligned arguments
+    rejected before any launch."""
+    d = desc(d_state=17)
+    assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.ssm_scan_bwd(ctypes.byref(d), *([4096] * 5), None, None, None, 1, None, 4096,
+                            None, *([4096] * 5), None, None, None, None, None) == 3
+    assert (lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(flags=ssm.SSM_FLAG_ZOH))) ==
+            lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc())) > 0)
     d = desc(chunk_size=16)              # 128 chunks asked: the backward uses at most 32
     need16 = lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
     d64 = desc(chunk_size=64)            # exactly 32 chunks

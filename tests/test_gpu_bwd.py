@@ -35,7 +35,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_case(dev, batch, d_inner, N, L, io, gate, with_state, K, seed):
+def run_case(dev, batch, d_inner, N, L, io, gate, with_state, K, seed, zoh=False):
     import torch
     inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=seed)
     rng = np.random.default_rng(seed + 100)
@@ -47,13 +47,13 @@ def run_case(dev, batch, d_inner, N, L, io, gate, with_state, K, seed):
     g = lambda a: None if a is None else torch.from_numpy(a).to(dev)
     out = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], to_device(dy, dev),
                            t["D"], t["z"], t["delta_bias"], softplus=True, initial_state=g(h0),
-                           dlast=g(dlast), chunk_size=K)
+                           dlast=g(dlast), chunk_size=K, zoh=zoh)
     torch.cuda.synchronize()
     f = decoded(inp)
     ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], ssm_inputs.to_f64(dy, io),
                           f["D"], f["z"], f["delta_bias"], softplus=True,
                           initial_state=None if h0 is None else h0.astype(np.float64),
-                          dlast=None if dlast is None else dlast.astype(np.float64))
+                          dlast=None if dlast is None else dlast.astype(np.float64), zoh=zoh)
     errs = {}
     for k in NAMES:
         if out[k] is None or ref.get(k) is None:
@@ -133,7 +133,7 @@ LENS = {
 }
 
 
-def run_packed_case(dev, lens, N, io, K, with_state, seed, gate=True):
+def run_packed_case(dev, lens, N, io, K, with_state, seed, gate=True, zoh=False):
     import torch
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     L, n, d_inner = int(cu[-1]), len(lens), 40
@@ -147,14 +147,15 @@ def run_packed_case(dev, lens, N, io, K, with_state, seed, gate=True):
     g = lambda a: None if a is None else torch.from_numpy(a).to(dev)
     out = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], to_device(dy, dev),
                            t["D"], t["z"], t["delta_bias"], softplus=True, initial_state=g(h0),
-                           dlast=g(dlast), chunk_size=K, cu_seqlens=g(cu))
+                           dlast=g(dlast), chunk_size=K, cu_seqlens=g(cu), zoh=zoh)
     torch.cuda.synchronize()
     f = decoded(inp)
     ref = oracle.scan_bwd_varlen(f["u"], f["delta"], f["A"], f["B"], f["C"], cu,
                                  ssm_inputs.to_f64(dy, io), f["D"], f["z"], f["delta_bias"],
                                  softplus=True,
                                  initial_state=None if h0 is None else h0.astype(np.float64),
-                                 dlast=None if dlast is None else dlast.astype(np.float64))
+                                 dlast=None if dlast is None else dlast.astype(np.float64),
+                                 zoh=zoh)
     errs = {}
     for k in NAMES:
         if out[k] is None or ref.get(k) is None or (k == "dh0" and h0 is None):
@@ -220,3 +221,55 @@ def test_backward_single_sequence_packing_equals_unpacked(dev):
     torch.cuda.synchronize()
     for k in NAMES:
         assert floored_err(to_f64(b[k]), to_f64(a[k])) <= 1e-6, k
+
+
+# ---------------------------------------------------------------- zero-order hold
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,K", [((2, 40, 16, 300), 0), ((2, 40, 16, 300), 16),
+                                     ((1, 33, 5, 77), 32), ((3, 16, 1, 9), 0),
+                                     ((2, 24, 16, 513), 64)])
+@pytest.mark.parametrize("gate,with_state", [(True, True), (False, False)])
+def test_backward_zoh(dev, io, shape, K, gate, with_state):
+    """SSM_FLAG_ZOH: the input factor (e^{dt A} - 1) / A and its derivatives
+    (e^{dt A} for ddt, dt^2 psi(dt A) for dA) in every gradient."""
+    say(f"bwd zoh io={io} shape={shape} K={K} gate={gate} state={with_state}")
+    _, errs = run_case(dev, *shape, io, gate, with_state, K, seed=sum(shape) + K + 1, zoh=True)
+    for k, e in errs.items():
+        assert e <= GRAD_TOL, (k, e)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [0, 16])
+def test_backward_zoh_packed(dev, io, K):
+    say(f"bwd zoh packed io={io} K={K}")
+    _, _, errs = run_packed_case(dev, LENS["mixed"], 16, io, K, True, seed=41 + K, zoh=True)
+    for k, e in errs.items():
+        assert e <= GRAD_TOL, (k, e)
+
+
+def test_backward_zoh_random_a_small_and_large_steps(dev):
+    """A drawn at random (not -(n+1)), with rows whose dt*A lies around the
+    series/closed-form switch of phi and psi (|dt A| near 1/2) and far beyond."""
+    import torch
+    inp = ssm_inputs.make_scan_inputs(2, 40, 16, 200, io_dtype="f32", gate=True, seed=51,
+                                      random_a=True)
+    rng = np.random.default_rng(52)
+    A = inp["A"].copy()
+    A[:8] *= 20.0                      # large |dt A|
+    A[8:16] *= 0.01                    # tiny |dt A|
+    inp["A"] = A
+    t = {k: to_device(inp.get(k), dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                  "delta_bias")}
+    dy = rng.standard_normal((2, 40, 200)).astype(np.float32)
+    out = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                           torch.from_numpy(dy).to(dev), t["D"], t["z"], t["delta_bias"],
+                           softplus=True, chunk_size=32, zoh=True)
+    torch.cuda.synchronize()
+    f = decoded(inp)
+    ref = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["B"], f["C"], dy.astype(np.float64),
+                          f["D"], f["z"], f["delta_bias"], softplus=True, zoh=True)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        e = floored_err(to_f64(out[k]), ref[k])
+        say(f"  {k}={e:.2e}")
+        assert e <= GRAD_TOL, (k, e)

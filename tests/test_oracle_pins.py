@@ -544,18 +544,22 @@ def test_zoh_chunked_and_decode_agree():
 
 # ------------------------------------------------------------ backward
 
-def _loss(u, dt, A, B, C, D, z, bias, h0, dy, dlast):
-    y, last = oracle.scan_fwd(u, dt, A, B, C, D, z, bias, softplus=True, initial_state=h0)
+def _loss(u, dt, A, B, C, D, z, bias, h0, dy, dlast, zoh=False):
+    y, last = oracle.scan_fwd(u, dt, A, B, C, D, z, bias, softplus=True, initial_state=h0,
+                              zoh=zoh)
     return float(np.sum(dy * y) + np.sum(dlast * last))
 
 
-@pytest.mark.parametrize("gate", [False, True])
-def test_backward_against_finite_differences(gate):
+@pytest.mark.parametrize("gate,zoh", [(False, False), (True, False), (True, True),
+                                      (False, True)])
+def test_backward_against_finite_differences(gate, zoh):
     """Every gradient of sum(dy*y) + sum(dlast*last_state) from the hand-written
     reverse walk equals the central difference of the forward oracle's loss
     (step 1e-6, fp64) on a tiny problem: a dropped term or a wrong index in
-    any one gradient fails."""
-    rng = np.random.default_rng(7 + gate)
+    any one gradient fails.  With the zero-order-hold input term too, where
+    the steps dt*A fall on both sides of 1 in magnitude (the two branches of
+    the factor's A-derivative)."""
+    rng = np.random.default_rng(7 + gate + 2 * zoh)
     b, d, N, L = 2, 3, 4, 9
     u = rng.standard_normal((b, d, L))
     raw = 0.5 * rng.standard_normal((b, d, L))
@@ -568,8 +572,11 @@ def test_backward_against_finite_differences(gate):
     h0 = rng.standard_normal((b, d, N))
     dy = rng.standard_normal((b, d, L))
     dlast = rng.standard_normal((b, d, N))
+    if zoh:
+        A[0, 0] = -8.0          # dt*A beyond -1 for this state; the others within
+        A[1, 1] = 0.0           # the A = 0 limit: the factor is dt
     g = oracle.scan_bwd(u, raw, A, B, C, dy, D, z, bias, softplus=True, initial_state=h0,
-                        dlast=dlast)
+                        dlast=dlast, zoh=zoh)
     args = dict(u=u, dt=raw, A=A, B=B, C=C, D=D, z=z, bias=bias, h0=h0)
     names = {"u": "du", "dt": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
              "bias": "ddelta_bias", "h0": "dh0"}
@@ -584,7 +591,8 @@ def test_backward_against_finite_differences(gate):
             minus = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in args.items()}
             plus[key][idx] += eps
             minus[key][idx] -= eps
-            num[idx] = (_loss(**plus, dy=dy, dlast=dlast) - _loss(**minus, dy=dy, dlast=dlast)) / (2 * eps)
+            num[idx] = (_loss(**plus, dy=dy, dlast=dlast, zoh=zoh) -
+                        _loss(**minus, dy=dy, dlast=dlast, zoh=zoh)) / (2 * eps)
         assert rel(g[gname], num) < 1e-7, (gname, rel(g[gname], num))
 
 

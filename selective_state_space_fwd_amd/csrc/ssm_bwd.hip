@@ -85,12 +85,21 @@ __device__ __forceinline__ uint32_t tile_marks(const ScanArgs &a, int64_t t0, in
 // last-state gradient enters at the last token of every sequence, and
 // nothing leaves a sequence's first token (EXT: packed sequences; otherwise
 // the row's last token is in chunk J - 1).
-template <class IO, bool EXT>
+// Tiles as the forward quad kernel's: 16 channels x T tokens (T = 64 bytes of
+// a row), every lane one 16-byte piece of delta, dy, z and C per tile, loaded
+// one tile ahead; the walk runs backwards 4 tokens at a time:
+// G = (G + dO_t C_t) exp(dt_t A), dO_t = dy_t silu(z_t).
+template <class IO, bool EXT, bool VEC>
 __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
-    __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
-    __shared__ __attribute__((aligned(16))) float s_do[kQC * kT];
-    __shared__ __attribute__((aligned(16))) float s_C[kT * 16];
+    using S = Seg<IO>;
+    using V = typename S::V;
+    constexpr int VW = S::VW;
+    constexpr int T = 4 * VW;
+    constexpr int TP = T + 4;
+    __shared__ __attribute__((aligned(16))) float s_dt[kQC * TP];
+    __shared__ __attribute__((aligned(16))) float s_do[kQC * TP];
+    __shared__ __attribute__((aligned(16))) float s_C[16 * TP];
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
     const IT *__restrict__ z = static_cast<const IT *>(a.z);
     const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
@@ -108,7 +117,9 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
     const bool gate = a.z != nullptr;
 
-    const int r = lane >> 2, sc = (lane & 3) * kEPL;
+    // this lane's tile pieces: row r (channel d0 + r, and state r of C),
+    // tokens [sc, sc + VW) of the tile
+    const int r = lane >> 2, sc = (lane & 3) * VW;
     const int64_t dr = d0 + r;
     const bool row_ok = dr < a.D;
     const int64_t drc = row_ok ? dr : a.D - 1;
@@ -129,53 +140,91 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
     const bool packed = EXT && a.cu != nullptr;
     if (!packed && j == a.J - 1) load_state_row<4>(g.dlast, a, b, dcl, lane_ok, 4 * q, G);
     float dts = 0.0f;
-    const int64_t ntile = (t_end - t_begin + kT - 1) / kT;
-    // the next tile's raw values, loaded one tile ahead (named registers)
-    float px0 = 0.f, px1 = 0.f, pz0 = 0.f, pz1 = 0.f, py0 = 0.f, py1 = 0.f, pc0 = 0.f, pc1 = 0.f;
-    auto prefetch = [&](int64_t t0) {
+
+    // prefetched pieces (named vectors), tokens past the chunk clamped into it
+    V vd{}, vy{}, vz{}, vc{};
+    auto load_elems = [&](const IT *p, size_t base, int64_t t) {
+        float e[VW];
+#pragma unroll
+        for (int i = 0; i < VW; ++i) e[i] = IO::load(p, base + (t + i < t_end ? t + i : t_end - 1));
+        return S::pack(e);
+    };
+    auto load_tile = [&](int64_t t0) {
         const int64_t t = t0 + sc;
-        px0 = ld_clamped<IO>(dl, rbase, t, t_end);
-        if (gate) pz0 = ld_clamped<IO>(z, rbase, t, t_end);
-        py0 = ld_clamped<IO>(dy, rbase, t, t_end);
-        pc0 = ld_clamped<IO>(Cm, sbase, t, t_end);
-        if (kEPL > 1) {
-            px1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
-            if (gate) pz1 = ld_clamped<IO>(z, rbase, t + 1, t_end);
-            py1 = ld_clamped<IO>(dy, rbase, t + 1, t_end);
-            pc1 = ld_clamped<IO>(Cm, sbase, t + 1, t_end);
+        if (VEC) {
+            const int64_t tc = t < t_end ? t : t_end - VW;   // chunk lengths are multiples of VW
+            vd = *reinterpret_cast<const V *>(dl + rbase + tc);
+            vy = *reinterpret_cast<const V *>(dy + rbase + tc);
+            if (gate) vz = *reinterpret_cast<const V *>(z + rbase + tc);
+            vc = *reinterpret_cast<const V *>(Cm + sbase + tc);
+        } else {
+            vd = load_elems(dl, rbase, t);
+            vy = load_elems(dy, rbase, t);
+            if (gate) vz = load_elems(z, rbase, t);
+            vc = load_elems(Cm, sbase, t);
         }
     };
-    prefetch(t_begin + (ntile - 1) * kT);
+    const int64_t ntile = (t_end - t_begin + T - 1) / T;
+    load_tile(t_begin + (ntile - 1) * T);
     for (int64_t ti = ntile - 1; ti >= 0; --ti) {
-        const int64_t t0 = t_begin + ti * kT;
-        const float rx[2] = {px0, px1}, rz[2] = {pz0, pz1}, ry[2] = {py0, py1}, rc[2] = {pc0, pc1};
+        const int64_t t0 = t_begin + ti * T;
+        {
+            float xd[VW], xy[VW], xz[VW], xc[VW];
+            S::unpack(vd, xd);
+            S::unpack(vy, xy);
+            if (gate) S::unpack(vz, xz);
+            S::unpack(vc, xc);
+            const int o = r * TP + sc;
+            float odt[VW], odo[VW];
 #pragma unroll
-        for (int i = 0; i < kEPL; ++i) {
-            const int64_t t = t0 + sc + i;
-            const bool ok = row_ok && t < t_end;
-            const float x = rx[i] + rbias;
-            const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
-            const float gg = gate ? silu_f32(rz[i]) : 1.0f;
-            const float dO = ok ? ry[i] * gg : 0.0f;
-            s_dt[r * kT + sc + i] = dt;
-            s_do[r * kT + sc + i] = dO;
-            s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
+            for (int i = 0; i < VW; ++i) {
+                const bool ok = row_ok && t0 + sc + i < t_end;
+                const float x = xd[i] + rbias;
+                odt[i] = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
+                odo[i] = ok ? xy[i] * (gate ? silu_f32(xz[i]) : 1.0f) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < VW; i += 4) {
+                *reinterpret_cast<float4 *>(&s_dt[o + i]) = make_float4(odt[i], odt[i + 1], odt[i + 2], odt[i + 3]);
+                *reinterpret_cast<float4 *>(&s_do[o + i]) = make_float4(odo[i], odo[i + 1], odo[i + 2], odo[i + 3]);
+                *reinterpret_cast<float4 *>(&s_C[o + i]) =
+                    st_ok ? make_float4(xc[i], xc[i + 1], xc[i + 2], xc[i + 3])
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
-        if (ti > 0) prefetch(t0 - kT);
-        uint32_t lmask;
-        const uint32_t smask = tile_marks<EXT>(a, t0, t_end, &lmask);
+        if (ti > 0) load_tile(t0 - T);
+        uint32_t lmask = 0, smask = 0;
+        if (packed) {
+            const int64_t n = t_end - t0 < T ? t_end - t0 : T;
+            const uint32_t valid = n >= 32 ? 0xffffffffu : (1u << n) - 1u;
+            smask = seq_marks(a, t0, T, &lmask) & valid;
+            lmask &= valid;
+        }
         __syncthreads();
+        const int rowc = c * TP;
 #pragma unroll
-        for (int t = kT - 1; t >= 0; --t) {
-            const float dt = s_dt[c * kT + t], dO = s_do[c * kT + t];
-            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
-            const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
-            if (EXT && ((lmask >> t) & 1u))   // a sequence ends here: its dlast
-                load_state_row<4>(g.dlast, a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, G);
+        for (int c4 = T - 4; c4 >= 0; c4 -= 4) {
+            const float4 dt4 = *reinterpret_cast<const float4 *>(&s_dt[rowc + c4]);
+            const float4 do4 = *reinterpret_cast<const float4 *>(&s_do[rowc + c4]);
+            float4 Cq[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) G[k] = __builtin_fmaf(dO, cv[k], G[k]) * exp2_hw(dt * A2[k]);
-            if (EXT && ((smask >> t) & 1u)) G[0] = G[1] = G[2] = G[3] = 0.0f;   // starts here
-            dts += dt;
+            for (int k = 0; k < 4; ++k)
+                Cq[k] = *reinterpret_cast<const float4 *>(&s_C[(4 * q + k) * TP + c4]);
+            const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+            const float dov[4] = {do4.x, do4.y, do4.z, do4.w};
+#pragma unroll
+            for (int tt = 3; tt >= 0; --tt) {
+                const int t = c4 + tt;
+                if (EXT && ((lmask >> t) & 1u))   // a sequence ends here: its dlast
+                    load_state_row<4>(g.dlast, a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, G);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float ck = tt == 0 ? Cq[k].x : tt == 1 ? Cq[k].y : tt == 2 ? Cq[k].z : Cq[k].w;
+                    G[k] = __builtin_fmaf(dov[tt], ck, G[k]) * exp2_hw(dtv[tt] * A2[k]);
+                }
+                if (EXT && ((smask >> t) & 1u)) G[0] = G[1] = G[2] = G[3] = 0.0f;   // starts here
+                dts += dtv[tt];
+            }
         }
         __syncthreads();
     }
@@ -678,8 +727,17 @@ static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t
     if (a.J > 1) {
         const hipError_t e = launch_scan_agg(a, s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT>), dim3(gx, static_cast<unsigned>(a.J - 1)),
-                           dim3(64), 0, s, a, g);
+        // 16-byte pieces of delta, dy, z and C need whole pieces per row and
+        // aligned rows
+        constexpr int VW = Seg<IO>::VW;
+        auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+        const bool vec = a.L % VW == 0 && al(a.delta) && al(g.dy) && (!a.z || al(a.z)) &&
+                         al(a.C);
+        const dim3 ag(gx, static_cast<unsigned>(a.J - 1));
+        if (vec)
+            hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, true>), ag, dim3(64), 0, s, a, g);
+        else
+            hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, false>), ag, dim3(64), 0, s, a, g);
     }
     hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH>), dim3(gx, static_cast<unsigned>(a.J)), dim3(64),
                        0, s, a, g);

@@ -80,6 +80,40 @@ __device__ __forceinline__ float zoh_phi(float x, float e) {
     return fabsf(x) < 0.5f ? p : q;
 }
 
+template <class IO>
+struct Seg;   // one 16-byte piece of a row: VW consecutive tokens
+
+template <>
+struct Seg<F32> {
+    static constexpr int VW = 4;
+    using V = float4;
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[VW]) {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ V pack(const float (&o)[VW]) {
+        return make_float4(o[0], o[1], o[2], o[3]);
+    }
+};
+
+template <>
+struct Seg<BF16> {
+    static constexpr int VW = 8;
+    using V = uint4;
+    static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+    static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+    static __device__ __forceinline__ void unpack(const V &v, float (&o)[VW]) {
+        o[0] = lo(v.x); o[1] = hi(v.x); o[2] = lo(v.y); o[3] = hi(v.y);
+        o[4] = lo(v.z); o[5] = hi(v.z); o[6] = lo(v.w); o[7] = hi(v.w);
+    }
+    static __device__ __forceinline__ uint32_t pk(float a, float b) {
+        const __hip_bfloat162 h = __float22bfloat162_rn(make_float2(a, b));
+        return *reinterpret_cast<const uint32_t *>(&h);
+    }
+    static __device__ __forceinline__ V pack(const float (&o)[VW]) {
+        return make_uint4(pk(o[0], o[1]), pk(o[2], o[3]), pk(o[4], o[5]), pk(o[6], o[7]));
+    }
+};
+
 // psi(x) = (x e^x - e^x + 1) / x^2, x = dt A, e = e^x: the derivative of the
 // zero-order-hold factor (e^{dt A} - 1) / A with respect to A is dt^2 psi(dt A)
 // (backward pass).  Its power series is sum_{m >= 2} (m - 1) x^(m-2) / m!;

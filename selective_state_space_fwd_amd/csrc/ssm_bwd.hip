@@ -260,9 +260,10 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     // row partials of dh.B and of sum_n dh h_prev A a: [t][q][c]
     __shared__ __attribute__((aligned(16))) float s_rw[kT * kRT];
     __shared__ __attribute__((aligned(16))) float s_rd[kT * kRT];
-    // per-channel contributions to dB and dC: [t][c][n]
-    __shared__ __attribute__((aligned(16))) float s_gB[kT * kGT];
-    __shared__ __attribute__((aligned(16))) float s_gC[kT * kGT];
+    // per-channel contributions to dB, then to dC: [t][c][n] (one buffer for
+    // both keeps a wavefront's LDS under 20 KB, so that a CU's 160 KB holds
+    // two wavefronts per SIMD)
+    __shared__ __attribute__((aligned(16))) float s_g[kT * kGT];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -479,6 +480,10 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
         float part[kT];
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
+            // one token at a time: without this fence the scheduler hoists
+            // all kT tokens' LDS reads, which costs the registers of a
+            // second wavefront per SIMD (measured: 11-17% slower)
+            __builtin_amdgcn_sched_barrier(0);
             const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
@@ -518,12 +523,13 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
         // a sequence's last token; at its first token it leaves as dh0)
 #pragma unroll
         for (int t = kT - 1; t >= 0; --t) {
+            __builtin_amdgcn_sched_barrier(0);   // as in (b)
             const float dt = s_dt[c * kT + t], w = s_w[c * kT + t], dO = s_do[c * kT + t];
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
-            float gb[4], gc[4];
+            float gb[4];
             float dw = 0.0f, dd = 0.0f;
             if (EXT && ((lmask >> t) & 1u))
                 load_state_row<4>(g.dlast, a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, G);
@@ -537,7 +543,6 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float dh = __builtin_fmaf(dO, cv[k], G[k]);
                 const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
-                gc[k] = dO * hh[t][k];
                 const float da = dh * prev;
                 if (ZOH) {
                     const float x = dt * An[k];
@@ -561,8 +566,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 store_state_row<4>(g.dh0, a, s_st, d, lane_ok, 4 * q, G);
                 G[0] = G[1] = G[2] = G[3] = 0.0f;
             }
-            *reinterpret_cast<float4 *>(&s_gB[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
-            *reinterpret_cast<float4 *>(&s_gC[t * kGT + c * kGC + 4 * q]) = make_float4(gc[0], gc[1], gc[2], gc[3]);
+            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
             s_rw[t * kRT + q * kQC + c] = dw;
             s_rd[t * kRT + q * kQC + c] = dd;
         }
@@ -598,26 +602,36 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 db_acc[e] += ddl;
             }
         }
-        // (e) dB, dC: sum over the 16 channels; job = lane (2 x 4 x kT jobs):
-        // tensor job / (4 kT), states 4 ((job / kT) % 4) .. +3, token job % kT
-        if (lane < 8 * kT) {
-            const int which = lane / (4 * kT);
-            const int n4 = (lane / kT) & 3;
-            const int t = lane % kT;
-            const float *src = which ? s_gC : s_gB;
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        // (e) dB, then dC (one LDS buffer, two rounds): sum over the 16
+        // channels; job = lane (4 x kT jobs): states 4 ((job / kT) % 4) .. +3,
+        // token job % kT
+        auto channel_sums = [&](float *dstbase) {
+            if (lane < 4 * kT) {
+                const int n4 = (lane / kT) & 3;
+                const int t = lane % kT;
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int ch = 0; ch < kQC; ++ch) {
-                const float4 v = *reinterpret_cast<const float4 *>(&src[t * kGT + ch * kGC + 4 * n4]);
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+                for (int ch = 0; ch < kQC; ++ch) {
+                    const float4 v = *reinterpret_cast<const float4 *>(&s_g[t * kGT + ch * kGC + 4 * n4]);
+                    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+                }
+                const int64_t tok = t0 + t;
+                if (tok < t_end) {
+                    float *dst = dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
+                    dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
+                }
             }
-            const int64_t tok = t0 + t;
-            if (tok < t_end) {
-                float *dst = (which ? g.dCp : g.dBp) +
-                             ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
-                dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
-            }
+        };
+        channel_sums(g.dBp);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const float dO = s_do[c * kT + t];
+            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) =
+                make_float4(dO * hh[t][0], dO * hh[t][1], dO * hh[t][2], dO * hh[t][3]);
         }
+        __syncthreads();
+        channel_sums(g.dCp);
         __syncthreads();
     }
 

@@ -250,7 +250,14 @@ def bench_decode(args, torch, ssm, dev):
 def bench_backward(args, torch, ssm, dev):
     """The backward pass alone on the workload: every gradient of
     sum(dy * y) + sum(dlast * last_state).  Algorithmic bytes: the forward
-    inputs read once, dy read, and du, ddelta, dz (fp32) and dB, dC written."""
+    inputs read once, dy read, and du, ddelta, dz (fp32) and dB, dC written.
+    With --ckpt the backward reads the checkpoints that the forward pass of
+    the same inputs wrote (one forward with checkpoints, outside the timed
+    region, as a training step's forward would have); their 16 floats per
+    8 tokens per channel count as read bytes.  The algorithmic work is the
+    same either way: one recompute of the recurrence (from the checkpoints,
+    the tiles' recompute is that one; without them the forward sweep that
+    writes them comes on top and is not counted)."""
     cfg = dict(ssm_inputs.CONFIGS[args.config])
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
     io, gate = cfg["io_dtype"], cfg["gate"]
@@ -265,11 +272,16 @@ def bench_backward(args, torch, ssm, dev):
     lib = ssm.load_library()
     ws = torch.empty(max(1, int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc)))),
                      dtype=torch.uint8, device=dev)
+    ck = None
+    if args.ckpt:
+        ck = torch.empty(ssm.ckpt_shape(batch, d_inner, L), dtype=torch.float32, device=dev)
+        ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                         t["delta_bias"], softplus=True, ckpt=ck)
 
     def step():
         ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
                          t["delta_bias"], softplus=True, dlast=dlast, chunk_size=args.chunk,
-                         workspace=ws)
+                         workspace=ws, ckpt=ck)
 
     for _ in range(args.warmup):
         step()
@@ -285,6 +297,8 @@ def bench_backward(args, torch, ssm, dev):
     chtok = batch * d_inner * L
     nbytes = (chtok * ((4 if gate else 3) * e + (3 if gate else 2) * 4) +
               2 * batch * N * L * (e + 4) + d_inner * (N + 2) * 4)
+    if ck is not None:
+        nbytes += ck.numel() * 4
     slots = chtok * (N * BWD_SLOTS_PER_UPDATE + BWD_SLOTS_PER_CHTOK)
     tflops = 2.0 * slots / (ms * 1e-3) / 1e12
     return {
@@ -294,9 +308,10 @@ def bench_backward(args, torch, ssm, dev):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{args.config}: backward of the scan, batch={batch} "
                                f"d_inner={d_inner} N={N} L={L} {io} I/O"
-                               f"{' + gate' if gate else ''}",
+                               f"{' + gate' if gate else ''}"
+                               f"{', forward checkpoints given' if ck is not None else ''}",
                    "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
-                   "io_dtype": io, "gate": gate},
+                   "io_dtype": io, "gate": gate, "checkpoints": ck is not None},
         "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
                      "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
@@ -328,6 +343,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time only the backward pass (ssm_scan_bwd) of the workload, with "
                          "upstream gradients of y and last_state")
+    ap.add_argument("--ckpt", action="store_true",
+                    help="with --backward: the backward reads the forward pass's checkpoints "
+                         "(the state entering every 8-token tile) instead of recomputing them")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")

@@ -262,7 +262,9 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
  * starts over at each sequence's last token from that sequence's row of
  * dlast, and stops at its first token, where it gives that sequence's row of
  * dh0.  initial_state, dlast and dh0 are (n_seqs, d_inner, N); an empty
- * sequence's dh0 is its dlast.  With cu_seqlens NULL this is ssm_scan_bwd.
+ * sequence's dh0 is its dlast.  ckpt: the checkpoints written by
+ * ssm_scan_fwd_ckpt for the same call, or NULL (the backward recomputes them
+ * in its workspace).  With cu_seqlens and ckpt NULL this is ssm_scan_bwd.
  * Errors as ssm_scan_bwd, and SSM_ERR_BAD_SHAPE for packing with batch != 1
  * or n_seqs < 1.  A malformed offset table gives unspecified gradients but
  * no access out of bounds. */
@@ -270,9 +272,32 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
                            const float *A, const void *B, const void *C, const float *D,
                            const void *z, const float *delta_bias, int softplus_flag,
                            const float *initial_state, const int32_t *cu_seqlens, int64_t n_seqs,
-                           const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
-                           float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
-                           float *dh0, ssm_stream_t stream);
+                           const float *ckpt, const void *dy, const float *dlast, float *du,
+                           float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
+                           float *ddelta_bias, float *dh0, ssm_stream_t stream);
+
+/* The forward pass that also keeps what the backward pass would otherwise
+ * recompute (ufo.work article "Accelerating state-space models ...", §2.2:
+ * the forward keeps states at fine-grained boundaries, the backward
+ * recomputes the rest): as ssm_scan_fwd_ex, and in addition writes ckpt, the
+ * state entering every 8-token tile of every row,
+ *   ckpt           (batch, d_inner, ceil(L / 8), 16) float32, written; states
+ *                  n >= N of each 16 are zero; ssm_scan_ckpt_bytes(desc) bytes,
+ *                  16-byte aligned
+ * Given to ssm_scan_bwd_ex with the same descriptor (shapes, io_dtype, flags)
+ * and inputs, it spares the backward pass its forward recompute; with other
+ * inputs the gradients are unspecified.  d_state <= 16 only
+ * (SSM_ERR_UNSUPPORTED otherwise); ckpt NULL: SSM_ERR_NULL_ARG. */
+ssm_status ssm_scan_fwd_ckpt(const ssm_desc *desc, const void *u, const void *delta,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const void *z, const float *delta_bias, int softplus_flag,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int64_t n_seqs, void *y, float *last_state, float *ckpt,
+                             ssm_stream_t stream);
+
+/* Bytes of the checkpoint array of ssm_scan_fwd_ckpt for this descriptor
+ * (0 when invalid or d_state > 16).  Host-only. */
+size_t ssm_scan_ckpt_bytes(const ssm_desc *desc);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssm_status_string(int status);

@@ -18,7 +18,7 @@ import ctypes
 import os
 from pathlib import Path
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_state_update", "ssm_scan_workspace_bytes",
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ckpt_shape", "ssm_state_update", "ssm_scan_workspace_bytes",
            "ssm_scan_chunk_size", "ssm_status_string", "SsmError", "load_library",
            "LIB_PATH"]
 
@@ -87,7 +87,12 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_bwd.argtypes = [dp] + [vp] * 8 + [ctypes.c_int] + [vp] * 12 + [vp]
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_scan_bwd_ex.argtypes = ([dp] + [vp] * 8 + [ctypes.c_int] + [vp, vp, ctypes.c_int64] +
-                                    [vp] * 11 + [vp])
+                                    [vp] * 12 + [vp])
+    lib.ssm_scan_fwd_ckpt.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                      ctypes.c_int64, vp, vp, vp, vp]
+    lib.ssm_scan_fwd_ckpt.restype = ctypes.c_int
+    lib.ssm_scan_ckpt_bytes.argtypes = [dp]
+    lib.ssm_scan_ckpt_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_bwd_ex.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
@@ -173,7 +178,7 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  return_last_state=True, chunk_size=0, y=None, last_state=None,
                  workspace=None, profile_events=None, initial_state=None, cu_seqlens=None,
-                 zoh=False, independent_chunks=False):
+                 zoh=False, independent_chunks=False, ckpt=None):
     """Fused selective-scan forward pass on the GPU.
 
     u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
@@ -187,6 +192,9 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     zoh: zero-order-hold input term (exp(dt A) - 1) / A * B u instead of dt B u.
     independent_chunks: no chunk waits for the operators of the chunks before
     it; each computes them itself (same result bits, more work).
+    ckpt: optional float32 tensor of shape ckpt_shape(batch, d_inner, L)
+    (d_state <= 16): also filled with the state entering every 8-token tile,
+    for ssm_scan_bwd(ckpt=...).
     Returns (y, last_state); last_state is None unless requested.
     profile_events: optional pair of raw hipEvent_t handles recorded around
     the pass that writes y.
@@ -229,7 +237,13 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if profile_events is not None:
         desc.profile_begin, desc.profile_end = profile_events
-    if initial_state is None and cu_seqlens is None:
+    if ckpt is not None:
+        _expect(ckpt, "ckpt", ckpt_shape(batch, d_inner, L), torch.float32, dev)
+        st = lib.ssm_scan_fwd_ckpt(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                   int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
+                                   n_seqs, _ptr(y), _ptr(last_state), _ptr(ckpt), _stream(dev))
+    elif initial_state is None and cu_seqlens is None:
         st = lib.ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
                               _ptr(y), _ptr(last_state), _stream(dev))
@@ -311,16 +325,24 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
     return y, last_state, u_out
 
 
+def ckpt_shape(batch, d_inner, seqlen):
+    """Shape of the checkpoint tensor of ssm_scan_fwd(ckpt=...): the 16-float
+    state entering every 8-token tile of every (batch, channel) row."""
+    return (batch, d_inner, (seqlen + 7) // 8, 16)
+
+
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
                  initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None,
-                 zoh=False):
+                 zoh=False, ckpt=None):
     """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
     respect to all its inputs (d_state <= 16; zoh: the zero-order-hold input
     term, as in ssm_scan_fwd).  Returns a dict of
     float32 tensors: du, ddelta (of the raw delta), dA, dB, dC, dD (None
     without D), dz (None without z), ddelta_bias, dh0 (None without
     initial_state).  cu_seqlens: packed sequences as in ssm_scan_fwd; the
-    states (initial_state, dlast, dh0) then have one row per sequence."""
+    states (initial_state, dlast, dh0) then have one row per sequence.
+    ckpt: the checkpoints of the matching ssm_scan_fwd(ckpt=...) call, which
+    spare the backward its forward recompute."""
     torch = _torch()
     lib = load_library()
     batch, d_inner, L = u.shape
@@ -340,7 +362,8 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
     for t, name, shape in ((A, "A", (d_inner, N)), (D, "D", (d_inner,)),
                            (delta_bias, "delta_bias", (d_inner,)),
                            (initial_state, "initial_state", (rows, d_inner, N)),
-                           (dlast, "dlast", (rows, d_inner, N))):
+                           (dlast, "dlast", (rows, d_inner, N)),
+                           (ckpt, "ckpt", ckpt_shape(batch, d_inner, L))):
         _expect(t, name, shape, torch.float32, dev)
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     out = {"du": f32(batch, d_inner, L), "ddelta": f32(batch, d_inner, L), "dA": f32(d_inner, N),
@@ -358,7 +381,8 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib.ssm_scan_bwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                              _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                             _ptr(initial_state), _ptr(cu_seqlens), n_seqs, _ptr(dy), _ptr(dlast),
+                             _ptr(initial_state), _ptr(cu_seqlens), n_seqs, _ptr(ckpt), _ptr(dy),
+                             _ptr(dlast),
                              _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
                              _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
                              _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _stream(dev))

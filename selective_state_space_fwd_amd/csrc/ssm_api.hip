@@ -213,7 +213,7 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
                      const float *A, const void *B, const void *C, const float *D, const void *z,
                      const float *delta_bias, int softplus_flag, const float *initial_state,
                      const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
-                     ssm_stream_t stream) {
+                     float *ckpt, ssm_stream_t stream) {
     Plan p;
     ssm_status st = make_plan(desc, &p);
     if (st != SSM_OK) return st;
@@ -248,6 +248,8 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
         !aligned(y, esz) || !aligned(z, esz))
         return SSM_ERR_MISALIGNED;
+    if (ckpt && !p.quad) return SSM_ERR_UNSUPPORTED;
+    if (!aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
     if (p.bytes > 0) {
         if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
         if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
@@ -264,6 +266,8 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     a.h0 = initial_state; a.cu = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : desc->batch;
     a.conv_w = cv.width; a.conv_silu = cv.silu; a.conv_weight = cv.weight;
     a.conv_bias = cv.bias; a.conv_state = cv.state; a.u_out = cv.u_out;
+    a.ckpt = ckpt;
+    a.n_ck = (desc->seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile;
     if (p.J > 1) {
         a.hend = reinterpret_cast<float *>(ws + p.off_hend);
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
@@ -316,7 +320,7 @@ ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delt
                            const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
                            ssm_stream_t stream) {
     return scan_impl(desc, u, ConvSpec{}, delta, A, B, C, D, z, delta_bias, softplus_flag,
-                     initial_state, cu_seqlens, n_seqs, y, last_state, stream);
+                     initial_state, cu_seqlens, n_seqs, y, last_state, nullptr, stream);
 }
 
 ssm_status ssm_scan_fwd_conv(const ssm_desc *desc, const void *x, const float *conv_weight,
@@ -335,7 +339,26 @@ ssm_status ssm_scan_fwd_conv(const ssm_desc *desc, const void *x, const float *c
     cv.width = conv_width; cv.silu = conv_silu != 0; cv.weight = conv_weight;
     cv.bias = conv_bias; cv.state = conv_state; cv.u_out = u_out;
     return scan_impl(desc, x, cv, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state,
-                     cu_seqlens, n_seqs, y, last_state, stream);
+                     cu_seqlens, n_seqs, y, last_state, nullptr, stream);
+}
+
+ssm_status ssm_scan_fwd_ckpt(const ssm_desc *desc, const void *u, const void *delta,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const void *z, const float *delta_bias, int softplus_flag,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int64_t n_seqs, void *y, float *last_state, float *ckpt,
+                             ssm_stream_t stream) {
+    if (!ckpt) return SSM_ERR_NULL_ARG;
+    return scan_impl(desc, u, ConvSpec{}, delta, A, B, C, D, z, delta_bias, softplus_flag,
+                     initial_state, cu_seqlens, n_seqs, y, last_state, ckpt, stream);
+}
+
+size_t ssm_scan_ckpt_bytes(const ssm_desc *desc) {
+    Plan p;
+    if (make_plan(desc, &p) != SSM_OK || !p.quad) return 0;
+    const size_t tiles = static_cast<size_t>((desc->seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile);
+    return static_cast<size_t>(desc->batch) * static_cast<size_t>(desc->d_inner) * tiles * 16 *
+           sizeof(float);
 }
 
 ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,
@@ -380,16 +403,16 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
                            const float *A, const void *B, const void *C, const float *D,
                            const void *z, const float *delta_bias, int softplus_flag,
                            const float *initial_state, const int32_t *cu_seqlens, int64_t n_seqs,
-                           const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
-                           float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
-                           float *dh0, ssm_stream_t stream) {
+                           const float *ckpt, const void *dy, const float *dlast, float *du,
+                           float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
+                           float *ddelta_bias, float *dh0, ssm_stream_t stream) {
     BwdPlan p;
     ssm_status st = make_bwd_plan(desc, &p);
     if (st != SSM_OK) return st;
     if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
     const int64_t state_rows = cu_seqlens ? n_seqs : desc->batch;
     if (!dims_ok(state_rows, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
-    if (!aligned(cu_seqlens, 4)) return SSM_ERR_MISALIGNED;
+    if (!aligned(cu_seqlens, 4) || !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
     const int64_t rows = desc->batch * desc->d_inner;
     if (rows == 0 || desc->seqlen == 0) {
         // no tokens: every gradient of a token is empty; those of the
@@ -444,7 +467,9 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
         g.gend = reinterpret_cast<float *>(ws + p.off_gend);
         g.bdtsum = reinterpret_cast<float *>(ws + p.off_bdtsum);
     }
-    g.ckpt = reinterpret_cast<float *>(ws + p.off_ckpt);
+    // the forward pass's checkpoints (read only), or the workspace's
+    g.ckpt = ckpt ? const_cast<float *>(ckpt) : reinterpret_cast<float *>(ws + p.off_ckpt);
+    g.ckpt_given = ckpt != nullptr;
     g.dBp = reinterpret_cast<float *>(ws + p.off_dBp);
     g.dCp = reinterpret_cast<float *>(ws + p.off_dCp);
     g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
@@ -460,8 +485,8 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
                         float *dB, float *dC, float *dD, float *dz, float *ddelta_bias,
                         float *dh0, ssm_stream_t stream) {
     return ssm_scan_bwd_ex(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag,
-                           initial_state, nullptr, 0, dy, dlast, du, ddelta, dA, dB, dC, dD, dz,
-                           ddelta_bias, dh0, stream);
+                           initial_state, nullptr, 0, nullptr, dy, dlast, du, ddelta, dA, dB, dC,
+                           dD, dz, ddelta_bias, dh0, stream);
 }
 
 const char *ssm_status_string(int status) {

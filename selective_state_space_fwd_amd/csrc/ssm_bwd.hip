@@ -309,9 +309,12 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
 
     // ---- start state of the chunk (forward) and the gradient arriving at its
     // last token (backward)
+    // (with the forward pass's checkpoints given, neither the start state
+    // nor the forward sweep below is needed)
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const SeqPos sp0 = seq_pos<EXT>(a, b, t_begin);
-    if (sp0.reset) {
+    if (g.ckpt_given) {
+    } else if (sp0.reset) {
         load_start_state<4>(a, sp0.s, dcl, lane_ok, 4 * q, h);
     } else {
         for (int64_t i = 0; i < j; ++i) {
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             fb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
         }
     };
-    prefetch_fwd(t_begin);
-    for (int64_t ti = 0; ti < ntile; ++ti) {
+    if (!g.ckpt_given) prefetch_fwd(t_begin);
+    for (int64_t ti = 0; ti < (g.ckpt_given ? 0 : ntile); ++ti) {
         const int64_t t0 = t_begin + ti * kT;
         if (lane_ok)
             *reinterpret_cast<float4 *>(ck + (t0 / kT) * 16) = make_float4(h[0], h[1], h[2], h[3]);
@@ -395,7 +398,8 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float e = exp2_hw(dt * A2[k]);
-                const float wb = ZOH ? zoh_phi(dt * An[k], e) * (w * bv[k]) : w * bv[k];
+                // (ZOH: phi's argument formed as the forward pass forms it)
+                const float wb = ZOH ? zoh_phi((dt * A2[k]) * kLn2, e) * (w * bv[k]) : w * bv[k];
                 h[k] = __builtin_fmaf(e, h[k], wb);
             }
         }
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             for (int k = 0; k < 4; ++k) {
                 const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float e = exp2_hw(dt * A2[k]);
-                const float wb = ZOH ? zoh_phi(dt * An[k], e) * (w * bv[k]) : w * bv[k];
+                const float wb = ZOH ? zoh_phi((dt * A2[k]) * kLn2, e) * (w * bv[k]) : w * bv[k];
                 hh[t][k] = __builtin_fmaf(e, prev, wb);
                 p = __builtin_fmaf(cv[k], hh[t][k], p);
             }
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
                 const float da = dh * prev;
                 if (ZOH) {
-                    const float x = dt * An[k];
+                    const float x = (dt * A2[k]) * kLn2;
                     const float phi = zoh_phi(x, at);
                     const float dhb = dh * bv[k];
                     gb[k] = (w * phi) * dh;
@@ -739,8 +743,10 @@ template <class IO, bool EXT, bool ZOH>
 static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
     if (a.J > 1) {
-        const hipError_t e = launch_scan_agg(a, s);
-        if (e != hipSuccess) return e;
+        if (!g.ckpt_given) {   // the forward chunk operators, for the start states
+            const hipError_t e = launch_scan_agg(a, s);
+            if (e != hipSuccess) return e;
+        }
         // 16-byte pieces of delta, dy, z and C need whole pieces per row and
         // aligned rows
         constexpr int VW = Seg<IO>::VW;

@@ -45,6 +45,11 @@ struct ScanArgs {
     uint64_t *flags;
     uint64_t epoch;
     uint64_t spin_ticks;
+    // optional (quad path): the pass that writes y also writes the state
+    // entering every kBwdTile-token tile, (batch, d_inner, n_ck, 16), for
+    // the backward pass
+    float *ckpt;
+    int64_t n_ck;
     hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
 };
 
@@ -66,6 +71,7 @@ struct BwdArgs {
     float *dD, *dbias;          // (d_inner) or null
     float *dh0;                 // (batch, d_inner, N) or null
     int64_t n_tiles;            // backward tiles per row (checkpoints)
+    int ckpt_given;             // ckpt holds the forward pass's checkpoints: no forward sweep
     // workspace views
     float *ckpt;                // (batch, d_inner, n_tiles, 16) state entering each tile
     float *gend;                // (batch, d_inner, J, 16) gradient leaving each chunk to its left, from zero

@@ -355,6 +355,15 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
             s_w[r * TP + k] = tt >= 0 ? IO::load(u, rbase + tt) : 0.0f;
         }
     }
+    // checkpoints for the backward pass: the state entering every
+    // kBwdTile-token tile of the row (chunks start on such tiles)
+    float *ckp = (FULL && a.ckpt && lane_ok)
+                     ? a.ckpt + (static_cast<size_t>(b) * a.D + d) * a.n_ck * 16 + 4 * q
+                     : nullptr;
+    auto ckpt_at = [&](int64_t t) {   // h is the state entering token t
+        if (ckp) *reinterpret_cast<float4 *>(ckp + (t / kBwdTile) * 16) = make_float4(h[0], h[1], h[2], h[3]);
+    };
+    if (FULL) ckpt_at(t_begin);
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
         if (conv) {
@@ -502,6 +511,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
                 } else {
                     dt_sum += dt;
                 }
+                if (FULL && ckp && (t + 1) % kBwdTile == 0 && t + 1 < t_end) ckpt_at(t + 1);
             }
         } else {
 #pragma unroll
@@ -551,6 +561,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
                 const float ysum = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // token c4 + q
                 const int o = rowc + c4 + q;
                 s_du[o] = (ysum + s_du[o]) * s_g[o];
+                if ((c4 + 4) % kBwdTile == 0 && ckp && t0 + c4 + 4 < t_end) ckpt_at(t0 + c4 + 4);
             }
         }
         }

@@ -27,6 +27,7 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_ex",
+              "ssm_scan_fwd_ckpt", "ssm_scan_ckpt_bytes",
               "ssm_scan_bwd_workspace_bytes", "ssm_state_update", "ssm_scan_workspace_bytes",
               "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
         assert n in names
@@ -252,9 +253,9 @@ def test_backward_plan_and_validation(lib):
     assert lib.ssm_scan_bwd(ctypes.byref(d), *args, None) == 5
     # packed sequences: batch 1 and at least one sequence, an aligned table
     d.workspace, d.workspace_bytes = ok, 1 << 40
-    # (..., softplus, initial_state, cu_seqlens, n_seqs, dy, dlast, ...)
-    ex = args[:10] + [ok, 3] + args[10:]
-    assert len(ex) == 23
+    # (..., softplus, initial_state, cu_seqlens, n_seqs, ckpt, dy, dlast, ...)
+    ex = args[:10] + [ok, 3, None] + args[10:]
+    assert len(ex) == 24
     assert lib.ssm_scan_bwd_ex(ctypes.byref(d), *ex, None) == 2          # batch 2
     d1 = desc(batch=1, chunk_size=16)
     d1.workspace, d1.workspace_bytes = ok, 1 << 40
@@ -264,3 +265,22 @@ def test_backward_plan_and_validation(lib):
     bad = list(ex)
     bad[10] = ok + 2
     assert lib.ssm_scan_bwd_ex(ctypes.byref(d1), *bad, None) == 4        # misaligned table
+    bad = list(ex)
+    bad[12] = ok + 4
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d1), *bad, None) == 4        # misaligned checkpoints
+
+
+def test_checkpoint_plan_and_validation(lib):
+    """ssm_scan_ckpt_bytes: 16 floats per 8-token tile per (batch, channel)
+    row, d_state <= 16 only; ssm_scan_fwd_ckpt rejects a missing, misaligned
+    or d_state > 16 checkpoint array before any launch."""
+    d = desc(seqlen=2050)
+    assert lib.ssm_scan_ckpt_bytes(ctypes.byref(d)) == 2 * 64 * 257 * 16 * 4
+    assert lib.ssm_scan_ckpt_bytes(ctypes.byref(desc(d_state=17))) == 0
+    ok = 4096
+    d = desc(chunk_size=2048)
+    base = [ok, ok, ok, ok, ok, None, None, None, 1, None, None, 0, ok, None]
+    assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d), *base, None, None) == 1           # no ckpt
+    assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d), *base, ok + 4, None) == 4        # misaligned
+    d17 = desc(d_state=17, chunk_size=2048)
+    assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d17), *base, ok, None) == 3          # N > 16

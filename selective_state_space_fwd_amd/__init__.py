@@ -18,9 +18,9 @@ import ctypes
 import os
 from pathlib import Path
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ckpt_shape", "ssm_state_update", "ssm_scan_workspace_bytes",
-           "ssm_scan_chunk_size", "ssm_status_string", "SsmError", "load_library",
-           "LIB_PATH"]
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_state_update",
+           "ckpt_shape", "PreparedCall", "ssm_scan_workspace_bytes", "ssm_scan_chunk_size",
+           "ssm_status_string", "SsmError", "load_library", "LIB_PATH"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libssm.so"
 
@@ -150,6 +150,42 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+class PreparedCall:
+    """One entry point's call with its arguments checked and marshalled once:
+    the descriptor, the device pointers and the stream.  Calling it enqueues
+    the same work again on the same buffers, and returns what the plain call
+    returns (the same output tensors).  For loops in which the binding's own
+    checks would cost as much host time as the kernels take on the GPU.
+
+    It holds a reference to every tensor it points at, so none is freed while
+    it lives; new inputs are written into those tensors in place.  The stream
+    is the one current when it was prepared.
+    """
+
+    __slots__ = ("_fn", "desc", "_dref", "_args", "_keep", "result")
+
+    def __init__(self, fn, desc, args, keep, result):
+        self._fn, self.desc, self._args, self._keep, self.result = fn, desc, args, keep, result
+        self._dref = ctypes.byref(desc)
+
+    def __call__(self, profile_events=None):
+        """Enqueue the call; profile_events: optional pair of raw hipEvent_t
+        handles for entry points that record them."""
+        if profile_events is not None:
+            self.desc.profile_begin, self.desc.profile_end = profile_events
+        st = self._fn(self._dref, *self._args)
+        if st != 0:
+            _check(st)
+        return self.result
+
+
+def _issue(prepare, fn, desc, args, keep, result):
+    if prepare:
+        return PreparedCall(fn, desc, args, keep, result)
+    _check(fn(ctypes.byref(desc), *args))
+    return result
+
+
 SSM_FLAG_ZOH = 1
 SSM_FLAG_INDEPENDENT_CHUNKS = 2
 
@@ -178,7 +214,7 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
                  return_last_state=True, chunk_size=0, y=None, last_state=None,
                  workspace=None, profile_events=None, initial_state=None, cu_seqlens=None,
-                 zoh=False, independent_chunks=False, ckpt=None):
+                 zoh=False, independent_chunks=False, ckpt=None, prepare=False):
     """Fused selective-scan forward pass on the GPU.
 
     u, delta, z: (batch, d_inner, L); B, C: (batch, N, L), all float32 or all
@@ -195,6 +231,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     ckpt: optional float32 tensor of shape ckpt_shape(batch, d_inner, L)
     (d_state <= 16): also filled with the state entering every 8-token tile,
     for ssm_scan_bwd(ckpt=...).
+    prepare: check and marshal everything but launch nothing; return a
+    PreparedCall that launches this call each time it is called.
     Returns (y, last_state); last_state is None unless requested.
     profile_events: optional pair of raw hipEvent_t handles recorded around
     the pass that writes y.
@@ -237,23 +275,20 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if profile_events is not None:
         desc.profile_begin, desc.profile_end = profile_events
+    head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)))
     if ckpt is not None:
         _expect(ckpt, "ckpt", ckpt_shape(batch, d_inner, L), torch.float32, dev)
-        st = lib.ssm_scan_fwd_ckpt(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                                   _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                   int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
-                                   n_seqs, _ptr(y), _ptr(last_state), _ptr(ckpt), _stream(dev))
+        fn, args = lib.ssm_scan_fwd_ckpt, head + (_ptr(initial_state), _ptr(cu_seqlens), n_seqs,
+                                                  _ptr(y), _ptr(last_state), _ptr(ckpt))
     elif initial_state is None and cu_seqlens is None:
-        st = lib.ssm_scan_fwd(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                              _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                              _ptr(y), _ptr(last_state), _stream(dev))
+        fn, args = lib.ssm_scan_fwd, head + (_ptr(y), _ptr(last_state))
     else:
-        st = lib.ssm_scan_fwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                 int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
-                                 n_seqs, _ptr(y), _ptr(last_state), _stream(dev))
-    _check(st)
-    return y, last_state
+        fn, args = lib.ssm_scan_fwd_ex, head + (_ptr(initial_state), _ptr(cu_seqlens), n_seqs,
+                                                _ptr(y), _ptr(last_state))
+    keep = (u, delta, A, B, C, D, z, delta_bias, initial_state, cu_seqlens, y, last_state, ckpt,
+            workspace)
+    return _issue(prepare, fn, desc, args + (_stream(dev),), keep, (y, last_state))
 
 
 def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
@@ -261,7 +296,7 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
                       initial_state=None, cu_seqlens=None, return_last_state=True,
                       return_u=False, chunk_size=0, y=None, last_state=None, u_out=None,
                       workspace=None, profile_events=None, zoh=False,
-                      independent_chunks=False):
+                      independent_chunks=False, prepare=False):
     """The scan with the causal depthwise convolution fused in front: the scan
     input is u = silu(conv(x) + conv_bias) (identity instead of silu when
     conv_silu is False), computed on the fly.
@@ -270,7 +305,7 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
     float32, W <= 4, column W-1 on the current token; conv_bias: (d_inner,) or
     None; conv_state: (rows, d_inner, W-1) float32 inputs before each
     sequence, or None for zeros.  Returns (y, last_state, u) with u only when
-    return_u (else None).
+    return_u (else None).  prepare: as in ssm_scan_fwd.
     """
     torch = _torch()
     lib = load_library()
@@ -316,13 +351,13 @@ def ssm_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if profile_events is not None:
         desc.profile_begin, desc.profile_end = profile_events
-    st = lib.ssm_scan_fwd_conv(ctypes.byref(desc), _ptr(x), _ptr(conv_weight), _ptr(conv_bias),
-                               int(W), int(bool(conv_silu)), _ptr(conv_state), _ptr(delta),
-                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                               int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens),
-                               n_seqs, _ptr(y), _ptr(last_state), _ptr(u_out), _stream(dev))
-    _check(st)
-    return y, last_state, u_out
+    args = (_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(W), int(bool(conv_silu)),
+            _ptr(conv_state), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens), n_seqs,
+            _ptr(y), _ptr(last_state), _ptr(u_out), _stream(dev))
+    keep = (x, conv_weight, conv_bias, conv_state, delta, A, B, C, D, z, delta_bias,
+            initial_state, cu_seqlens, y, last_state, u_out, workspace)
+    return _issue(prepare, lib.ssm_scan_fwd_conv, desc, args, keep, (y, last_state, u_out))
 
 
 def ckpt_shape(batch, d_inner, seqlen):
@@ -333,7 +368,7 @@ def ckpt_shape(batch, d_inner, seqlen):
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True,
                  initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None,
-                 zoh=False, ckpt=None):
+                 zoh=False, ckpt=None, prepare=False):
     """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
     respect to all its inputs (d_state <= 16; zoh: the zero-order-hold input
     term, as in ssm_scan_fwd).  Returns a dict of
@@ -342,7 +377,7 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
     initial_state).  cu_seqlens: packed sequences as in ssm_scan_fwd; the
     states (initial_state, dlast, dh0) then have one row per sequence.
     ckpt: the checkpoints of the matching ssm_scan_fwd(ckpt=...) call, which
-    spare the backward its forward recompute."""
+    spare the backward its forward recompute.  prepare: as in ssm_scan_fwd."""
     torch = _torch()
     lib = load_library()
     batch, d_inner, L = u.shape
@@ -379,23 +414,23 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         desc.workspace = workspace.data_ptr()
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = lib.ssm_scan_bwd_ex(ctypes.byref(desc), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                             _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                             _ptr(initial_state), _ptr(cu_seqlens), n_seqs, _ptr(ckpt), _ptr(dy),
-                             _ptr(dlast),
-                             _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
-                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
-                             _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _stream(dev))
-    _check(st)
-    return out
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(initial_state), _ptr(cu_seqlens), n_seqs, _ptr(ckpt),
+            _ptr(dy), _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+            _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _stream(dev))
+    keep = (u, delta, A, B, C, D, z, delta_bias, initial_state, cu_seqlens, ckpt, dy, dlast,
+            workspace)
+    return _issue(prepare, lib.ssm_scan_bwd_ex, desc, args, keep, out)
 
 
-def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None, zoh=False):
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None, zoh=False,
+                     prepare=False):
     """One single-token update of ``state`` (batch, d_inner, N) float32, in place.
 
     u, delta, z: (batch, d_inner); B, C: (batch, N); float32 or bfloat16.
     delta is the final step size; zoh selects the zero-order-hold input term.
-    Returns y (batch, d_inner).
+    prepare: as in ssm_scan_fwd.  Returns y (batch, d_inner).
     """
     torch = _torch()
     lib = load_library()
@@ -414,7 +449,7 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, y=None, zoh=False
         y = torch.empty((batch, d_inner), dtype=io, device=dev)
     _expect(y, "y", (batch, d_inner), io, dev)
     desc = make_desc(batch, d_inner, N, 0, code, 0, SSM_FLAG_ZOH if zoh else 0)
-    st = lib.ssm_state_update(ctypes.byref(desc), _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
-                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(dev))
-    _check(st)
-    return y
+    args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(y), _stream(dev))
+    return _issue(prepare, lib.ssm_state_update, desc, args, (state, u, delta, A, B, C, D, z, y),
+                  y)

@@ -1,0 +1,126 @@
+"""GPU tests of PreparedCall: an entry point's call checked and marshalled
+once (prepare=True), then launched again and again on the same buffers.
+
+Every launch of a prepared call gives the bits of the plain call on the
+inputs the buffers hold at that moment: inputs are overwritten in place
+between launches, and each result is compared with a plain call on the same
+inputs.  Covered: the forward pass (plain, with start states and packed
+sequences, with checkpoints), the fused convolution, the decode step (whose
+state is updated in place), and the backward pass.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import selective_state_space_fwd_amd as ssm
+import ssm_inputs
+from ssm_testutil import to_device
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("u", "delta", "B", "C", "z", "A", "D", "delta_bias")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ssm.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def fresh(dev, batch, d_inner, N, L, io, seed):
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=True, seed=seed)
+    return {k: to_device(inp.get(k), dev) for k in KEYS}
+
+
+def refill(t, new):
+    for k in KEYS:
+        t[k].copy_(new[k])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["plain", "ex", "ckpt", "chunked"])
+def test_prepared_forward(dev, io, variant):
+    import torch
+    batch, d_inner, N, L = (1, 40, 16, 700) if variant == "ex" else (2, 40, 16, 700)
+    K = 64 if variant == "chunked" else 0
+    t = fresh(dev, batch, d_inner, N, L, io, 1)
+    extra = {}
+    if variant == "ex":
+        cu = torch.tensor([0, 100, 100, 450, 700], dtype=torch.int32, device=dev)
+        h0 = torch.randn(4, d_inner, N, device=dev)
+        extra = dict(cu_seqlens=cu, initial_state=h0)
+    if variant == "ckpt":
+        extra = dict(ckpt=torch.empty(ssm.ckpt_shape(batch, d_inner, L), device=dev))
+    args = [t[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    call = ssm.ssm_scan_fwd(*args, chunk_size=K, prepare=True, **extra)
+    assert isinstance(call, ssm.PreparedCall)
+    y, last = call.result
+    for r in range(3):
+        refill(t, fresh(dev, batch, d_inner, N, L, io, 10 + r))
+        got = call()
+        assert got[0] is y and got[1] is last
+        snap = (y.clone(), last.clone(), extra["ckpt"].clone() if "ckpt" in extra else None)
+        plain_extra = dict(extra)
+        if "ckpt" in extra:
+            plain_extra["ckpt"] = torch.empty_like(extra["ckpt"])
+        yp, lp = ssm.ssm_scan_fwd(*args, chunk_size=K, **plain_extra)
+        torch.cuda.synchronize()
+        assert torch.equal(snap[0], yp) and torch.equal(snap[1], lp), r
+        if "ckpt" in extra:
+            assert torch.equal(snap[2], plain_extra["ckpt"]), r
+    say(f"prepared forward {variant} io={io}: 3 launches equal to plain calls")
+
+
+def test_prepared_conv_and_backward(dev):
+    import torch
+    batch, d_inner, N, L = 2, 40, 16, 300
+    t = fresh(dev, batch, d_inner, N, L, "f32", 3)
+    w, cb = (torch.from_numpy(a).to(dev) for a in ssm_inputs.make_conv_params(d_inner, 4, seed=4))
+    conv = ssm.ssm_scan_fwd_conv(t["u"], w, cb, t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                 t["z"], t["delta_bias"], return_u=True, prepare=True)
+    dy = torch.randn(batch, d_inner, L, device=dev)
+    bwd = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                           t["delta_bias"], prepare=True)
+    for r in range(2):
+        refill(t, fresh(dev, batch, d_inner, N, L, "f32", 20 + r))
+        dy.copy_(torch.randn(batch, d_inner, L, device=dev))
+        yc = [x.clone() for x in conv()]
+        gb = {k: (None if v is None else v.clone()) for k, v in bwd().items()}
+        yc2 = ssm.ssm_scan_fwd_conv(t["u"], w, cb, t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                    t["z"], t["delta_bias"], return_u=True)
+        gb2 = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                               t["delta_bias"])
+        torch.cuda.synchronize()
+        for a, b in zip(yc, yc2):
+            assert torch.equal(a, b), r
+        for k, v in gb.items():
+            if v is not None:
+                assert torch.equal(v, gb2[k]), (r, k)
+
+
+def test_prepared_state_update(dev):
+    import torch
+    batch, d_inner, N = 8, 96, 16
+    inp = ssm_inputs.make_update_inputs(batch, d_inner, N, io_dtype="f32", gate=True, seed=5)
+    t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                        "state")}
+    call = ssm.ssm_state_update(t["state"], t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                t["z"], prepare=True)
+    for r in range(3):
+        before = t["state"].clone()
+        t["u"].copy_(torch.randn_like(t["u"]))
+        y = call().clone()
+        after = t["state"].clone()
+        twin = before.clone()
+        y2 = ssm.ssm_state_update(twin, t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                  t["z"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2) and torch.equal(after, twin), r

@@ -48,7 +48,49 @@ constexpr int kQC = 16;        // channels per wavefront
 // channel, lanes over tokens) spread over the banks:
 constexpr int kGC = 20;             // dB / dC partials: channel stride (16 states + 4)
 constexpr int kGT = kQC * kGC + 4;  //   token stride, 81 four-float groups (odd)
-constexpr int kRT = 4 * kQC + 4;    // dw / dd row partials [t][q][c]: token stride
+
+// Slot of (channel ch, token t) in the per-channel arrays of a tile: token
+// major, so that the 16 channels a token step reads are 16 consecutive floats
+// (one per bank), and the 4 lane-rows reading the same slot share it.
+__device__ __forceinline__ int pc(int ch, int t) { return t * kQC + ch; }
+
+// A token's LDS values in the recompute (TokB) and in the walk back (TokC).
+struct TokB {
+    float dt, w;
+    float4 B, C;
+};
+struct TokC {
+    float dt, w, dO, u;
+    float4 B, C, E;
+};
+
+// x of lanes l and l ^ 32 added, in the same order in both: (lower + upper).
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// x of lanes l and l ^ 16 added, in the same order in both: (even row + odd row).
+__device__ __forceinline__ float rows_pair_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Transposing sum over the 4 lane-rows of 4 tokens' row partials v0..v3:
+// row q returns the full sum of token q, ((r0 + r1) + (r2 + r3)).
+__device__ __forceinline__ float row_transpose_sum(float v0, float v1, float v2, float v3) {
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1),
+                                                      false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3),
+                                                      false, false);
+    const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+    const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01), __float_as_uint(p23),
+                                                    false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 
 template <class IO>
 __device__ __forceinline__ float ld_clamped(const typename IO::T *p, size_t base, int64_t t,
@@ -240,13 +282,13 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 // sequence end) and, with ZOH, the zero-order-hold input term: its factor
 // c = (e^{dt A} - 1) / A = phi(dt A) dt scales B u, enters dB and du, adds
 // dh.B u e^{dt A} to ddt (dc/ddt = e^{dt A}) and dh.B u dt^2 psi(dt A) to dA.
-#ifndef SSM_BWD_WAVES_PER_SIMD
-#define SSM_BWD_WAVES_PER_SIMD 1
-#endif
+// Two wavefronts per SIMD (at most 256 registers a lane; the LDS of a
+// wavefront is under 16 KB) for the Euler instances; the ZOH instance needs
+// more registers and runs one.
 template <class IO, bool EXT, bool ZOH>
-__global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArgs a, BwdArgs g) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2))) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
-    // per (channel, token) values of the tile: [c][t]
+    // per (channel, token) values of the tile: [t][c], see pc()
     __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
     __shared__ __attribute__((aligned(16))) float s_w[kQC * kT];
     __shared__ __attribute__((aligned(16))) float s_do[kQC * kT];
@@ -257,12 +299,9 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     // B and C of the tile, token-major: [t][n]
     __shared__ __attribute__((aligned(16))) float s_B[kT * 16];
     __shared__ __attribute__((aligned(16))) float s_C[kT * 16];
-    // row partials of dh.B and of sum_n dh h_prev A a: [t][q][c]
-    __shared__ __attribute__((aligned(16))) float s_rw[kT * kRT];
-    __shared__ __attribute__((aligned(16))) float s_rd[kT * kRT];
-    // per-channel contributions to dB, then to dC: [t][c][n] (one buffer for
-    // both keeps a wavefront's LDS under 20 KB, so that a CU's 160 KB holds
-    // two wavefronts per SIMD)
+    // [t][c][n]: the recompute's decays e^{dt A}, then the per-channel
+    // contributions to dB, then to dC (one buffer for the three keeps a
+    // wavefront's LDS small enough for two wavefronts per SIMD)
     __shared__ __attribute__((aligned(16))) float s_g[kT * kGT];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
@@ -380,8 +419,8 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const float x = rx[i] + rbias;
             const float dt = ok ? (a.softplus ? softplus_f32(x) : x) : 0.0f;
             const float uu = ok ? ru[i] : 0.0f;
-            s_dt[r * kT + sc + i] = dt;
-            s_w[r * kT + sc + i] = dt * uu;
+            s_dt[pc(r, sc + i)] = dt;
+            s_w[pc(r, sc + i)] = dt * uu;
             s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
         }
         if (ti + 1 < ntile) prefetch_fwd(t0 + kT);
@@ -390,7 +429,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
+            const float dt = s_dt[pc(c, t)], w = s_w[pc(c, t)];
             const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             if (EXT && ((fs >> t) & 1u))   // a sequence starts: its start state
@@ -408,16 +447,10 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
 
     // ---- reverse sweep
     float dA_acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float dD_acc[kT / 4] = {}, db_acc[kT / 4] = {};
+    float dD_acc = 0.0f, db_acc = 0.0f;   // this lane's tokens of channel c
+    // D of the lane's channel, loaded once: a global load inside the tile
+    // loop would wait for the next tile's prefetch too
     const float Dv_lane = (lane_ok && a.Dskip) ? a.Dskip[dcl] : 0.0f;
-    // D of the channels this lane serves in step (d), loaded once: a global
-    // load inside the tile loop would wait for the next tile's prefetch too
-    float Dv_d[kT / 4];
-#pragma unroll
-    for (int e = 0; e < kT / 4; ++e) {
-        const int64_t dch = d0 + lane / kT + (64 / kT) * e;
-        Dv_d[e] = (dch < a.D && a.Dskip) ? a.Dskip[dch] : 0.0f;
-    }
     float qx0 = 0.f, qx1 = 0.f, qu0 = 0.f, qu1 = 0.f, qy0 = 0.f, qy1 = 0.f, qz0 = 0.f, qz1 = 0.f;
     float qb0 = 0.f, qb1 = 0.f, qc0 = 0.f, qc1 = 0.f;
     float4 qh = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -463,7 +496,7 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 gg = zz * sz;
                 dsl = sz * __builtin_fmaf(zz, 1.0f - sz, 1.0f);
             }
-            const int o = r * kT + sc + i;
+            const int o = pc(r, sc + i);
             s_dt[o] = dt;
             s_w[o] = dt * uu;
             s_do[o] = dyv * gg;
@@ -479,22 +512,38 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
         __syncthreads();
 
         // (b) recompute the tile's states from its checkpoint (a token that
-        // starts a sequence continues from that sequence's start state)
+        // starts a sequence continues from that sequence's start state); the
+        // decays e^{dt A} go to s_g for the walk back, which reads each one
+        // just before it overwrites it with a dB contribution
         float hh[kT][4];
         float part[kT];
+        // a token's LDS values are read one token ahead, so that their
+        // latency passes under the previous token's arithmetic
+        auto ld_b = [&](int t) {
+            TokB v;
+            v.dt = s_dt[pc(c, t)];
+            v.w = s_w[pc(c, t)];
+            v.B = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
+            v.C = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            return v;
+        };
+        TokB nb = ld_b(0);
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
             // one token at a time: without this fence the scheduler hoists
             // all kT tokens' LDS reads, which costs the registers of a
             // second wavefront per SIMD (measured: 11-17% slower)
             __builtin_amdgcn_sched_barrier(0);
-            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t];
-            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
-            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            const TokB cb = nb;
+            if (t + 1 < kT) nb = ld_b(t + 1);
+            const float dt = cb.dt, w = cb.w;
+            const float4 B4 = cb.B;
+            const float4 C4 = cb.C;
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
             float p = 0.0f;
             float h0v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float ev[4];
             const bool st = EXT && ((smask >> t) & 1u);
             if (st) load_start_state<4>(a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, h0v);
 #pragma unroll
@@ -504,8 +553,10 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 const float wb = ZOH ? zoh_phi((dt * A2[k]) * kLn2, e) * (w * bv[k]) : w * bv[k];
                 hh[t][k] = __builtin_fmaf(e, prev, wb);
                 p = __builtin_fmaf(cv[k], hh[t][k], p);
+                ev[k] = e;
             }
             part[t] = p;
+            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) = make_float4(ev[0], ev[1], ev[2], ev[3]);
         }
         // o_t = C_t . h_t + D u_t: the 4 row partials meet in a transposing
         // butterfly (as in the forward kernel); row q ends with token g4 + q
@@ -519,20 +570,42 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
             const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01),
                                                             __float_as_uint(p23), false, false);
-            const int o = c * kT + g4 + q;
+            const int o = pc(c, g4 + q);
             s_o[o] = __builtin_fmaf(Dv_lane, s_u[o], __uint_as_float(s[0]) + __uint_as_float(s[1]));
         }
 
         // (c) walk the tile back (EXT: the gradient starts over from dlast at
-        // a sequence's last token; at its first token it leaves as dh0)
+        // a sequence's last token; at its first token it leaves as dh0).  The
+        // row partials of dh.B and of sum_n dh h_prev A a of every 4 tokens
+        // meet in a transposing butterfly: row q ends with token 4e + q.
+        float rw[kT], rd[kT];
+        float rws[kT / 4], rds[kT / 4];
+        auto ld_c = [&](int t) {
+            TokC v;
+            v.dt = s_dt[pc(c, t)];
+            v.w = s_w[pc(c, t)];
+            v.dO = s_do[pc(c, t)];
+            v.u = ZOH ? s_u[pc(c, t)] : 0.0f;
+            v.B = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
+            v.C = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            v.E = *reinterpret_cast<const float4 *>(&s_g[t * kGT + c * kGC + 4 * q]);
+            return v;
+        };
+        TokC nc = ld_c(kT - 1);
 #pragma unroll
         for (int t = kT - 1; t >= 0; --t) {
             __builtin_amdgcn_sched_barrier(0);   // as in (b)
-            const float dt = s_dt[c * kT + t], w = s_w[c * kT + t], dO = s_do[c * kT + t];
-            const float4 B4 = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
-            const float4 C4 = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            // token t - 1's values, read before token t's dB contribution
+            // overwrites its decays in s_g (a different slot)
+            const TokC cc = nc;
+            if (t > 0) nc = ld_c(t - 1);
+            const float dt = cc.dt, w = cc.w, dO = cc.dO;
+            const float4 B4 = cc.B;
+            const float4 C4 = cc.C;
+            const float4 E4 = cc.E;
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
+            const float ev[4] = {E4.x, E4.y, E4.z, E4.w};
             float gb[4];
             float dw = 0.0f, dd = 0.0f;
             if (EXT && ((lmask >> t) & 1u))
@@ -541,12 +614,12 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
             const bool st = EXT && ((smask >> t) & 1u);
             const int64_t s_st = st ? seq_of(a, t0 + t) : 0;
             if (st) load_start_state<4>(a, s_st, dcl, lane_ok, 4 * q, h0v);
-            const float uc = ZOH ? s_u[c * kT + t] : 0.0f;
+            const float uc = cc.u;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float prev = st ? h0v[k] : t == 0 ? hs[k] : hh[t > 0 ? t - 1 : 0][k];
                 const float dh = __builtin_fmaf(dO, cv[k], G[k]);
-                const float at = exp2_hw(dt * A2[k]);   // the same value as in (b): CSE
+                const float at = ev[k];   // e^{dt A}, from (b)
                 const float da = dh * prev;
                 if (ZOH) {
                     const float x = (dt * A2[k]) * kLn2;
@@ -571,66 +644,65 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
                 G[0] = G[1] = G[2] = G[3] = 0.0f;
             }
             *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
-            s_rw[t * kRT + q * kQC + c] = dw;
-            s_rd[t * kRT + q * kQC + c] = dd;
+            rw[t] = dw;
+            rd[t] = dd;
+            if (t % 4 == 0) {
+                rws[t / 4] = row_transpose_sum(rw[t], rw[t + 1], rw[t + 2], rw[t + 3]);
+                rds[t / 4] = row_transpose_sum(rd[t], rd[t + 1], rd[t + 2], rd[t + 3]);
+            }
         }
         __syncthreads();
 
-        // (d) per (channel, token): du, ddelta, dz; lane -> token lane % kT,
-        // channels lane / kT + (64 / kT) e
+        // (d) per (channel, token): du, ddelta, dz; lane (q, c) -> channel c,
+        // tokens q and 4 + q (where the butterflies left their row sums)
 #pragma unroll
         for (int e = 0; e < kT / 4; ++e) {
-            const int ch = lane / kT + (64 / kT) * e;
-            const int t = lane % kT;
+            const int t = 4 * e + q;
             const int64_t tok = t0 + t;
-            const int o = ch * kT + t;
-            float dw = 0.0f, dd = 0.0f;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                dw += s_rw[t * kRT + qq * kQC + ch];
-                dd += s_rd[t * kRT + qq * kQC + ch];
-            }
-            const int64_t dch = d0 + ch;
-            const bool ok = dch < a.D && tok < t_end;
+            const int o = pc(c, t);
+            const float dw = rws[e], dd = rds[e];
+            const bool ok = lane_ok && tok < t_end;
             const float dt = s_dt[o], uu = s_u[o], dO = s_do[o];
-            const float Dv = ok ? Dv_d[e] : 0.0f;
-            const float du = __builtin_fmaf(dO, Dv, dw * dt);
+            const float du = __builtin_fmaf(dO, Dv_lane, dw * dt);
             // (with ZOH the u term of ddt is already in dd)
             const float ddl = (ZOH ? dd : __builtin_fmaf(dw, uu, dd)) * s_sig[o];
             if (ok) {
-                const size_t off = (static_cast<size_t>(b) * a.D + dch) * L + tok;
+                const size_t off = (static_cast<size_t>(b) * a.D + d) * L + tok;
                 g.du[off] = du;
                 g.ddelta[off] = ddl;
                 if (gate) g.dz[off] = s_ds[o] * s_o[o];
-                dD_acc[e] = __builtin_fmaf(dO, uu, dD_acc[e]);
-                db_acc[e] += ddl;
+                dD_acc = __builtin_fmaf(dO, uu, dD_acc);
+                db_acc += ddl;
             }
         }
         // (e) dB, then dC (one LDS buffer, two rounds): sum over the 16
-        // channels; job = lane (4 x kT jobs): states 4 ((job / kT) % 4) .. +3,
-        // token job % kT
+        // channels.  Lane -> states 4 ((lane / kT) % 4) .. +3 of token
+        // lane % kT, over channels 8 h .. 8 h + 7, h = lane / 32; the two
+        // halves then meet (channels 0-7 + channels 8-15) in every lane.
+        static_assert(kT == 8, "channel_sums maps 64 lanes to 4 x kT x 2 jobs");
         auto channel_sums = [&](float *dstbase) {
-            if (lane < 4 * kT) {
-                const int n4 = (lane / kT) & 3;
-                const int t = lane % kT;
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int n4 = (lane / kT) & 3;
+            const int t = lane % kT;
+            const int h8 = 8 * (lane / 32);
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int ch = 0; ch < kQC; ++ch) {
-                    const float4 v = *reinterpret_cast<const float4 *>(&s_g[t * kGT + ch * kGC + 4 * n4]);
-                    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-                }
-                const int64_t tok = t0 + t;
-                if (tok < t_end) {
-                    float *dst = dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
-                    dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
-                }
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = *reinterpret_cast<const float4 *>(&s_g[t * kGT + (h8 + k) * kGC + 4 * n4]);
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            acc.x = halves_sum(acc.x); acc.y = halves_sum(acc.y);
+            acc.z = halves_sum(acc.z); acc.w = halves_sum(acc.w);
+            const int64_t tok = t0 + t;
+            if (lane < 32 && tok < t_end) {
+                float *dst = dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
+                dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
             }
         };
         channel_sums(g.dBp);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            const float dO = s_do[c * kT + t];
+            const float dO = s_do[pc(c, t)];
             *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) =
                 make_float4(dO * hh[t][0], dO * hh[t][1], dO * hh[t][2], dO * hh[t][3]);
         }
@@ -640,26 +712,15 @@ __global__ __launch_bounds__(64, SSM_BWD_WAVES_PER_SIMD) void bwd_kernel(ScanArg
     }
 
     // ---- chunk results
-    // dD, dbias: the kT lanes of a channel meet in a butterfly
-#pragma unroll
-    for (int e = 0; e < kT / 4; ++e) {
-        for (int off = 1; off < kT; off <<= 1) {
-            dD_acc[e] += __shfl_xor(dD_acc[e], off, 64);
-            db_acc[e] += __shfl_xor(db_acc[e], off, 64);
-        }
-    }
-    if (lane % kT == 0) {
-#pragma unroll
-        for (int e = 0; e < kT / 4; ++e) {
-            const int64_t dch = d0 + lane / kT + (64 / kT) * e;
-            if (dch < a.D) {
-                const size_t o = (static_cast<size_t>(b) * a.D + dch) * a.J + j;
-                g.dDp[o] = dD_acc[e];
-                g.dbp[o] = db_acc[e];
-            }
-        }
-    }
+    // dD, dbias: the 4 lane-rows of a channel meet, (r0 + r1) + (r2 + r3)
+    dD_acc = halves_sum(rows_pair_sum(dD_acc));
+    db_acc = halves_sum(rows_pair_sum(db_acc));
     if (!lane_ok) return;
+    if (q == 0) {
+        const size_t o = (static_cast<size_t>(b) * a.D + d) * a.J + j;
+        g.dDp[o] = dD_acc;
+        g.dbp[o] = db_acc;
+    }
     *reinterpret_cast<float4 *>(g.dAp + cd * 16 + 4 * q) =
         make_float4(dA_acc[0], dA_acc[1], dA_acc[2], dA_acc[3]);
     if (!packed && j == 0 && g.dh0) {

@@ -223,6 +223,24 @@ def bench_decode(args, torch, ssm, dev):
     ms = start.elapsed_time(end) / args.steps
     nbytes = (batch * d_inner * (N * 8 + 4 * 4) + 2 * batch * N * 4 + d_inner * (N + 1) * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
+
+    # The practical ceiling of such a stream on this GPU: torch's own
+    # device-to-device copy of as many bytes (half read, half written), over
+    # as many buffers in rotation as the step has input sets.
+    half = nbytes // 2 // 4
+    src = [torch.empty(half, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(n_sets)]
+    dst = [torch.empty_like(x) for x in src]
+    for i in range(n_sets):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        dst[i % n_sets].copy_(src[i % n_sets])
+    end.record()
+    torch.cuda.synchronize()
+    copy_ms = start.elapsed_time(end) / args.steps
+    copy_gbs = 2 * half * 4 / (copy_ms * 1e-3) / 1e9
+    del src, dst
     traffic = None
     try:
         with open(args.traffic_json) as f:
@@ -242,7 +260,7 @@ def bench_decode(args, torch, ssm, dev):
                    "d_state": N, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": nbytes,
-                     "kernel_ms": ms},
+                     "kernel_ms": ms, "copy_gbs": copy_gbs, "frac_of_copy": gbs / copy_gbs},
         "versions": versions(),
     }
 

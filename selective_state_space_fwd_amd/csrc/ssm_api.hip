@@ -162,6 +162,45 @@ struct BwdPlan {
            off_dDp = 0, off_dbp = 0, bytes = 0;
 };
 
+// The backward kernel holds two wavefronts per SIMD (one with ZOH): this many
+// run at once on 256 CUs x 4 SIMDs.
+constexpr int64_t kBwdSlots = 2048;
+
+// Chunk length of the backward's own plan (chunk_size 0), from the
+// wavefronts w = batch x channel blocks of one chunk.  When the chunks of one
+// round fit (w <= slots): the most chunks (at most 32, of at least 64 tokens)
+// whose J x w wavefronts still run in a single round.  Otherwise: the J that
+// minimises rounds x chunk length, ceil(J w / slots) K, with each chunk after
+// the first counted as 1% more (its reverse aggregate and fold).  Measured on
+// MI355X with the forward checkpoints given: 2 x 1536 channels x 2048 tokens
+// (w = 192) 252 us at 11 chunks (2112 wavefronts, a second round of 64),
+// 246 us at 10, 281 us at 12; 8 x 5120 channels x 2048 tokens (w = 2560)
+// 2945 us in one chunk (1.25 rounds), 2787 us in 2, 2693 us in 4 (5 rounds).
+int64_t bwd_auto_chunk(int64_t L, int64_t w, int64_t slots) {
+    auto chunk = [&](int64_t J) {
+        int64_t k = (L + J - 1) / J;
+        k = (k + 15) / 16 * 16;
+        return k < L ? k : L;
+    };
+    if (w <= slots) {
+        int64_t J = slots / w;
+        if (J > kFoldMaxChunks) J = kFoldMaxChunks;
+        if (J > L / kMinAutoChunk) J = L / kMinAutoChunk;
+        return J > 1 ? chunk(J) : L;
+    }
+    int64_t best_k = L;
+    double best = 1e300;
+    for (int64_t J = 1; J <= kFoldMaxChunks; ++J) {
+        const int64_t k = chunk(J);
+        if (J > 1 && k < kMinAutoChunk) break;
+        const int64_t jr = (L + k - 1) / k;
+        const int64_t rounds = (jr * w + slots - 1) / slots;
+        const double cost = static_cast<double>(rounds) * k * (1.0 + 0.01 * (jr - 1));
+        if (cost < best) { best = cost; best_k = k; }
+    }
+    return best_k;
+}
+
 ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     const ssm_status st = make_plan(d, &p->f, false);
     if (st != SSM_OK) return st;
@@ -169,6 +208,11 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     Plan &f = p->f;
     const int64_t L = d->seqlen;
     if (L == 0 || d->batch * d->d_inner == 0) { p->bytes = 0; return SSM_OK; }
+    if (d->chunk_size == 0) {
+        const int64_t slots = (d->flags & SSM_FLAG_ZOH) ? kBwdSlots / 2 : kBwdSlots;
+        f.K = bwd_auto_chunk(L, d->batch * f.n_cblk, slots);
+        f.J = (L + f.K - 1) / f.K;
+    }
     if (f.J > kFoldMaxChunks) {
         int64_t k = (L + kFoldMaxChunks - 1) / kFoldMaxChunks;
         k = (k + 15) / 16 * 16;

@@ -283,7 +283,9 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
  * state entering every 8-token tile of every row,
  *   ckpt           (batch, d_inner, ceil(L / 8), 16) float32, written; states
  *                  n >= N of each 16 are zero; ssm_scan_ckpt_bytes(desc) bytes,
- *                  16-byte aligned
+ *                  16-byte aligned.  With packed sequences the entry of a tile
+ *                  whose first token starts a sequence is unspecified (the
+ *                  backward starts that tile from the sequence's initial state)
  * Given to ssm_scan_bwd_ex with the same descriptor (shapes, io_dtype, flags)
  * and inputs, it spares the backward pass its forward recompute; with other
  * inputs the gradients are unspecified.  d_state <= 16 only

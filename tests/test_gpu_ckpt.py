@@ -127,6 +127,7 @@ def test_forward_checkpoints_equal_oracle_states(dev, shape, io, zoh):
     err = max(floored_err(ck[:, :, i, :N], r) for i, r in ref.items())
     say(f"ckpt {shape} io={io} zoh={zoh}: {len(ref)} tiles, err={err:.3e}")
     assert err <= TOL[io]
+    assert np.all(ck[:, :, :, N:] == 0.0)   # states past d_state
 
 
 def test_forward_checkpoints_packed_sequences(dev):
@@ -146,6 +147,7 @@ def test_forward_checkpoints_packed_sequences(dev):
         err = max(floored_err(ck[:, :, i, :N], r) for i, r in ref.items())
         say(f"ckpt packed K={K}: {len(ref)} tiles, err={err:.3e}")
         assert err <= TOL["f32"]
+        assert np.isfinite(ck).all()   # every tile written, starts of sequences included
 
 
 def backward_pair(dev, inp, io, N, L, K_fwd, K_bwd, zoh, with_state, cu=None, seed=0):

@@ -55,13 +55,14 @@ constexpr int kGT = kQC * kGC + 4;  //   token stride, 81 four-float groups (odd
 __device__ __forceinline__ int pc(int ch, int t) { return t * kQC + ch; }
 
 // A token's LDS values in the recompute (TokB) and in the walk back (TokC).
+// H: at the tile's first token, the state entering the tile.
 struct TokB {
     float dt, w;
-    float4 B, C;
+    float4 B, C, H;
 };
 struct TokC {
     float dt, w, dO, u;
-    float4 B, C, E;
+    float4 B, C, E, H;
 };
 
 // x of lanes l and l ^ 32 added, in the same order in both: (lower + upper).
@@ -303,6 +304,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     // contributions to dB, then to dC (one buffer for the three keeps a
     // wavefront's LDS small enough for two wavefronts per SIMD)
     __shared__ __attribute__((aligned(16))) float s_g[kT * kGT];
+    // the state entering the tile, one float4 a lane (a register copy would be
+    // live across the next tile's checkpoint prefetch, and the copy back at
+    // the loop's end would wait for every store of the tile)
+    __shared__ __attribute__((aligned(16))) float s_h0[64 * 4];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -454,32 +459,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     float qx0 = 0.f, qx1 = 0.f, qu0 = 0.f, qu1 = 0.f, qy0 = 0.f, qy1 = 0.f, qz0 = 0.f, qz1 = 0.f;
     float qb0 = 0.f, qb1 = 0.f, qc0 = 0.f, qc1 = 0.f;
     float4 qh = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Every tile issues the same vector-memory instructions, whatever the
+    // gate and however many of its tokens and channels are real (the loads
+    // without a gate read u, the stores of lanes with nothing to store go to
+    // g.sink): the wait for the next tile's prefetch can then count the
+    // tile's stores instead of waiting for all of them to complete.
+    const IT *zsrc = gate ? z : u;
     auto prefetch_rev = [&](int64_t t0) {
         const int64_t t = t0 + sc;
         qx0 = ld_clamped<IO>(dl, rbase, t, t_end);
         qu0 = ld_clamped<IO>(u, rbase, t, t_end);
         qy0 = ld_clamped<IO>(dy, rbase, t, t_end);
-        if (gate) qz0 = ld_clamped<IO>(z, rbase, t, t_end);
+        qz0 = ld_clamped<IO>(zsrc, rbase, t, t_end);
         qb0 = ld_clamped<IO>(Bm, sbase, t, t_end);
         qc0 = ld_clamped<IO>(Cm, sbase, t, t_end);
         if (kEPL > 1) {
             qx1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
             qu1 = ld_clamped<IO>(u, rbase, t + 1, t_end);
             qy1 = ld_clamped<IO>(dy, rbase, t + 1, t_end);
-            if (gate) qz1 = ld_clamped<IO>(z, rbase, t + 1, t_end);
+            qz1 = ld_clamped<IO>(zsrc, rbase, t + 1, t_end);
             qb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
             qc1 = ld_clamped<IO>(Cm, sbase, t + 1, t_end);
         }
         qh = *reinterpret_cast<const float4 *>(ck + (t0 / kT) * 16);
     };
-    prefetch_rev(t_begin + (ntile - 1) * kT);
-    for (int64_t ti = ntile - 1; ti >= 0; --ti) {
-        const int64_t t0 = t_begin + ti * kT;
-        // (a) the tile's inputs
+    // (a) a tile's inputs from the prefetch registers into LDS.  Each tile
+    // stages the next one at its end, after its own stores: the wait for the
+    // prefetch then counts those stores instead of waiting for them.
+    auto stage = [&](int64_t t0) {
         const float rx[2] = {qx0, qx1}, ru[2] = {qu0, qu1}, ry[2] = {qy0, qy1},
                     rz[2] = {qz0, qz1}, rb[2] = {qb0, qb1}, rc[2] = {qc0, qc1};
-        float hs[4] = {lane_ok ? qh.x : 0.0f, lane_ok ? qh.y : 0.0f, lane_ok ? qh.z : 0.0f,
-                       lane_ok ? qh.w : 0.0f};
+        *reinterpret_cast<float4 *>(&s_h0[4 * lane]) = lane_ok ? qh : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < kEPL; ++i) {
             const int64_t t = t0 + sc + i;
@@ -506,7 +516,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
             s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
         }
-        if (ti > 0) prefetch_rev(t0 - kT);
+    };
+    prefetch_rev(t_begin + (ntile - 1) * kT);
+    stage(t_begin + (ntile - 1) * kT);
+    for (int64_t ti = ntile - 1; ti >= 0; --ti) {
+        const int64_t t0 = t_begin + ti * kT;
+        // (unconditional: the last tile reloads its own inputs, so that every
+        // path has issued the same loads)
+        prefetch_rev(ti > 0 ? t0 - kT : t0);
         uint32_t lmask;
         const uint32_t smask = tile_marks<EXT>(a, t0, t_end, &lmask);
         __syncthreads();
@@ -525,6 +542,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             v.w = s_w[pc(c, t)];
             v.B = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             v.C = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
+            v.H = t == 0 ? *reinterpret_cast<const float4 *>(&s_h0[4 * lane])
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
             return v;
         };
         TokB nb = ld_b(0);
@@ -544,6 +563,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             float p = 0.0f;
             float h0v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             float ev[4];
+            const float hs[4] = {cb.H.x, cb.H.y, cb.H.z, cb.H.w};
             const bool st = EXT && ((smask >> t) & 1u);
             if (st) load_start_state<4>(a, seq_of(a, t0 + t), dcl, lane_ok, 4 * q, h0v);
 #pragma unroll
@@ -589,6 +609,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             v.B = *reinterpret_cast<const float4 *>(&s_B[t * 16 + 4 * q]);
             v.C = *reinterpret_cast<const float4 *>(&s_C[t * 16 + 4 * q]);
             v.E = *reinterpret_cast<const float4 *>(&s_g[t * kGT + c * kGC + 4 * q]);
+            v.H = t == 0 ? *reinterpret_cast<const float4 *>(&s_h0[4 * lane])
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
             return v;
         };
         TokC nc = ld_c(kT - 1);
@@ -606,6 +628,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             const float bv[4] = {B4.x, B4.y, B4.z, B4.w};
             const float cv[4] = {C4.x, C4.y, C4.z, C4.w};
             const float ev[4] = {E4.x, E4.y, E4.z, E4.w};
+            const float hs[4] = {cc.H.x, cc.H.y, cc.H.z, cc.H.w};
             float gb[4];
             float dw = 0.0f, dd = 0.0f;
             if (EXT && ((lmask >> t) & 1u))
@@ -666,14 +689,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             const float du = __builtin_fmaf(dO, Dv_lane, dw * dt);
             // (with ZOH the u term of ddt is already in dd)
             const float ddl = (ZOH ? dd : __builtin_fmaf(dw, uu, dd)) * s_sig[o];
-            if (ok) {
-                const size_t off = (static_cast<size_t>(b) * a.D + d) * L + tok;
-                g.du[off] = du;
-                g.ddelta[off] = ddl;
-                if (gate) g.dz[off] = s_ds[o] * s_o[o];
-                dD_acc = __builtin_fmaf(dO, uu, dD_acc);
-                db_acc += ddl;
-            }
+            const size_t off = (static_cast<size_t>(b) * a.D + d) * L + tok;
+            *(ok ? g.du + off : g.sink) = du;
+            *(ok ? g.ddelta + off : g.sink) = ddl;
+            *((ok && gate) ? g.dz + off : g.sink) = s_ds[o] * s_o[o];
+            dD_acc = ok ? __builtin_fmaf(dO, uu, dD_acc) : dD_acc;
+            db_acc = ok ? db_acc + ddl : db_acc;
         }
         // (e) dB, then dC (one LDS buffer, two rounds): sum over the 16
         // channels.  Lane -> states 4 ((lane / kT) % 4) .. +3 of token
@@ -693,10 +714,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             acc.x = halves_sum(acc.x); acc.y = halves_sum(acc.y);
             acc.z = halves_sum(acc.z); acc.w = halves_sum(acc.w);
             const int64_t tok = t0 + t;
-            if (lane < 32 && tok < t_end) {
-                float *dst = dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok;
-                dst[0] = acc.x; dst[L] = acc.y; dst[2 * L] = acc.z; dst[3 * L] = acc.w;
-            }
+            const bool ok = lane < 32 && tok < t_end;
+            float *dst = ok ? dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok
+                            : g.sink;
+            const int64_t st = ok ? L : 0;
+            dst[0] = acc.x; dst[st] = acc.y; dst[2 * st] = acc.z; dst[3 * st] = acc.w;
         };
         channel_sums(g.dBp);
         __syncthreads();
@@ -709,6 +731,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
         __syncthreads();
         channel_sums(g.dCp);
         __syncthreads();
+        if (ti > 0) stage(t0 - kT);
     }
 
     // ---- chunk results

@@ -79,6 +79,7 @@ struct BwdArgs {
     float *dBp, *dCp;           // (batch, n_cblk, 16, L) per 16-channel block
     float *dAp;                 // (batch, d_inner, J, 16)
     float *dDp, *dbp;           // (batch, d_inner, J)
+    float *sink;                // 64 floats that take the stores of lanes with nothing to store
 };
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);

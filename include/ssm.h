@@ -92,9 +92,11 @@ typedef struct ssm_desc {
                                  covers tokens [kK, min((k+1)K, L)). */
     void *workspace;          /* scan only: device scratch, >= workspace_bytes */
     size_t workspace_bytes;   /* scan only */
-    void *profile_begin;      /* scan only, optional hipEvent_t: when both are set, */
-    void *profile_end;        /* recorded on `stream` right before and right after
-                                 the pass that writes y (measurement hook) */
+    void *profile_begin;      /* scan only, optional hipEvent_t (timing enabled): when */
+    void *profile_end;        /* both are set, the dispatch of the pass that writes y
+                                 records them at its start and its end, so that
+                                 hipEventElapsedTime gives that kernel's execution
+                                 time (measurement hook) */
     uint32_t flags;           /* SSM_FLAG_* bits; unknown bits: SSM_ERR_UNSUPPORTED */
     uint32_t reserved;        /* must be 0 */
 } ssm_desc;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void update_vec_kernel(UpdateArgs a, int P, in
     const int64_t base = static_cast<int64_t>(blockIdx.x) * per_block * ITER + (threadIdx.x >> log2P);
 
     float4 sv[ITER], A4[ITER];
-    float bv[ITER][4], cv[ITER][4], dt[ITER], uu[ITER];
+    float bv[ITER][4], cv[ITER][4], dt[ITER], uu[ITER], dk[ITER], zk[ITER];
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
         const int64_t ch = base + static_cast<int64_t>(k) * per_block;
@@ -74,6 +74,10 @@ __global__ __launch_bounds__(256) void update_vec_kernel(UpdateArgs a, int P, in
         load4<IO>(Cm + bo, cv[k]);
         uu[k] = IO::load(u, chs);
         dt[k] = IO::load(dl, chs);
+        // D and z too, with the rest: the output step then waits for no
+        // second round trip to memory
+        dk[k] = a.Dskip ? a.Dskip[d] : 0.0f;
+        zk[k] = a.z ? IO::load(z, chs) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
@@ -99,9 +103,8 @@ __global__ __launch_bounds__(256) void update_vec_kernel(UpdateArgs a, int P, in
         if (!lane_on) acc = 0.0f;
         for (int off = P >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
         if (ok && l == 0) {
-            const int64_t d = chs % a.D;
-            if (a.Dskip) acc = __builtin_fmaf(a.Dskip[d], uu[k], acc);
-            if (a.z) acc *= silu_f32(IO::load(z, chs));
+            if (a.Dskip) acc = __builtin_fmaf(dk[k], uu[k], acc);
+            if (a.z) acc *= silu_f32(zk[k]);
             IO::store(y, chs, acc);
         }
     }

@@ -345,6 +345,67 @@ def bench_backward(args, torch, ssm, dev):
     }
 
 
+def bench_train(args, torch, ssm, dev):
+    """One training step of the scan on the workload: the forward pass that
+    keeps the state entering every 8-token tile (ssm_scan_fwd_ckpt), then the
+    backward pass that reads them (every gradient).  Algorithmic work: the
+    forward's slots plus the backward's (its one recompute of the recurrence
+    included)."""
+    cfg = dict(ssm_inputs.CONFIGS[args.config])
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    io, gate = cfg["io_dtype"], cfg["gate"]
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=0)
+    t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z", "A", "D", "delta_bias")}
+    rng = np.random.default_rng(1)
+    dy = upload(ssm_inputs.encode(rng.standard_normal((batch, d_inner, L)).astype(np.float32),
+                                  io), dev)
+    dlast = upload(rng.standard_normal((batch, d_inner, N)).astype(np.float32), dev)
+    ck = torch.empty(ssm.ckpt_shape(batch, d_inner, L), dtype=torch.float32, device=dev)
+    args_f = (t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+    fwd = ssm.ssm_scan_fwd(*args_f, softplus=True, chunk_size=args.chunk, ckpt=ck, prepare=True)
+    bwd = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                           t["delta_bias"], softplus=True, dlast=dlast, chunk_size=args.chunk,
+                           ckpt=ck, prepare=True)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    chtok = batch * d_inner * L
+    slots = (algorithmic_slots(batch, d_inner, N, L, gate) +
+             chtok * (N * BWD_SLOTS_PER_UPDATE + BWD_SLOTS_PER_CHTOK))
+    tflops = 2.0 * slots / (ms * 1e-3) / 1e12
+    return {
+        "metric": "selective-scan training step (forward keeping checkpoints + backward) "
+                  "channel-tokens/sec",
+        "value": chtok / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config}: forward with checkpoints + backward, "
+                               f"batch={batch} d_inner={d_inner} N={N} L={L} {io} I/O"
+                               f"{' + gate' if gate else ''}",
+                   "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
+                   "io_dtype": io, "gate": gate},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
+                     "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
+                     "frac_nonpacked": tflops / VALU_PEAK_NONPACKED_TFLOPS,
+                     "kernel": "the whole step (forward passes, backward passes)",
+                     "kernel_ms": ms, "algorithmic_slots": slots},
+        "versions": versions(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +422,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time only the backward pass (ssm_scan_bwd) of the workload, with "
                          "upstream gradients of y and last_state")
+    ap.add_argument("--train", action="store_true",
+                    help="time one training step of the scan: the forward pass keeping "
+                         "checkpoints, then the backward pass reading them")
     ap.add_argument("--ckpt", action="store_true",
                     help="with --backward: the backward reads the forward pass's checkpoints "
                          "(the state entering every 8-token tile) instead of recomputing them")
@@ -393,6 +457,9 @@ def main():
         return
     if args.backward:
         print(json.dumps(bench_backward(args, torch, ssm, dev)), flush=True)
+        return
+    if args.train:
+        print(json.dumps(bench_train(args, torch, ssm, dev)), flush=True)
         return
     cfg = dict(ssm_inputs.CONFIGS[args.config])
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]

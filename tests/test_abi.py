@@ -284,3 +284,21 @@ def test_checkpoint_plan_and_validation(lib):
     assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d), *base, ok + 4, None) == 4        # misaligned
     d17 = desc(d_state=17, chunk_size=2048)
     assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d17), *base, ok, None) == 3          # N > 16
+
+
+def test_backward_auto_chunking(lib):
+    """The backward's own chunk plan, seen through its workspace size (which
+    depends on the chunk count): one round of two wavefronts per SIMD when a
+    chunk's wavefronts fit (2 x 1536 channels: 10 chunks of 208 tokens, not the
+    forward's 11 of 192; 1 x 2048 channels x 64 Ki tokens: 16 of 4096), else
+    the fewest rounds x chunk length (8 x 5120 channels: 4 chunks of 512)."""
+    def ws(**kw):
+        return lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(**kw)))
+    c1 = dict(batch=2, d_inner=1536, seqlen=2048)
+    assert ws(**c1) == ws(chunk_size=208, **c1) != ws(chunk_size=192, **c1)
+    c2 = dict(batch=8, d_inner=5120, seqlen=2048, io_dtype=1)
+    assert ws(**c2) == ws(chunk_size=512, **c2) != ws(chunk_size=2048, **c2)
+    c3 = dict(batch=1, d_inner=2048, seqlen=65536, io_dtype=1)
+    assert ws(**c3) == ws(chunk_size=4096, **c3) != ws(chunk_size=2048, **c3)
+    tiny = dict(batch=1, d_inner=64, seqlen=256)     # 4 wavefronts a chunk: 4 chunks of 64
+    assert ws(**tiny) == ws(chunk_size=64, **tiny) != ws(chunk_size=256, **tiny)

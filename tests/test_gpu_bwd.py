@@ -273,3 +273,80 @@ def test_backward_zoh_random_a_small_and_large_steps(dev):
         e = floored_err(to_f64(out[k]), ref[k])
         say(f"  {k}={e:.2e}")
         assert e <= GRAD_TOL, (k, e)
+
+
+# ---------------------------------------------------------------- full-size shapes
+
+FULL_SHAPES = {
+    "mamba2p8b": (8, 5120, 16, 2048),       # bf16 I/O, gate
+    "long": (1, 2048, 16, 65536),           # bf16 I/O, gate
+}
+
+
+@pytest.mark.parametrize("name", sorted(FULL_SHAPES))
+def test_backward_full_size_sampled(dev, name):
+    """The Mamba-2.8B-shaped layer and the 64 Ki-token sequence, bf16 I/O,
+    with the library's own chunking and the forward pass's checkpoints.
+
+    Per-channel gradients (du, ddelta, dz of every token, dA, dD, d(bias))
+    of 24 channels spread over the layer against the oracle on those channels
+    alone (a channel's gradients depend on its own inputs and the shared B, C
+    only).  dB and dC sum over all channels, which no sample can check: they
+    are held to their additivity over channels instead, dB(all) = dB(first
+    half) + dB(second half) with the halves run as layers of their own, and
+    the first 24 channels' dB, dC against the oracle on those channels."""
+    import torch
+    batch, d_inner, N, L = FULL_SHAPES[name]
+    say(f"bwd full size {name} {FULL_SHAPES[name]}")
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype="bf16", gate=True, seed=3)
+    rng = np.random.default_rng(4)
+    dy = ssm_inputs.encode(rng.standard_normal((batch, d_inner, L)).astype(np.float32), "bf16")
+    dlast = rng.standard_normal((batch, d_inner, N)).astype(np.float32)
+    t = {k: to_device(inp.get(k), dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                  "delta_bias")}
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    dy_t, dlast_t = to_device(dy, dev), g(dlast)
+
+    def backward(ch):
+        """The GPU backward of the layer restricted to channels ch (None: all)."""
+        sel = (lambda x: x) if ch is None else (lambda x: x[:, ch].contiguous())
+        pc = (lambda x: x) if ch is None else (lambda x: x[ch].contiguous())
+        u, dl, z, dyc = sel(t["u"]), sel(t["delta"]), sel(t["z"]), sel(dy_t)
+        A, D, bias, dls = pc(t["A"]), pc(t["D"]), pc(t["delta_bias"]), sel(dlast_t)
+        ck = torch.empty(ssm.ckpt_shape(batch, u.shape[1], L), dtype=torch.float32, device=dev)
+        ssm.ssm_scan_fwd(u, dl, A, t["B"], t["C"], D, z, bias, ckpt=ck)
+        out = ssm.ssm_scan_bwd(u, dl, A, t["B"], t["C"], dyc, D, z, bias, dlast=dls, ckpt=ck)
+        torch.cuda.synchronize()
+        return out
+
+    full = backward(None)
+    half = d_inner // 2
+    lo = backward(torch.arange(0, half, device=dev))
+    hi = backward(torch.arange(half, d_inner, device=dev))
+    for k in ("dB", "dC"):
+        e = floored_err(to_f64(lo[k]) + to_f64(hi[k]), to_f64(full[k]))
+        say(f"  {k} additivity over channel halves: {e:.2e}")
+        assert e <= GRAD_TOL, k
+
+    ch = np.linspace(0, d_inner - 1, 24).astype(np.int64)
+    f = decoded(inp)
+    ref = oracle.scan_bwd(f["u"][:, ch], f["delta"][:, ch], f["A"][ch], f["B"], f["C"],
+                          ssm_inputs.to_f64(dy, "bf16")[:, ch], f["D"][ch], f["z"][:, ch],
+                          f["delta_bias"][ch], softplus=True,
+                          dlast=dlast[:, ch].astype(np.float64))
+    errs = {}
+    for k in ("du", "ddelta", "dz"):
+        errs[k] = floored_err(to_f64(full[k])[:, ch], ref[k])
+    for k in ("dA", "dD", "ddelta_bias"):
+        errs[k] = floored_err(to_f64(full[k])[ch], ref[k])
+    first = np.arange(24)
+    sub = backward(torch.from_numpy(first).to(dev))
+    ref0 = oracle.scan_bwd(f["u"][:, first], f["delta"][:, first], f["A"][first], f["B"], f["C"],
+                           ssm_inputs.to_f64(dy, "bf16")[:, first], f["D"][first],
+                           f["z"][:, first], f["delta_bias"][first], softplus=True,
+                           dlast=dlast[:, first].astype(np.float64))
+    for k in ("dB", "dC"):
+        errs[k + "(24 ch)"] = floored_err(to_f64(sub[k]), ref0[k])
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= GRAD_TOL, (k, e)

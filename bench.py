@@ -406,6 +406,117 @@ def bench_train(args, torch, ssm, dev):
     }
 
 
+# Extra minimal work of the forward variants:
+# ZOH, per (channel-token, state): x = dt A (1), e^x - 1 (1), rcp(x) (2 slots),
+# the quotient (1) and its product with w B (1);
+# the fused convolution, per channel-token: 4 taps (4 FMA) and silu (7).
+ZOH_SLOTS_PER_UPDATE = 4 + TRANS_SLOTS
+CONV_SLOTS_PER_CHTOK = 4 + SLOTS_PER_CHTOK["gate"]
+# Packed sequences: the workload's batch x seqlen tokens of every channel,
+# cut into sequences of this length mix (fractions of the total), each with a
+# start state.
+VARLEN_MIX = (0.25, 0.125, 0.375, 0.0625, 0.1875)
+
+
+def bench_variant(args, torch, ssm, dev):
+    """The forward scan alone with one of the method's variants on the
+    workload: the zero-order-hold input term (zoh), the causal convolution
+    fused in front (conv, width 4, silu), or the tokens packed as sequences of
+    mixed lengths with start states (varlen).  `achieved` is the variant's
+    algorithmic slots over the pass that writes y, timed by events its own
+    dispatch records."""
+    cfg = dict(ssm_inputs.CONFIGS[args.config])
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    io, gate = cfg["io_dtype"], cfg["gate"]
+    v = args.variant
+    cu = None
+    if v == "varlen":
+        total = batch * L
+        lens = [int(round(f * total)) for f in VARLEN_MIX]
+        lens[-1] = total - sum(lens[:-1])
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        batch, L = 1, total
+    rows = len(cu) - 1 if cu is not None else batch
+    n_sets = max(2, min(8, -(-3 * CACHE_BYTES // algorithmic_bytes(batch, d_inner, N, L, io,
+                                                                  gate))))
+    sets = []
+    for s_ in range(n_sets):
+        inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=s_)
+        t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                "delta_bias")}
+        t["y"] = torch.empty_like(t["u"])
+        t["last"] = torch.empty((rows, d_inner, N), dtype=torch.float32, device=dev)
+        if v == "varlen":
+            h0 = np.random.default_rng(50 + s_).standard_normal((rows, d_inner, N))
+            t["h0"] = upload(h0.astype(np.float32), dev)
+        sets.append(t)
+        del inp
+    cu_t = torch.from_numpy(cu).to(dev) if cu is not None else None
+    if v == "conv":
+        w, cb = ssm_inputs.make_conv_params(d_inner, 4, seed=7)
+        w_t, cb_t = upload(w, dev), upload(cb, dev)
+    calls = []
+    for t in sets:
+        common = dict(softplus=True, chunk_size=args.chunk, y=t["y"], last_state=t["last"],
+                      prepare=True)
+        if v == "conv":
+            calls.append(ssm.ssm_scan_fwd_conv(t["u"], w_t, cb_t, t["delta"], t["A"], t["B"],
+                                               t["C"], t["D"], t["z"], t["delta_bias"],
+                                               **common))
+        else:
+            calls.append(ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                          t["z"], t["delta_bias"], zoh=(v == "zoh"),
+                                          initial_state=t.get("h0"), cu_seqlens=cu_t,
+                                          **common))
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    ev = hip.create(2 * (args.steps + args.warmup))
+    for i in range(args.warmup):
+        calls[i % n_sets]((ev[2 * i], ev[2 * i + 1]))
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    base = 2 * args.warmup
+    start.record()
+    for i in range(args.steps):
+        calls[i % n_sets]((ev[base + 2 * i], ev[base + 2 * i + 1]))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kavg = float(np.mean([hip.elapsed_ms(ev[base + 2 * i], ev[base + 2 * i + 1])
+                          for i in range(args.steps)]))
+    hip.destroy(ev)
+    chtok = batch * d_inner * L
+    slots = algorithmic_slots(batch, d_inner, N, L, gate)
+    if v == "zoh":
+        slots += chtok * N * ZOH_SLOTS_PER_UPDATE
+    if v == "conv":
+        slots += chtok * CONV_SLOTS_PER_CHTOK
+    tflops = 2.0 * slots / (kavg * 1e-3) / 1e12
+    K = ssm.ssm_scan_chunk_size(batch, d_inner, N, L, 1 if io == "bf16" else 0, args.chunk)
+    what = {"zoh": "zero-order-hold input term", "conv": "causal convolution (width 4, silu) "
+            "fused in front", "varlen": f"{rows} packed sequences of lengths "
+            f"{[int(x) for x in np.diff(cu)] if cu is not None else ''} with start states"}[v]
+    return {
+        "metric": f"selective-scan channel-tokens/sec, {v}", "value": chtok / (ms * 1e-3),
+        "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config}: selective scan, {what}, batch={batch} "
+                               f"d_inner={d_inner} N={N} L={L} {io} I/O"
+                               f"{' + silu gate' if gate else ''}",
+                   "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
+                   "io_dtype": io, "gate": gate, "variant": v, "chunk": K,
+                   "input_sets": n_sets},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
+                     "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
+                     "frac_nonpacked": tflops / VALU_PEAK_NONPACKED_TFLOPS,
+                     "kernel": "the pass that writes y (EXT instance)", "kernel_ms": kavg,
+                     "algorithmic_slots": slots},
+        "versions": versions(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,6 +536,9 @@ def main():
     ap.add_argument("--train", action="store_true",
                     help="time one training step of the scan: the forward pass keeping "
                          "checkpoints, then the backward pass reading them")
+    ap.add_argument("--variant", choices=("zoh", "conv", "varlen"),
+                    help="time only the forward scan of the workload with the zero-order-hold "
+                         "term, the fused causal convolution, or packed sequences")
     ap.add_argument("--ckpt", action="store_true",
                     help="with --backward: the backward reads the forward pass's checkpoints "
                          "(the state entering every 8-token tile) instead of recomputing them")
@@ -460,6 +574,9 @@ def main():
         return
     if args.train:
         print(json.dumps(bench_train(args, torch, ssm, dev)), flush=True)
+        return
+    if args.variant:
+        print(json.dumps(bench_variant(args, torch, ssm, dev)), flush=True)
         return
     cfg = dict(ssm_inputs.CONFIGS[args.config])
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]

@@ -64,20 +64,19 @@ __device__ __forceinline__ float silu_f32(float z) {
 // Zero-order-hold input factor (SSM engineering essay, §1.2: B_bar =
 // (dt A)^-1 (exp(dt A) - 1) dt B), per unit of dt: phi(x) = (e^x - 1) / x at
 // x = dt A, given e = e^x; (exp(dt A) - 1) / A = dt phi(dt A), and phi(0) = 1
-// (the Euler factor).  Below |x| = 1/2 the difference e - 1 would lose up to
-// 2^-24 / |x| relative, so there phi is its Taylor polynomial to x^7
-// (truncation below 1e-8 relative); above, (e - 1) / x.
+// (the Euler factor).  Near 0 the difference e - 1 loses about 2^-24 / |x|
+// relative, so below |x| = 1/8 phi is its Taylor polynomial; above, (e - 1) / x.
 __device__ __forceinline__ float zoh_phi(float x, float e) {
-    float p = 1.0f / 40320.0f;
-    p = __builtin_fmaf(p, x, 1.0f / 5040.0f);
-    p = __builtin_fmaf(p, x, 1.0f / 720.0f);
-    p = __builtin_fmaf(p, x, 1.0f / 120.0f);
+    // |x| < 1/8: the series to x^4 (the first omitted term, x^5 / 720, is
+    // below 4.3e-8 relative there); otherwise the quotient, whose relative
+    // error, that of e - 1, is at most about 7.5 times that of e at |x| = 1/8
+    float p = 1.0f / 120.0f;
     p = __builtin_fmaf(p, x, 1.0f / 24.0f);
     p = __builtin_fmaf(p, x, 1.0f / 6.0f);
     p = __builtin_fmaf(p, x, 0.5f);
     p = __builtin_fmaf(p, x, 1.0f);
     const float q = (e - 1.0f) * rcp_hw(x);
-    return fabsf(x) < 0.5f ? p : q;
+    return fabsf(x) < 0.125f ? p : q;
 }
 
 template <class IO>

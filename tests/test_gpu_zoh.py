@@ -95,9 +95,10 @@ def test_zoh_decode(dev, io, N):
 def test_zoh_factor_accuracy(dev):
     """One token from a zero state with B = C = u = 1 and A = -1 gives
     y = (1 - exp(-dt)): the hold factor itself, for dt from 1e-7 to 20,
-    including both sides of the polynomial / quotient switch at |dt A| = 1/2."""
+    including both sides of the polynomial / quotient switch at |dt A| = 1/8."""
     import torch
-    dts = np.concatenate([np.logspace(-7, np.log10(20.0), 400), [0.4999, 0.5, 0.5001]])
+    dts = np.concatenate([np.logspace(-7, np.log10(20.0), 400), [0.1249, 0.125, 0.1251],
+                          np.linspace(0.12, 0.2, 41)])
     n = dts.size
     one = lambda *s: torch.ones(*s, device=dev)
     delta = torch.from_numpy(dts.astype(np.float32)).to(dev).view(1, n, 1)

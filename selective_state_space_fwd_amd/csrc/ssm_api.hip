@@ -152,8 +152,9 @@ uint64_t next_epoch() {
     return e != 0 ? e : counter.fetch_add(1, std::memory_order_relaxed);
 }
 
-// Backward plan: the forward plan's chunks, at most 32 of them (each chunk
-// folds its neighbours' operators itself), and the workspace of the backward.
+// Backward plan: its own chunks (bwd_auto_chunk, or the caller's chunk
+// length), at most 32 of them (each chunk folds its neighbours' operators
+// itself), and the workspace of the backward.
 
 struct BwdPlan {
     Plan f;

@@ -159,7 +159,7 @@ class PreparedCall:
 
     It holds a reference to every tensor it points at, so none is freed while
     it lives; new inputs are written into those tensors in place.  The stream
-    is the one current when it was prepared.
+    is the one current when it was prepared, unless a call names another.
     """
 
     __slots__ = ("_fn", "desc", "_dref", "_args", "_keep", "result")
@@ -168,12 +168,15 @@ class PreparedCall:
         self._fn, self.desc, self._args, self._keep, self.result = fn, desc, args, keep, result
         self._dref = ctypes.byref(desc)
 
-    def __call__(self, profile_events=None):
+    def __call__(self, profile_events=None, stream=None):
         """Enqueue the call; profile_events: optional pair of raw hipEvent_t
-        handles for entry points that record them."""
+        handles for entry points that record them; stream: a raw hipStream_t
+        to enqueue on instead of the prepared one (for instance the stream
+        that a graph capture makes current)."""
         if profile_events is not None:
             self.desc.profile_begin, self.desc.profile_end = profile_events
-        st = self._fn(self._dref, *self._args)
+        args = self._args if stream is None else self._args[:-1] + (stream,)
+        st = self._fn(self._dref, *args)
         if st != 0:
             _check(st)
         return self.result

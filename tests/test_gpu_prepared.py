@@ -124,3 +124,44 @@ def test_prepared_state_update(dev):
                                   t["z"])
         torch.cuda.synchronize()
         assert torch.equal(y, y2) and torch.equal(after, twin), r
+
+
+@pytest.mark.parametrize("K", [0, 1024])
+def test_training_step_in_a_graph(dev, K):
+    """The forward pass keeping checkpoints and the backward pass reading them,
+    captured as one graph (chunked in two passes, and in one launch with
+    K = 1024) and replayed three times with new inputs written in place, host
+    work and synchronisation in between: every replay gives the bits of an
+    eager step on the same inputs."""
+    import torch
+    batch, d_inner, N, L = 2, 64, 16, 4096
+    t = fresh(dev, batch, d_inner, N, L, "f32", 30)
+    dy = torch.randn(batch, d_inner, L, device=dev)
+    ck = torch.empty(ssm.ckpt_shape(batch, d_inner, L), device=dev)
+    args = [t[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    fwd = ssm.ssm_scan_fwd(*args, chunk_size=K, ckpt=ck, prepare=True)
+    bwd = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                           t["delta_bias"], ckpt=ck, prepare=True)
+    fwd(); bwd()                      # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream     # the capturing stream
+        fwd(stream=cap)
+        bwd(stream=cap)
+    for r in range(3):
+        refill(t, fresh(dev, batch, d_inner, N, L, "f32", 40 + r))
+        dy.copy_(torch.randn(batch, d_inner, L, device=dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_g, h_g = (x.clone() for x in fwd.result)
+        grads_g = {k: (None if v is None else v.clone()) for k, v in bwd.result.items()}
+        y_e, h_e = fwd()
+        grads_e = bwd()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e) and torch.equal(h_g, h_e), r
+        for k, v in grads_g.items():
+            if v is not None:
+                assert torch.equal(v, grads_e[k]), (r, k)
+        say(f"graph training step K={K} replay {r}: equal to eager")

@@ -24,9 +24,11 @@
 //      arriving gradient (fold of pass 2 from the right, starting at dlast);
 //      a forward sweep stores the state entering every tile of kBwdTile
 //      tokens; then the tiles are walked in reverse: each recomputes its
-//      states from its checkpoint (in registers) and walks them back.  dB and dC sum over
-//      the 16 channels of the wavefront through LDS, and over channel blocks
-//      in pass 4;
+//      states from its checkpoint (in registers) and walks them back.  dB and
+//      dC sum over the 16 channels of the wavefront through LDS, and over
+//      channel blocks in pass 4.  Given the forward pass's checkpoints
+//      (ssm_scan_fwd_ckpt), pass 1, the fold of the start state and the
+//      forward sweep are skipped;
 //   4. bwd_reduce_kernel: the fixed-order sums of the per-block partials of
 //      dB, dC and the per-chunk partials of dA, dD and dbias.
 // Lane mapping as the forward quad kernel: lane l serves channel l % 16 and

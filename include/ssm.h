@@ -233,9 +233,11 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
  * checkpoints, recompute inside the chunk); the reverse recurrence of the
  * state gradient is joined across chunks by transfer operators like the
  * forward one (§3.1).
- * Supported: d_state <= 16 (otherwise SSM_ERR_UNSUPPORTED), Euler or, with
- * SSM_FLAG_ZOH in desc->flags, the zero-order-hold input term; the fused
- * convolution has no backward here (its input u is an input of this call).
+ * Supported: d_state 1 .. 256, Euler or, with SSM_FLAG_ZOH in desc->flags,
+ * the zero-order-hold input term; the fused convolution has no backward here
+ * (its input u is an input of this call).  Above 16 states the pass runs once
+ * per group of 16 states (their recurrences are independent, §3.2) and the
+ * groups' per-token sums are added in group order.
  * Packed sequences: see ssm_scan_bwd_ex.
  * Inputs: as ssm_scan_fwd_ex (initial_state may be NULL), plus
  *   dy             (batch, d_inner, L) io_dtype
@@ -266,7 +268,8 @@ ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, 
  * dh0.  initial_state, dlast and dh0 are (n_seqs, d_inner, N); an empty
  * sequence's dh0 is its dlast.  ckpt: the checkpoints written by
  * ssm_scan_fwd_ckpt for the same call, or NULL (the backward recomputes them
- * in its workspace).  With cu_seqlens and ckpt NULL this is ssm_scan_bwd.
+ * in its workspace).  Both need d_state <= 16 (SSM_ERR_UNSUPPORTED above).
+ * With cu_seqlens and ckpt NULL this is ssm_scan_bwd.
  * Errors as ssm_scan_bwd, and SSM_ERR_BAD_SHAPE for packing with batch != 1
  * or n_seqs < 1.  A malformed offset table gives unspecified gradients but
  * no access out of bounds. */

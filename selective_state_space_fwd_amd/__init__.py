@@ -373,8 +373,9 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
                  initial_state=None, dlast=None, chunk_size=0, workspace=None, cu_seqlens=None,
                  zoh=False, ckpt=None, prepare=False):
     """Gradients of sum(dy * y) + sum(dlast * last_state) of ssm_scan_fwd with
-    respect to all its inputs (d_state <= 16; zoh: the zero-order-hold input
-    term, as in ssm_scan_fwd).  Returns a dict of
+    respect to all its inputs (d_state up to 256; above 16 without
+    cu_seqlens or ckpt; zoh: the zero-order-hold input term, as in
+    ssm_scan_fwd).  Returns a dict of
     float32 tensors: du, ddelta (of the raw delta), dA, dB, dC, dD (None
     without D), dz (None without z), ddelta_bias, dh0 (None without
     initial_state).  cu_seqlens: packed sequences as in ssm_scan_fwd; the

@@ -244,6 +244,57 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     return SSM_OK;
 }
 
+// Backward with d_state > 16 (ufo.work article, §3.2: the state dimension
+// splits into groups that recur independently): the 16-state pass runs once
+// per group of 16 states on that group's slices of A, B, C, the start state
+// and dlast.  The per-token sums over states add: group 0 writes du, ddelta,
+// dz and d(bias) (and alone sees D, so that D's terms enter once), the later
+// groups add theirs in group order; dA, dB, dC and dh0 are the groups'
+// slices.  No packed sequences or forward checkpoints on this path.
+struct BwdGroupPlan {
+    ssm_desc sd{};   // the 16-state descriptor of one group
+    BwdPlan sub;
+    int64_t NG = 0;
+    size_t off_sub = 0, off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_dl = 0, off_du = 0,
+           off_dd = 0, off_dz = 0, off_dA = 0, off_dB = 0, off_dC = 0, off_db = 0, off_dh0 = 0,
+           bytes = 0;
+};
+
+ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
+    const ssm_status st = check_desc(d);
+    if (st != SSM_OK) return st;
+    if (d->d_state <= 16) return SSM_ERR_UNSUPPORTED;
+    p->sd = *d;
+    p->sd.d_state = 16;
+    p->sd.workspace = nullptr;
+    p->sd.workspace_bytes = 0;
+    p->sd.profile_begin = p->sd.profile_end = nullptr;
+    const ssm_status s2 = make_bwd_plan(&p->sd, &p->sub);
+    if (s2 != SSM_OK) return s2;
+    p->NG = (d->d_state + 15) / 16;
+    const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
+    const size_t L = static_cast<size_t>(d->seqlen);
+    const size_t esz = d->io_dtype == SSM_BF16 ? 2 : 4;
+    size_t off = 0;
+    auto take = [&](size_t &o, size_t bytes) { o = off; off += align_up(bytes); };
+    take(p->off_sub, p->sub.bytes);
+    take(p->off_B, B * 16 * L * esz);
+    take(p->off_C, B * 16 * L * esz);
+    take(p->off_A, D * 16 * sizeof(float));
+    take(p->off_h0, B * D * 16 * sizeof(float));
+    take(p->off_dl, B * D * 16 * sizeof(float));
+    take(p->off_du, B * D * L * sizeof(float));
+    take(p->off_dd, B * D * L * sizeof(float));
+    take(p->off_dz, B * D * L * sizeof(float));
+    take(p->off_dA, D * 16 * sizeof(float));
+    take(p->off_dB, B * 16 * L * sizeof(float));
+    take(p->off_dC, B * 16 * L * sizeof(float));
+    take(p->off_db, D * sizeof(float));
+    take(p->off_dh0, B * D * 16 * sizeof(float));
+    p->bytes = off;
+    return SSM_OK;
+}
+
 }  // namespace
 
 namespace {
@@ -346,6 +397,87 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z,
+                      const float *delta_bias, int softplus_flag, const float *initial_state,
+                      const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                      float *dB, float *dC, float *dD, float *dz, float *ddelta_bias, float *dh0,
+                      ssm_stream_t stream) {
+    BwdGroupPlan p;
+    const ssm_status st = make_bwd_group_plan(desc, &p);
+    if (st != SSM_OK) return st;
+    const int64_t Bn = desc->batch, Dn = desc->d_inner, N = desc->d_state, L = desc->seqlen;
+    const hipStream_t s = stream;
+    if (Bn * Dn == 0 || L == 0) {
+        // no tokens: as the 16-state pass, over all N states
+        auto zero = [&](float *ptr, size_t n) {
+            return ptr ? ssm::launch_fill_zero(ptr, n, s) : hipSuccess;
+        };
+        hipError_t e = zero(dA, static_cast<size_t>(Dn * N));
+        if (e == hipSuccess) e = zero(dD, static_cast<size_t>(Dn));
+        if (e == hipSuccess) e = zero(ddelta_bias, static_cast<size_t>(Dn));
+        if (e == hipSuccess && dh0) {
+            const size_t n = static_cast<size_t>(Bn * Dn * N);
+            e = dlast ? hipMemcpyAsync(dh0, dlast, n * sizeof(float), hipMemcpyDeviceToDevice, s)
+                      : ssm::launch_fill_zero(dh0, n, s);
+        }
+        return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+        return SSM_ERR_NULL_ARG;
+    if (z && !dz) return SSM_ERR_NULL_ARG;
+    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
+    if (!aligned(B, esz) || !aligned(C, esz) || !aligned(A, 4) || !aligned(initial_state, 4) ||
+        !aligned(dlast, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) ||
+        !aligned(dh0, 4) || !aligned(du, 4) || !aligned(ddelta, 4) || !aligned(dz, 4) ||
+        !aligned(ddelta_bias, 4))
+        return SSM_ERR_MISALIGNED;
+    if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
+    if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
+    char *ws = static_cast<char *>(desc->workspace);
+    auto at = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+    ssm_desc sd = p.sd;
+    sd.workspace = ws + p.off_sub;
+    sd.workspace_bytes = p.sub.bytes;
+    void *Bg = ws + p.off_B, *Cg = ws + p.off_C;
+    float *Ag = at(p.off_A), *h0g = initial_state ? at(p.off_h0) : nullptr;
+    float *dlg = dlast ? at(p.off_dl) : nullptr;
+    float *dAg = at(p.off_dA), *dBg = at(p.off_dB), *dCg = at(p.off_dC);
+    float *dh0g = dh0 ? at(p.off_dh0) : nullptr;
+    for (int64_t g = 0; g < p.NG; ++g) {
+        const int64_t n0 = 16 * g;
+        hipError_t e = ssm::launch_gather_rows(Bg, B, Bn, N, n0, L, static_cast<int>(esz), s);
+        if (e == hipSuccess) e = ssm::launch_gather_rows(Cg, C, Bn, N, n0, L, static_cast<int>(esz), s);
+        if (e == hipSuccess) e = ssm::launch_gather_cols(Ag, A, Dn, N, n0, s);
+        if (e == hipSuccess && h0g) e = ssm::launch_gather_cols(h0g, initial_state, Bn * Dn, N, n0, s);
+        if (e == hipSuccess && dlg) e = ssm::launch_gather_cols(dlg, dlast, Bn * Dn, N, n0, s);
+        if (e != hipSuccess) return SSM_ERR_HIP;
+        const bool first = g == 0;
+        float *du_o = first ? du : at(p.off_du);
+        float *dd_o = first ? ddelta : at(p.off_dd);
+        float *dz_o = z ? (first ? dz : at(p.off_dz)) : nullptr;
+        float *db_o = ddelta_bias ? (first ? ddelta_bias : at(p.off_db)) : nullptr;
+        const ssm_status sst = ssm_scan_bwd_ex(
+            &sd, u, delta, Ag, Bg, Cg, first ? D : nullptr, z, delta_bias, softplus_flag, h0g,
+            nullptr, 0, nullptr, dy, dlg, du_o, dd_o, dAg, dBg, dCg, first ? dD : nullptr, dz_o,
+            db_o, dh0g, stream);
+        if (sst != SSM_OK) return sst;
+        const int64_t tok = Bn * Dn * L;
+        if (!first) {
+            e = ssm::launch_accumulate(du, du_o, tok, s);
+            if (e == hipSuccess) e = ssm::launch_accumulate(ddelta, dd_o, tok, s);
+            if (e == hipSuccess && dz_o) e = ssm::launch_accumulate(dz, dz_o, tok, s);
+            if (e == hipSuccess && db_o) e = ssm::launch_accumulate(ddelta_bias, db_o, Dn, s);
+        }
+        if (e == hipSuccess) e = ssm::launch_scatter_cols(dA, dAg, Dn, N, n0, s);
+        if (e == hipSuccess) e = ssm::launch_scatter_rows(dB, dBg, Bn, N, n0, L, s);
+        if (e == hipSuccess) e = ssm::launch_scatter_rows(dC, dCg, Bn, N, n0, L, s);
+        if (e == hipSuccess && dh0g) e = ssm::launch_scatter_cols(dh0, dh0g, Bn * Dn, N, n0, s);
+        if (e != hipSuccess) return SSM_ERR_HIP;
+    }
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -441,6 +573,10 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
 }
 
 size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc) {
+    if (desc && desc->d_state > 16) {
+        BwdGroupPlan p;
+        return make_bwd_group_plan(desc, &p) == SSM_OK ? p.bytes : 0;
+    }
     BwdPlan p;
     return make_bwd_plan(desc, &p) == SSM_OK ? p.bytes : 0;
 }
@@ -452,6 +588,12 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
                            const float *ckpt, const void *dy, const float *dlast, float *du,
                            float *ddelta, float *dA, float *dB, float *dC, float *dD, float *dz,
                            float *ddelta_bias, float *dh0, ssm_stream_t stream) {
+    if (desc && desc->d_state > 16) {
+        if (cu_seqlens || ckpt) return SSM_ERR_UNSUPPORTED;
+        return bwd_groups(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag,
+                          initial_state, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                          dh0, stream);
+    }
     BwdPlan p;
     ssm_status st = make_bwd_plan(desc, &p);
     if (st != SSM_OK) return st;

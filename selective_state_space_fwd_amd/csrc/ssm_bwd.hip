@@ -864,4 +864,97 @@ hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
     return a.bf16 ? launch_bwd_sel<BF16>(a, g, s) : launch_bwd_sel<F32>(a, g, s);
 }
 
+// ------------------------------------------------------------ state groups
+// The backward for d_state > 16 runs the pass above once per group of 16
+// states (the recurrences of different states are independent; only the
+// per-token sums over states meet, and they add).  These copies move one
+// group's slice in and out; one thread per element.
+namespace {
+
+template <class T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(T *dst, const T *src, int64_t R,
+                                                          int64_t N, int64_t n0, int64_t L) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= R * 16 * L) return;
+    const int64_t t = i % L, k = (i / L) % 16, r = i / (16 * L);
+    const int64_t n = n0 + k;
+    dst[i] = n < N ? src[(r * N + n) * L + t] : T(0);
+}
+
+__global__ __launch_bounds__(256) void gather_cols_kernel(float *dst, const float *src, int64_t R,
+                                                          int64_t N, int64_t n0) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= R * 16) return;
+    const int64_t n = n0 + i % 16, r = i / 16;
+    dst[i] = n < N ? src[r * N + n] : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void scatter_rows_kernel(float *dst, const float *src, int64_t R,
+                                                           int64_t N, int64_t n0, int64_t L) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= R * 16 * L) return;
+    const int64_t t = i % L, k = (i / L) % 16, r = i / (16 * L);
+    const int64_t n = n0 + k;
+    if (n < N) dst[(r * N + n) * L + t] = src[i];
+}
+
+__global__ __launch_bounds__(256) void scatter_cols_kernel(float *dst, const float *src, int64_t R,
+                                                           int64_t N, int64_t n0) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= R * 16) return;
+    const int64_t n = n0 + i % 16, r = i / 16;
+    if (n < N) dst[r * N + n] = src[i];
+}
+
+__global__ __launch_bounds__(256) void accumulate_kernel(float *dst, const float *src, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] += src[i];
+}
+
+dim3 grid_of(int64_t n) { return dim3(static_cast<unsigned>((n + 255) / 256)); }
+
+}  // namespace
+
+hipError_t launch_gather_rows(void *dst, const void *src, int64_t R, int64_t N, int64_t n0,
+                              int64_t L, int esz, hipStream_t s) {
+    const int64_t n = R * 16 * L;
+    if (n == 0) return hipSuccess;
+    if (esz == 2)
+        hipLaunchKernelGGL(gather_rows_kernel<uint16_t>, grid_of(n), dim3(256), 0, s,
+                           static_cast<uint16_t *>(dst), static_cast<const uint16_t *>(src), R, N,
+                           n0, L);
+    else
+        hipLaunchKernelGGL(gather_rows_kernel<float>, grid_of(n), dim3(256), 0, s,
+                           static_cast<float *>(dst), static_cast<const float *>(src), R, N, n0, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                              hipStream_t s) {
+    if (R == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_cols_kernel, grid_of(R * 16), dim3(256), 0, s, dst, src, R, N, n0);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                               int64_t L, hipStream_t s) {
+    const int64_t n = R * 16 * L;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(scatter_rows_kernel, grid_of(n), dim3(256), 0, s, dst, src, R, N, n0, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                               hipStream_t s) {
+    if (R == 0) return hipSuccess;
+    hipLaunchKernelGGL(scatter_cols_kernel, grid_of(R * 16), dim3(256), 0, s, dst, src, R, N, n0);
+    return hipGetLastError();
+}
+
+hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(accumulate_kernel, grid_of(n), dim3(256), 0, s, dst, src, n);
+    return hipGetLastError();
+}
+
 }  // namespace ssm

@@ -84,6 +84,20 @@ struct BwdArgs {
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);
 
+// One group of 16 states (n0 .. n0 + 15) out of N, for the backward with
+// d_state > 16.  Rows: dst (R, 16, L) <-> src (R, N, L); columns: dst (R, 16)
+// <-> src (R, N).  Gathers zero-fill states n >= N; scatters skip them.
+hipError_t launch_gather_rows(void *dst, const void *src, int64_t R, int64_t N, int64_t n0,
+                              int64_t L, int esz, hipStream_t s);
+hipError_t launch_gather_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                              hipStream_t s);
+hipError_t launch_scatter_rows(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                               int64_t L, hipStream_t s);
+hipError_t launch_scatter_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
+                               hipStream_t s);
+// dst[i] += src[i], i < n
+hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s);
+
 struct UpdateArgs {
     int64_t Bsz, D, N;
     int bf16;

@@ -223,13 +223,25 @@ def test_flags_validation(lib):
 
 
 def test_backward_plan_and_validation(lib):
-    """ssm_scan_bwd: d_state <= 16 only (Euler or ZOH, same workspace);
-    workspace sized for at most 32 chunks; null and misaligned arguments
-    rejected before any launch."""
-    d = desc(d_state=17)
+    """ssm_scan_bwd: any d_state up to 256 (Euler or ZOH, same workspace;
+    above 16 in groups of 16 states, without packed sequences or forward
+    checkpoints); workspace sized for at most 32 chunks; null and misaligned
+    arguments rejected before any launch."""
+    d = desc(d_state=257)
     assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) == 0
     assert lib.ssm_scan_bwd(ctypes.byref(d), *([4096] * 5), None, None, None, 1, None, 4096,
                             None, *([4096] * 5), None, None, None, None, None) == 3
+    d17 = desc(d_state=17)
+    assert lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d17)) > \
+        lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc())) > 0
+    ok = 4096
+    d17.workspace, d17.workspace_bytes = ok, 1 << 40
+    base = [ok, ok, ok, ok, ok, None, None, None, 1, None]
+    # d_state > 16: no packed sequences, no forward checkpoints
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d17), *base, ok, 1, None, ok, None,
+                               *([ok] * 5), None, None, None, None, None) == 3
+    assert lib.ssm_scan_bwd_ex(ctypes.byref(d17), *base, None, 0, ok, ok, None,
+                               *([ok] * 5), None, None, None, None, None) == 3
     assert (lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(flags=ssm.SSM_FLAG_ZOH))) ==
             lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc())) > 0)
     d = desc(chunk_size=16)              # 128 chunks asked: the backward uses at most 32

@@ -350,3 +350,20 @@ def test_backward_full_size_sampled(dev, name):
     say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= GRAD_TOL, (k, e)
+
+
+# ---------------------------------------------------------------- d_state > 16
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N,zoh,K", [(17, False, 0), (32, False, 64), (40, True, 0),
+                                     (64, False, 32), (256, False, 0)])
+@pytest.mark.parametrize("gate,with_state", [(True, True), (False, False)])
+def test_backward_state_groups(dev, io, N, zoh, K, gate, with_state):
+    """d_state above 16: the 16-state pass per group of 16 states, the groups'
+    per-token sums added (D's terms once), the padded states of a last partial
+    group left out.  Every gradient against the oracle's reverse walk."""
+    d_inner, L = (24, 200) if N > 64 else (40, 300)
+    say(f"bwd state groups N={N} io={io} zoh={zoh} K={K} gate={gate} state={with_state}")
+    _, errs = run_case(dev, 2, d_inner, N, L, io, gate, with_state, K, seed=N + K, zoh=zoh)
+    for k, e in errs.items():
+        assert e <= GRAD_TOL, (k, e)

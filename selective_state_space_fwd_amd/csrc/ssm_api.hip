@@ -73,6 +73,38 @@ constexpr int64_t kFoldMaxChunks = 32;
 // Longest wait of a chunk for its predecessors' operators: 20 ms of the
 // 100 MHz real-time clock.
 constexpr uint64_t kMaxSpinTicks = 2000000;
+// SIMDs of the chip: 256 CUs x 4.
+constexpr int64_t kSimds = 1024;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunk length of the two-pass schedule of the d_state <= 16 path, for
+// `waves` wavefronts per chunk: among J0 .. 2 J0 chunks (J0 puts kTargetWaves
+// in flight), the count whose busiest SIMD scans the fewest tokens, both
+// passes counted.  A pass's wavefronts spread evenly over the SIMDs and share
+// each one fairly (quad_kernel lowers its priority as it advances), so the
+// pass takes about ceil(wavefronts / kSimds) chunk lengths; the aggregate
+// pass, over chunks 0 .. J-2, costs about 4/5 of the y pass per token.
+// Measured on MI355X (2 x 1536 channels x 2048 tokens, fp32, both passes):
+// 128-token chunks, three wavefronts on every SIMD, 66 us; 96, 160 and 192
+// tokens 71-75 us.
+int64_t quad_auto_chunk(int64_t L, int64_t waves) {
+    const int64_t J0 = ceil_div(kTargetWaves, waves);
+    int64_t best_k = L, best_cost = -1;
+    for (int64_t J = J0; J <= 2 * J0; ++J) {
+        int64_t k = ceil_div(ceil_div(L, J), 16) * 16;
+        if (k < kMinAutoChunk) k = kMinAutoChunk;
+        if (k > L) k = L;
+        const int64_t nj = ceil_div(L, k);
+        const int64_t cost = k * (5 * ceil_div(waves * nj, kSimds) +
+                                  4 * ceil_div(waves * (nj - 1), kSimds));
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_k = k;
+        }
+    }
+    return best_k;
+}
 
 // fused_ok: the quad path may run as one launch (the forward scan, long
 // chunks); the backward, which reuses the chunk-aggregate pass on its own,
@@ -104,6 +136,8 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fused_ok = true) {
             int64_t k = (L + J - 1) / J;
             k = (k + 15) / 16 * 16;
             if (k < kMinAutoChunk) k = kMinAutoChunk;
+            // chunks this short run as two passes: balance their SIMDs
+            if (p->quad && k < kFusedMinChunk) k = quad_auto_chunk(L, waves);
             if (k < L) K = k;
         }
     }

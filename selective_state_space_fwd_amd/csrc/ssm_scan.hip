@@ -224,7 +224,21 @@ struct QuadTile {
     static constexpr int n_C = FULL ? 16 * TP : 4;
 };
 
-template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH, bool GIVEN>
+// Wavefronts that share a SIMD get its issue slots oldest first, so of two
+// wavefronts with equal work the younger runs its last tiles alone, at the
+// issue rate of a single wavefront.  With FAIR the priority falls as the
+// wavefront's own tiles are done (3 in the first quarter, then 2, 1, 0): the
+// wavefront that is behind issues first, and those on a SIMD finish close
+// together.
+__device__ __forceinline__ void fair_prio(int64_t done, int64_t total) {
+    const int64_t p = 3 - (4 * done) / total;
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
+template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH, bool GIVEN, bool FAIR = false>
 __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&h)[4],
                                           float &dt_sum_out, float &keep_out,
                                           float *__restrict__ s_dt, float *__restrict__ s_w,
@@ -367,7 +381,9 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
     };
     if (FULL) ckpt_at(t_begin);
 
+    const int64_t n_tiles = (t_end - t_begin + T - 1) / T;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        if (FAIR) fair_prio((t0 - t_begin) / T, n_tiles);
         if (conv) {
             // (a0) the scan input u = act(conv(x)) of this lane's piece: stage
             // the raw inputs, convolve, keep the tile's last 4 inputs for the
@@ -622,8 +638,8 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     const int64_t j = blockIdx.y;
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dt_sum = 0.0f, keep = 0.0f;
-    quad_pass<IO, FULL, VEC, EXT, ZOH, false>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g, s_B,
-                                              s_C);
+    quad_pass<IO, FULL, VEC, EXT, ZOH, false, true>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g,
+                                                    s_B, s_C);
     if (!FULL) {
         const int lane = threadIdx.x;
         const int q = lane >> 4;

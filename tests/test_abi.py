@@ -298,6 +298,35 @@ def test_checkpoint_plan_and_validation(lib):
     assert lib.ssm_scan_fwd_ckpt(ctypes.byref(d17), *base, ok, None) == 3          # N > 16
 
 
+def test_forward_auto_chunking(lib):
+    """The forward's own chunk length (chunk_size 0).  Two-pass chunks (under
+    1024 tokens, d_state <= 16) are chosen so that the busiest SIMD scans the
+    fewest tokens over both passes, with 1024 SIMDs: 2 x 1536 channels are 192
+    wavefronts per chunk, and 16 chunks of 128 put exactly three on every SIMD
+    (11 chunks of 192 would leave 64 SIMDs with a third wavefront for a whole
+    chunk).  Long chunks (one launch) keep two wavefronts per SIMD: 1 x 2048
+    channels x 64 Ki tokens, 16 chunks of 4096.  For d_state > 16 the group
+    path keeps 2048 wavefronts in flight: 4 x 2048 channels x 4096 tokens,
+    N = 256 are 4096 wavefronts, one chunk."""
+    def K(**kw):
+        return lib.ssm_scan_chunk_size(ctypes.byref(desc(**kw)))
+    assert K(batch=2, d_inner=1536, seqlen=2048) == 128
+    assert K(batch=1, d_inner=2048, seqlen=65536, io_dtype=1) == 4096
+    assert K(batch=8, d_inner=5120, seqlen=2048, io_dtype=1) == 2048
+    assert K(batch=4, d_inner=2048, d_state=256, seqlen=4096) == 4096
+    assert K(batch=1, d_inner=64, seqlen=256) == 64
+    # the choice is a minimum of the cost over the candidate chunk counts
+    def cost(k, waves, L):
+        nj = -(-L // k)
+        return k * (5 * -(-waves * nj // 1024) + 4 * -(-waves * (nj - 1) // 1024))
+    for b, dI, L in ((2, 1536, 2048), (1, 768, 4096), (3, 1000, 3000), (1, 16, 300)):
+        waves = b * -(-dI // 16)
+        got = K(batch=b, d_inner=dI, seqlen=L)
+        J0 = -(-2048 // waves)
+        cands = {min(L, max(64, -(-(-(-L // J)) // 16) * 16)) for J in range(J0, 2 * J0 + 1)}
+        assert got in cands and cost(got, waves, L) == min(cost(k, waves, L) for k in cands), (b, dI, L)
+
+
 def test_backward_auto_chunking(lib):
     """The backward's own chunk plan, seen through its workspace size (which
     depends on the chunk count): one round of two wavefronts per SIMD when a

@@ -41,6 +41,20 @@ __device__ __forceinline__ cfloat *as_constant(const float *p) {
 }
 
 // ---------------------------------------------------------------- math
+// Wavefronts that share a SIMD get its issue slots oldest first, so of two
+// wavefronts with equal work the younger runs its last tiles alone, at the
+// issue rate of a single wavefront.  Here the priority falls as the
+// wavefront's own tiles are done (3 in the first quarter, then 2, 1, 0): the
+// wavefront that is behind issues first, and those on a SIMD finish close
+// together.
+__device__ __forceinline__ void fair_prio(int64_t done, int64_t total) {
+    const int64_t p = 3 - (4 * done) / total;
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -224,20 +224,8 @@ struct QuadTile {
     static constexpr int n_C = FULL ? 16 * TP : 4;
 };
 
-// Wavefronts that share a SIMD get its issue slots oldest first, so of two
-// wavefronts with equal work the younger runs its last tiles alone, at the
-// issue rate of a single wavefront.  With FAIR the priority falls as the
-// wavefront's own tiles are done (3 in the first quarter, then 2, 1, 0): the
-// wavefront that is behind issues first, and those on a SIMD finish close
-// together.
-__device__ __forceinline__ void fair_prio(int64_t done, int64_t total) {
-    const int64_t p = 3 - (4 * done) / total;
-    if (p >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (p == 2) __builtin_amdgcn_s_setprio(2);
-    else if (p == 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-}
-
+// FAIR: fair_prio on every tile (the two-pass kernels; the one-launch
+// kernel sets its own priorities).
 template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH, bool GIVEN, bool FAIR = false>
 __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&h)[4],
                                           float &dt_sum_out, float &keep_out,
@@ -986,7 +974,9 @@ __global__ __launch_bounds__(64 * G, SSM_GROUP_WAVES_PER_SIMD) void group_kernel
         }
     }
 
+    const int64_t n_tiles = (t_end - t_begin + T - 1) / T;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+        fair_prio((t0 - t_begin) / T, n_tiles);
         float uc[EPT];
         if (conv) {
             // (a0) the scan input u = act(conv(x)) of this thread's elements

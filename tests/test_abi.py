@@ -331,7 +331,7 @@ def test_backward_auto_chunking(lib):
     """The backward's own chunk plan, seen through its workspace size (which
     depends on the chunk count): one round of two wavefronts per SIMD when a
     chunk's wavefronts fit (2 x 1536 channels: 10 chunks of 208 tokens, not the
-    forward's 11 of 192; 1 x 2048 channels x 64 Ki tokens: 16 of 4096), else
+    forward's 16 of 128; 1 x 2048 channels x 64 Ki tokens: 16 of 4096), else
     the fewest rounds x chunk length (8 x 5120 channels: 4 chunks of 512)."""
     def ws(**kw):
         return lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(**kw)))

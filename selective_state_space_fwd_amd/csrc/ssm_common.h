@@ -40,7 +40,7 @@ __device__ __forceinline__ cfloat *as_constant(const float *p) {
     return (cfloat *)(p);
 }
 
-// ---------------------------------------------------------------- math
+// ---------------------------------------------------------------- scheduling
 // Wavefronts that share a SIMD get its issue slots oldest first, so of two
 // wavefronts with equal work the younger runs its last tiles alone, at the
 // issue rate of a single wavefront.  Here the priority falls as the
@@ -55,6 +55,7 @@ __device__ __forceinline__ void fair_prio(int64_t done, int64_t total) {
     else __builtin_amdgcn_s_setprio(0);
 }
 
+// ---------------------------------------------------------------- math
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -60,10 +60,10 @@ constexpr int64_t kEnoughWaves = 1024;
 // operator and waits for its predecessors') from this chunk length on.
 // Measured on MI355X: at 4096-token chunks (1 x 2048 channels x 64 Ki tokens,
 // bf16) one launch takes 934 us against 974-1029 us for the two passes; at
-// 128-208 token chunks (2 x 1536 channels x 2048 tokens, fp32) it is no
-// faster (68-75 us against 70 us): a SIMD serves its oldest wavefront first,
-// and with short chunks the waits of the younger chunks cost what the
-// saved kernel boundary gains.
+// 128-192 token chunks (2 x 1536 channels x 2048 tokens, fp32) it is slower
+// (74-76 us against 66-70 us for the two passes with fair priorities): with
+// short chunks the waits of the younger chunks cost more than the saved
+// kernel boundary gains.
 constexpr int64_t kFusedMinChunk = 1024;
 constexpr int64_t kMinAutoChunk = 64;
 // Up to this many chunks, each chunk of the quad path folds the transfer

@@ -315,6 +315,12 @@ def test_forward_auto_chunking(lib):
     assert K(batch=8, d_inner=5120, seqlen=2048, io_dtype=1) == 2048
     assert K(batch=4, d_inner=2048, d_state=256, seqlen=4096) == 4096
     assert K(batch=1, d_inner=64, seqlen=256) == 64
+    # one wavefront per chunk: the minimum chunk length, or one chunk when the
+    # sequence is no longer than it
+    assert K(batch=1, d_inner=16, seqlen=16) == 16
+    assert K(batch=1, d_inner=16, seqlen=64) == 64
+    assert K(batch=1, d_inner=16, seqlen=65) == 64
+    assert K(batch=1, d_inner=16, seqlen=1) == 1
     # the choice is a minimum of the cost over the candidate chunk counts
     def cost(k, waves, L):
         nj = -(-L // k)

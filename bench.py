@@ -46,7 +46,12 @@ VALU_PEAK_TFLOPS = 157.3
 # ceiling they can reach is one FMA per lane per clock:
 # 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s.
 VALU_PEAK_NONPACKED_TFLOPS = 78.6
-DEFAULT_CONFIG = "c1_mamba130m_f32"
+DEFAULT_CONFIG = "c3_long_bf16"
+# Chunk lengths a workload names (the long-sequence layer: K in {256, 512,
+# 1024} with the state carried from chunk to chunk), and the one the headline
+# line runs at; the others, and the library's own choice, are timed beside it.
+CONFIG_CHUNKS = {"c3_long_bf16": (256, 512, 1024)}
+HEADLINE_CHUNK = {"c3_long_bf16": 1024}
 CACHE_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 
 # Minimal instruction mix of the method, in FMA-equivalent slots.
@@ -517,13 +522,198 @@ def bench_variant(args, torch, ssm, dev):
     }
 
 
+def kernel_sources_sha():
+    """Digest of the kernel sources: counter figures taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(path, key):
+    """HBM bytes per scan (FETCH_SIZE + WRITE_SIZE of every pass, scaled by
+    the copy calibration) recorded for this workload, or None when none was
+    taken or the kernels have changed since."""
+    try:
+        with open(path) as f:
+            tj = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not tj or not tj.get("bytes_per_scan") or tj.get("src_sha") != kernel_sources_sha():
+        return None
+    return tj["bytes_per_scan"]
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def time_scan_steps(torch, ssm, sets, cfg, chunk, steps, warmup, hip, decode=True):
+    """Warm up, then time `steps` steps, each the scan of one input set (the
+    sets in rotation) followed by one decode token per channel.  Returns the
+    total time and the per-step durations of the scan's kernels, from the
+    events that its first and last dispatch record."""
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    code = 1 if cfg["io_dtype"] == "bf16" else 0
+    ws = torch.empty(max(1, ssm.ssm_scan_workspace_bytes(batch, d_inner, N, L, code, chunk)),
+                     dtype=torch.uint8, device=sets[0]["u"].device)
+    # Each input set's two calls are checked and marshalled once: the binding's
+    # per-call checks would otherwise leave the GPU waiting between short steps.
+    calls = []
+    for t in sets:
+        scan = ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                t["delta_bias"], softplus=True, chunk_size=chunk,
+                                y=t["y"], last_state=t["last"], workspace=ws, prepare=True)
+        dec = ssm.ssm_state_update(t["last"], t["dec_u"], t["dec_delta"], t["A"], t["dec_B"],
+                                   t["dec_C"], t["D"], t["dec_z"], y=t["dec_y"],
+                                   prepare=True) if decode else None
+        calls.append((scan, dec))
+    n_sets = len(sets)
+    ev = hip.create(2 * (steps + warmup))
+
+    def step(i, evs):
+        scan, dec = calls[i % n_sets]
+        scan(evs)
+        if dec is not None:
+            dec()
+
+    for i in range(warmup):
+        step(i, (ev[2 * i], ev[2 * i + 1]))
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    base = 2 * warmup
+    start.record()
+    for i in range(steps):
+        step(i, (ev[base + 2 * i], ev[base + 2 * i + 1]))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kern_ms = [hip.elapsed_ms(ev[base + 2 * i], ev[base + 2 * i + 1]) for i in range(steps)]
+    hip.destroy(ev)
+    del ws
+    return total_ms, kern_ms
+
+
+def bench_scan_step(args, torch, ssm, dev):
+    """The default line: one step = the scan of the workload + one decode
+    token per channel; the roofline covers every pass of the scan."""
+    cfg = dict(ssm_inputs.CONFIGS[args.config])
+    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
+    io, gate = cfg["io_dtype"], cfg["gate"]
+    code = 1 if io == "bf16" else 0
+    set_bytes = algorithmic_bytes(batch, d_inner, N, L, io, gate)
+    n_sets = max(2, min(8, -(-3 * CACHE_BYTES // set_bytes)))
+    named = CONFIG_CHUNKS.get(args.config, ())
+    chunk = args.chunk if args.chunk is not None else HEADLINE_CHUNK.get(args.config, 0)
+
+    # ---- inputs, resident in HBM
+    sets = []
+    for s in range(n_sets):
+        inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=s)
+        dec = ssm_inputs.make_update_inputs(batch, d_inner, N, io_dtype=io, gate=gate,
+                                            seed=1000 + s)
+        t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z")}
+        t.update({k: upload(inp[k], dev) for k in ("A", "D", "delta_bias")})
+        t["y"] = torch.empty_like(t["u"])
+        t["last"] = torch.empty((batch, d_inner, N), dtype=torch.float32, device=dev)
+        t.update({"dec_" + k: upload(dec[k], dev) for k in ("u", "delta", "B", "C", "z")})
+        t["dec_y"] = torch.empty_like(t["dec_u"])
+        sets.append(t)
+        del inp, dec
+    torch.cuda.synchronize()
+    hip = HipEvents()
+
+    total_ms, kern_ms = time_scan_steps(torch, ssm, sets, cfg, chunk, args.steps, args.warmup,
+                                        hip)
+    K = ssm.ssm_scan_chunk_size(batch, d_inner, N, L, code, chunk)
+    plan = ssm.scan_plan(batch, d_inner, N, L, code, chunk)
+
+    ms_per_step = total_ms / args.steps
+    chtok = batch * d_inner * (L + 1)
+    value = chtok / (ms_per_step * 1e-3)
+    kmed = pct(kern_ms, 50)
+    hbm_gbs = set_bytes / (kmed * 1e-3) / 1e9
+    slots = algorithmic_slots(batch, d_inner, N, L, gate)
+    alu_tflops = 2.0 * slots / (kmed * 1e-3) / 1e12
+    traffic = load_traffic(args.traffic_json, f"{args.config}@{chunk}")
+
+    # the other chunk lengths the workload names, and the library's own
+    # choice, each timed briefly beside the headline (scan and decode steps)
+    variants = {}
+    if not args.no_variants:
+        for k in [c for c in named if c != chunk] + ([0] if chunk != 0 else []):
+            vt, vk = time_scan_steps(torch, ssm, sets, cfg, k, max(3, args.steps // 2), 2, hip)
+            variants[str(k) if k else "auto"] = {
+                "chunk": ssm.ssm_scan_chunk_size(batch, d_inner, N, L, code, k),
+                "plan": ssm.scan_plan(batch, d_inner, N, L, code, k),
+                "ms_per_step": vt / max(3, args.steps // 2),
+                "scan_ms_p50": pct(vk, 50),
+                "hbm_frac": set_bytes / (pct(vk, 50) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            }
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: selective scan batch={batch} d_inner={d_inner} "
+                        f"N={N} L={L} {io} I/O (fp32 state and arithmetic)"
+                        f"{' + silu gate' if gate else ''}, chunk {K} ({plan}), then one "
+                        f"decode token per channel",
+            "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L, "io_dtype": io,
+            "gate": gate, "chunk": K, "chunk_requested": chunk, "plan": plan,
+            "input_sets": n_sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": hbm_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": hbm_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": f"the whole scan: every dispatch of ssm_scan_fwd ({plan})",
+            "kernel_ms": kmed,
+            "kernel_ms_p10": pct(kern_ms, 10),
+            "kernel_ms_p90": pct(kern_ms, 90),
+            "kernel_ms_mean": float(np.mean(kern_ms)),
+            "algorithmic_bytes": set_bytes,
+            "alu_tflops": alu_tflops,
+            "alu_frac_nonpacked": alu_tflops / VALU_PEAK_NONPACKED_TFLOPS,
+            "alu_peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
+            "alu_frac_packed": alu_tflops / VALU_PEAK_TFLOPS,
+            "algorithmic_slots": slots,
+        },
+        "chunk_variants": variants,
+        "versions": versions(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(ssm_inputs.CONFIGS))
-    ap.add_argument("--chunk", type=int, default=0, help="chunk size (0 = library choice)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="chunk length (0 = the library's choice; default: the workload's "
+                         "headline chunk length, else the library's choice)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the brief timings of the workload's other chunk lengths")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
@@ -547,6 +737,8 @@ def main():
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     args = ap.parse_args()
 
+    if args.chunk is None and (args.decode or args.backward or args.train or args.variant):
+        args.chunk = 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         sys.exit(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, "
@@ -578,133 +770,7 @@ def main():
     if args.variant:
         print(json.dumps(bench_variant(args, torch, ssm, dev)), flush=True)
         return
-    cfg = dict(ssm_inputs.CONFIGS[args.config])
-    batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
-    io, gate = cfg["io_dtype"], cfg["gate"]
-    set_bytes = algorithmic_bytes(batch, d_inner, N, L, io, gate)
-    n_sets = max(2, min(8, -(-3 * CACHE_BYTES // set_bytes)))
-
-    # ---- inputs, resident in HBM
-    sets = []
-    for s in range(n_sets):
-        inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=gate, seed=s)
-        dec = ssm_inputs.make_update_inputs(batch, d_inner, N, io_dtype=io, gate=gate,
-                                            seed=1000 + s)
-        t = {k: upload(inp[k], dev) for k in ("u", "delta", "B", "C", "z")}
-        t.update({k: upload(inp[k], dev) for k in ("A", "D", "delta_bias")})
-        t["y"] = torch.empty_like(t["u"])
-        t["last"] = torch.empty((batch, d_inner, N), dtype=torch.float32, device=dev)
-        t.update({"dec_" + k: upload(dec[k], dev) for k in ("u", "delta", "B", "C", "z")})
-        t["dec_y"] = torch.empty_like(t["dec_u"])
-        sets.append(t)
-        del inp, dec
-    K = ssm.ssm_scan_chunk_size(batch, d_inner, N, L, 1 if io == "bf16" else 0, args.chunk)
-    ws = torch.empty(max(1, ssm.ssm_scan_workspace_bytes(batch, d_inner, N, L,
-                                                         1 if io == "bf16" else 0, args.chunk)),
-                     dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    hip = HipEvents()
-    ev = hip.create(2 * (args.steps + args.warmup))
-
-    # Each input set's two calls are checked and marshalled once: the step is
-    # tens of microseconds of GPU work, about what the binding's checks cost
-    # on the host, which would otherwise leave the GPU waiting between steps.
-    calls = []
-    for t in sets:
-        scan = ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
-                                t["delta_bias"], softplus=True, chunk_size=args.chunk,
-                                y=t["y"], last_state=t["last"], workspace=ws, prepare=True)
-        dec = ssm.ssm_state_update(t["last"], t["dec_u"], t["dec_delta"], t["A"], t["dec_B"],
-                                   t["dec_C"], t["D"], t["dec_z"], y=t["dec_y"], prepare=True)
-        calls.append((scan, dec))
-
-    def step(i, evs):
-        scan, dec = calls[i % n_sets]
-        scan(evs)
-        dec()
-
-    for i in range(args.warmup):
-        step(i, (ev[2 * i], ev[2 * i + 1]))
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    base = 2 * args.warmup
-    start.record()
-    for i in range(args.steps):
-        step(i, (ev[base + 2 * i], ev[base + 2 * i + 1]))
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    kern_ms = [hip.elapsed_ms(ev[base + 2 * i], ev[base + 2 * i + 1]) for i in range(args.steps)]
-    hip.destroy(ev)
-
-    ms_per_step = total_ms / args.steps
-    chtok = batch * d_inner * (L + 1)
-    value = chtok / (ms_per_step * 1e-3)
-    kavg = float(np.mean(kern_ms))
-    hbm_gbs = set_bytes / (kavg * 1e-3) / 1e9
-    slots = algorithmic_slots(batch, d_inner, N, L, gate)
-    alu_tflops = 2.0 * slots / (kavg * 1e-3) / 1e12
-    J = -(-L // K)
-    if N <= 16 and 1 < J <= 32 and K >= FUSED_MIN_CHUNK:
-        kernel_name = ("quad_fused_kernel: the whole chunked scan (chunk aggregates, fold, "
-                       "y) in one launch")
-    elif N <= 16:
-        kernel_name = "quad_kernel pass writing y (after the chunk-aggregate pass)" if J > 1 \
-            else "quad_kernel pass writing y (one chunk)"
-    else:
-        kernel_name = "group_kernel pass writing y"
-
-    traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            tj = json.load(f).get(args.config)
-        if tj and tj.get("bytes_per_launch") and not tj.get("stale"):
-            traffic = tj["bytes_per_launch"]
-    except (OSError, ValueError):
-        traffic = None
-
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "channel-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{args.config}: selective scan batch={batch} d_inner={d_inner} "
-                        f"N={N} L={L} {io} I/O{' + silu gate' if gate else ''}, then one "
-                        f"decode token per channel",
-            "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L, "io_dtype": io,
-            "gate": gate, "chunk": K, "input_sets": n_sets,
-        },
-        "roofline": {
-            "bound": "alu",
-            "achieved": alu_tflops,
-            "peak": VALU_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": alu_tflops / VALU_PEAK_TFLOPS,
-            "traffic": traffic,
-            "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
-            "frac_nonpacked": alu_tflops / VALU_PEAK_NONPACKED_TFLOPS,
-            "kernel": kernel_name,
-            "kernel_ms": kavg,
-            "algorithmic_slots": slots,
-            "hbm_achieved_gbs": hbm_gbs,
-            "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": set_bytes,
-        },
-        "versions": versions(),
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
-    print(json.dumps(out), flush=True)
+    print(json.dumps(bench_scan_step(args, torch, ssm, dev)), flush=True)
 
 
 if __name__ == "__main__":

@@ -93,10 +93,11 @@ typedef struct ssm_desc {
     void *workspace;          /* scan only: device scratch, >= workspace_bytes */
     size_t workspace_bytes;   /* scan only */
     void *profile_begin;      /* scan only, optional hipEvent_t (timing enabled): when */
-    void *profile_end;        /* both are set, the dispatch of the pass that writes y
-                                 records them at its start and its end, so that
-                                 hipEventElapsedTime gives that kernel's execution
-                                 time (measurement hook) */
+    void *profile_end;        /* both are set, the scan's first kernel dispatch
+                                 records profile_begin at its start and its last
+                                 dispatch profile_end at its end, so that
+                                 hipEventElapsedTime gives the execution time of
+                                 every pass of the scan together (measurement hook) */
     uint32_t flags;           /* SSM_FLAG_* bits; unknown bits: SSM_ERR_UNSUPPORTED */
     uint32_t reserved;        /* must be 0 */
 } ssm_desc;
@@ -129,6 +130,12 @@ size_t ssm_scan_workspace_bytes(const ssm_desc *desc);
  * the library's choice when it is 0); seqlen means a single chunk.  Returns
  * -1 for an invalid descriptor.  Host-only. */
 int64_t ssm_scan_chunk_size(const ssm_desc *desc);
+
+/* The schedule that ssm_scan_fwd runs for this descriptor, as a short
+ * static string (for example "one chunk", or "two passes, 64 chunks, carry
+ * kernel"), for logs and measurements; "invalid" for an invalid
+ * descriptor.  Host-only. */
+const char *ssm_scan_plan(const ssm_desc *desc);
 
 /* Fused selective-scan forward pass.
  *   u, delta       (batch, d_inner, L) io_dtype; delta is the raw step size

@@ -19,7 +19,7 @@ import os
 from pathlib import Path
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_state_update",
-           "ckpt_shape", "PreparedCall", "ssm_scan_workspace_bytes", "ssm_scan_chunk_size",
+           "ckpt_shape", "PreparedCall", "ssm_scan_workspace_bytes", "ssm_scan_chunk_size", "scan_plan",
            "ssm_status_string", "SsmError", "load_library", "LIB_PATH"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libssm.so"
@@ -71,6 +71,8 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_chunk_size.argtypes = [dp]
     lib.ssm_scan_chunk_size.restype = ctypes.c_int64
+    lib.ssm_scan_plan.argtypes = [dp]
+    lib.ssm_scan_plan.restype = ctypes.c_char_p
     lib.ssm_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
@@ -212,6 +214,12 @@ def ssm_scan_chunk_size(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0)
     return int(load_library().ssm_scan_chunk_size(ctypes.byref(d)))
 
 
+def scan_plan(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> str:
+    """The schedule ssm_scan_fwd runs for these shapes (ssm_scan_plan)."""
+    d = make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size)
+    return load_library().ssm_scan_plan(ctypes.byref(d)).decode()
+
+
 # ---------------------------------------------------------------- entry points
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
@@ -237,8 +245,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tr
     prepare: check and marshal everything but launch nothing; return a
     PreparedCall that launches this call each time it is called.
     Returns (y, last_state); last_state is None unless requested.
-    profile_events: optional pair of raw hipEvent_t handles recorded around
-    the pass that writes y.
+    profile_events: optional pair of raw hipEvent_t handles, recorded at the
+    start of the scan's first kernel and the end of its last.
     """
     torch = _torch()
     lib = load_library()

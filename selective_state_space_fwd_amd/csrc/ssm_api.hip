@@ -526,6 +526,15 @@ int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
     return make_plan(desc, &p) == SSM_OK ? p.K : -1;
 }
 
+const char *ssm_scan_plan(const ssm_desc *desc) {
+    Plan p;
+    if (make_plan(desc, &p) != SSM_OK) return "invalid";
+    if (p.J <= 1) return "one chunk";
+    if (p.fused) return "one launch: chunk aggregates, fold and y";
+    if (p.fold) return "two passes: chunk aggregates, then y with the fold";
+    return "two passes and the carry kernel";
+}
+
 ssm_status ssm_scan_fwd_ex(const ssm_desc *desc, const void *u, const void *delta, const float *A,
                            const void *B, const void *C, const float *D, const void *z,
                            const float *delta_bias, int softplus_flag, const float *initial_state,

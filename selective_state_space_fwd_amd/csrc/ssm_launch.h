@@ -50,7 +50,7 @@ struct ScanArgs {
     // the backward pass
     float *ckpt;
     int64_t n_ck;
-    hipEvent_t ev_begin, ev_end;  // optional, around the pass that writes y
+    hipEvent_t ev_begin, ev_end;  // optional: start of the first dispatch, end of the last
 };
 
 // Tokens per backward tile: the spacing of the state checkpoints.

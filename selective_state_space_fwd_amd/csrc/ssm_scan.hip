@@ -673,6 +673,16 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
 // Flags hold a 64-bit epoch that is new for every launch, so the workspace
 // needs no clearing between launches (graph capture clears it, see the
 // launch).
+// Wait until this wavefront's stores have completed, before the flag store
+// that announces them.  s_waitcnt alone is not a memory operation to the
+// compiler, so compiler-only fences on both sides keep the operator stores
+// before it and the flag store after it (no cache write-back is emitted).
+__device__ __forceinline__ void publish_wait() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <class IO, bool VEC, bool EXT, bool ZOH>
 __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
     using Q = QuadTile<IO, true>;
@@ -706,7 +716,7 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
             for (int k = 0; k < 4; ++k) __hip_atomic_store(he + k, h[k], __ATOMIC_RELAXED, kAgent);
             if (q == 0) __hip_atomic_store(a.dtsum + cd0 + j, dt_sum, __ATOMIC_RELAXED, kAgent);
         }
-        __builtin_amdgcn_s_waitcnt(0);   // the operator stores are complete
+        publish_wait();   // the operator stores are complete
         if (lane == 0) __hip_atomic_store(flags + j, a.epoch, __ATOMIC_RELAXED, kAgent);
     }
 
@@ -748,7 +758,7 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
                     if (q == 0) __hip_atomic_store(a.dtsum + cd0 + i, sdt, __ATOMIC_RELAXED, kAgent);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            publish_wait();
         }
         // 8 operators at a time: their loads are issued together
         constexpr int kBatch = 8;
@@ -1268,52 +1278,62 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
 }
 
 // ============================================================ launchers
-// The pass that writes y: given both profiling events, the dispatch itself
-// records them (hipExtLaunchKernelGGL), so that their interval is the
-// kernel's own execution, as a profiler's kernel trace measures it, without
-// the queue's event packets around it.
-template <class Kern>
-static void launch_timed(const ScanArgs &a, Kern kernel, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.ev_begin && a.ev_end)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a.ev_begin, a.ev_end, 0, a);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
-}
+// Profiling events (optional, both or neither): the scan's first dispatch
+// records ev_begin at its start and its last dispatch ev_end at its end
+// (hipExtLaunchKernelGGL), so that their interval covers every pass of the
+// scan -- aggregate pass, carry kernel and the pass that writes y -- as a
+// profiler's kernel trace measures them, without event packets in the queue.
+struct Dispatch {
+    hipEvent_t begin = nullptr, end = nullptr;
+    hipStream_t s = nullptr;
+    Dispatch(const ScanArgs &a, hipStream_t st) : s(st) {
+        if (a.ev_begin && a.ev_end) { begin = a.ev_begin; end = a.ev_end; }
+    }
+    template <class Kern, class... Args>
+    void operator()(bool last, Kern kernel, dim3 grid, dim3 block, Args... args) {
+        if (begin || (last && end)) {
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, begin, last ? end : nullptr, 0,
+                                  args...);
+            begin = nullptr;
+        } else {
+            hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+        }
+    }
+};
 
 template <class IO, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
+    Dispatch go(a, s);
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.flags) {
-        launch_timed(a, quad_fused_kernel<IO, VEC, EXT, ZOH>, grid, dim3(64), s);
+        go(true, quad_fused_kernel<IO, VEC, EXT, ZOH>, grid, dim3(64), a);
         return hipGetLastError();
     }
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((quad_kernel<IO, false, VEC, EXT, ZOH>), agrid, dim3(64), 0, s, a);
+        go(false, quad_kernel<IO, false, VEC, EXT, ZOH>, agrid, dim3(64), a);
         if (a.hstart) {   // otherwise every chunk folds its predecessors itself
             const int64_t waves = a.Bsz * a.D * a.G;
-            hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
-                               dim3(256), 0, s, a);
+            go(false, carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), a);
         }
     }
-    launch_timed(a, quad_kernel<IO, true, VEC, EXT, ZOH>, grid, dim3(64), s);
+    go(true, quad_kernel<IO, true, VEC, EXT, ZOH>, grid, dim3(64), a);
     return hipGetLastError();
 }
 
 template <class IO, int GW, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_group(const ScanArgs &a, hipStream_t s) {
+    Dispatch go(a, s);
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.J > 1) {
         const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
-        hipLaunchKernelGGL((group_kernel<IO, GW, false, VEC, EXT, ZOH>), agrid, dim3(64 * GW), 0, s,
-                           a);
+        go(false, group_kernel<IO, GW, false, VEC, EXT, ZOH>, agrid, dim3(64 * GW), a);
         if (a.hstart) {
             const int64_t waves = a.Bsz * a.D * a.G;
-            hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)),
-                               dim3(256), 0, s, a);
+            go(false, carry_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), a);
         }
     }
-    launch_timed(a, group_kernel<IO, GW, true, VEC, EXT, ZOH>, grid, dim3(64 * GW), s);
+    go(true, group_kernel<IO, GW, true, VEC, EXT, ZOH>, grid, dim3(64 * GW), a);
     return hipGetLastError();
 }
 

@@ -23,6 +23,15 @@ def to_f64(t):
     return t.detach().to(torch.float64).cpu().numpy()
 
 
+def to_f32(t):
+    """torch tensor (float32 or bfloat16, any device) -> float32 numpy array
+    (exact for both)."""
+    import torch
+    if t is None:
+        return None
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
 def decoded(inp):
     """Float64 view of a generated input dict, for the oracle."""
     out = {k: ssm_inputs.to_f64(inp.get(k)) for k in ("u", "delta", "B", "C", "z")}
@@ -30,16 +39,27 @@ def decoded(inp):
     return out
 
 
-def floored_err(got, ref):
+def floored_err(got, ref, block=1 << 24):
     """max_i |g_i - r_i| / max(|r_i|, rms(r)): relative error with a floor at
-    the tensor's RMS, so outputs that cross zero do not divide by ~0."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    the tensor's RMS, so outputs that cross zero do not divide by ~0.  Large
+    tensors are taken in blocks of `block` elements (same result)."""
+    got = np.asarray(got).reshape(-1)
+    ref = np.asarray(ref).reshape(-1)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
     if ref.size == 0:
         return 0.0
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    denom = np.maximum(np.abs(ref), rms if rms > 0 else 1e-300)
-    return float(np.max(np.abs(got - ref) / denom))
+    ss = 0.0
+    for i in range(0, ref.size, block):
+        r = ref[i:i + block].astype(np.float64)
+        ss += float(np.dot(r, r))
+    rms = float(np.sqrt(ss / ref.size))
+    floor = rms if rms > 0 else 1e-300
+    worst = 0.0
+    for i in range(0, ref.size, block):
+        r = ref[i:i + block].astype(np.float64)
+        g = got[i:i + block].astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(g - r) / np.maximum(np.abs(r), floor))))
+    return worst
 
 
 # Bar for floating-point parity: float32 I/O 1e-4, bfloat16 I/O (float32 state

@@ -29,7 +29,7 @@ def test_header_declares_expected_entry_points():
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_ex",
               "ssm_scan_fwd_ckpt", "ssm_scan_ckpt_bytes",
               "ssm_scan_bwd_workspace_bytes", "ssm_state_update", "ssm_scan_workspace_bytes",
-              "ssm_scan_chunk_size", "ssm_status_string", "ssm_version"):
+              "ssm_scan_chunk_size", "ssm_scan_plan", "ssm_status_string", "ssm_version"):
         assert n in names
 
 

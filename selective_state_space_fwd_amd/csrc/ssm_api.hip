@@ -36,6 +36,8 @@ struct Plan {
     int quad = 0;         // d_state <= 16: quad-row kernel
     int fold = 0;         // chunks fold their predecessors' operators (no carry kernel)
     int fused = 0;        // one launch: chunks publish operators and wait for each other
+    int tile_ts = 0;      // > 0: in-wave scan (tscan_kernel), chunks of 16 tile_ts tokens in
+                          // sequence on one wavefront per channel, segments of tile_ts tokens
     size_t off_hend = 0, off_dtsum = 0, off_keep = 0, off_hstart = 0, off_flags = 0, bytes = 0;
 };
 
@@ -106,10 +108,24 @@ int64_t quad_auto_chunk(int64_t L, int64_t waves) {
     return best_k;
 }
 
-// fused_ok: the quad path may run as one launch (the forward scan, long
-// chunks); the backward, which reuses the chunk-aggregate pass on its own,
-// passes false.
-ssm_status make_plan(const ssm_desc *d, Plan *p, bool fused_ok = true) {
+// The in-wave scan (tscan_kernel): one wavefront per channel, the time
+// parallelism inside it.  Chosen by the library when one wavefront per 16
+// channels would leave the chip short of wavefronts (so that the serial
+// mapping would need chunks on separate workgroups, scanned twice) while one
+// wavefront per channel gives at least one per SIMD; up to kTsMaxRows
+// channels (about 2.7 rounds of three wavefronts per SIMD), above which two
+// passes over few chunks cost less than the in-wave scan's extra work.
+// Segments of 16 tokens (chunks of 256) hold two wavefronts per SIMD,
+// segments of 8 (chunks of 128) three.
+constexpr int64_t kTsMinRows = 1024;
+constexpr int64_t kTsMaxRows = 8192;
+constexpr int64_t kTsRows16 = 2048;
+
+// fwd: the plan of a forward scan, which may run the chunked quad path as
+// one launch (long chunks) and, for calls without packed sequences, the
+// fused convolution or checkpoints (lean), the in-wave scan.  The
+// backward, which reuses the chunk-aggregate pass on its own, passes false.
+ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = true) {
     const ssm_status st = check_desc(d);
     if (st != SSM_OK) return st;
     if (d->chunk_size < 0 || (d->chunk_size > 0 && d->chunk_size % 16 != 0))
@@ -123,6 +139,21 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fused_ok = true) {
     p->n_cblk = (d->d_inner + 15) / 16;
     if (L == 0 || d->batch * d->d_inner == 0) {
         p->K = L; p->J = L > 0 ? 1 : 0; p->bytes = 0;
+        return SSM_OK;
+    }
+    const int64_t rows = d->batch * d->d_inner;
+    const bool ts_ok = fwd && lean && p->quad;
+    if (ts_ok && (d->chunk_size == 128 || d->chunk_size == 256)) {
+        // chunks of 128 or 256 tokens run in sequence on a wavefront per channel
+        p->tile_ts = d->chunk_size / 16;
+    } else if (ts_ok && d->chunk_size == 0 && d->batch * p->n_cblk < kEnoughWaves &&
+               rows >= kTsMinRows && rows <= kTsMaxRows && L > 64) {
+        p->tile_ts = rows <= kTsRows16 ? 16 : 8;
+    }
+    if (p->tile_ts > 0) {
+        p->K = 16 * p->tile_ts < L ? 16 * p->tile_ts : L;
+        p->J = 1;
+        p->bytes = 0;
         return SSM_OK;
     }
     int64_t K;
@@ -147,7 +178,7 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fused_ok = true) {
     if (p->J > kMaxGridY) return SSM_ERR_UNSUPPORTED;
     if (p->n_cblk * d->batch > static_cast<int64_t>(UINT_MAX)) return SSM_ERR_UNSUPPORTED;
     p->fold = p->J <= kFoldMaxChunks;
-    p->fused = fused_ok && p->quad && p->fold && p->J > 1 && K >= kFusedMinChunk;
+    p->fused = fwd && p->quad && p->fold && p->J > 1 && K >= kFusedMinChunk;
     // workspace layout: the chunk operators and, without folding, the chunk
     // start states; rows of G * 16 floats per (batch, channel, chunk)
     size_t off = 0;
@@ -346,7 +377,8 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
                      const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
                      float *ckpt, ssm_stream_t stream) {
     Plan p;
-    ssm_status st = make_plan(desc, &p);
+    const bool lean = !cu_seqlens && cv.width == 0 && !ckpt;
+    ssm_status st = make_plan(desc, &p, true, lean);
     if (st != SSM_OK) return st;
     const hipStream_t s = stream;
     if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
@@ -428,6 +460,10 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     }
     a.ev_begin = static_cast<hipEvent_t>(desc->profile_begin);
     a.ev_end = static_cast<hipEvent_t>(desc->profile_end);
+    if (p.tile_ts > 0) {
+        a.tile_ts = p.tile_ts;
+        return ssm::launch_tscan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
     return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -517,8 +553,11 @@ ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, co
 extern "C" {
 
 size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
+    // enough for every forward entry point: calls with packed sequences, the
+    // fused convolution or checkpoints may plan chunks where a plain call
+    // runs the in-wave scan, which needs none
     Plan p;
-    return make_plan(desc, &p) == SSM_OK ? p.bytes : 0;
+    return make_plan(desc, &p, true, false) == SSM_OK ? p.bytes : 0;
 }
 
 int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
@@ -529,6 +568,8 @@ int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
 const char *ssm_scan_plan(const ssm_desc *desc) {
     Plan p;
     if (make_plan(desc, &p) != SSM_OK) return "invalid";
+    if (p.tile_ts == 16) return "in-wave scan: chunks of 256 tokens in sequence, 16 segments of 16";
+    if (p.tile_ts == 8) return "in-wave scan: chunks of 128 tokens in sequence, 16 segments of 8";
     if (p.J <= 1) return "one chunk";
     if (p.fused) return "one launch: chunk aggregates, fold and y";
     if (p.fold) return "two passes: chunk aggregates, then y with the fold";

@@ -51,6 +51,9 @@ struct ScanArgs {
     float *ckpt;
     int64_t n_ck;
     hipEvent_t ev_begin, ev_end;  // optional: start of the first dispatch, end of the last
+    // > 0: the in-wave scan with segments of tile_ts tokens (tscan_kernel),
+    // whose launcher sets n_cblk to its own channel blocks
+    int tile_ts;
 };
 
 // Tokens per backward tile: the spacing of the state checkpoints.
@@ -109,6 +112,8 @@ struct UpdateArgs {
 };
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// The in-wave scan (d_state <= 16, no packed sequences or convolution).
+hipError_t launch_tscan(const ScanArgs &a, hipStream_t s);
 // Only the forward chunk-aggregate pass (chunks 0 .. J-2), d_state <= 16.
 hipError_t launch_scan_agg(const ScanArgs &a, hipStream_t s);
 hipError_t launch_update(const UpdateArgs &a, hipStream_t s);

@@ -1,0 +1,554 @@
+// ssm_tscan.hip -- the in-wave time-parallel selective scan (d_state <= 16).
+//
+// Sources (web pages on the Mamba selective scan):
+//   "From FlashAttention to Mamba" (kj168168) -- §三.2: the recurrence
+//     h_t = a_t h_{t-1} + b_t is a prefix scan under the associative
+//     composition (a2, b2) o (a1, b1) = (a1 a2, a2 b1 + b2), computable in
+//     logarithmic depth;
+//   ufo.work article "Mamba hardware-aware operator fusion and selective-scan
+//     parallelisation" -- §1.1 recurrence and discretisation, §2.1 every
+//     element-wise step fused into the one kernel, §3.1 the sequence cut into
+//     chunks that are scanned locally, whose transfer operators are combined
+//     and whose start states are then broadcast;
+//   SSM engineering essay (discosf.com) -- §1.1 skip term D, §1.2 the
+//     zero-order-hold input term, §1.3 softplus step size.
+//
+// When the channels of a call are too few for one wavefront per 16 channels
+// to fill the chip, the serial mapping of quad_kernel needs sequence chunks
+// on separate workgroups, and every chunk but the last is then scanned twice
+// (once for its transfer operator, once for y), every exponential included.
+// This kernel gets the time parallelism inside the wavefront instead, and
+// evaluates each exp(dt A) once:
+//
+//   one wavefront = one channel; lane l holds states 4q .. 4q+3 (q = l / 16,
+//   its row) of time segment s = l % 16.  The sequence is walked in tiles of
+//   K = 16 TS tokens; segment s of a tile is its tokens s TS .. s TS + TS-1.
+//   Per tile:
+//   (a) per-token work, 64 lanes x K/64 tokens: dt = softplus(delta + bias),
+//       w = dt u, D u and silu(z); dt and w go to LDS, D u and silu(z) stay
+//       in the converting lane for (e).  The workgroup's 4 wavefronts (4
+//       channels of one batch row) stage the tile's B and C rows in LDS
+//       together, state-major, one segment row per thread;
+//   (b) local scan: for its TS tokens and 4 states the lane forms
+//       dA = exp2(dt A log2 e) and dBu = w B (times the zero-order-hold
+//       factor), keeps both in VGPRs, and folds them from a zero state into
+//       the segment's operator (a, b): b = dA b + dBu, a = exp(A sum dt);
+//   (c) the inclusive scan of the 16 segment operators of each row with the
+//       composition above: four wave64 DPP steps (row_shr:1, 2, 4, 8);
+//   (d) the state entering each segment: the incoming tile state h_c carried
+//       through the prefix (a h_c + b, shifted one segment by row_shr:1);
+//       the tile's final state, broadcast from segment 15 (row_newbcast:15),
+//       is the next tile's h_c -- the tiles are chunks of K tokens whose
+//       transfer operators carry the state from one to the next;
+//   (e) replay from the VGPRs: h = dA h + dBu and C.h per token; the four
+//       rows' partial sums of 4 tokens meet in a transposing butterfly of
+//       v_permlane16_swap / v_permlane32_swap; y = (C.h + D u) silu(z) is
+//       written by the lane that converted the token, coalesced.
+// Per (token, state) this is 7 FMA-slots of the method's arithmetic (exp
+// counted as 2, the segment fold as 1 more than the serial recurrence) plus
+// about 1 for the scan and carry amortised over the segment, against about
+// 11 for the two-pass chunked schedule.  Each input is read once; there is
+// no workspace.
+#include <type_traits>
+
+#include <hip/hip_ext.h>
+
+#include "ssm_common.h"
+#include "ssm_launch.h"
+#include "ssm_seq.h"
+
+namespace ssm {
+
+namespace {
+
+// DPP within rows of 16 lanes.  `old` is what a lane whose source lies
+// outside its row receives (row_shr) -- the identity of the operand.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float old, float src) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowNewBcast15 = 0x15F;
+
+// One step of the inclusive scan along a row, for the 4 states of a lane:
+// with (a', b') the operator of the lane SHR places back in the row,
+// (a, b) := (a', b') then (a, b), i.e. b += a b', a *= a'.  The DPP operand
+// is folded into v_fmac_f32 / v_mul_f32; with bound_ctrl off a lane whose
+// source lies outside the row is not written and keeps (a, b), which is the
+// composition with the identity.  (The compiler keeps the identity in a
+// register of its own and adds two moves per state and step.)  s_nop 1
+// gives the two wait states that a DPP read needs after a VALU write of the
+// same register; inside the block every DPP source was written at least
+// four instructions earlier.
+#define SSM_TSCAN_STEP(SHR, a, b)                                                          \
+    asm volatile(                                                                          \
+        "s_nop 1\n\t"                                                                       \
+        "v_fmac_f32_dpp %4, %4, %0 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"          \
+        "v_fmac_f32_dpp %5, %5, %1 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"          \
+        "v_fmac_f32_dpp %6, %6, %2 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"          \
+        "v_fmac_f32_dpp %7, %7, %3 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"          \
+        "v_mul_f32_dpp %0, %0, %0 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_mul_f32_dpp %1, %1, %1 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_mul_f32_dpp %2, %2, %2 row_shr:" #SHR " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_mul_f32_dpp %3, %3, %3 row_shr:" #SHR " row_mask:0xf bank_mask:0xf"                 \
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), \
+          "+v"(b[3]))
+
+// NE consecutive elements of a row as raw 32-bit words (two bf16 per word).
+template <class IO, int NE>
+struct Raw {
+    static constexpr int NW = NE * static_cast<int>(sizeof(typename IO::T)) / 4;
+    uint32_t w[NW];
+};
+
+// Load NE elements at token t of a row (base = the row's first element).
+// VEC: one vector access (16-byte pieces); the row length L is a multiple of
+// 16 and the pointer 16-byte aligned, so a run that would pass L is moved
+// back to end at L (its values past L are never used).  Otherwise element
+// loads with the token index clamped to L - 1.
+template <class IO, int NE, bool VEC, bool CLAMP = true>
+__device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ p, size_t base,
+                                         int64_t t, int64_t L, Raw<IO, NE> &r) {
+    using R = Raw<IO, NE>;
+    if (VEC) {
+        const int64_t tc = (!CLAMP || t + NE <= L) ? t : L - NE;
+        const typename IO::T *q = p + base + tc;
+        if constexpr (R::NW % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < R::NW / 4; ++i) {
+                const uint4 v = reinterpret_cast<const uint4 *>(q)[i];
+                r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+            }
+        } else if constexpr (R::NW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(q);
+            r.w[0] = v.x; r.w[1] = v.y;
+        } else {
+            r.w[0] = *reinterpret_cast<const uint32_t *>(q);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int64_t tc = t + i < L ? t + i : L - 1;
+            if constexpr (std::is_same<IO, F32>::value) {
+                r.w[i] = __float_as_uint(p[base + tc]);
+            } else {
+                const uint32_t v = p[base + tc];
+                if (i % 2 == 0) r.w[i / 2] = v; else r.w[i / 2] |= v << 16;
+            }
+        }
+    }
+}
+
+template <class IO, int NE>
+__device__ __forceinline__ void unpack_raw(const Raw<IO, NE> &r, float (&o)[NE]) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        if constexpr (std::is_same<IO, F32>::value)
+            o[i] = __uint_as_float(r.w[i]);
+        else
+            o[i] = (i % 2 == 0) ? __uint_as_float(r.w[i / 2] << 16)
+                                : __uint_as_float(r.w[i / 2] & 0xffff0000u);
+    }
+}
+
+// Store NE values at token t of a row, converting to the I/O type (bf16:
+// round to nearest even); tokens at or past L are not written.
+template <class IO, int NE, bool VEC>
+__device__ __forceinline__ void store_run(typename IO::T *__restrict__ p, size_t base, int64_t t,
+                                          int64_t L, const float (&v)[NE]) {
+    if (VEC && t + NE <= L) {
+        if constexpr (std::is_same<IO, F32>::value) {
+            if constexpr (NE == 4)
+                *reinterpret_cast<float4 *>(p + base + t) = make_float4(v[0], v[1], v[2], v[3]);
+            else if constexpr (NE == 2)
+                *reinterpret_cast<float2 *>(p + base + t) = make_float2(v[0], v[1]);
+            else
+#pragma unroll
+                for (int i = 0; i < NE; ++i) p[base + t + i] = v[i];
+        } else {
+            if constexpr (NE == 4)
+                *reinterpret_cast<uint2 *>(p + base + t) =
+                    make_uint2(Seg<BF16>::pk(v[0], v[1]), Seg<BF16>::pk(v[2], v[3]));
+            else if constexpr (NE == 2)
+                *reinterpret_cast<uint32_t *>(p + base + t) = Seg<BF16>::pk(v[0], v[1]);
+            else
+#pragma unroll
+                for (int i = 0; i < NE; ++i) IO::store(p, base + t + i, v[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NE; ++i)
+            if (t + i < L) IO::store(p, base + t + i, v[i]);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read(const float *p, float (&o)[N]) {
+    static_assert(N % 4 == 0, "LDS runs of whole float4");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + i);
+        o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_write(float *p, const float (&v)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4)
+            *reinterpret_cast<float4 *>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) p[i] = v[i];
+    }
+}
+
+}  // namespace
+
+constexpr int kTsSegs = 16;         // time segments per tile (lanes of a row)
+
+// Wavefronts (channels) per workgroup: the B and C rows of a tile are
+// staged once for all of them.  Segments of 16 tokens: 8 wavefronts, two per
+// SIMD of a CU, the B and C tiles double-buffered (one barrier per tile) and
+// two tiles' inputs in flight for bfloat16 I/O; segments of 8: 4 wavefronts,
+// so that three workgroups fill a CU at three wavefronts per SIMD, with
+// single buffers.
+template <int TS>
+constexpr int ts_waves() { return TS == 16 ? 8 : 4; }
+
+template <class IO, int TS>
+struct TsShape {
+    static constexpr int W = ts_waves<TS>();
+    static constexpr int NBUF = TS == 16 ? 2 : 1;          // B/C tile buffers in LDS
+    static constexpr int PF = (TS == 16 && std::is_same<IO, BF16>::value) ? 2 : 1;   // tiles in flight
+};
+
+// TS: tokens per segment (8 or 16); tiles of 16 TS tokens.
+// Occupancy: TS = 16 keeps 128 VGPRs of dA/dBu (two wavefronts per SIMD),
+// TS = 8 keeps 64 (three per SIMD).
+template <class IO, int TS, bool VEC, bool ZOH>
+__global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_kernel(ScanArgs a) {
+    using IT = typename IO::T;
+    using SH = TsShape<IO, TS>;
+    constexpr int W = SH::W;
+    constexpr int NBUF = SH::NBUF;
+    constexpr int PF = SH::PF;
+    constexpr int S = kTsSegs;
+    constexpr int K = S * TS;           // tokens per tile
+    constexpr int SP = TS + 4;          // LDS segment row, padded (bank spread)
+    constexpr int RS = S * SP;          // LDS row of one state (or channel): the tile
+    constexpr int PT = K / kWave;       // tokens per lane in the per-token stages
+    constexpr int TPR = 4 * W;          // staging threads per state row
+    constexpr int BT = K / TPR;         // tokens of B (and C) per staging thread
+    static_assert(TS % 4 == 0 && PT % 2 == 0 && PT * 4 == TS, "tile shape");
+    static_assert(BT % 4 == 0 && TS % BT == 0, "staging pieces within a segment");
+
+    __shared__ __attribute__((aligned(16))) float sB[NBUF * 16 * RS];
+    __shared__ __attribute__((aligned(16))) float sC[NBUF * 16 * RS];
+    __shared__ __attribute__((aligned(16))) float sDT[W * RS];
+    __shared__ __attribute__((aligned(16))) float sW[W * RS];
+    __shared__ __attribute__((aligned(16))) float sY[W * RS];
+
+    const IT *__restrict__ u = static_cast<const IT *>(a.u);
+    const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
+    const IT *__restrict__ z = static_cast<const IT *>(a.z);
+    const IT *__restrict__ Bm = static_cast<const IT *>(a.B);
+    const IT *__restrict__ Cm = static_cast<const IT *>(a.C);
+    IT *__restrict__ y = static_cast<IT *>(a.y);
+
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;                    // wavefront: channel of the block
+    const int lane = tid & 63;
+    const int q = lane >> 4;                    // row: states 4q .. 4q+3
+    const int s = lane & 15;                    // time segment
+    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t d = static_cast<int64_t>(blockIdx.x % a.n_cblk) * W + wv;
+    const bool ch_ok = d < a.D;                 // wave-uniform
+    const int64_t dc = ch_ok ? d : a.D - 1;
+    const int64_t L = a.L;
+    const bool gate = a.z != nullptr;
+    const size_t rbase = (static_cast<size_t>(b) * a.D + dc) * L;
+
+    // per-token stage: lane covers tokens lane PT .. lane PT + PT-1 of the
+    // tile, in segment lane / 4
+    const int pseg = lane >> 2;
+    const int poff = pseg * SP + (lane & 3) * PT;
+    // B/C staging: thread covers tokens bt0 .. bt0 + BT-1 of state row bn,
+    // inside one segment
+    const int bn = tid / TPR;
+    const int bt0 = (tid % TPR) * BT;
+    const int boff = bn * RS + (bt0 / TS) * SP + bt0 % TS;
+    const bool bn_ok = bn < a.N;
+    const size_t sbase = (static_cast<size_t>(b) * a.N + (bn_ok ? bn : a.N - 1)) * L;
+    if (!bn_ok) {
+        // states n >= N: B = 0 keeps their state at zero (A = 0 there too), so
+        // their C, read from row N - 1, adds nothing; these rows are never
+        // written again
+        float zb[BT];
+#pragma unroll
+        for (int i = 0; i < BT; ++i) zb[i] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NBUF; ++nb) lds_write<BT>(sB + nb * 16 * RS + boff, zb);
+    }
+
+    const float rbias = a.delta_bias ? a.delta_bias[dc] : 0.0f;
+    const float rD = a.Dskip ? a.Dskip[dc] : 0.0f;
+    float A2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int n = 4 * q + k;
+        const float v = a.A[dc * a.N + (n < a.N ? n : a.N - 1)];
+        A2[k] = n < a.N ? v * kLog2e : 0.0f;
+    }
+    // the state entering the tile (the start state at token 0)
+    float hc[4];
+    load_start_state<4>(a, b, dc, ch_ok, 4 * q, hc);
+
+    float *sdt = sDT + wv * RS;
+    float *sw = sW + wv * RS;
+    float *sy = sY + wv * RS;
+
+    // a tile's inputs in registers (raw words), loaded PF tiles ahead
+    struct Regs {
+        Raw<IO, PT> u, d, z;
+        Raw<IO, BT> b, c;
+    };
+    auto load_tile = [&](Regs &r, int64_t t0) {
+        auto go = [&](auto clamp_tag) {
+            constexpr bool CL = decltype(clamp_tag)::value;
+            load_raw<IO, PT, VEC, CL>(u, rbase, t0 + lane * PT, L, r.u);
+            load_raw<IO, PT, VEC, CL>(dl, rbase, t0 + lane * PT, L, r.d);
+            if (gate) load_raw<IO, PT, VEC, CL>(z, rbase, t0 + lane * PT, L, r.z);
+            if (bn_ok) load_raw<IO, BT, VEC, CL>(Bm, sbase, t0 + bt0, L, r.b);
+            load_raw<IO, BT, VEC, CL>(Cm, sbase, t0 + bt0, L, r.c);
+        };
+        // a tile inside the row needs no clamping (wave-uniform)
+        if (VEC && t0 + K <= L) go(std::false_type{}); else go(std::true_type{});
+    };
+
+    // One tile: tokens t0 .. t0 + K-1, inputs in r (which then takes the
+    // inputs of the tile PF tiles later), B and C rows in LDS buffer nb.
+    auto tile = [&](const int64_t t0, Regs &r, const int nb) {
+        float *bB = sB + nb * 16 * RS;
+        float *bC = sC + nb * 16 * RS;
+        // ---- (a) per-token values of this lane's tokens; B and C rows
+        float du[PT], g[PT];
+        {
+            float xu[PT], xd[PT], xz[PT], xdt[PT], xw[PT];
+            unpack_raw<IO, PT>(r.u, xu);
+            unpack_raw<IO, PT>(r.d, xd);
+            if (gate) unpack_raw<IO, PT>(r.z, xz);
+            auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
+                constexpr bool SPL = decltype(sp_tag)::value;
+                constexpr bool GT = decltype(gate_tag)::value;
+                constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+                for (int i = 0; i < PT; ++i) {
+                    const float x = xd[i] + rbias;
+                    float dt = SPL ? softplus_f32(x) : x;
+                    float uu = xu[i];
+                    if (MASK && t0 + lane * PT + i >= L) {   // padding: identity steps
+                        dt = 0.0f;
+                        uu = 0.0f;
+                    }
+                    xdt[i] = dt;
+                    xw[i] = dt * uu;
+                    du[i] = rD * uu;
+                    g[i] = GT ? silu_f32(xz[i]) : 1.0f;
+                }
+            };
+            using T_ = std::true_type;
+            using F_ = std::false_type;
+            if (t0 + K <= L) {   // wave-uniform: a whole tile
+                if (a.softplus) {
+                    if (gate) convert(T_{}, T_{}, F_{}); else convert(T_{}, F_{}, F_{});
+                } else {
+                    if (gate) convert(F_{}, T_{}, F_{}); else convert(F_{}, F_{}, F_{});
+                }
+            } else {
+                if (a.softplus) {
+                    if (gate) convert(T_{}, T_{}, T_{}); else convert(T_{}, F_{}, T_{});
+                } else {
+                    if (gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
+                }
+            }
+            lds_write<PT>(sdt + poff, xdt);
+            lds_write<PT>(sw + poff, xw);
+            float xb[BT], xc[BT];
+            if (bn_ok) {
+                unpack_raw<IO, BT>(r.b, xb);
+                lds_write<BT>(bB + boff, xb);
+            }
+            unpack_raw<IO, BT>(r.c, xc);
+            lds_write<BT>(bC + boff, xc);
+        }
+        // the inputs of the tile PF tiles later, in flight during this one's
+        // scan (addresses are clamped into the row: the same loads on every path)
+        load_tile(r, t0 + PF * K);
+        // with one buffer, every wavefront must be done with the previous
+        // tile's B and C rows before they are overwritten: a barrier before
+        // the writes above (at the end of the previous tile); with two, the
+        // barrier below also orders the writes of the next tile into the
+        // other buffer after every read of it during the previous tile
+        __syncthreads();
+
+        // ---- (b) local scan of the segment from a zero state; dA and dBu stay
+        // in VGPRs for the replay
+        float eA[TS][4], eB[TS][4];
+        float bs[4];
+        float dtsum = 0.0f;
+#pragma unroll
+        for (int g4 = 0; g4 < TS; g4 += 4) {
+            float dt4[4], w4[4], B4[4][4];
+            lds_read<4>(sdt + s * SP + g4, dt4);
+            lds_read<4>(sw + s * SP + g4, w4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) lds_read<4>(bB + (4 * q + k) * RS + s * SP + g4, B4[k]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = g4 + j;
+                dtsum += dt4[j];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float xa = dt4[j] * A2[k];
+                    const float e = exp2_hw(xa);
+                    float v = w4[j] * B4[k][j];
+                    if (ZOH) v *= zoh_phi(xa * kLn2, e);
+                    eA[t][k] = e;
+                    eB[t][k] = v;
+                    bs[k] = t == 0 ? v : __builtin_fmaf(e, bs[k], v);
+                }
+            }
+        }
+
+        // ---- (c) inclusive scan of the segment operators along the row
+        float as[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) as[k] = exp2_hw(A2[k] * dtsum);
+        SSM_TSCAN_STEP(1, as, bs);
+        SSM_TSCAN_STEP(2, as, bs);
+        SSM_TSCAN_STEP(4, as, bs);
+        SSM_TSCAN_STEP(8, as, bs);
+
+        // ---- (d) state entering this segment; the next tile's state
+        float h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float hout = __builtin_fmaf(as[k], hc[k], bs[k]);
+            h[k] = dpp_row<kRowShr1>(hc[k], hout);
+            hc[k] = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(hout), kRowNewBcast15, 0xF, 0xF, true));
+        }
+
+        // ---- (e) replay, C.h, butterfly over the rows; y sums to LDS
+#pragma unroll
+        for (int g4 = 0; g4 < TS; g4 += 4) {
+            float C4[4][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) lds_read<4>(bC + (4 * q + k) * RS + s * SP + g4, C4[k]);
+            float acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = g4 + j;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) h[k] = __builtin_fmaf(eA[t][k], h[k], eB[t][k]);
+                acc[j] = __builtin_fmaf(C4[0][j], h[0], __builtin_fmaf(C4[1][j], h[1],
+                         __builtin_fmaf(C4[2][j], h[2], C4[3][j] * h[3])));
+            }
+            // rows (0,1) and (2,3): even rows keep tokens 0/2, odd rows 1/3;
+            // then halves: rows 0,1 keep tokens 0,1, rows 2,3 tokens 2,3
+            const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0]),
+                                                              __float_as_uint(acc[1]), false, false);
+            const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2]),
+                                                              __float_as_uint(acc[3]), false, false);
+            const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+            const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+            const auto sw32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p01),
+                                                               __float_as_uint(p23), false, false);
+            sy[s * SP + g4 + q] = __uint_as_float(sw32[0]) + __uint_as_float(sw32[1]);
+        }
+
+        // ---- y of this lane's tokens, coalesced
+        {
+            float ys[PT];
+#pragma unroll
+            for (int i = 0; i < PT; i += 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(sy + poff + i);
+                ys[i] = v.x;
+                ys[i + 1] = v.y;
+            }
+#pragma unroll
+            for (int i = 0; i < PT; ++i) ys[i] = (ys[i] + du[i]) * g[i];
+            if (ch_ok) store_run<IO, PT, VEC>(y, rbase, t0 + lane * PT, L, ys);
+        }
+        if (NBUF == 1) __syncthreads();   // every wavefront is done with this tile's B and C
+    };
+
+    Regs r0, r1;
+    load_tile(r0, 0);
+    if (PF == 2) load_tile(r1, K);
+    if (PF == 2) {
+        // two tiles per iteration, one register set each (static indexing);
+        // buffers alternate with the tile
+        for (int64_t t0 = 0; t0 < L; t0 += 2 * K) {
+            tile(t0, r0, 0);
+            if (t0 + K >= L) break;
+            tile(t0 + K, r1, NBUF - 1);
+        }
+    } else {
+        int64_t it = 0;
+        for (int64_t t0 = 0; t0 < L; t0 += K, ++it)
+            tile(t0, r0, NBUF == 2 ? static_cast<int>(it & 1) : 0);
+    }
+
+    // the state after the last token
+    if (a.last_state && ch_ok && s == 0) {
+        float *ls = a.last_state + (static_cast<size_t>(b) * a.D + d) * a.N;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * q + k < a.N) ls[4 * q + k] = hc[k];
+    }
+}
+
+template <class IO, int TS, bool VEC>
+static hipError_t launch_tscan_zoh(const ScanArgs &a0, hipStream_t s) {
+    constexpr int W = TsShape<IO, TS>::W;
+    ScanArgs a = a0;
+    a.n_cblk = (a.D + W - 1) / W;      // workgroups of W channels per batch row
+    if (a.n_cblk * a.Bsz > static_cast<int64_t>(UINT32_MAX)) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz));
+    const dim3 block(64 * W);
+    const bool ev = a.ev_begin && a.ev_end;
+    if (a.zoh) {
+        if (ev) hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, true>), grid, block, 0, s,
+                                      a.ev_begin, a.ev_end, 0, a);
+        else hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, true>), grid, block, 0, s, a);
+    } else {
+        if (ev) hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, false>), grid, block, 0, s,
+                                      a.ev_begin, a.ev_end, 0, a);
+        else hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <class IO>
+static hipError_t launch_tscan_io(const ScanArgs &a, hipStream_t s) {
+    auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool vec = a.L % 16 == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z)) &&
+                     al(a.B) && al(a.C);
+    if (a.tile_ts == 16)
+        return vec ? launch_tscan_zoh<IO, 16, true>(a, s) : launch_tscan_zoh<IO, 16, false>(a, s);
+    if (a.tile_ts == 8)
+        return vec ? launch_tscan_zoh<IO, 8, true>(a, s) : launch_tscan_zoh<IO, 8, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_tscan(const ScanArgs &a, hipStream_t s) {
+    return a.bf16 ? launch_tscan_io<BF16>(a, s) : launch_tscan_io<F32>(a, s);
+}
+
+}  // namespace ssm

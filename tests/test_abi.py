@@ -108,6 +108,37 @@ def test_workspace_and_chunk_plan(lib):
             _al(2 * 64 * 8 * NS * 4) + _al(2 * 64 * 8 * 4) + _al(2 * 8 * 4))
 
 
+def test_in_wave_plan_choice(lib):
+    """Chunks of 128 or 256 tokens requested, or chosen by the library for
+    1024 to 8192 channels, run as the in-wave scan (no workspace for a plain
+    call); the workspace query still covers the chunked plan that calls with
+    packed sequences, the convolution or checkpoints run."""
+    def plan(**kw):
+        d = desc(**kw)
+        return (lib.ssm_scan_plan(ctypes.byref(d)).decode(),
+                lib.ssm_scan_chunk_size(ctypes.byref(d)),
+                lib.ssm_scan_workspace_bytes(ctypes.byref(d)))
+    # the Mamba-130M-shaped layer (3072 channels): chunks of 128
+    p, K, ws = plan(batch=2, d_inner=1536)
+    assert p.startswith("in-wave") and K == 128 and ws > 0
+    # the long sequence (2048 channels): chunks of 256
+    p, K, _ = plan(batch=1, d_inner=2048, seqlen=65536, io_dtype=1)
+    assert p.startswith("in-wave") and K == 256
+    # enough channels for the serial mapping in one chunk
+    assert plan(batch=8, d_inner=5120)[0] == "one chunk"
+    # few channels: chunks on separate workgroups
+    assert plan(batch=1, d_inner=64, seqlen=256)[0].startswith("two passes")
+    assert plan(batch=1, d_inner=512, seqlen=65536)[0].startswith("two passes")
+    # asked for explicitly, at any channel count, also with zero-order hold
+    for k in (128, 256):
+        p, K, _ = plan(chunk_size=k)
+        assert p.startswith("in-wave") and K == k
+        assert plan(chunk_size=k, flags=ssm.SSM_FLAG_ZOH)[0].startswith("in-wave")
+    assert plan(chunk_size=512)[0].startswith("two passes")
+    # d_state above 16: the group kernel
+    assert not plan(d_state=17, chunk_size=256)[0].startswith("in-wave")
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(d_inner=-1), 2),
     (dict(d_state=0), 3), (dict(d_state=257), 3), (dict(io_dtype=7), 3),
@@ -123,7 +154,7 @@ def test_invalid_descriptors(lib, kw, status):
 
 
 def test_null_and_misaligned_arguments(lib):
-    d = desc(chunk_size=256)                # 8 chunks: needs a workspace
+    d = desc(chunk_size=512)                # 4 chunks: needs a workspace
     d.workspace, d.workspace_bytes = 4096, 1 << 30
     ok = 4096
     args = [ok, ok, ok, ok, ok, None, None, None, 1, ok, None, None]
@@ -299,19 +330,24 @@ def test_checkpoint_plan_and_validation(lib):
 
 
 def test_forward_auto_chunking(lib):
-    """The forward's own chunk length (chunk_size 0).  Two-pass chunks (under
-    1024 tokens, d_state <= 16) are chosen so that the busiest SIMD scans the
-    fewest tokens over both passes, with 1024 SIMDs: 2 x 1536 channels are 192
-    wavefronts per chunk, and 16 chunks of 128 put exactly three on every SIMD
-    (11 chunks of 192 would leave 64 SIMDs with a third wavefront for a whole
-    chunk).  Long chunks (one launch) keep two wavefronts per SIMD: 1 x 2048
-    channels x 64 Ki tokens, 16 chunks of 4096.  For d_state > 16 the group
-    path keeps 2048 wavefronts in flight: 4 x 2048 channels x 4096 tokens,
-    N = 256 are 4096 wavefronts, one chunk."""
+    """The forward's own chunk length (chunk_size 0).  With 1024 to 8192
+    channels (d_state <= 16) the in-wave scan runs chunks of 256 tokens (up
+    to 2048 channels, two wavefronts per SIMD) or 128 (three per SIMD).
+    Otherwise, two-pass chunks (under 1024 tokens, d_state <= 16) are chosen
+    so that the busiest SIMD scans the fewest tokens over both passes, with
+    1024 SIMDs.  For d_state > 16 the group path keeps 2048 wavefronts in
+    flight: 4 x 2048 channels x 4096 tokens, N = 256 are 4096 wavefronts, one
+    chunk."""
     def K(**kw):
         return lib.ssm_scan_chunk_size(ctypes.byref(desc(**kw)))
     assert K(batch=2, d_inner=1536, seqlen=2048) == 128
-    assert K(batch=1, d_inner=2048, seqlen=65536, io_dtype=1) == 4096
+    assert K(batch=1, d_inner=2048, seqlen=65536, io_dtype=1) == 256
+    assert K(batch=1, d_inner=1024, seqlen=65536) == 256
+    assert K(batch=4, d_inner=2048, seqlen=2048) == 128
+    # past 8192 channels: two-pass chunks (4 x 2560 channels: 640 wavefronts
+    # per chunk)
+    d = desc(batch=4, d_inner=2560, seqlen=2048)
+    assert lib.ssm_scan_plan(ctypes.byref(d)).decode().startswith("two passes")
     assert K(batch=8, d_inner=5120, seqlen=2048, io_dtype=1) == 2048
     assert K(batch=4, d_inner=2048, d_state=256, seqlen=4096) == 4096
     assert K(batch=1, d_inner=64, seqlen=256) == 64
@@ -325,7 +361,7 @@ def test_forward_auto_chunking(lib):
     def cost(k, waves, L):
         nj = -(-L // k)
         return k * (5 * -(-waves * nj // 1024) + 4 * -(-waves * (nj - 1) // 1024))
-    for b, dI, L in ((2, 1536, 2048), (1, 768, 4096), (3, 1000, 3000), (1, 16, 300)):
+    for b, dI, L in ((1, 768, 4096), (1, 1000, 3000), (4, 2560, 2048), (1, 16, 300)):
         waves = b * -(-dI // 16)
         got = K(batch=b, d_inner=dI, seqlen=L)
         J0 = -(-2048 // waves)

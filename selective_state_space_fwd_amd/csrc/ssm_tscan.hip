@@ -217,14 +217,24 @@ constexpr int kTsSegs = 16;         // time segments per tile (lanes of a row)
 // two tiles' inputs in flight for bfloat16 I/O; segments of 8: 4 wavefronts,
 // so that three workgroups fill a CU at three wavefronts per SIMD, with
 // single buffers.
+#ifndef SSM_TS16_WAVES
+#define SSM_TS16_WAVES 8
+#endif
+#ifndef SSM_TS16_BUFFERS
+#define SSM_TS16_BUFFERS 2
+#endif
+#ifndef SSM_TS16_PREFETCH_BF16
+#define SSM_TS16_PREFETCH_BF16 2
+#endif
 template <int TS>
-constexpr int ts_waves() { return TS == 16 ? 8 : 4; }
+constexpr int ts_waves() { return TS == 16 ? SSM_TS16_WAVES : 4; }
 
 template <class IO, int TS>
 struct TsShape {
     static constexpr int W = ts_waves<TS>();
-    static constexpr int NBUF = TS == 16 ? 2 : 1;          // B/C tile buffers in LDS
-    static constexpr int PF = (TS == 16 && std::is_same<IO, BF16>::value) ? 2 : 1;   // tiles in flight
+    static constexpr int NBUF = TS == 16 ? SSM_TS16_BUFFERS : 1;   // B/C tile buffers in LDS
+    static constexpr int PF = (TS == 16 && std::is_same<IO, BF16>::value) ? SSM_TS16_PREFETCH_BF16
+                                                                          : 1;   // tiles in flight
 };
 
 // TS: tokens per segment (8 or 16); tiles of 16 TS tokens.

@@ -171,19 +171,20 @@ def test_graph_replays_with_new_inputs(dev):
         say(f"graph replay {r}: equal to eager")
 
 
-def test_long_sequence_auto_plan(dev):
+def test_long_sequence_one_launch(dev):
     """The long-sequence workload (1 x 2048 channels, N = 16, 64 Ki tokens,
-    bf16) with the library's own chunking: 16 chunks of 4096 tokens in one
-    launch.  Equal to the independent-chunk launch bit for bit; 64 channels
-    spread over the row against the oracle (the scan of a channel depends
-    only on its own inputs and the shared B, C)."""
+    bf16) in 16 chunks of 4096 tokens: one launch.  Equal to the
+    independent-chunk launch bit for bit; 64 channels spread over the row
+    against the oracle (the scan of a channel depends only on its own inputs
+    and the shared B, C)."""
     import torch
-    assert ssm.ssm_scan_chunk_size(1, 2048, 16, 65536, 1) == 4096
+    K = 4096
+    assert ssm.scan_plan(1, 2048, 16, 65536, 1, K).startswith("one launch")
     inp = ssm_inputs.make_scan_inputs(1, 2048, 16, 65536, io_dtype="bf16", gate=True, seed=0)
     t = {k: to_device(inp.get(k), dev) for k in KEYS}
     args = (t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
-    y1, h1 = ssm.ssm_scan_fwd(*args)
-    y2, h2 = ssm.ssm_scan_fwd(*args, independent_chunks=True)
+    y1, h1 = ssm.ssm_scan_fwd(*args, chunk_size=K)
+    y2, h2 = ssm.ssm_scan_fwd(*args, chunk_size=K, independent_chunks=True)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     f = decoded(inp)

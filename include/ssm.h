@@ -156,6 +156,26 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
                         const float *delta_bias, int softplus_flag, void *y, float *last_state,
                         ssm_stream_t stream);
 
+/* ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, result and errors as ssm_scan_fwd, except that the
+ * descriptor's workspace fields are ignored: the chunked schedules use a
+ * scratch array that the library holds in device memory, one copy of
+ * SSM_NOALLOC_SCRATCH_BYTES (32 MiB) on every GPU it runs on, until the
+ * process ends.  Nothing is allocated by the call.  A descriptor whose plan
+ * needs more than that (ssm_scan_workspace_bytes of a plain call above the
+ * limit, for example 65536 tokens of 2048 channels in chunks of 512) returns
+ * SSM_ERR_WORKSPACE before anything is launched.  All calls on one GPU share
+ * its array: calls that may overlap on one GPU (different streams, or other
+ * host threads) race and must be serialised by the caller; calls in order on
+ * one stream are safe, whatever the array holds from the last call (the
+ * schedules never read state they have not written in the same call). */
+#define SSM_NOALLOC_SCRATCH_BYTES (32u << 20)
+ssm_status ssm_scan_fwd_noalloc(const ssm_desc *desc, const void *u, const void *delta,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const void *z, const float *delta_bias, int softplus_flag,
+                                void *y, float *last_state, ssm_stream_t stream);
+
 /* The same scan with explicit start states and, optionally, several
  * variable-length sequences packed along the token axis (packed-sequence
  * batching with a cu_seqlens offset table, the state reset at every sequence

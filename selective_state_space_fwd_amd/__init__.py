@@ -75,6 +75,9 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_plan.restype = ctypes.c_char_p
     lib.ssm_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                         vp, vp]
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_scan_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
                                     ctypes.c_int64, vp, vp, vp]
     lib.ssm_scan_fwd_ex.restype = ctypes.c_int

@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "ssm_launch.h"
 
@@ -548,6 +549,42 @@ ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, co
     return SSM_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation scratch
+// The workspace of ssm_scan_fwd_noalloc.  Each GPU that the library runs on
+// holds its own copy of this array.  In host code its name is only a
+// host-side stand-in: the device address of each GPU's copy is looked up
+// with hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the scratch array of the GPU that `stream` runs on
+// (the current device for the null stream).
+ssm_status scratch_address(hipStream_t stream, void **out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SSM_ERR_HIP;
+    int dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return SSM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return SSM_ERR_UNSUPPORTED;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (dev != cur && hipSetDevice(dev) != hipSuccess) return SSM_ERR_HIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur && hipSetDevice(cur) != hipSuccess) return SSM_ERR_HIP;
+            if (e != hipSuccess || !p) return SSM_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -629,6 +666,29 @@ ssm_status ssm_scan_fwd(const ssm_desc *desc, const void *u, const void *delta, 
                         ssm_stream_t stream) {
     return ssm_scan_fwd_ex(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
                            nullptr, 0, y, last_state, stream);
+}
+
+ssm_status ssm_scan_fwd_noalloc(const ssm_desc *desc, const void *u, const void *delta,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const void *z, const float *delta_bias, int softplus_flag,
+                                void *y, float *last_state, ssm_stream_t stream) {
+    if (!desc) return SSM_ERR_NULL_ARG;
+    ssm_desc d = *desc;
+    d.workspace = nullptr;
+    d.workspace_bytes = 0;
+    Plan p;
+    const ssm_status st = make_plan(&d, &p);   // the plan of a plain call
+    if (st != SSM_OK) return st;
+    if (p.bytes > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_WORKSPACE;
+    if (p.bytes > 0) {
+        void *ws = nullptr;
+        const ssm_status s2 = scratch_address(stream, &ws);
+        if (s2 != SSM_OK) return s2;
+        d.workspace = ws;
+        d.workspace_bytes = SSM_NOALLOC_SCRATCH_BYTES;
+    }
+    return ssm_scan_fwd(&d, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state,
+                        stream);
 }
 
 ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, const void *delta,

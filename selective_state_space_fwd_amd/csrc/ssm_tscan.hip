@@ -498,21 +498,18 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
         if (NBUF == 1) __syncthreads();   // every wavefront is done with this tile's B and C
     };
 
-    Regs r0, r1;
-    load_tile(r0, 0);
-    if (PF == 2) load_tile(r1, K);
-    if (PF == 2) {
-        // two tiles per iteration, one register set each (static indexing);
-        // buffers alternate with the tile
-        for (int64_t t0 = 0; t0 < L; t0 += 2 * K) {
-            tile(t0, r0, 0);
-            if (t0 + K >= L) break;
-            tile(t0 + K, r1, NBUF - 1);
+    // PF register sets, used in turn: PF tiles per iteration, so that every
+    // set is named statically; the LDS buffers alternate with the tile
+    Regs rs[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_tile(rs[p], p * K);
+    for (int64_t t0 = 0; t0 < L; t0 += PF * K) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int64_t tt = t0 + p * K;
+            if (tt >= L) break;
+            tile(tt, rs[p], NBUF == 2 ? static_cast<int>((tt / K) & 1) : 0);
         }
-    } else {
-        int64_t it = 0;
-        for (int64_t t0 = 0; t0 < L; t0 += K, ++it)
-            tile(t0, r0, NBUF == 2 ? static_cast<int>(it & 1) : 0);
     }
 
     // the state after the last token

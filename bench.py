@@ -179,11 +179,25 @@ def cpu_baseline(cfg, budget_s=12.0):
         passes += 1
         if rows < total_rows and dt < budget_s / 8:
             rows = min(total_rows, rows * 2)
+    # the same oracle on one core: whole channels, one after another, for about
+    # a quarter of the budget
+    one_done, one_spent, c = 0, 0.0, 0
+    while one_spent < budget_s / 4 and c < total_rows:
+        sl = slice(c, c + 1)
+        t0 = time.perf_counter()
+        oracle.scan_fwd(f["u"][:, sl], f["delta"][:, sl], inp["A"][sl], f["B"], f["C"],
+                        inp["D"][sl], None if f["z"] is None else f["z"][:, sl],
+                        inp["delta_bias"][sl], softplus=True, threads=1)
+        one_spent += time.perf_counter() - t0
+        one_done += L
+        c += 1
     return {"value": done_chtok / spent, "unit": "channel-tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{passes} passes over up to {rows} whole channels of batch row 0 "
                       f"({done_chtok // L} channel rows x {L} tokens, N={N}, "
-                      f"{cfg['io_dtype']} inputs), {spent:.1f} s of oracle time"}
+                      f"{cfg['io_dtype']} inputs), {spent:.1f} s of oracle time",
+            "one_core": {"value": one_done / one_spent, "unit": "channel-tokens/s", "cores": 1,
+                         "sample": f"{c} whole channels of batch row 0, {one_spent:.1f} s"}}
 
 
 def bench_decode(args, torch, ssm, dev):

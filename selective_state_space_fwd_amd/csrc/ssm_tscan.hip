@@ -102,18 +102,20 @@ struct Raw {
     uint32_t w[NW];
 };
 
-// Load NE elements at token t of a row (base = the row's first element).
+// Load NE elements at token t of a row (row = the row's first element).
 // VEC: one vector access (16-byte pieces); the row length L is a multiple of
 // 16 and the pointer 16-byte aligned, so a run that would pass L is moved
-// back to end at L (its values past L are never used).  Otherwise element
-// loads with the token index clamped to L - 1.
-template <class IO, int NE, bool VEC, bool CLAMP = true>
-__device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ p, size_t base,
-                                         int64_t t, int64_t L, Raw<IO, NE> &r) {
+// back to end at L (min(t, L - NE): its values past L are never used).  The
+// same instructions run for every tile -- no branch, so that the register
+// sets of the tiles in flight are never merged (a merge copies registers,
+// which waits for every load in flight).  Otherwise element loads with the
+// token index clamped to L - 1.
+template <class IO, int NE, bool VEC>
+__device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ row, int t, int L,
+                                         Raw<IO, NE> &r) {
     using R = Raw<IO, NE>;
     if (VEC) {
-        const int64_t tc = (!CLAMP || t + NE <= L) ? t : L - NE;
-        const typename IO::T *q = p + base + tc;
+        const typename IO::T *q = row + min(t, L - NE);
         if constexpr (R::NW % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < R::NW / 4; ++i) {
@@ -129,11 +131,11 @@ __device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ p, s
     } else {
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
-            const int64_t tc = t + i < L ? t + i : L - 1;
+            const int tc = t + i < L ? t + i : L - 1;
             if constexpr (std::is_same<IO, F32>::value) {
-                r.w[i] = __float_as_uint(p[base + tc]);
+                r.w[i] = __float_as_uint(row[tc]);
             } else {
-                const uint32_t v = p[base + tc];
+                const uint32_t v = row[tc];
                 if (i % 2 == 0) r.w[i / 2] = v; else r.w[i / 2] |= v << 16;
             }
         }
@@ -153,11 +155,16 @@ __device__ __forceinline__ void unpack_raw(const Raw<IO, NE> &r, float (&o)[NE])
 }
 
 // Store NE values at token t of a row, converting to the I/O type (bf16:
-// round to nearest even); tokens at or past L are not written.
+// round to nearest even); tokens at or past L are not written.  VEC: L is a
+// multiple of 16, so a run never straddles L and one predicated vector store
+// serves every lane (the same store instructions on every path keep the
+// compiler's count of memory operations in flight exact, so that a later
+// wait for a tile's loads does not also wait for these stores).
 template <class IO, int NE, bool VEC>
 __device__ __forceinline__ void store_run(typename IO::T *__restrict__ p, size_t base, int64_t t,
                                           int64_t L, const float (&v)[NE]) {
-    if (VEC && t + NE <= L) {
+    if (VEC) {
+        if (t >= L) return;
         if constexpr (std::is_same<IO, F32>::value) {
             if constexpr (NE == 4)
                 *reinterpret_cast<float4 *>(p + base + t) = make_float4(v[0], v[1], v[2], v[3]);
@@ -240,7 +247,9 @@ struct TsShape {
 // TS: tokens per segment (8 or 16); tiles of 16 TS tokens.
 // Occupancy: TS = 16 keeps 128 VGPRs of dA/dBu (two wavefronts per SIMD),
 // TS = 8 keeps 64 (three per SIMD).
-template <class IO, int TS, bool VEC, bool ZOH>
+// GT: with the silu gate (z given); SPL: softplus on the step size.  Both are
+// template flags so that the tile loop holds no branch on them.
+template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL>
 __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using SH = TsShape<IO, TS>;
@@ -280,7 +289,6 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     const bool ch_ok = d < a.D;                 // wave-uniform
     const int64_t dc = ch_ok ? d : a.D - 1;
     const int64_t L = a.L;
-    const bool gate = a.z != nullptr;
     const size_t rbase = (static_cast<size_t>(b) * a.D + dc) * L;
 
     // per-token stage: lane covers tokens lane PT .. lane PT + PT-1 of the
@@ -294,17 +302,6 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     const int boff = bn * RS + (bt0 / TS) * SP + bt0 % TS;
     const bool bn_ok = bn < a.N;
     const size_t sbase = (static_cast<size_t>(b) * a.N + (bn_ok ? bn : a.N - 1)) * L;
-    if (!bn_ok) {
-        // states n >= N: B = 0 keeps their state at zero (A = 0 there too), so
-        // their C, read from row N - 1, adds nothing; these rows are never
-        // written again
-        float zb[BT];
-#pragma unroll
-        for (int i = 0; i < BT; ++i) zb[i] = 0.0f;
-#pragma unroll
-        for (int nb = 0; nb < NBUF; ++nb) lds_write<BT>(sB + nb * 16 * RS + boff, zb);
-    }
-
     const float rbias = a.delta_bias ? a.delta_bias[dc] : 0.0f;
     const float rD = a.Dskip ? a.Dskip[dc] : 0.0f;
     float A2[4];
@@ -327,22 +324,30 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
         Raw<IO, PT> u, d, z;
         Raw<IO, BT> b, c;
     };
+    // row pointers of this lane's pieces (token indices fit in int: L <= 2^25)
+    const IT *u_row = u + rbase;
+    const IT *d_row = dl + rbase;
+    // without a gate z reads u's row again (cached, unused): the same loads on
+    // every path keep the compiler's count of loads in flight exact
+    const IT *z_row = GT ? z + rbase : u_row;
+    const IT *b_row = Bm + sbase;
+    const IT *c_row = Cm + sbase;
+    const int Li = static_cast<int>(L);
     auto load_tile = [&](Regs &r, int64_t t0) {
-        auto go = [&](auto clamp_tag) {
-            constexpr bool CL = decltype(clamp_tag)::value;
-            load_raw<IO, PT, VEC, CL>(u, rbase, t0 + lane * PT, L, r.u);
-            load_raw<IO, PT, VEC, CL>(dl, rbase, t0 + lane * PT, L, r.d);
-            if (gate) load_raw<IO, PT, VEC, CL>(z, rbase, t0 + lane * PT, L, r.z);
-            if (bn_ok) load_raw<IO, BT, VEC, CL>(Bm, sbase, t0 + bt0, L, r.b);
-            load_raw<IO, BT, VEC, CL>(Cm, sbase, t0 + bt0, L, r.c);
-        };
-        // a tile inside the row needs no clamping (wave-uniform)
-        if (VEC && t0 + K <= L) go(std::false_type{}); else go(std::true_type{});
+        const int tl = static_cast<int>(t0) + lane * PT;
+        const int tb = static_cast<int>(t0) + bt0;
+        load_raw<IO, PT, VEC>(u_row, tl, Li, r.u);
+        load_raw<IO, PT, VEC>(d_row, tl, Li, r.d);
+        load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
+        load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
+        load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
     };
 
     // One tile: tokens t0 .. t0 + K-1, inputs in r (which then takes the
     // inputs of the tile PF tiles later), B and C rows in LDS buffer nb.
-    auto tile = [&](const int64_t t0, Regs &r, const int nb) {
+    auto tile = [&](const int64_t t0, Regs &r, const int nb, auto mask_tag) {
+        // MASK: a tile that reaches past L (only the last group of tiles)
+        constexpr bool MASK = decltype(mask_tag)::value;
         float *bB = sB + nb * 16 * RS;
         float *bC = sC + nb * 16 * RS;
         // ---- (a) per-token values of this lane's tokens; B and C rows
@@ -351,48 +356,30 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             float xu[PT], xd[PT], xz[PT], xdt[PT], xw[PT];
             unpack_raw<IO, PT>(r.u, xu);
             unpack_raw<IO, PT>(r.d, xd);
-            if (gate) unpack_raw<IO, PT>(r.z, xz);
-            auto convert = [&](auto sp_tag, auto gate_tag, auto mask_tag) {
-                constexpr bool SPL = decltype(sp_tag)::value;
-                constexpr bool GT = decltype(gate_tag)::value;
-                constexpr bool MASK = decltype(mask_tag)::value;
+            if (GT) unpack_raw<IO, PT>(r.z, xz);
 #pragma unroll
-                for (int i = 0; i < PT; ++i) {
-                    const float x = xd[i] + rbias;
-                    float dt = SPL ? softplus_f32(x) : x;
-                    float uu = xu[i];
-                    if (MASK && t0 + lane * PT + i >= L) {   // padding: identity steps
-                        dt = 0.0f;
-                        uu = 0.0f;
-                    }
-                    xdt[i] = dt;
-                    xw[i] = dt * uu;
-                    du[i] = rD * uu;
-                    g[i] = GT ? silu_f32(xz[i]) : 1.0f;
+            for (int i = 0; i < PT; ++i) {
+                const float x = xd[i] + rbias;
+                float dt = SPL ? softplus_f32(x) : x;
+                float uu = xu[i];
+                if (MASK && t0 + lane * PT + i >= L) {   // padding: identity steps
+                    dt = 0.0f;
+                    uu = 0.0f;
                 }
-            };
-            using T_ = std::true_type;
-            using F_ = std::false_type;
-            if (t0 + K <= L) {   // wave-uniform: a whole tile
-                if (a.softplus) {
-                    if (gate) convert(T_{}, T_{}, F_{}); else convert(T_{}, F_{}, F_{});
-                } else {
-                    if (gate) convert(F_{}, T_{}, F_{}); else convert(F_{}, F_{}, F_{});
-                }
-            } else {
-                if (a.softplus) {
-                    if (gate) convert(T_{}, T_{}, T_{}); else convert(T_{}, F_{}, T_{});
-                } else {
-                    if (gate) convert(F_{}, T_{}, T_{}); else convert(F_{}, F_{}, T_{});
-                }
+                xdt[i] = dt;
+                xw[i] = dt * uu;
+                du[i] = rD * uu;
+                g[i] = GT ? silu_f32(xz[i]) : 1.0f;
             }
             lds_write<PT>(sdt + poff, xdt);
             lds_write<PT>(sw + poff, xw);
+            // branch-free (a branch here would make the compiler wait for
+            // every load in flight): rows n >= N store B = 0
             float xb[BT], xc[BT];
-            if (bn_ok) {
-                unpack_raw<IO, BT>(r.b, xb);
-                lds_write<BT>(bB + boff, xb);
-            }
+            unpack_raw<IO, BT>(r.b, xb);
+#pragma unroll
+            for (int i = 0; i < BT; ++i) xb[i] = bn_ok ? xb[i] : 0.0f;
+            lds_write<BT>(bB + boff, xb);
             unpack_raw<IO, BT>(r.c, xc);
             lds_write<BT>(bC + boff, xc);
         }
@@ -499,17 +486,24 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     };
 
     // PF register sets, used in turn: PF tiles per iteration, so that every
-    // set is named statically; the LDS buffers alternate with the tile
+    // set is named statically; the LDS buffers alternate with the tile.  The
+    // loop runs whole groups of PF tiles only: its body is straight-line (no
+    // padding masks, no exit in the middle), so the compiler's count of loads
+    // in flight stays exact and each tile waits only for its own inputs.  The
+    // last, partial group follows with masks.
     Regs rs[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_tile(rs[p], p * K);
-    for (int64_t t0 = 0; t0 < L; t0 += PF * K) {
+    auto nbuf = [&](int64_t tt) { return NBUF == 2 ? static_cast<int>((tt / K) & 1) : 0; };
+    int64_t t0 = 0;
+    for (; t0 + PF * K <= L; t0 += PF * K) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int64_t tt = t0 + p * K;
-            if (tt >= L) break;
-            tile(tt, rs[p], NBUF == 2 ? static_cast<int>((tt / K) & 1) : 0);
-        }
+        for (int p = 0; p < PF; ++p) tile(t0 + p * K, rs[p], nbuf(t0 + p * K), std::false_type{});
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int64_t tt = t0 + p * K;
+        if (tt < L) tile(tt, rs[p], nbuf(tt), std::true_type{});
     }
 
     // the state after the last token
@@ -521,25 +515,36 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     }
 }
 
+template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL>
+static hipError_t launch_tscan_one(const ScanArgs &a, hipStream_t s) {
+    constexpr int W = TsShape<IO, TS>::W;
+    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz));
+    const dim3 block(64 * W);
+    if (a.ev_begin && a.ev_end)
+        hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL>), grid, block, 0, s,
+                              a.ev_begin, a.ev_end, 0, a);
+    else
+        hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <class IO, int TS, bool VEC>
 static hipError_t launch_tscan_zoh(const ScanArgs &a0, hipStream_t s) {
     constexpr int W = TsShape<IO, TS>::W;
     ScanArgs a = a0;
     a.n_cblk = (a.D + W - 1) / W;      // workgroups of W channels per batch row
     if (a.n_cblk * a.Bsz > static_cast<int64_t>(UINT32_MAX)) return hipErrorInvalidConfiguration;
-    const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz));
-    const dim3 block(64 * W);
-    const bool ev = a.ev_begin && a.ev_end;
+    const bool gt = a.z != nullptr, sp = a.softplus != 0;
     if (a.zoh) {
-        if (ev) hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, true>), grid, block, 0, s,
-                                      a.ev_begin, a.ev_end, 0, a);
-        else hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, true>), grid, block, 0, s, a);
-    } else {
-        if (ev) hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, false>), grid, block, 0, s,
-                                      a.ev_begin, a.ev_end, 0, a);
-        else hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, false>), grid, block, 0, s, a);
+        if (gt) return sp ? launch_tscan_one<IO, TS, VEC, true, true, true>(a, s)
+                          : launch_tscan_one<IO, TS, VEC, true, true, false>(a, s);
+        return sp ? launch_tscan_one<IO, TS, VEC, true, false, true>(a, s)
+                  : launch_tscan_one<IO, TS, VEC, true, false, false>(a, s);
     }
-    return hipGetLastError();
+    if (gt) return sp ? launch_tscan_one<IO, TS, VEC, false, true, true>(a, s)
+                      : launch_tscan_one<IO, TS, VEC, false, true, false>(a, s);
+    return sp ? launch_tscan_one<IO, TS, VEC, false, false, true>(a, s)
+              : launch_tscan_one<IO, TS, VEC, false, false, false>(a, s);
 }
 
 template <class IO>

@@ -39,6 +39,7 @@ struct Plan {
     int fused = 0;        // one launch: chunks publish operators and wait for each other
     int tile_ts = 0;      // > 0: in-wave scan (tscan_kernel), chunks of 16 tile_ts tokens in
                           // sequence on one wavefront per channel, segments of tile_ts tokens
+    int64_t split_full = 0;   // > 0: quad_split_kernel, blocks past this many in two chunks
     size_t off_hend = 0, off_dtsum = 0, off_keep = 0, off_hstart = 0, off_flags = 0, bytes = 0;
 };
 
@@ -156,6 +157,46 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = tr
         p->J = 1;
         p->bytes = 0;
         return SSM_OK;
+    }
+    // One wavefront per 16-channel block, whole sequence, leaves the SIMDs
+    // unevenly loaded when the blocks are not a whole number of rounds: then
+    // the blocks past the last whole round run as two chunks each, on two
+    // wavefronts that fill the next slot of every SIMD (quad_split_kernel).
+    // The first chunk scans its tokens twice (aggregate, then y; about 1.8 y
+    // passes), so it takes 1/2.8 of the sequence and both chunks cost about
+    // the same: a SIMD then scans about 0.64 of a block instead of a whole
+    // one on top of its whole rounds.  Used when that shortens the busiest
+    // SIMD's work by at least a tenth, three wavefronts per SIMD hold the
+    // grid, and rows take whole 16-byte pieces (the element path needs more
+    // registers than three wavefronts per SIMD leave it).
+    const int64_t vw = d->io_dtype == SSM_BF16 ? 8 : 4;
+    if (fwd && lean && p->quad && (d->flags & SSM_FLAG_ZOH) == 0 && d->chunk_size == 0 &&
+        L >= 256 && L % vw == 0) {
+        const int64_t W = d->batch * p->n_cblk;
+        const int64_t rounds = W / kSimds, surplus = W - rounds * kSimds;
+        const int64_t waves = rounds * kSimds + 2 * surplus;
+        const double m0 = static_cast<double>(ceil_div(W, kSimds));
+        const double m1 = static_cast<double>(rounds) + ceil_div(2 * surplus, kSimds) / 2.8 * 1.8;
+        if (rounds >= 1 && surplus > 0 && waves <= 3 * kSimds && m1 < 0.9 * m0) {
+            int64_t k = (L * 10 / 28 + 15) / 16 * 16;
+            if (k < 16) k = 16;
+            p->split_full = rounds * kSimds;
+            p->K = k;
+            p->J = 2;
+            p->fold = 1;
+            const size_t cj = static_cast<size_t>(d->batch) * d->d_inner * 2;
+            size_t off = 0;
+            p->off_hend = off;
+            off += align_up(cj * 16 * sizeof(float));
+            p->off_dtsum = off;
+            off += align_up(cj * sizeof(float));
+            p->off_keep = off;
+            off += align_up(static_cast<size_t>(d->batch) * 2 * sizeof(float));
+            p->off_flags = off;
+            off += align_up(static_cast<size_t>(W) * 2 * sizeof(uint64_t));
+            p->bytes = off;
+            return SSM_OK;
+        }
     }
     int64_t K;
     if (d->chunk_size > 0) {
@@ -437,7 +478,8 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
         a.dtsum = reinterpret_cast<float *>(ws + p.off_dtsum);
         a.keep = reinterpret_cast<float *>(ws + p.off_keep);
         if (!p.fold) a.hstart = reinterpret_cast<float *>(ws + p.off_hstart);
-        if (p.fused) {
+        if (p.fused || p.split_full > 0) {
+            a.n_full = p.split_full;
             a.flags = reinterpret_cast<uint64_t *>(ws + p.off_flags);
             a.epoch = next_epoch();
             // a chunk's aggregate pass takes ~0.1 us per token; wait up to
@@ -453,6 +495,7 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SSM_ERR_HIP;
             if (cs != hipStreamCaptureStatusNone) {
+                // 8-byte flags, cleared as pairs of floats
                 const size_t n = static_cast<size_t>(desc->batch) * p.n_cblk * p.J * 2;
                 if (ssm::launch_fill_zero(reinterpret_cast<float *>(a.flags), n, s) != hipSuccess)
                     return SSM_ERR_HIP;
@@ -592,9 +635,11 @@ extern "C" {
 size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
     // enough for every forward entry point: calls with packed sequences, the
     // fused convolution or checkpoints may plan chunks where a plain call
-    // runs the in-wave scan, which needs none
-    Plan p;
-    return make_plan(desc, &p, true, false) == SSM_OK ? p.bytes : 0;
+    // runs the in-wave scan (none) or the balanced serial walks (their own)
+    Plan plain, other;
+    if (make_plan(desc, &plain, true, true) != SSM_OK) return 0;
+    if (make_plan(desc, &other, true, false) != SSM_OK) return 0;
+    return plain.bytes > other.bytes ? plain.bytes : other.bytes;
 }
 
 int64_t ssm_scan_chunk_size(const ssm_desc *desc) {
@@ -607,6 +652,7 @@ const char *ssm_scan_plan(const ssm_desc *desc) {
     if (make_plan(desc, &p) != SSM_OK) return "invalid";
     if (p.tile_ts == 16) return "in-wave scan: chunks of 256 tokens in sequence, 16 segments of 16";
     if (p.tile_ts == 8) return "in-wave scan: chunks of 128 tokens in sequence, 16 segments of 8";
+    if (p.split_full > 0) return "one chunk, the blocks past the last whole round in two chunks (one launch)";
     if (p.J <= 1) return "one chunk";
     if (p.fused) return "one launch: chunk aggregates, fold and y";
     if (p.fold) return "two passes: chunk aggregates, then y with the fold";

@@ -51,6 +51,10 @@ struct ScanArgs {
     float *ckpt;
     int64_t n_ck;
     hipEvent_t ev_begin, ev_end;  // optional: start of the first dispatch, end of the last
+    // > 0: 16-channel blocks 0 .. n_full-1 walk the whole sequence and each
+    // later block runs as two chunks, tokens 0 .. K-1 and K .. L-1, on two
+    // wavefronts (quad_split_kernel; J = 2 workspace layout, flags, epoch)
+    int64_t n_full;
     // > 0: the in-wave scan with segments of tile_ts tokens (tscan_kernel),
     // whose launcher sets n_cblk to its own channel blocks
     int tile_ts;

@@ -181,13 +181,14 @@ __device__ __forceinline__ float state_step(float dt, float A2, float h, float w
 // 16-byte piece of each of u, delta, z, B and C per tile, one tile ahead.
 // Per tile:
 //  (a) convert the lane's pieces (dt = softplus(delta + bias), w = dt u,
-//      du = D u, g = silu(z); B and C widened to fp32, states n >= N zeroed)
-//      into LDS rows padded to T + 4 floats;
+//      du = D u; B and C widened to fp32, states n >= N zeroed) into LDS
+//      rows padded to T + 4 floats; g = silu(z) stays in the lane's VGPRs;
 //  (b) walk the tile 4 tokens at a time.  ds_read_b128 gives 4 tokens of
 //      dt, of w and of B[4q + (lane % 4)]; B_t[4q + k] enters w B through
 //      the DPP operand row_newbcast:k (lane 16q + k holds state 4q + k), and
 //      C[4q + k] for 4 tokens is one more ds_read_b128 per state;
-//  (c) coalesced 16-byte stores of y.
+//  (c) y = (C h + D u) g from the LDS row and the lane's g, coalesced
+//      16-byte stores.
 // A FULL pass that starts inside the sequence takes its start state either
 // from the carry kernel (h_start) or, when the chunks before it are few, by
 // folding their transfer operators itself: h = exp(A sum dt) h + h_end, in
@@ -219,18 +220,25 @@ struct QuadTile {
     // tile when the scan input is computed by the causal convolution
     static constexpr int n_w = QC * TP + 4;
     static constexpr int n_du = FULL ? QC * TP : 4;   // D u, then y
-    static constexpr int n_g = FULL ? QC * TP : 4;    // silu(z)
     static constexpr int n_B = 16 * TP;               // state-major
     static constexpr int n_C = FULL ? 16 * TP : 4;
 };
 
+// Token range of chunk j on the uniform chunking: j K .. min(j K + K, L).
+__device__ __forceinline__ int64_t chunk_end(const ScanArgs &a, int64_t j) {
+    return j * a.K + a.K < a.L ? j * a.K + a.K : a.L;
+}
+
 // FAIR: fair_prio on every tile (the two-pass kernels; the one-launch
 // kernel sets its own priorities).
+// blk: the 16-channel block (batch row blk / n_cblk); chunk j covers tokens
+// t_begin .. t_end - 1 (j K .. min(j K + K, L) on the uniform chunking).
 template <class IO, bool FULL, bool VEC, bool EXT, bool ZOH, bool GIVEN, bool FAIR = false>
-__device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&h)[4],
+__device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_t j,
+                                          int64_t t_begin, int64_t t_end, float (&h)[4],
                                           float &dt_sum_out, float &keep_out,
                                           float *__restrict__ s_dt, float *__restrict__ s_w,
-                                          float *__restrict__ s_du, float *__restrict__ s_g,
+                                          float *__restrict__ s_du,
                                           float *__restrict__ s_B, float *__restrict__ s_C) {
     using IT = typename IO::T;
     using S = Seg<IO>;
@@ -250,13 +258,11 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
     const int lane = threadIdx.x;
     const int c = lane & 15;                        // channel within the block
     const int q = lane >> 4;                        // lane-row: states 4q .. 4q+3
-    const int64_t b = blockIdx.x / a.n_cblk;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * QC;
+    const int64_t b = blk / a.n_cblk;
+    const int64_t d0 = static_cast<int64_t>(blk % a.n_cblk) * QC;
     const int64_t d = d0 + c;
     const bool lane_ok = d < a.D;
     const int64_t L = a.L;
-    const int64_t t_begin = j * a.K;
-    const int64_t t_end = t_begin + a.K < L ? t_begin + a.K : L;
     const bool gate = a.z != nullptr;
 
     // ---- this lane's tile pieces: row r (channel d0 + r, and state r of B
@@ -369,6 +375,10 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
     };
     if (FULL) ckpt_at(t_begin);
 
+    // silu(z) (1 without a gate) of this lane's piece of the tile: the lane
+    // that converts a piece is the one that stores its y, so the gate stays
+    // in registers from (a) to (c)
+    float gk[VW];
     const int64_t n_tiles = (t_end - t_begin + T - 1) / T;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
         if (FAIR) fair_prio((t0 - t_begin) / T, n_tiles);
@@ -444,8 +454,11 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
                 *reinterpret_cast<float4 *>(&s_w[4 + o + i]) = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
                 if (FULL) {
                     *reinterpret_cast<float4 *>(&s_du[o + i]) = make_float4(xdu[i], xdu[i + 1], xdu[i + 2], xdu[i + 3]);
-                    *reinterpret_cast<float4 *>(&s_g[o + i]) = make_float4(xg[i], xg[i + 1], xg[i + 2], xg[i + 3]);
                 }
+            }
+            if (FULL) {
+#pragma unroll
+                for (int i = 0; i < VW; ++i) gk[i] = xg[i];
             }
         };
         using T_ = std::true_type;
@@ -513,7 +526,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
                     acc = __builtin_fmaf(s_C[crow + 3 * TP + k], h[3], acc);
                     acc += __shfl_xor(acc, 16);
                     acc += __shfl_xor(acc, 32);
-                    if (q == 0) s_du[rowc + k] = (acc + s_du[rowc + k]) * s_g[rowc + k];
+                    if (q == 0) s_du[rowc + k] = acc + s_du[rowc + k];
                 } else {
                     dt_sum += dt;
                 }
@@ -566,7 +579,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
                                                                 __float_as_uint(p23), false, false);
                 const float ysum = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // token c4 + q
                 const int o = rowc + c4 + q;
-                s_du[o] = (ysum + s_du[o]) * s_g[o];
+                s_du[o] = ysum + s_du[o];
                 if ((c4 + 4) % kBwdTile == 0 && ckp && t0 + c4 + 4 < t_end) ckpt_at(t0 + c4 + 4);
             }
         }
@@ -581,7 +594,10 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t j, float (&
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(&s_du[o + i]);
-                yo[i] = v.x; yo[i + 1] = v.y; yo[i + 2] = v.z; yo[i + 3] = v.w;
+                yo[i] = v.x * gk[i];
+                yo[i + 1] = v.y * gk[i + 1];
+                yo[i + 2] = v.z * gk[i + 2];
+                yo[i + 3] = v.w * gk[i + 3];
             }
             if (VEC) {
                 if (row_ok && t < t_end)
@@ -620,14 +636,13 @@ __global__ __launch_bounds__(64) void quad_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) float s_dt[Q::n_dt];
     __shared__ __attribute__((aligned(16))) float s_w[Q::n_w];
     __shared__ __attribute__((aligned(16))) float s_du[Q::n_du];
-    __shared__ __attribute__((aligned(16))) float s_g[Q::n_g];
     __shared__ __attribute__((aligned(16))) float s_B[Q::n_B];
     __shared__ __attribute__((aligned(16))) float s_C[Q::n_C];
     const int64_t j = blockIdx.y;
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dt_sum = 0.0f, keep = 0.0f;
-    quad_pass<IO, FULL, VEC, EXT, ZOH, false, true>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g,
-                                                    s_B, s_C);
+    quad_pass<IO, FULL, VEC, EXT, ZOH, false, true>(a, blockIdx.x, j, j * a.K, chunk_end(a, j), h,
+                                                    dt_sum, keep, s_dt, s_w, s_du, s_B, s_C);
     if (!FULL) {
         const int lane = threadIdx.x;
         const int q = lane >> 4;
@@ -689,7 +704,6 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) float s_dt[Q::n_dt];
     __shared__ __attribute__((aligned(16))) float s_w[Q::n_w];
     __shared__ __attribute__((aligned(16))) float s_du[Q::n_du];
-    __shared__ __attribute__((aligned(16))) float s_g[Q::n_g];
     __shared__ __attribute__((aligned(16))) float s_B[Q::n_B];
     __shared__ __attribute__((aligned(16))) float s_C[Q::n_C];
     const int lane = threadIdx.x;
@@ -708,8 +722,8 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
     // when chunks do not wait)
     __builtin_amdgcn_s_setprio(3);
     if (j + 1 < a.J && a.spin_ticks != 0) {
-        quad_pass<IO, false, VEC, EXT, ZOH, false>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g,
-                                                   s_B, s_C);
+        quad_pass<IO, false, VEC, EXT, ZOH, false>(a, blockIdx.x, j, j * a.K, chunk_end(a, j), h,
+                                                   dt_sum, keep, s_dt, s_w, s_du, s_B, s_C);
         if (lane_ok) {
             float *he = a.hend + (cd0 + j) * 16 + 4 * q;
 #pragma unroll
@@ -748,8 +762,9 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
             for (int64_t i = 0; i < j; ++i) {
                 if ((ready >> i) & 1) continue;
                 float e[4], sdt, kp;
-                quad_pass<IO, false, VEC, EXT, ZOH, false>(a, i, e, sdt, kp, s_dt, s_w, s_du, s_g,
-                                                           s_B, s_C);
+                quad_pass<IO, false, VEC, EXT, ZOH, false>(a, blockIdx.x, i, i * a.K,
+                                                           chunk_end(a, i), e, sdt, kp, s_dt, s_w,
+                                                           s_du, s_B, s_C);
                 if (lane_ok) {
                     float *he = a.hend + (cd0 + i) * 16 + 4 * q;
 #pragma unroll
@@ -792,8 +807,89 @@ __global__ __launch_bounds__(64) void quad_fused_kernel(ScanArgs a) {
 
     // 3. y and the final states
     __builtin_amdgcn_s_setprio(0);
-    quad_pass<IO, true, VEC, EXT, ZOH, true>(a, j, h, dt_sum, keep, s_dt, s_w, s_du, s_g, s_B,
-                                             s_C);
+    quad_pass<IO, true, VEC, EXT, ZOH, true>(a, blockIdx.x, j, j * a.K, chunk_end(a, j), h,
+                                             dt_sum, keep, s_dt, s_w, s_du, s_B, s_C);
+}
+
+// Serial walks balanced over the SIMDs (d_state <= 16, no packed sequences,
+// convolution or ZOH).  When the 16-channel blocks number, say, 2.5 per SIMD,
+// one wavefront per block leaves half the SIMDs with a third whole sequence
+// to scan and the other half idle for that long.  Here the first n_full
+// blocks (a whole number of rounds) each walk the whole sequence, and each
+// block after them is cut into two chunks on two wavefronts, which take the
+// next slot on every SIMD:
+//   chunk 0 (tokens 0 .. K-1): the aggregate pass of its tokens at raised
+//     wave priority, published with this launch's epoch (as the one-launch
+//     kernel does), then its y pass;
+//   chunk 1 (tokens K .. L-1): waits for chunk 0's end state (bounded; past
+//     the deadline it computes it itself), then its y pass from it.
+// K is chosen so that both chunks cost about the same (chunk 0 scans its
+// tokens twice).  Workspace: the J = 2 layout of the chunked plans.
+template <class IO, bool VEC>
+__global__ __launch_bounds__(64, 3) void quad_split_kernel(ScanArgs a) {
+    using Q = QuadTile<IO, true>;
+    __shared__ __attribute__((aligned(16))) float s_dt[Q::n_dt];
+    __shared__ __attribute__((aligned(16))) float s_w[Q::n_w];
+    __shared__ __attribute__((aligned(16))) float s_du[Q::n_du];
+    __shared__ __attribute__((aligned(16))) float s_B[Q::n_B];
+    __shared__ __attribute__((aligned(16))) float s_C[Q::n_C];
+    constexpr int kAgent = __HIP_MEMORY_SCOPE_AGENT;
+    const int64_t w = blockIdx.x;
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dt_sum = 0.0f, keep = 0.0f;
+    if (w < a.n_full) {
+        quad_pass<IO, true, VEC, false, false, false, true>(a, w, 0, 0, a.L, h, dt_sum, keep, s_dt,
+                                                            s_w, s_du, s_B, s_C);
+        return;
+    }
+    const int64_t blk = a.n_full + (w - a.n_full) / 2;
+    const int64_t j = (w - a.n_full) % 2;
+    const int lane = threadIdx.x;
+    const int q = lane >> 4;
+    const int64_t b = blk / a.n_cblk;
+    const int64_t d = static_cast<int64_t>(blk % a.n_cblk) * 16 + (lane & 15);
+    const bool lane_ok = d < a.D;
+    const int64_t dcl = lane_ok ? d : a.D - 1;
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * 2;
+    uint64_t *flag = a.flags + static_cast<size_t>(blk) * 2;
+    float *he = a.hend + cd0 * 16 + 4 * q;
+    if (j == 0) {
+        // chunk 0's end state (from the start state), for chunk 1
+        if (a.spin_ticks != 0) {
+            __builtin_amdgcn_s_setprio(3);
+            quad_pass<IO, false, VEC, false, false, false>(a, blk, 0, 0, a.K, h, dt_sum, keep,
+                                                           s_dt, s_w, s_du, s_B, s_C);
+            if (lane_ok) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) __hip_atomic_store(he + k, h[k], __ATOMIC_RELAXED, kAgent);
+            }
+            publish_wait();   // the end state is stored
+            if (lane == 0) __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, kAgent);
+        }
+        quad_pass<IO, true, VEC, false, false, false, true>(a, blk, 0, 0, a.K, h, dt_sum, keep,
+                                                            s_dt, s_w, s_du, s_B, s_C);
+        return;
+    }
+    // chunk 1: chunk 0 begins the sequence, so the state entering chunk 1 is
+    // chunk 0's end state itself
+    bool ready = false;
+    const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + a.spin_ticks;
+    while (a.spin_ticks != 0) {
+        ready = __ballot(lane == 0 && __hip_atomic_load(flag, __ATOMIC_RELAXED, kAgent) == a.epoch) != 0;
+        if (ready || __builtin_amdgcn_s_memrealtime() >= deadline) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the end-state loads stay after the flag's
+    if (ready) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = __hip_atomic_load(he + k, __ATOMIC_RELAXED, kAgent);
+    } else {
+        // not published in time: compute it here (the same bits)
+        quad_pass<IO, false, VEC, false, false, false>(a, blk, 0, 0, a.K, h, dt_sum, keep, s_dt,
+                                                       s_w, s_du, s_B, s_C);
+    }
+    quad_pass<IO, true, VEC, false, false, true, true>(a, blk, 1, a.K, a.L, h, dt_sum, keep, s_dt,
+                                                       s_w, s_du, s_B, s_C);
 }
 
 // ============================================================ group kernel (N > 16)
@@ -1304,6 +1400,12 @@ struct Dispatch {
 template <class IO, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     Dispatch go(a, s);
+    if (!EXT && !ZOH && a.n_full > 0) {
+        const int64_t split = a.n_cblk * a.Bsz - a.n_full;
+        go(true, quad_split_kernel<IO, VEC>, dim3(static_cast<unsigned>(a.n_full + 2 * split)),
+           dim3(64), a);
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J));
     if (a.flags) {
         go(true, quad_fused_kernel<IO, VEC, EXT, ZOH>, grid, dim3(64), a);

@@ -125,7 +125,7 @@ def test_in_wave_plan_choice(lib):
     p, K, _ = plan(batch=1, d_inner=2048, seqlen=65536, io_dtype=1)
     assert p.startswith("in-wave") and K == 256
     # enough channels for the serial mapping in one chunk
-    assert plan(batch=8, d_inner=5120)[0] == "one chunk"
+    assert plan(batch=8, d_inner=4096)[0] == "one chunk"
     # few channels: chunks on separate workgroups
     assert plan(batch=1, d_inner=64, seqlen=256)[0].startswith("two passes")
     assert plan(batch=1, d_inner=512, seqlen=65536)[0].startswith("two passes")
@@ -348,7 +348,14 @@ def test_forward_auto_chunking(lib):
     # per chunk)
     d = desc(batch=4, d_inner=2560, seqlen=2048)
     assert lib.ssm_scan_plan(ctypes.byref(d)).decode().startswith("two passes")
-    assert K(batch=8, d_inner=5120, seqlen=2048, io_dtype=1) == 2048
+    # 8 x 5120 channels: 2560 blocks of 16, 2.5 per SIMD: the 512 past the
+    # second whole round run as two chunks, cut at 1/2.8 of the sequence
+    d = desc(batch=8, d_inner=5120, seqlen=2048, io_dtype=1)
+    assert lib.ssm_scan_plan(ctypes.byref(d)).decode().startswith("one chunk, the blocks past")
+    assert K(batch=8, d_inner=5120, seqlen=2048, io_dtype=1) == 736
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) >= 2560 * 2 * 8
+    # a whole number of rounds: one chunk
+    assert K(batch=8, d_inner=4096, seqlen=2048, io_dtype=1) == 2048
     assert K(batch=4, d_inner=2048, d_state=256, seqlen=4096) == 4096
     assert K(batch=1, d_inner=64, seqlen=256) == 64
     # one wavefront per chunk: the minimum chunk length, or one chunk when the

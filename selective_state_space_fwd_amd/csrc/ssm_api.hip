@@ -267,7 +267,7 @@ struct BwdPlan {
     Plan f;
     int64_t n_tiles = 0;
     size_t off_gend = 0, off_bdtsum = 0, off_ckpt = 0, off_dBp = 0, off_dCp = 0, off_dAp = 0,
-           off_dDp = 0, off_dbp = 0, off_sink = 0, bytes = 0;
+           off_dDp = 0, off_dbp = 0, bytes = 0;
 };
 
 // The backward kernel holds two wavefronts per SIMD (one with ZOH): this many
@@ -346,7 +346,6 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
     p->off_dAp = off; off += align_up(B * D * J * 16 * sizeof(float));
     p->off_dDp = off; off += align_up(B * D * J * sizeof(float));
     p->off_dbp = off; off += align_up(B * D * J * sizeof(float));
-    p->off_sink = off; off += align_up(64 * sizeof(float));
     p->bytes = off;
     return SSM_OK;
 }
@@ -853,7 +852,6 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
     g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
     g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
     g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
-    g.sink = reinterpret_cast<float *>(ws + p.off_sink);
     return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -95,10 +95,33 @@ __device__ __forceinline__ float row_transpose_sum(float v0, float v1, float v2,
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Raw buffer views (a gfx9 buffer resource: base address, byte range, 32-bit
+// data format, no stride).  A load at or past the range returns 0 and a store
+// there is dropped: rows past d_inner or d_state read as zeros, and a lane
+// with nothing to store aims its store at kDrop.  Ranges are at most 2^31
+// bytes, so kDrop lies past every one of them.
+constexpr int kRsrcFormat = 0x00020000;
+constexpr uint32_t kDrop = 0x80000000u;
+using Rsrc = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ Rsrc view(const void *p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
+                                             kRsrcFormat);
+}
+
 template <class IO>
-__device__ __forceinline__ float ld_clamped(const typename IO::T *p, size_t base, int64_t t,
-                                           int64_t t_end) {
-    return IO::load(p, base + (t < t_end ? t : t_end - 1));
+__device__ __forceinline__ float ld_view(Rsrc r, uint32_t off);
+template <>
+__device__ __forceinline__ float ld_view<F32>(Rsrc r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float ld_view<BF16>(Rsrc r, uint32_t off) {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0))
+                           << 16);
+}
+__device__ __forceinline__ void st_view(Rsrc r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
 __device__ __forceinline__ float sigmoid_f32(float x) {
@@ -336,10 +359,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     const int64_t dr = d0 + r;
     const bool row_ok = dr < a.D;
     const int64_t drc = row_ok ? dr : a.D - 1;
-    const size_t rbase = (static_cast<size_t>(b) * a.D + drc) * L;
     const float rbias = (row_ok && a.delta_bias) ? a.delta_bias[drc] : 0.0f;
     const bool st_ok = r < a.N;
-    const size_t sbase = (static_cast<size_t>(b) * a.N + (st_ok ? r : a.N - 1)) * L;
+
+    // Buffer views of the block: rows d0 .. d0 + 15 of u, delta, dy, z and of
+    // du, ddelta, dz (rows past d_inner fall outside); the batch row's B and
+    // C; the block's dB and dC partials.  Offsets in bytes: a lane's tile
+    // piece sits at row r, its output tokens at row c.  (Each view spans at
+    // most 16 rows of SSM_MAX_SEQLEN floats, 2^31 bytes.)
+    const int64_t nrow = a.D - d0 < kQC ? a.D - d0 : kQC;
+    const size_t blk0 = (static_cast<size_t>(b) * a.D + d0) * L;
+    const uint64_t io_bytes = static_cast<uint64_t>(nrow) * L * sizeof(IT);
+    const uint64_t f_bytes = static_cast<uint64_t>(nrow) * L * sizeof(float);
+    const Rsrc v_u = view(u + blk0, io_bytes), v_dl = view(dl + blk0, io_bytes);
+    const Rsrc v_dy = view(dy + blk0, io_bytes);
+    // (without a gate the z loads read u, so that every tile issues the same loads)
+    const Rsrc v_z = view((gate ? z : u) + blk0, io_bytes);
+    const size_t st0 = static_cast<size_t>(b) * a.N * L;
+    const uint64_t st_bytes = static_cast<uint64_t>(a.N) * L * sizeof(IT);
+    const Rsrc v_B = view(Bm + st0, st_bytes), v_C = view(Cm + st0, st_bytes);
+    const Rsrc v_du = view(g.du + blk0, f_bytes), v_dd = view(g.ddelta + blk0, f_bytes);
+    const Rsrc v_dz = gate ? view(g.dz + blk0, f_bytes) : view(g.du, 0);
+    const size_t pblk = (static_cast<size_t>(b) * a.n_cblk + cblk) * 16 * L;
+    const uint64_t p_bytes = static_cast<uint64_t>(16) * L * sizeof(float);
+    const Rsrc v_dBp = view(g.dBp + pblk, p_bytes), v_dCp = view(g.dCp + pblk, p_bytes);
+    const uint32_t o_piece = static_cast<uint32_t>(r * L) * sizeof(IT);
+    const uint32_t o_out = static_cast<uint32_t>(c * L) * sizeof(float);
 
     const int64_t dcl = lane_ok ? d : a.D - 1;
     float A2[4], An[4];
@@ -402,15 +447,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
 
     // ---- forward sweep: the state entering every tile (inputs one tile ahead)
     float fx0 = 0.f, fx1 = 0.f, fu0 = 0.f, fu1 = 0.f, fb0 = 0.f, fb1 = 0.f;
+    // (tokens past the chunk read neighbouring data or zeros: every value
+    // taken from them is masked)
     auto prefetch_fwd = [&](int64_t t0) {
-        const int64_t t = t0 + sc;
-        fx0 = ld_clamped<IO>(dl, rbase, t, t_end);
-        fu0 = ld_clamped<IO>(u, rbase, t, t_end);
-        fb0 = ld_clamped<IO>(Bm, sbase, t, t_end);
+        const uint32_t o = o_piece + static_cast<uint32_t>(t0 + sc) * sizeof(IT);
+        fx0 = ld_view<IO>(v_dl, o);
+        fu0 = ld_view<IO>(v_u, o);
+        fb0 = ld_view<IO>(v_B, o);
         if (kEPL > 1) {
-            fx1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
-            fu1 = ld_clamped<IO>(u, rbase, t + 1, t_end);
-            fb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
+            fx1 = ld_view<IO>(v_dl, o + sizeof(IT));
+            fu1 = ld_view<IO>(v_u, o + sizeof(IT));
+            fb1 = ld_view<IO>(v_B, o + sizeof(IT));
         }
     };
     if (!g.ckpt_given) prefetch_fwd(t_begin);
@@ -428,7 +475,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             const float uu = ok ? ru[i] : 0.0f;
             s_dt[pc(r, sc + i)] = dt;
             s_w[pc(r, sc + i)] = dt * uu;
-            s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
+            s_B[(sc + i) * 16 + r] = (st_ok && t < t_end) ? rb[i] : 0.0f;
         }
         if (ti + 1 < ntile) prefetch_fwd(t0 + kT);
         uint32_t fl;
@@ -463,25 +510,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     float4 qh = make_float4(0.f, 0.f, 0.f, 0.f);
     // Every tile issues the same vector-memory instructions, whatever the
     // gate and however many of its tokens and channels are real (the loads
-    // without a gate read u, the stores of lanes with nothing to store go to
-    // g.sink): the wait for the next tile's prefetch can then count the
-    // tile's stores instead of waiting for all of them to complete.
-    const IT *zsrc = gate ? z : u;
+    // without a gate read u, the stores of lanes with nothing to store are
+    // aimed at kDrop): the wait for the next tile's prefetch can then count
+    // the tile's stores instead of waiting for all of them to complete.
     auto prefetch_rev = [&](int64_t t0) {
-        const int64_t t = t0 + sc;
-        qx0 = ld_clamped<IO>(dl, rbase, t, t_end);
-        qu0 = ld_clamped<IO>(u, rbase, t, t_end);
-        qy0 = ld_clamped<IO>(dy, rbase, t, t_end);
-        qz0 = ld_clamped<IO>(zsrc, rbase, t, t_end);
-        qb0 = ld_clamped<IO>(Bm, sbase, t, t_end);
-        qc0 = ld_clamped<IO>(Cm, sbase, t, t_end);
+        const uint32_t o = o_piece + static_cast<uint32_t>(t0 + sc) * sizeof(IT);
+        qx0 = ld_view<IO>(v_dl, o);
+        qu0 = ld_view<IO>(v_u, o);
+        qy0 = ld_view<IO>(v_dy, o);
+        qz0 = ld_view<IO>(v_z, o);
+        qb0 = ld_view<IO>(v_B, o);
+        qc0 = ld_view<IO>(v_C, o);
         if (kEPL > 1) {
-            qx1 = ld_clamped<IO>(dl, rbase, t + 1, t_end);
-            qu1 = ld_clamped<IO>(u, rbase, t + 1, t_end);
-            qy1 = ld_clamped<IO>(dy, rbase, t + 1, t_end);
-            qz1 = ld_clamped<IO>(zsrc, rbase, t + 1, t_end);
-            qb1 = ld_clamped<IO>(Bm, sbase, t + 1, t_end);
-            qc1 = ld_clamped<IO>(Cm, sbase, t + 1, t_end);
+            qx1 = ld_view<IO>(v_dl, o + sizeof(IT));
+            qu1 = ld_view<IO>(v_u, o + sizeof(IT));
+            qy1 = ld_view<IO>(v_dy, o + sizeof(IT));
+            qz1 = ld_view<IO>(v_z, o + sizeof(IT));
+            qb1 = ld_view<IO>(v_B, o + sizeof(IT));
+            qc1 = ld_view<IO>(v_C, o + sizeof(IT));
         }
         qh = *reinterpret_cast<const float4 *>(ck + (t0 / kT) * 16);
     };
@@ -508,15 +554,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
                 gg = zz * sz;
                 dsl = sz * __builtin_fmaf(zz, 1.0f - sz, 1.0f);
             }
+            // (tokens past the chunk: zeros, whatever the neighbouring data)
+            const bool tok_ok = t < t_end;
             const int o = pc(r, sc + i);
             s_dt[o] = dt;
             s_w[o] = dt * uu;
-            s_do[o] = dyv * gg;
+            s_do[o] = ok ? dyv * gg : 0.0f;
             s_sig[o] = sig;
             s_u[o] = uu;
-            s_ds[o] = dyv * dsl;
-            s_B[(sc + i) * 16 + r] = st_ok ? rb[i] : 0.0f;
-            s_C[(sc + i) * 16 + r] = st_ok ? rc[i] : 0.0f;
+            s_ds[o] = ok ? dyv * dsl : 0.0f;
+            s_B[(sc + i) * 16 + r] = (st_ok && tok_ok) ? rb[i] : 0.0f;
+            s_C[(sc + i) * 16 + r] = (st_ok && tok_ok) ? rc[i] : 0.0f;
         }
     };
     prefetch_rev(t_begin + (ntile - 1) * kT);
@@ -691,10 +739,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             const float du = __builtin_fmaf(dO, Dv_lane, dw * dt);
             // (with ZOH the u term of ddt is already in dd)
             const float ddl = (ZOH ? dd : __builtin_fmaf(dw, uu, dd)) * s_sig[o];
-            const size_t off = (static_cast<size_t>(b) * a.D + d) * L + tok;
-            *(ok ? g.du + off : g.sink) = du;
-            *(ok ? g.ddelta + off : g.sink) = ddl;
-            *((ok && gate) ? g.dz + off : g.sink) = s_ds[o] * s_o[o];
+            const uint32_t off = ok ? o_out + static_cast<uint32_t>(tok) * 4 : kDrop;
+            st_view(v_du, off, du);
+            st_view(v_dd, off, ddl);
+            st_view(v_dz, off, s_ds[o] * s_o[o]);
             dD_acc = ok ? __builtin_fmaf(dO, uu, dD_acc) : dD_acc;
             db_acc = ok ? db_acc + ddl : db_acc;
         }
@@ -703,7 +751,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
         // lane % kT, over channels 8 h .. 8 h + 7, h = lane / 32; the two
         // halves then meet (channels 0-7 + channels 8-15) in every lane.
         static_assert(kT == 8, "channel_sums maps 64 lanes to 4 x kT x 2 jobs");
-        auto channel_sums = [&](float *dstbase) {
+        auto channel_sums = [&](Rsrc dst) {
             const int n4 = (lane / kT) & 3;
             const int t = lane % kT;
             const int h8 = 8 * (lane / 32);
@@ -717,12 +765,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             acc.z = halves_sum(acc.z); acc.w = halves_sum(acc.w);
             const int64_t tok = t0 + t;
             const bool ok = lane < 32 && tok < t_end;
-            float *dst = ok ? dstbase + ((static_cast<size_t>(b) * a.n_cblk + cblk) * 16 + 4 * n4) * L + tok
-                            : g.sink;
-            const int64_t st = ok ? L : 0;
-            dst[0] = acc.x; dst[st] = acc.y; dst[2 * st] = acc.z; dst[3 * st] = acc.w;
+            const uint32_t o = static_cast<uint32_t>(4 * n4 * L + tok) * 4;
+            const uint32_t rs = static_cast<uint32_t>(L) * 4;
+            st_view(dst, ok ? o : kDrop, acc.x);
+            st_view(dst, ok ? o + rs : kDrop, acc.y);
+            st_view(dst, ok ? o + 2 * rs : kDrop, acc.z);
+            st_view(dst, ok ? o + 3 * rs : kDrop, acc.w);
         };
-        channel_sums(g.dBp);
+        channel_sums(v_dBp);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
@@ -731,7 +781,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
                 make_float4(dO * hh[t][0], dO * hh[t][1], dO * hh[t][2], dO * hh[t][3]);
         }
         __syncthreads();
-        channel_sums(g.dCp);
+        channel_sums(v_dCp);
         __syncthreads();
         if (ti > 0) stage(t0 - kT);
     }

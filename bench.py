@@ -230,6 +230,7 @@ def bench_decode(args, torch, ssm, dev):
         if st != 0:
             raise RuntimeError(ssm.ssm_status_string(st))
 
+    settled = settle_clocks(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -271,7 +272,8 @@ def bench_decode(args, torch, ssm, dev):
     return {
         "metric": "single-token state update, channels/sec",
         "value": batch * d_inner / (ms * 1e-3), "unit": "channels/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "steps": settled}, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"decode: {batch} sequences x {d_inner} channels x N={N}, "
@@ -320,6 +322,7 @@ def bench_backward(args, torch, ssm, dev):
                          t["delta_bias"], softplus=True, dlast=dlast, chunk_size=args.chunk,
                          workspace=ws, ckpt=ck)
 
+    settled = settle_clocks(torch, lambda i: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -341,6 +344,7 @@ def bench_backward(args, torch, ssm, dev):
     return {
         "metric": "selective-scan backward channel-tokens/sec", "value": chtok / (ms * 1e-3),
         "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "steps": settled},
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{args.config}: backward of the scan, batch={batch} "
@@ -390,6 +394,7 @@ def bench_train(args, torch, ssm, dev):
         fwd()
         bwd()
 
+    settled = settle_clocks(torch, lambda i: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -408,8 +413,10 @@ def bench_train(args, torch, ssm, dev):
         "metric": "selective-scan training step (forward keeping checkpoints + backward) "
                   "channel-tokens/sec",
         "value": chtok / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "steps": args.steps, "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "steps": settled}, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
         "config": {"workload": f"{args.config}: forward with checkpoints + backward, "
                                f"batch={batch} d_inner={d_inner} N={N} L={L} {io} I/O"
                                f"{' + gate' if gate else ''}",
@@ -490,6 +497,7 @@ def bench_variant(args, torch, ssm, dev):
     torch.cuda.synchronize()
     hip = HipEvents()
     ev = hip.create(2 * (args.steps + args.warmup))
+    settled = settle_clocks(torch, lambda i: calls[i % n_sets](None), args.settle_ms)
     for i in range(args.warmup):
         calls[i % n_sets]((ev[2 * i], ev[2 * i + 1]))
     torch.cuda.synchronize()
@@ -518,6 +526,7 @@ def bench_variant(args, torch, ssm, dev):
     return {
         "metric": f"selective-scan channel-tokens/sec, {v}", "value": chtok / (ms * 1e-3),
         "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "steps": settled},
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{args.config}: selective scan, {what}, batch={batch} "
@@ -530,7 +539,8 @@ def bench_variant(args, torch, ssm, dev):
                      "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
                      "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,
                      "frac_nonpacked": tflops / VALU_PEAK_NONPACKED_TFLOPS,
-                     "kernel": "the pass that writes y (EXT instance)", "kernel_ms": kavg,
+                     "kernel": "the whole call: every dispatch of the scan (first to last, "
+                               "mean of the timed steps)", "kernel_ms": kavg,
                      "algorithmic_slots": slots},
         "versions": versions(),
     }
@@ -565,11 +575,30 @@ def pct(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
-def time_scan_steps(torch, ssm, sets, cfg, chunk, steps, warmup, hip, decode=True):
+def settle_clocks(torch, step, ms):
+    """Untimed calls of step(i) for `ms` of wall time, synchronising every 8,
+    so that the warmup and timed steps that follow run at settled clocks.
+    Returns the number of calls."""
+    n = 0
+    deadline = time.perf_counter() + ms * 1e-3
+    while ms > 0 and time.perf_counter() < deadline:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def time_scan_steps(torch, ssm, sets, cfg, chunk, steps, warmup, hip, decode=True,
+                    settle_ms=0.0):
     """Warm up, then time `steps` steps, each the scan of one input set (the
     sets in rotation) followed by one decode token per channel.  Returns the
-    total time and the per-step durations of the scan's kernels, from the
-    events that its first and last dispatch record."""
+    total time, the per-step durations of the scan's kernels (from the events
+    that its first and last dispatch record) and the number of clock-settling
+    steps: before the warmup steps, untimed steps run for `settle_ms` of wall
+    time, since the GPU's clocks rise over the first few hundred
+    milliseconds of work (the long sequence's scan: 0.86-0.89 ms in the first
+    steps of a fresh process, 0.75-0.78 ms after about a second)."""
     batch, d_inner, N, L = cfg["batch"], cfg["d_inner"], cfg["d_state"], cfg["seqlen"]
     code = 1 if cfg["io_dtype"] == "bf16" else 0
     ws = torch.empty(max(1, ssm.ssm_scan_workspace_bytes(batch, d_inner, N, L, code, chunk)),
@@ -594,6 +623,14 @@ def time_scan_steps(torch, ssm, sets, cfg, chunk, steps, warmup, hip, decode=Tru
         if dec is not None:
             dec()
 
+    settle_steps = 0
+    if settle_ms > 0:
+        deadline = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < deadline:
+            for _ in range(8):
+                step(settle_steps, None)
+                settle_steps += 1
+            torch.cuda.synchronize()
     for i in range(warmup):
         step(i, (ev[2 * i], ev[2 * i + 1]))
     torch.cuda.synchronize()
@@ -608,7 +645,7 @@ def time_scan_steps(torch, ssm, sets, cfg, chunk, steps, warmup, hip, decode=Tru
     kern_ms = [hip.elapsed_ms(ev[base + 2 * i], ev[base + 2 * i + 1]) for i in range(steps)]
     hip.destroy(ev)
     del ws
-    return total_ms, kern_ms
+    return total_ms, kern_ms, settle_steps
 
 
 def bench_scan_step(args, torch, ssm, dev):
@@ -640,8 +677,8 @@ def bench_scan_step(args, torch, ssm, dev):
     torch.cuda.synchronize()
     hip = HipEvents()
 
-    total_ms, kern_ms = time_scan_steps(torch, ssm, sets, cfg, chunk, args.steps, args.warmup,
-                                        hip)
+    total_ms, kern_ms, settle_steps = time_scan_steps(torch, ssm, sets, cfg, chunk, args.steps,
+                                                      args.warmup, hip, settle_ms=args.settle_ms)
     K = ssm.ssm_scan_chunk_size(batch, d_inner, N, L, code, chunk)
     plan = ssm.scan_plan(batch, d_inner, N, L, code, chunk)
 
@@ -659,7 +696,7 @@ def bench_scan_step(args, torch, ssm, dev):
     variants = {}
     if not args.no_variants:
         for k in [c for c in named if c != chunk] + ([0] if chunk != 0 else []):
-            vt, vk = time_scan_steps(torch, ssm, sets, cfg, k, max(3, args.steps // 2), 2, hip)
+            vt, vk, _ = time_scan_steps(torch, ssm, sets, cfg, k, max(3, args.steps // 2), 2, hip)
             variants[str(k) if k else "auto"] = {
                 "chunk": ssm.ssm_scan_chunk_size(batch, d_inner, N, L, code, k),
                 "plan": ssm.scan_plan(batch, d_inner, N, L, code, k),
@@ -675,6 +712,7 @@ def bench_scan_step(args, torch, ssm, dev):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -722,6 +760,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed steps for this much wall time before the warmup steps, so "
+                         "that the timed steps run at settled clocks (0: none)")
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(ssm_inputs.CONFIGS))
     ap.add_argument("--chunk", type=int, default=None,
                     help="chunk length (0 = the library's choice; default: the workload's "

@@ -45,14 +45,16 @@ namespace {
 constexpr int kT = kBwdTile;   // tokens per backward tile
 constexpr int kEPL = kT / 4;   // tokens per lane in a tile piece (16 rows x kT tokens)
 constexpr int kQC = 16;        // channels per wavefront
-// Padded LDS strides (floats) of the per-channel partials, chosen so that
-// their writes (one token, 16 channels of 4 states a pass) and the channel
-// sums' reads (a pass: 8 tokens x 2 state quads of one channel) each touch
-// every bank group once: channel stride 20 floats (16 states + 4), token
-// stride 328 = 8 (mod 64), so the 16 lanes of a read pass land on bank
-// groups 2t + n4.
-constexpr int kGC = 20;
-constexpr int kGT = kQC * kGC + 8;
+// LDS layout of the per-channel partials ([token][channel][state]), chosen so
+// that their writes (a pass: one token, 16 channels, one state quad) and the
+// channel sums' reads (a pass: 8 tokens x 2 state quads of one channel) each
+// touch every group of 4 banks once: token stride 264 floats (66 float4, 2
+// mod 16), channel stride 16 floats, and the state quad q of channel c kept
+// in quad position q ^ ((c / 4) mod 4).
+constexpr int kGT = kQC * 16 + 8;
+__device__ __forceinline__ int gslot(int t, int ch, int quad) {
+    return t * kGT + ch * 16 + 4 * (quad ^ ((ch >> 2) & 3));
+}
 
 // Slot of (channel ch, token t) in the per-channel arrays of a tile: token
 // major, so that the 16 channels a token step reads are 16 consecutive floats
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             p = fmac_bc<t, 2>(p, cc0, cc1, hh[t][2]);
             p = fmac_bc<t, 3>(p, cc0, cc1, hh[t][3]);
             part[t] = p;
-            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+            *reinterpret_cast<float4 *>(&s_g[gslot(t, c, q)]) = make_float4(ev[0], ev[1], ev[2], ev[3]);
         });
         // o_t = C_t . h_t + D u_t: the 4 row partials meet in a transposing
         // butterfly (as in the forward kernel); row q ends with token g4 + q
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             v.w = s_w[pc(c, t)];
             v.dO = s_do[pc(c, t)];
             v.u = ZOH ? s_u[pc(c, t)] : 0.0f;
-            v.E = *reinterpret_cast<const float4 *>(&s_g[t * kGT + c * kGC + 4 * q]);
+            v.E = *reinterpret_cast<const float4 *>(&s_g[gslot(t, c, q)]);
             v.H = t == 0 ? *reinterpret_cast<const float4 *>(&s_h0[4 * lane])
                          : make_float4(0.f, 0.f, 0.f, 0.f);
             return v;
@@ -760,16 +762,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
                          : k == 1 ? fmac_bc<t, 1>(dw, cb0, cb1, dh)
                          : k == 2 ? fmac_bc<t, 2>(dw, cb0, cb1, dh)
                                   : fmac_bc<t, 3>(dw, cb0, cb1, dh);
-                    dd = __builtin_fmaf(da * An[k], at, dd);
-                    dA_acc[k] = __builtin_fmaf(da * at, dt, dA_acc[k]);
+                    // dh h_prev e^{dt A} once for both sums; dd here in units of
+                    // A log2 e (scaled by ln 2 once per token below)
+                    const float xa = da * at;
+                    dd = __builtin_fmaf(xa, A2[k], dd);
+                    dA_acc[k] = __builtin_fmaf(xa, dt, dA_acc[k]);
                 }
                 G[k] = dh * at;
             }
+            if (!ZOH) dd *= kLn2;
             if (st) {
                 store_state_row<4>(g.dh0, a, s_st, d, lane_ok, 4 * q, G);
                 G[0] = G[1] = G[2] = G[3] = 0.0f;
             }
-            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
+            *reinterpret_cast<float4 *>(&s_g[gslot(t, c, q)]) = make_float4(gb[0], gb[1], gb[2], gb[3]);
             rw[t] = dw;
             rd[t] = dd;
             if constexpr (t % 4 == 0) {
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float4 v = *reinterpret_cast<const float4 *>(&s_g[t * kGT + (h8 + k) * kGC + 4 * n4]);
+                const float4 v = *reinterpret_cast<const float4 *>(&s_g[gslot(t, h8 + k, n4)]);
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             acc.x = halves_sum(acc.x); acc.y = halves_sum(acc.y);
@@ -830,7 +836,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
             const float dO = s_do[pc(c, t)];
-            *reinterpret_cast<float4 *>(&s_g[t * kGT + c * kGC + 4 * q]) =
+            *reinterpret_cast<float4 *>(&s_g[gslot(t, c, q)]) =
                 make_float4(dO * hh[t][0], dO * hh[t][1], dO * hh[t][2], dO * hh[t][3]);
         }
         __syncthreads();

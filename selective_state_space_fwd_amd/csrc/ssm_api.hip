@@ -361,9 +361,8 @@ struct BwdGroupPlan {
     ssm_desc sd{};   // the 16-state descriptor of one group
     BwdPlan sub;
     int64_t NG = 0;
-    size_t off_sub = 0, off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_dl = 0, off_du = 0,
-           off_dd = 0, off_dz = 0, off_dA = 0, off_dB = 0, off_dC = 0, off_db = 0, off_dh0 = 0,
-           bytes = 0;
+    size_t off_sub = 0, off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_dl = 0, off_dA = 0,
+           off_dB = 0, off_dC = 0, off_db = 0, off_dh0 = 0, bytes = 0;
 };
 
 ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
@@ -389,9 +388,6 @@ ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
     take(p->off_A, D * 16 * sizeof(float));
     take(p->off_h0, B * D * 16 * sizeof(float));
     take(p->off_dl, B * D * 16 * sizeof(float));
-    take(p->off_du, B * D * L * sizeof(float));
-    take(p->off_dd, B * D * L * sizeof(float));
-    take(p->off_dz, B * D * L * sizeof(float));
     take(p->off_dA, D * 16 * sizeof(float));
     take(p->off_dB, B * 16 * L * sizeof(float));
     take(p->off_dC, B * 16 * L * sizeof(float));
@@ -510,6 +506,90 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
     return ssm::launch_scan(a, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+// The backward for d_state <= 16 (ssm_scan_bwd_ex's own path).  accumulate:
+// du, ddelta and dz are added to what they hold instead of overwritten (the
+// later groups of states of bwd_groups); never with packed sequences.
+ssm_status bwd_single(const ssm_desc *desc, const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z,
+                      const float *delta_bias, int softplus_flag, const float *initial_state,
+                      const int32_t *cu_seqlens, int64_t n_seqs, const float *ckpt,
+                      const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
+                      float *dB, float *dC, float *dD, float *dz, float *ddelta_bias, float *dh0,
+                      int accumulate, ssm_stream_t stream) {
+    BwdPlan p;
+    ssm_status st = make_bwd_plan(desc, &p);
+    if (st != SSM_OK) return st;
+    if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
+    if (cu_seqlens && accumulate) return SSM_ERR_UNSUPPORTED;
+    const int64_t state_rows = cu_seqlens ? n_seqs : desc->batch;
+    if (!dims_ok(state_rows, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
+    if (!aligned(cu_seqlens, 4) || !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
+    const int64_t rows = desc->batch * desc->d_inner;
+    if (rows == 0 || desc->seqlen == 0) {
+        // no tokens: every gradient of a token is empty; those of the
+        // parameters are zero and dh0 = dlast
+        const hipStream_t s = stream;
+        auto zero = [&](float *ptr, size_t n) {
+            return ptr ? ssm::launch_fill_zero(ptr, n, s) : hipSuccess;
+        };
+        const size_t N = static_cast<size_t>(desc->d_state), Dn = static_cast<size_t>(desc->d_inner);
+        hipError_t e = zero(dA, Dn * N);
+        if (e == hipSuccess) e = zero(dD, Dn);
+        if (e == hipSuccess) e = zero(ddelta_bias, Dn);
+        if (e == hipSuccess && dh0) {
+            const size_t n = static_cast<size_t>(state_rows) * Dn * N;
+            e = dlast ? hipMemcpyAsync(dh0, dlast, n * sizeof(float), hipMemcpyDeviceToDevice, s)
+                      : ssm::launch_fill_zero(dh0, n, s);
+        }
+        return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+        return SSM_ERR_NULL_ARG;
+    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
+    if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+        !aligned(z, esz) || !aligned(dy, esz) || !aligned(A, 4) || !aligned(D, 4) ||
+        !aligned(delta_bias, 4) || !aligned(initial_state, 4) || !aligned(dlast, 4) ||
+        !aligned(du, 4) || !aligned(ddelta, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dz, 4) || !aligned(ddelta_bias, 4) ||
+        !aligned(dh0, 4))
+        return SSM_ERR_MISALIGNED;
+    if (z && !dz) return SSM_ERR_NULL_ARG;
+    if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
+    if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
+    char *ws = static_cast<char *>(desc->workspace);
+    const Plan &f = p.f;
+    ScanArgs a{};
+    a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state; a.L = desc->seqlen;
+    a.G = f.G; a.K = f.K; a.J = f.J; a.n_cblk = f.n_cblk; a.quad = f.quad;
+    a.bf16 = desc->io_dtype == SSM_BF16;
+    a.softplus = softplus_flag != 0;
+    a.zoh = (desc->flags & SSM_FLAG_ZOH) != 0;
+    a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.h0 = initial_state;
+    a.cu = cu_seqlens;
+    a.n_seqs = state_rows;
+    ssm::BwdArgs g{};
+    g.accumulate = accumulate;
+    g.dy = dy; g.dlast = dlast; g.du = du; g.ddelta = ddelta; g.dz = dz; g.dA = dA; g.dB = dB;
+    g.dC = dC; g.dD = dD; g.dbias = ddelta_bias; g.dh0 = dh0; g.n_tiles = p.n_tiles;
+    if (f.J > 1) {
+        a.hend = reinterpret_cast<float *>(ws + f.off_hend);
+        a.dtsum = reinterpret_cast<float *>(ws + f.off_dtsum);
+        a.keep = reinterpret_cast<float *>(ws + f.off_keep);
+        g.gend = reinterpret_cast<float *>(ws + p.off_gend);
+        g.bdtsum = reinterpret_cast<float *>(ws + p.off_bdtsum);
+    }
+    // the forward pass's checkpoints (read only), or the workspace's
+    g.ckpt = ckpt ? const_cast<float *>(ckpt) : reinterpret_cast<float *>(ws + p.off_ckpt);
+    g.ckpt_given = ckpt != nullptr;
+    g.dBp = reinterpret_cast<float *>(ws + p.off_dBp);
+    g.dCp = reinterpret_cast<float *>(ws + p.off_dCp);
+    g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
+    g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
+    g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
+    return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, const float *A,
                       const void *B, const void *C, const float *D, const void *z,
                       const float *delta_bias, int softplus_flag, const float *initial_state,
@@ -565,23 +645,17 @@ ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, co
         if (e == hipSuccess && h0g) e = ssm::launch_gather_cols(h0g, initial_state, Bn * Dn, N, n0, s);
         if (e == hipSuccess && dlg) e = ssm::launch_gather_cols(dlg, dlast, Bn * Dn, N, n0, s);
         if (e != hipSuccess) return SSM_ERR_HIP;
+        // group 0 writes du, ddelta, dz and d(bias); each later group adds
+        // its share to du, ddelta and dz in place (old + new, in group
+        // order) and its d(bias) through a small buffer
         const bool first = g == 0;
-        float *du_o = first ? du : at(p.off_du);
-        float *dd_o = first ? ddelta : at(p.off_dd);
-        float *dz_o = z ? (first ? dz : at(p.off_dz)) : nullptr;
         float *db_o = ddelta_bias ? (first ? ddelta_bias : at(p.off_db)) : nullptr;
-        const ssm_status sst = ssm_scan_bwd_ex(
+        const ssm_status sst = bwd_single(
             &sd, u, delta, Ag, Bg, Cg, first ? D : nullptr, z, delta_bias, softplus_flag, h0g,
-            nullptr, 0, nullptr, dy, dlg, du_o, dd_o, dAg, dBg, dCg, first ? dD : nullptr, dz_o,
-            db_o, dh0g, stream);
+            nullptr, 0, nullptr, dy, dlg, du, ddelta, dAg, dBg, dCg, first ? dD : nullptr,
+            z ? dz : nullptr, db_o, dh0g, first ? 0 : 1, stream);
         if (sst != SSM_OK) return sst;
-        const int64_t tok = Bn * Dn * L;
-        if (!first) {
-            e = ssm::launch_accumulate(du, du_o, tok, s);
-            if (e == hipSuccess) e = ssm::launch_accumulate(ddelta, dd_o, tok, s);
-            if (e == hipSuccess && dz_o) e = ssm::launch_accumulate(dz, dz_o, tok, s);
-            if (e == hipSuccess && db_o) e = ssm::launch_accumulate(ddelta_bias, db_o, Dn, s);
-        }
+        if (!first && db_o) e = ssm::launch_accumulate(ddelta_bias, db_o, Dn, s);
         if (e == hipSuccess) e = ssm::launch_scatter_cols(dA, dAg, Dn, N, n0, s);
         if (e == hipSuccess) e = ssm::launch_scatter_rows(dB, dBg, Bn, N, n0, L, s);
         if (e == hipSuccess) e = ssm::launch_scatter_rows(dC, dCg, Bn, N, n0, L, s);
@@ -783,76 +857,9 @@ ssm_status ssm_scan_bwd_ex(const ssm_desc *desc, const void *u, const void *delt
                           initial_state, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
                           dh0, stream);
     }
-    BwdPlan p;
-    ssm_status st = make_bwd_plan(desc, &p);
-    if (st != SSM_OK) return st;
-    if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
-    const int64_t state_rows = cu_seqlens ? n_seqs : desc->batch;
-    if (!dims_ok(state_rows, desc->d_inner, desc->d_state)) return SSM_ERR_BAD_SHAPE;
-    if (!aligned(cu_seqlens, 4) || !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
-    const int64_t rows = desc->batch * desc->d_inner;
-    if (rows == 0 || desc->seqlen == 0) {
-        // no tokens: every gradient of a token is empty; those of the
-        // parameters are zero and dh0 = dlast
-        const hipStream_t s = stream;
-        auto zero = [&](float *ptr, size_t n) {
-            return ptr ? ssm::launch_fill_zero(ptr, n, s) : hipSuccess;
-        };
-        const size_t N = static_cast<size_t>(desc->d_state), Dn = static_cast<size_t>(desc->d_inner);
-        hipError_t e = zero(dA, Dn * N);
-        if (e == hipSuccess) e = zero(dD, Dn);
-        if (e == hipSuccess) e = zero(ddelta_bias, Dn);
-        if (e == hipSuccess && dh0) {
-            const size_t n = static_cast<size_t>(state_rows) * Dn * N;
-            e = dlast ? hipMemcpyAsync(dh0, dlast, n * sizeof(float), hipMemcpyDeviceToDevice, s)
-                      : ssm::launch_fill_zero(dh0, n, s);
-        }
-        return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
-    }
-    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
-        return SSM_ERR_NULL_ARG;
-    const size_t esz = desc->io_dtype == SSM_BF16 ? 2 : 4;
-    if (!aligned(u, esz) || !aligned(delta, esz) || !aligned(B, esz) || !aligned(C, esz) ||
-        !aligned(z, esz) || !aligned(dy, esz) || !aligned(A, 4) || !aligned(D, 4) ||
-        !aligned(delta_bias, 4) || !aligned(initial_state, 4) || !aligned(dlast, 4) ||
-        !aligned(du, 4) || !aligned(ddelta, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
-        !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dz, 4) || !aligned(ddelta_bias, 4) ||
-        !aligned(dh0, 4))
-        return SSM_ERR_MISALIGNED;
-    if (z && !dz) return SSM_ERR_NULL_ARG;
-    if (!desc->workspace || desc->workspace_bytes < p.bytes) return SSM_ERR_WORKSPACE;
-    if (!aligned(desc->workspace, 16)) return SSM_ERR_MISALIGNED;
-    char *ws = static_cast<char *>(desc->workspace);
-    const Plan &f = p.f;
-    ScanArgs a{};
-    a.Bsz = desc->batch; a.D = desc->d_inner; a.N = desc->d_state; a.L = desc->seqlen;
-    a.G = f.G; a.K = f.K; a.J = f.J; a.n_cblk = f.n_cblk; a.quad = f.quad;
-    a.bf16 = desc->io_dtype == SSM_BF16;
-    a.softplus = softplus_flag != 0;
-    a.zoh = (desc->flags & SSM_FLAG_ZOH) != 0;
-    a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
-    a.A = A; a.Dskip = D; a.delta_bias = delta_bias; a.h0 = initial_state;
-    a.cu = cu_seqlens;
-    a.n_seqs = state_rows;
-    ssm::BwdArgs g{};
-    g.dy = dy; g.dlast = dlast; g.du = du; g.ddelta = ddelta; g.dz = dz; g.dA = dA; g.dB = dB;
-    g.dC = dC; g.dD = dD; g.dbias = ddelta_bias; g.dh0 = dh0; g.n_tiles = p.n_tiles;
-    if (f.J > 1) {
-        a.hend = reinterpret_cast<float *>(ws + f.off_hend);
-        a.dtsum = reinterpret_cast<float *>(ws + f.off_dtsum);
-        a.keep = reinterpret_cast<float *>(ws + f.off_keep);
-        g.gend = reinterpret_cast<float *>(ws + p.off_gend);
-        g.bdtsum = reinterpret_cast<float *>(ws + p.off_bdtsum);
-    }
-    // the forward pass's checkpoints (read only), or the workspace's
-    g.ckpt = ckpt ? const_cast<float *>(ckpt) : reinterpret_cast<float *>(ws + p.off_ckpt);
-    g.ckpt_given = ckpt != nullptr;
-    g.dBp = reinterpret_cast<float *>(ws + p.off_dBp);
-    g.dCp = reinterpret_cast<float *>(ws + p.off_dCp);
-    g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
-    g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
-    g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
-    return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return bwd_single(desc, u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state,
+                      cu_seqlens, n_seqs, ckpt, dy, dlast, du, ddelta, dA, dB, dC, dD, dz,
+                      ddelta_bias, dh0, 0, stream);
 }
 
 ssm_status ssm_scan_bwd(const ssm_desc *desc, const void *u, const void *delta, const float *A,

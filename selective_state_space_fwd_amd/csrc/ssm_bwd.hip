@@ -358,8 +358,10 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 // dh.B u e^{dt A} to ddt (dc/ddt = e^{dt A}) and dh.B u dt^2 psi(dt A) to dA.
 // Two wavefronts per SIMD (at most 256 registers a lane; the LDS of a
 // wavefront is under 16 KB) for the Euler instances; the ZOH instance needs
-// more registers and runs one.
-template <class IO, bool EXT, bool ZOH>
+// more registers and runs one.  ACC: du, ddelta and dz are added to what the
+// outputs already hold (the later groups of states of a d_state > 16 call),
+// in the order old + new.
+template <class IO, bool EXT, bool ZOH, bool ACC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2))) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
     // per (channel, token) values of the tile: [t][c], see pc()
@@ -622,6 +624,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     stage(t_begin + (ntile - 1) * kT);
     for (int64_t ti = ntile - 1; ti >= 0; --ti) {
         const int64_t t0 = t_begin + ti * kT;
+        // ACC: the values du, ddelta and dz already hold at this tile's
+        // output tokens (those of step (d)), loaded before the prefetch so
+        // that step (d) can wait for them without waiting for it
+        float old[3][kT / 4];
+        if constexpr (ACC) {
+#pragma unroll
+            for (int e = 0; e < kT / 4; ++e) {
+                const int64_t tok = t0 + 4 * e + q;
+                const uint32_t off = (lane_ok && tok < t_end)
+                                         ? o_out + static_cast<uint32_t>(tok) * 4 : kDrop;
+                old[0][e] = ld_view<F32>(v_du, off);
+                old[1][e] = ld_view<F32>(v_dd, off);
+                old[2][e] = ld_view<F32>(v_dz, off);
+            }
+        }
         // (unconditional: the last tile reloads its own inputs, so that every
         // path has issued the same loads)
         prefetch_rev(ti > 0 ? t0 - kT : t0);
@@ -799,9 +816,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
             // (with ZOH the u term of ddt is already in dd)
             const float ddl = (ZOH ? dd : __builtin_fmaf(dw, uu, dd)) * s_sig[o];
             const uint32_t off = ok ? o_out + static_cast<uint32_t>(tok) * 4 : kDrop;
-            st_view(v_du, off, du);
-            st_view(v_dd, off, ddl);
-            st_view(v_dz, off, s_ds[o] * s_o[o]);
+            const float dzv = s_ds[o] * s_o[o];
+            st_view(v_du, off, ACC ? old[0][e] + du : du);
+            st_view(v_dd, off, ACC ? old[1][e] + ddl : ddl);
+            st_view(v_dz, off, ACC ? old[2][e] + dzv : dzv);
             dD_acc = ok ? __builtin_fmaf(dO, uu, dD_acc) : dD_acc;
             db_acc = ok ? db_acc + ddl : db_acc;
         }
@@ -933,7 +951,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
 
 // ------------------------------------------------------------ launch
 // Instances: lean; EXT (packed sequences); EXT + ZOH (either, with the
-// zero-order-hold input term).
+// zero-order-hold input term); the lean and ZOH ones also with ACC (packed
+// sequences never accumulate: the groups of states are not run for them).
 template <class IO, bool EXT, bool ZOH>
 static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
@@ -954,8 +973,11 @@ static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t
         else
             hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, false>), ag, dim3(64), 0, s, a, g);
     }
-    hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH>), dim3(gx, static_cast<unsigned>(a.J)), dim3(64),
-                       0, s, a, g);
+    const dim3 grid(gx, static_cast<unsigned>(a.J));
+    if (g.accumulate && (ZOH || !EXT))
+        hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, (ZOH || !EXT)>), grid, dim3(64), 0, s, a, g);
+    else
+        hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, false>), grid, dim3(64), 0, s, a, g);
     const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
                        dim3(256), 0, s, a, g);

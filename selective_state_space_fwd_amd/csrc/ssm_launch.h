@@ -86,6 +86,7 @@ struct BwdArgs {
     float *dBp, *dCp;           // (batch, n_cblk, 16, L) per 16-channel block
     float *dAp;                 // (batch, d_inner, J, 16)
     float *dDp, *dbp;           // (batch, d_inner, J)
+    int accumulate;             // du, ddelta, dz: add to what they hold (lean and ZOH instances)
 };
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);

@@ -367,3 +367,29 @@ def test_backward_state_groups(dev, io, N, zoh, K, gate, with_state):
     _, errs = run_case(dev, 2, d_inner, N, L, io, gate, with_state, K, seed=N + K, zoh=zoh)
     for k, e in errs.items():
         assert e <= GRAD_TOL, (k, e)
+
+
+def test_backward_state_groups_integer_bit_exact(dev):
+    """Exact-integer inputs with 48 states (three groups of 16, the later two
+    adding their du, ddelta and dz to the first's in place): every gradient
+    equals the oracle bit for bit, and two runs agree bit for bit."""
+    import torch
+    batch, d_inner, N, L = 2, 24, 48, 40
+    rng = np.random.default_rng(29)
+    ri = lambda *s: rng.integers(-2, 3, size=s).astype(np.float32)
+    u, B, C, dy = ri(batch, d_inner, L), ri(batch, N, L), ri(batch, N, L), ri(batch, d_inner, L)
+    D, h0, dlast = ri(d_inner), ri(batch, d_inner, N), ri(batch, d_inner, N)
+    dt = np.ones((batch, d_inner, L), np.float32)
+    A = np.zeros((d_inner, N), np.float32)
+    ref = oracle.scan_bwd(u, dt, A, B, C, dy, D, softplus=False, initial_state=h0, dlast=dlast)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    say(f"bwd state groups, integers, N={N}")
+    out = ssm.ssm_scan_bwd(g(u), g(dt), g(A), g(B), g(C), g(dy), g(D), softplus=False,
+                           initial_state=g(h0), dlast=g(dlast))
+    again = ssm.ssm_scan_bwd(g(u), g(dt), g(A), g(B), g(C), g(dy), g(D), softplus=False,
+                             initial_state=g(h0), dlast=g(dlast))
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert np.array_equal(to_f64(out[k]), ref[k]), k
+        assert torch.equal(out[k], again[k]), k
+

@@ -233,15 +233,24 @@ constexpr int kTsSegs = 16;         // time segments per tile (lanes of a row)
 #ifndef SSM_TS16_PREFETCH_BF16
 #define SSM_TS16_PREFETCH_BF16 2
 #endif
+#ifndef SSM_TS16_AHEAD
+#define SSM_TS16_AHEAD 1
+#endif
 template <int TS>
 constexpr int ts_waves() { return TS == 16 ? SSM_TS16_WAVES : 4; }
 
+// AHEAD (segments of 16, two tiles in flight): each tile stages the next
+// tile's B and C rows into the third of three LDS buffers, and the wavefronts order their accesses
+// through progress counters in LDS instead of a barrier per tile (see the
+// tile loop).
 template <class IO, int TS>
 struct TsShape {
     static constexpr int W = ts_waves<TS>();
-    static constexpr int NBUF = TS == 16 ? SSM_TS16_BUFFERS : 1;   // B/C tile buffers in LDS
     static constexpr int PF = (TS == 16 && std::is_same<IO, BF16>::value) ? SSM_TS16_PREFETCH_BF16
                                                                           : 1;   // tiles in flight
+    // (staging one tile ahead takes the next tile's register set: two in flight)
+    static constexpr bool AHEAD = TS == 16 && PF == 2 && SSM_TS16_AHEAD;
+    static constexpr int NBUF = AHEAD ? 3 : TS == 16 ? SSM_TS16_BUFFERS : 1;   // B/C tile buffers
 };
 
 // TS: tokens per segment (8 or 16); tiles of 16 TS tokens.
@@ -256,6 +265,7 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     constexpr int W = SH::W;
     constexpr int NBUF = SH::NBUF;
     constexpr int PF = SH::PF;
+    constexpr bool AHEAD = SH::AHEAD;
     constexpr int S = kTsSegs;
     constexpr int K = S * TS;           // tokens per tile
     constexpr int SP = TS + 4;          // LDS segment row, padded (bank spread)
@@ -271,6 +281,8 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     __shared__ __attribute__((aligned(16))) float sDT[W * RS];
     __shared__ __attribute__((aligned(16))) float sW[W * RS];
     __shared__ __attribute__((aligned(16))) float sY[W * RS];
+    // AHEAD: per wavefront, its count of ordering events (see the tile loop)
+    __shared__ int sEv[W];
 
     const IT *__restrict__ u = static_cast<const IT *>(a.u);
     const IT *__restrict__ dl = static_cast<const IT *>(a.delta);
@@ -336,20 +348,105 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     auto load_tile = [&](Regs &r, int64_t t0) {
         const int tl = static_cast<int>(t0) + lane * PT;
         const int tb = static_cast<int>(t0) + bt0;
+        // AHEAD stages B and C a tile before the tile's own loads are needed:
+        // issued first, they can be waited for while u, delta and z are
+        // still in flight (loads complete in issue order).  z next: the
+        // compiler copies its registers at the loop's back edge, which then
+        // waits for it alone.  The scheduling barriers keep that order.
+        if constexpr (AHEAD) {
+            load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);
+            load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+            __builtin_amdgcn_sched_barrier(0);
+            load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         load_raw<IO, PT, VEC>(u_row, tl, Li, r.u);
         load_raw<IO, PT, VEC>(d_row, tl, Li, r.d);
-        load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
-        load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
-        load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+        if constexpr (!AHEAD) load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
+        if constexpr (!AHEAD) {
+            load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
+            load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+        }
     };
 
-    // One tile: tokens t0 .. t0 + K-1, inputs in r (which then takes the
-    // inputs of the tile PF tiles later), B and C rows in LDS buffer nb.
-    auto tile = [&](const int64_t t0, Regs &r, const int nb, auto mask_tag) {
+    // This thread's pieces of a tile's B and C rows into LDS buffer nb
+    // (branch-free: a branch here would make the compiler wait for every load
+    // in flight); rows n >= N store B = 0.
+    auto stage_bc = [&](const Regs &r, const int nb) {
+        float xb[BT], xc[BT];
+        unpack_raw<IO, BT>(r.b, xb);
+#pragma unroll
+        for (int i = 0; i < BT; ++i) xb[i] = bn_ok ? xb[i] : 0.0f;
+        lds_write<BT>(sB + nb * 16 * RS + boff, xb);
+        unpack_raw<IO, BT>(r.c, xc);
+        lds_write<BT>(sC + nb * 16 * RS + boff, xc);
+    };
+    // AHEAD: wait until every wavefront's event count has reached target;
+    // returns the smallest count seen.  The poll is one asm block: its loop
+    // is invisible to the compiler, which would otherwise keep more of the
+    // tile's values live across it (and spill them), and its LDS reads are
+    // waited for inside the block.  All lanes read the same words, so the
+    // test is uniform; the wavefront sleeps between polls.  The wait always
+    // ends (see the tile loop); the bound on the polls is a guard only.
+    static_assert(!AHEAD || W == 8, "the poll reads 8 counters");
+    using LdsInt = __attribute__((address_space(3))) int;
+    LdsInt *const ev_lds = (LdsInt *)sEv;
+    auto wait_all = [&](const int target) -> int {
+        int c0, c1, c2, c3, c4, c5, c6, c7, sm, it;
+        asm volatile(
+            "s_mov_b32 %[it], 0\n"
+            "1:\n\t"
+            "ds_read_b32 %[c0], %[ea]\n\t"
+            "ds_read_b32 %[c1], %[ea] offset:4\n\t"
+            "ds_read_b32 %[c2], %[ea] offset:8\n\t"
+            "ds_read_b32 %[c3], %[ea] offset:12\n\t"
+            "ds_read_b32 %[c4], %[ea] offset:16\n\t"
+            "ds_read_b32 %[c5], %[ea] offset:20\n\t"
+            "ds_read_b32 %[c6], %[ea] offset:24\n\t"
+            "ds_read_b32 %[c7], %[ea] offset:28\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "v_min3_i32 %[c0], %[c0], %[c1], %[c2]\n\t"
+            "v_min3_i32 %[c0], %[c0], %[c3], %[c4]\n\t"
+            "v_min3_i32 %[c0], %[c0], %[c5], %[c6]\n\t"
+            "v_min_i32 %[c0], %[c0], %[c7]\n\t"
+            "s_nop 4\n\t"
+            "v_readfirstlane_b32 %[sm], %[c0]\n\t"
+            "s_nop 4\n\t"
+            "s_cmp_ge_i32 %[sm], %[tg]\n\t"
+            "s_cbranch_scc1 2f\n\t"
+            "s_add_u32 %[it], %[it], 1\n\t"
+            "s_cmp_lt_u32 %[it], %[lim]\n\t"
+            "s_cbranch_scc0 2f\n\t"
+            "s_sleep 1\n\t"
+            "s_branch 1b\n"
+            "2:"
+            : [c0] "=&v"(c0), [c1] "=&v"(c1), [c2] "=&v"(c2), [c3] "=&v"(c3), [c4] "=&v"(c4),
+              [c5] "=&v"(c5), [c6] "=&v"(c6), [c7] "=&v"(c7), [sm] "=&s"(sm), [it] "=&s"(it)
+            : [ea] "v"(ev_lds), [tg] "s"(target), [lim] "s"(1 << 24)
+            : "memory", "scc");
+        return sm;
+    };
+    // AHEAD: publish this wavefront's event count once its LDS accesses
+    // before it are complete (lgkmcnt(0)); every lane stores the same value.
+    auto signal = [&](const int value) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        reinterpret_cast<volatile LdsInt *>(ev_lds)[wv] = value;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    // One tile: tokens t0 .. t0 + K-1 (tile index ti), inputs in r (which
+    // then takes the inputs of the tile PF tiles later).  Without AHEAD its B
+    // and C rows go from r to LDS buffer nb here; with AHEAD they were staged
+    // by the tile before, into buffer ti % 3, and this tile stages the next
+    // one's from rn into buffer (ti + 1) % 3.
+    auto tile = [&](const int64_t t0, Regs &r, Regs &rn, const int nb, auto mask_tag) {
         // MASK: a tile that reaches past L (only the last group of tiles)
         constexpr bool MASK = decltype(mask_tag)::value;
-        float *bB = sB + nb * 16 * RS;
-        float *bC = sC + nb * 16 * RS;
+        const int ti = static_cast<int>(t0 / K);
+        const int nr = AHEAD ? ti % 3 : nb;
+        float *bB = sB + nr * 16 * RS;
+        float *bC = sC + nr * 16 * RS;
         // ---- (a) per-token values of this lane's tokens; B and C rows
         float du[PT], g[PT];
         {
@@ -373,25 +470,34 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             }
             lds_write<PT>(sdt + poff, xdt);
             lds_write<PT>(sw + poff, xw);
-            // branch-free (a branch here would make the compiler wait for
-            // every load in flight): rows n >= N store B = 0
-            float xb[BT], xc[BT];
-            unpack_raw<IO, BT>(r.b, xb);
-#pragma unroll
-            for (int i = 0; i < BT; ++i) xb[i] = bn_ok ? xb[i] : 0.0f;
-            lds_write<BT>(bB + boff, xb);
-            unpack_raw<IO, BT>(r.c, xc);
-            lds_write<BT>(bC + boff, xc);
+        }
+        if constexpr (AHEAD) {
+            // every wavefront has staged its pieces of this tile and is done
+            // reading buffer (ti + 1) % 3, which last held tile ti - 2, before
+            // it is overwritten (event count >= 2 ti; >= 1 for tile 0)
+            const int slowest = wait_all(ti == 0 ? 1 : 2 * ti);
+            // This wavefront's count is 2 ti + 1 (1 at tile 0).  One ahead of
+            // the slowest gives way: the SIMD's instruction arbiter favours the
+            // older of its wavefronts, which would otherwise run ahead until
+            // it must wait, leaving its SIMD to the younger one alone.
+            if (slowest < 2 * ti + 1) __builtin_amdgcn_s_setprio(0);
+            else __builtin_amdgcn_s_setprio(2);
+            stage_bc(rn, (ti + 1) % 3);
+            signal(2 * ti + 2);
+        } else {
+            stage_bc(r, nb);
         }
         // the inputs of the tile PF tiles later, in flight during this one's
         // scan (addresses are clamped into the row: the same loads on every path)
         load_tile(r, t0 + PF * K);
-        // with one buffer, every wavefront must be done with the previous
-        // tile's B and C rows before they are overwritten: a barrier before
-        // the writes above (at the end of the previous tile); with two, the
-        // barrier below also orders the writes of the next tile into the
-        // other buffer after every read of it during the previous tile
-        __syncthreads();
+        if constexpr (!AHEAD) {
+            // with one buffer, every wavefront must be done with the previous
+            // tile's B and C rows before they are overwritten: a barrier before
+            // the writes above (at the end of the previous tile); with two, the
+            // barrier below also orders the writes of the next tile into the
+            // other buffer after every read of it during the previous tile
+            __syncthreads();
+        }
 
         // ---- (b) local scan of the segment from a zero state; dA and dBu stay
         // in VGPRs for the replay
@@ -482,6 +588,7 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             for (int i = 0; i < PT; ++i) ys[i] = (ys[i] + du[i]) * g[i];
             if (ch_ok) store_run<IO, PT, VEC>(y, rbase, t0 + lane * PT, L, ys);
         }
+        if constexpr (AHEAD) signal(2 * ti + 3);   // done reading buffer ti % 3
         if (NBUF == 1) __syncthreads();   // every wavefront is done with this tile's B and C
     };
 
@@ -491,19 +598,41 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     // padding masks, no exit in the middle), so the compiler's count of loads
     // in flight stays exact and each tile waits only for its own inputs.  The
     // last, partial group follows with masks.
+    //
+    // AHEAD ordering.  Each wavefront counts its events in sEv: 1 once tile
+    // 0's B and C are staged, then per tile i: 2i + 2 once tile i + 1's are
+    // staged, 2i + 3 once it is done reading tile i's.  Tile i > 0 waits until
+    // every count is >= 2i, i.e. every wavefront has staged tile i (a count of
+    // 2i or more) and is done with tile i - 2 (more than 2i - 1); tile 0 until
+    // every count is >= 1 (tile 0 staged).  Then it stages
+    // tile i + 1 into buffer (i + 1) % 3 (which held tile i - 2), reads tile
+    // i's rows from buffer i % 3 and finishes.  A wavefront therefore runs at
+    // most one tile ahead of the slowest, and the slowest, at tile j, never
+    // waits: every wavefront, itself included, is at a tile j' >= j, so it
+    // has finished tile j' - 1 and its count is at least 2j' + 1 (at least 1
+    // at tile 0, after the prologue).  So every wait ends.
     Regs rs[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_tile(rs[p], p * K);
+    if constexpr (AHEAD) {
+        // counters start at zero (the LDS may hold a previous workgroup's),
+        // then tile 0's rows are staged
+        sEv[wv] = 0;
+        __syncthreads();
+        stage_bc(rs[0], 0);
+        signal(1);
+    }
     auto nbuf = [&](int64_t tt) { return NBUF == 2 ? static_cast<int>((tt / K) & 1) : 0; };
     int64_t t0 = 0;
     for (; t0 + PF * K <= L; t0 += PF * K) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) tile(t0 + p * K, rs[p], nbuf(t0 + p * K), std::false_type{});
+        for (int p = 0; p < PF; ++p)
+            tile(t0 + p * K, rs[p], rs[(p + 1) % PF], nbuf(t0 + p * K), std::false_type{});
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int64_t tt = t0 + p * K;
-        if (tt < L) tile(tt, rs[p], nbuf(tt), std::true_type{});
+        if (tt < L) tile(tt, rs[p], rs[(p + 1) % PF], nbuf(tt), std::true_type{});
     }
 
     // the state after the last token

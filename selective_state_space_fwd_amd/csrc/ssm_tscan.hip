@@ -445,6 +445,11 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
         constexpr bool MASK = decltype(mask_tag)::value;
         const int ti = static_cast<int>(t0 / K);
         const int nr = AHEAD ? ti % 3 : nb;
+        // barrier-ordered instances: the workgroups that share a CU (three at
+        // segments of 8) get issue slots oldest first; priority falling with
+        // the tiles done lets the ones behind catch up, so that they end
+        // together rather than the youngest alone
+        if constexpr (!AHEAD) fair_prio(ti, (L + K - 1) / K);
         float *bB = sB + nr * 16 * RS;
         float *bC = sC + nr * 16 * RS;
         // ---- (a) per-token values of this lane's tokens; B and C rows

@@ -159,6 +159,57 @@ def test_tscan_integers_bit_exact(dev, shape, K):
     assert np.array_equal(to_f64(h), hr)
 
 
+def sparse_integer_inputs(batch, d_inner, N, L, seed, n_imp=12):
+    """Decay 1, unit step; u holds n_imp impulses of +-1 per channel, B and C
+    take -1, 0 or 1 at every token, D small integers.  Every state is an
+    integer of magnitude <= n_imp and every y one of magnitude <= N n_imp + 2
+    (< 256 here): exact in bf16, while every tile's B and C rows differ."""
+    rng = np.random.default_rng(seed)
+    u = np.zeros((batch, d_inner, L), np.float32)
+    pos = rng.integers(0, L, (batch, d_inner, n_imp))
+    np.put_along_axis(u, pos, rng.choice(np.array([-1.0, 1.0], np.float32),
+                                         (batch, d_inner, n_imp)), axis=2)
+    return dict(u=u, delta=np.ones_like(u), A=np.zeros((d_inner, N), np.float32),
+                B=rng.integers(-1, 2, (batch, N, L)).astype(np.float32),
+                C=rng.integers(-1, 2, (batch, N, L)).astype(np.float32),
+                D=rng.integers(-2, 3, d_inner).astype(np.float32))
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 8, 16, 256),       # one tile
+    (1, 13, 16, 512),      # two tiles; the second workgroup has 5 channels of 8
+    (2, 16, 16, 800),      # three tiles and a ragged fourth, 16-byte accesses
+    (2, 16, 16, 808),      # the same, element path (L not a multiple of 16)
+    (1, 24, 16, 1280),     # five tiles
+    (1, 64, 16, 16384),    # 64 tiles, 8 workgroups
+    (1, 9, 5, 1300),       # d_state 5
+])
+def test_tscan_bf16_segments16_bit_exact(dev, shape):
+    """bf16 I/O with segments of 16: each tile stages the next tile's B and C
+    into the third of three LDS buffers and the wavefronts order their reads
+    through event counters (no barrier per tile).  A row read from the wrong
+    buffer or before it is written changes y; integer inputs make every value
+    exact, so y and the last state must equal the oracle bit for bit."""
+    import torch
+    batch, d_inner, N, L = shape
+    say(f"in-wave bf16 segments of 16, integers b={batch} d={d_inner} N={N} L={L}")
+    case = sparse_integer_inputs(batch, d_inner, N, L, seed=L + d_inner)
+    enc = {k: ssm_inputs.encode(case[k], "bf16") for k in ("u", "delta", "B", "C")}
+    plan = ssm.scan_plan(batch, d_inner, N, L, 1, 256)
+    assert plan.startswith("in-wave") and "segments of 16" in plan, plan
+    t = {k: to_device(v, dev) for k, v in enc.items()}
+    t.update({k: to_device(case[k], dev) for k in ("A", "D")})
+    for rep in range(2):
+        y, h = ssm.ssm_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], None,
+                                None, softplus=False, chunk_size=256)
+        torch.cuda.synchronize()
+        yr, hr = oracle.scan_fwd(case["u"], case["delta"], case["A"], case["B"], case["C"],
+                                 case["D"], softplus=False)
+        assert np.max(np.abs(yr)) < 256
+        assert np.array_equal(to_f64(y), yr), rep
+        assert np.array_equal(to_f64(h), hr), rep
+
+
 def test_tscan_deterministic_and_matches_chunked(dev):
     """Run to run bit-identical; within the float32 bar of the two-pass
     chunked schedule on the same inputs (chunks of 512)."""

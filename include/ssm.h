@@ -264,7 +264,10 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
  * the zero-order-hold input term; the fused convolution has no backward here
  * (its input u is an input of this call).  Above 16 states the pass runs once
  * per group of 16 states (their recurrences are independent, §3.2) and the
- * groups' per-token sums are added in group order.
+ * groups' per-token sums (du, ddelta, dz, ddelta_bias) are added in a fixed
+ * order; when one group's channel blocks leave most of the GPU idle and
+ * chunk_size is 0, up to four groups run side by side, each over the whole
+ * sequence, and the workspace then also holds their per-token sums.
  * Packed sequences: see ssm_scan_bwd_ex.
  * Inputs: as ssm_scan_fwd_ex (initial_state may be NULL), plus
  *   dy             (batch, d_inner, L) io_dtype

@@ -353,46 +353,84 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
 // Backward with d_state > 16 (ufo.work article, §3.2: the state dimension
 // splits into groups that recur independently): the 16-state pass runs once
 // per group of 16 states on that group's slices of A, B, C, the start state
-// and dlast.  The per-token sums over states add: group 0 writes du, ddelta,
-// dz and d(bias) (and alone sees D, so that D's terms enter once), the later
-// groups add theirs in group order; dA, dB, dC and dh0 are the groups'
+// and dlast.  The per-token sums over states add (du, ddelta, dz, d(bias));
+// D's terms enter with group 0 alone; dA, dB, dC and dh0 are the groups'
 // slices.  No packed sequences or forward checkpoints on this path.
+//
+// When one group's 16-channel blocks fill under half of the backward's
+// wavefront slots, P groups (up to 4) run side by side in one launch, each
+// as one chunk: no chunk operators to compute, where one group alone would
+// need its sequence cut into chunks to fill the chip.  Group z of a launch
+// adds its du, ddelta and dz to buffer slot z (groups z, z + P, ... in turn,
+// old + new), and the slots are summed in slot order at the end.  Otherwise
+// (P = 1) the groups run one launch each, group 0 writing du, ddelta and dz
+// and each later one adding to them in place.
 struct BwdGroupPlan {
     ssm_desc sd{};   // the 16-state descriptor of one group
     BwdPlan sub;
-    int64_t NG = 0;
+    int64_t NG = 0, P = 1;
+    // per-slot sizes (bytes; multiples of kAlign) of the P slots of each buffer
+    size_t s_sub = 0, s_BC = 0, s_A = 0, s_S = 0, s_dBC = 0, s_db = 0, s_out = 0;
     size_t off_sub = 0, off_B = 0, off_C = 0, off_A = 0, off_h0 = 0, off_dl = 0, off_dA = 0,
-           off_dB = 0, off_dC = 0, off_db = 0, off_dh0 = 0, bytes = 0;
+           off_dB = 0, off_dC = 0, off_db = 0, off_dh0 = 0, off_du = 0, off_dd = 0, off_dz = 0,
+           bytes = 0;
 };
 
 ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
     const ssm_status st = check_desc(d);
     if (st != SSM_OK) return st;
     if (d->d_state <= 16) return SSM_ERR_UNSUPPORTED;
+    p->NG = (d->d_state + 15) / 16;
+    const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
+    const size_t L = static_cast<size_t>(d->seqlen);
+    const size_t esz = d->io_dtype == SSM_BF16 ? 2 : 4;
     p->sd = *d;
     p->sd.d_state = 16;
     p->sd.workspace = nullptr;
     p->sd.workspace_bytes = 0;
     p->sd.profile_begin = p->sd.profile_end = nullptr;
-    const ssm_status s2 = make_bwd_plan(&p->sd, &p->sub);
+    // groups side by side: P of them fill at least 3/4 of the slots
+    const int64_t w = d->batch * ((d->d_inner + 15) / 16);
+    const int64_t slots = (d->flags & SSM_FLAG_ZOH) ? kBwdSlots / 2 : kBwdSlots;
+    p->P = 1;
+    if (d->chunk_size == 0 && w > 0 && L > 0) {
+        int64_t P = slots / w;
+        if (P > 4) P = 4;
+        if (P > p->NG) P = p->NG;
+        if (P >= 2 && 4 * P * w >= 3 * slots) p->P = P;
+    }
+    if (p->P > 1) p->sd.chunk_size = static_cast<int64_t>((L + 15) / 16 * 16);   // one chunk
+    ssm_status s2 = make_bwd_plan(&p->sd, &p->sub);
+    if (s2 == SSM_OK && p->P > 1 && p->sub.f.J != 1) {
+        p->P = 1;
+        p->sd.chunk_size = d->chunk_size;
+        s2 = make_bwd_plan(&p->sd, &p->sub);
+    }
     if (s2 != SSM_OK) return s2;
-    p->NG = (d->d_state + 15) / 16;
-    const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
-    const size_t L = static_cast<size_t>(d->seqlen);
-    const size_t esz = d->io_dtype == SSM_BF16 ? 2 : 4;
+    const size_t P = static_cast<size_t>(p->P);
+    p->s_sub = align_up(p->sub.bytes);
+    p->s_BC = align_up(B * 16 * L * esz);
+    p->s_A = align_up(D * 16 * sizeof(float));
+    p->s_S = align_up(B * D * 16 * sizeof(float));
+    p->s_dBC = align_up(B * 16 * L * sizeof(float));
+    p->s_db = align_up(D * sizeof(float));
+    p->s_out = P > 1 ? align_up(B * D * L * sizeof(float)) : 0;
     size_t off = 0;
-    auto take = [&](size_t &o, size_t bytes) { o = off; off += align_up(bytes); };
-    take(p->off_sub, p->sub.bytes);
-    take(p->off_B, B * 16 * L * esz);
-    take(p->off_C, B * 16 * L * esz);
-    take(p->off_A, D * 16 * sizeof(float));
-    take(p->off_h0, B * D * 16 * sizeof(float));
-    take(p->off_dl, B * D * 16 * sizeof(float));
-    take(p->off_dA, D * 16 * sizeof(float));
-    take(p->off_dB, B * 16 * L * sizeof(float));
-    take(p->off_dC, B * 16 * L * sizeof(float));
-    take(p->off_db, D * sizeof(float));
-    take(p->off_dh0, B * D * 16 * sizeof(float));
+    auto take = [&](size_t &o, size_t slot) { o = off; off += P * slot; };
+    take(p->off_sub, p->s_sub);
+    take(p->off_B, p->s_BC);
+    take(p->off_C, p->s_BC);
+    take(p->off_A, p->s_A);
+    take(p->off_h0, p->s_S);
+    take(p->off_dl, p->s_S);
+    take(p->off_dA, p->s_A);
+    take(p->off_dB, p->s_dBC);
+    take(p->off_dC, p->s_dBC);
+    take(p->off_db, p->s_db);
+    take(p->off_dh0, p->s_S);
+    take(p->off_du, p->s_out);
+    take(p->off_dd, p->s_out);
+    take(p->off_dz, p->s_out);
     p->bytes = off;
     return SSM_OK;
 }
@@ -515,7 +553,8 @@ ssm_status bwd_single(const ssm_desc *desc, const void *u, const void *delta, co
                       const int32_t *cu_seqlens, int64_t n_seqs, const float *ckpt,
                       const void *dy, const float *dlast, float *du, float *ddelta, float *dA,
                       float *dB, float *dC, float *dD, float *dz, float *ddelta_bias, float *dh0,
-                      int accumulate, ssm_stream_t stream) {
+                      int accumulate, ssm_stream_t stream,
+                      const ssm::BwdArgs *side_by_side = nullptr) {
     BwdPlan p;
     ssm_status st = make_bwd_plan(desc, &p);
     if (st != SSM_OK) return st;
@@ -587,6 +626,13 @@ ssm_status bwd_single(const ssm_desc *desc, const void *u, const void *delta, co
     g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
     g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
     g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
+    if (side_by_side) {   // groups of states side by side: one chunk each
+        if (f.J != 1 || cu_seqlens || ckpt) return SSM_ERR_UNSUPPORTED;
+        const ssm::BwdArgs &x = *side_by_side;
+        g.gz = x.gz;
+        g.gs_A = x.gs_A; g.gs_BC = x.gs_BC; g.gs_S = x.gs_S; g.gs_out = x.gs_out;
+        g.gs_ws = x.gs_ws; g.gs_dBC = x.gs_dBC; g.gs_db = x.gs_db;
+    }
     return ssm::launch_bwd(a, g, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -631,38 +677,93 @@ ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, co
     auto at = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
     ssm_desc sd = p.sd;
     sd.workspace = ws + p.off_sub;
-    sd.workspace_bytes = p.sub.bytes;
+    sd.workspace_bytes = p.P * p.s_sub;
     void *Bg = ws + p.off_B, *Cg = ws + p.off_C;
     float *Ag = at(p.off_A), *h0g = initial_state ? at(p.off_h0) : nullptr;
     float *dlg = dlast ? at(p.off_dl) : nullptr;
     float *dAg = at(p.off_dA), *dBg = at(p.off_dB), *dCg = at(p.off_dC);
     float *dh0g = dh0 ? at(p.off_dh0) : nullptr;
-    for (int64_t g = 0; g < p.NG; ++g) {
+    const int ie = static_cast<int>(esz);
+    // groups g .. g + np - 1 into (out of) slots 0 .. np - 1, one launch per buffer
+    const int64_t e_BC = static_cast<int64_t>(p.s_BC / esz), e_A = static_cast<int64_t>(p.s_A / 4),
+                  e_S = static_cast<int64_t>(p.s_S / 4), e_dBC = static_cast<int64_t>(p.s_dBC / 4);
+    auto gather = [&](int64_t g, int np) {
         const int64_t n0 = 16 * g;
-        hipError_t e = ssm::launch_gather_rows(Bg, B, Bn, N, n0, L, static_cast<int>(esz), s);
-        if (e == hipSuccess) e = ssm::launch_gather_rows(Cg, C, Bn, N, n0, L, static_cast<int>(esz), s);
-        if (e == hipSuccess) e = ssm::launch_gather_cols(Ag, A, Dn, N, n0, s);
-        if (e == hipSuccess && h0g) e = ssm::launch_gather_cols(h0g, initial_state, Bn * Dn, N, n0, s);
-        if (e == hipSuccess && dlg) e = ssm::launch_gather_cols(dlg, dlast, Bn * Dn, N, n0, s);
+        hipError_t e = ssm::launch_gather_rows(Bg, B, Bn, N, n0, L, ie, s, np, e_BC);
+        if (e == hipSuccess) e = ssm::launch_gather_rows(Cg, C, Bn, N, n0, L, ie, s, np, e_BC);
+        if (e == hipSuccess) e = ssm::launch_gather_cols(Ag, A, Dn, N, n0, s, np, e_A);
+        if (e == hipSuccess && h0g)
+            e = ssm::launch_gather_cols(h0g, initial_state, Bn * Dn, N, n0, s, np, e_S);
+        if (e == hipSuccess && dlg)
+            e = ssm::launch_gather_cols(dlg, dlast, Bn * Dn, N, n0, s, np, e_S);
+        return e;
+    };
+    auto scatter = [&](int64_t g, int np) {
+        const int64_t n0 = 16 * g;
+        hipError_t e = ssm::launch_scatter_cols(dA, dAg, Dn, N, n0, s, np, e_A);
+        if (e == hipSuccess) e = ssm::launch_scatter_rows(dB, dBg, Bn, N, n0, L, s, np, e_dBC);
+        if (e == hipSuccess) e = ssm::launch_scatter_rows(dC, dCg, Bn, N, n0, L, s, np, e_dBC);
+        if (e == hipSuccess && dh0g)
+            e = ssm::launch_scatter_cols(dh0, dh0g, Bn * Dn, N, n0, s, np, e_S);
+        return e;
+    };
+    if (p.P == 1) {
+        for (int64_t g = 0; g < p.NG; ++g) {
+            hipError_t e = gather(g, 1);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+            // group 0 writes du, ddelta, dz and d(bias); each later group adds
+            // its share to du, ddelta and dz in place (old + new, in group
+            // order) and its d(bias) through a small buffer
+            const bool first = g == 0;
+            float *db_o = ddelta_bias ? (first ? ddelta_bias : at(p.off_db)) : nullptr;
+            const ssm_status sst = bwd_single(
+                &sd, u, delta, Ag, Bg, Cg, first ? D : nullptr, z, delta_bias, softplus_flag, h0g,
+                nullptr, 0, nullptr, dy, dlg, du, ddelta, dAg, dBg, dCg, first ? dD : nullptr,
+                z ? dz : nullptr, db_o, dh0g, first ? 0 : 1, stream);
+            if (sst != SSM_OK) return sst;
+            if (!first && db_o) e = ssm::launch_accumulate(ddelta_bias, db_o, Dn, s);
+            if (e == hipSuccess) e = scatter(g, 1);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
+        return SSM_OK;
+    }
+    // P groups side by side per launch
+    ssm::BwdArgs x{};
+    x.gs_A = static_cast<int64_t>(p.s_A / sizeof(float));
+    x.gs_BC = static_cast<int64_t>(p.s_BC);
+    x.gs_S = static_cast<int64_t>(p.s_S / sizeof(float));
+    x.gs_out = static_cast<int64_t>(p.s_out / sizeof(float));
+    x.gs_ws = static_cast<int64_t>(p.s_sub);
+    x.gs_dBC = static_cast<int64_t>(p.s_dBC / sizeof(float));
+    x.gs_db = static_cast<int64_t>(p.s_db / sizeof(float));
+    float *du_s = at(p.off_du), *dd_s = at(p.off_dd), *dz_s = z ? at(p.off_dz) : nullptr;
+    float *db_s = ddelta_bias ? at(p.off_db) : nullptr;
+    hipError_t e = ddelta_bias ? ssm::launch_fill_zero(ddelta_bias, static_cast<size_t>(Dn), s)
+                               : hipSuccess;
+    if (e != hipSuccess) return SSM_ERR_HIP;
+    for (int64_t g0 = 0; g0 < p.NG; g0 += p.P) {
+        const int np = static_cast<int>(p.NG - g0 < p.P ? p.NG - g0 : p.P);
+        e = gather(g0, np);
         if (e != hipSuccess) return SSM_ERR_HIP;
-        // group 0 writes du, ddelta, dz and d(bias); each later group adds
-        // its share to du, ddelta and dz in place (old + new, in group
-        // order) and its d(bias) through a small buffer
-        const bool first = g == 0;
-        float *db_o = ddelta_bias ? (first ? ddelta_bias : at(p.off_db)) : nullptr;
+        x.gz = np;
+        const bool first = g0 == 0;
         const ssm_status sst = bwd_single(
             &sd, u, delta, Ag, Bg, Cg, first ? D : nullptr, z, delta_bias, softplus_flag, h0g,
-            nullptr, 0, nullptr, dy, dlg, du, ddelta, dAg, dBg, dCg, first ? dD : nullptr,
-            z ? dz : nullptr, db_o, dh0g, first ? 0 : 1, stream);
+            nullptr, 0, nullptr, dy, dlg, du_s, dd_s, dAg, dBg, dCg, first ? dD : nullptr, dz_s,
+            db_s, dh0g, first ? 0 : 1, stream, &x);
         if (sst != SSM_OK) return sst;
-        if (!first && db_o) e = ssm::launch_accumulate(ddelta_bias, db_o, Dn, s);
-        if (e == hipSuccess) e = ssm::launch_scatter_cols(dA, dAg, Dn, N, n0, s);
-        if (e == hipSuccess) e = ssm::launch_scatter_rows(dB, dBg, Bn, N, n0, L, s);
-        if (e == hipSuccess) e = ssm::launch_scatter_rows(dC, dCg, Bn, N, n0, L, s);
-        if (e == hipSuccess && dh0g) e = ssm::launch_scatter_cols(dh0, dh0g, Bn * Dn, N, n0, s);
+        e = scatter(g0, np);
+        if (e == hipSuccess && db_s)   // d(bias) in group order
+            e = ssm::launch_accumulate(ddelta_bias, db_s, Dn, s, np, x.gs_db);
         if (e != hipSuccess) return SSM_ERR_HIP;
     }
-    return SSM_OK;
+    // du, ddelta, dz: the slots summed in slot order
+    const int P = static_cast<int>(p.P);
+    const int64_t n = Bn * Dn * L;
+    e = ssm::launch_sum_slots(du, du_s, P, x.gs_out, n, s);
+    if (e == hipSuccess) e = ssm::launch_sum_slots(ddelta, dd_s, P, x.gs_out, n, s);
+    if (e == hipSuccess && dz_s) e = ssm::launch_sum_slots(dz, dz_s, P, x.gs_out, n, s);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 // ---------------------------------------------------------------- no-allocation scratch

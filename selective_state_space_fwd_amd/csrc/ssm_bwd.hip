@@ -172,6 +172,40 @@ __device__ __forceinline__ void st_view(Rsrc r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Groups of states side by side: the pointers of group blockIdx.z (those in
+// a and g are group 0's).  D's terms and dD stay with group 0.
+__device__ __forceinline__ void select_group(ScanArgs &a, BwdArgs &g) {
+    const int64_t z = blockIdx.z;
+    if (z == 0) return;
+    auto bytes = [&](const void *p, int64_t n) {
+        return static_cast<const void *>(static_cast<const char *>(p) + n);
+    };
+    auto ws = [&](float *p) {
+        return reinterpret_cast<float *>(reinterpret_cast<char *>(p) + z * g.gs_ws);
+    };
+    a.A += z * g.gs_A;
+    a.B = bytes(a.B, z * g.gs_BC);
+    a.C = bytes(a.C, z * g.gs_BC);
+    if (a.h0) a.h0 += z * g.gs_S;
+    if (g.dlast) g.dlast += z * g.gs_S;
+    if (g.dh0) g.dh0 += z * g.gs_S;
+    g.du += z * g.gs_out;
+    g.ddelta += z * g.gs_out;
+    if (g.dz) g.dz += z * g.gs_out;
+    g.ckpt = ws(g.ckpt);
+    g.dBp = ws(g.dBp);
+    g.dCp = ws(g.dCp);
+    g.dAp = ws(g.dAp);
+    g.dDp = ws(g.dDp);
+    g.dbp = ws(g.dbp);
+    g.dA += z * g.gs_A;
+    g.dB += z * g.gs_dBC;
+    g.dC += z * g.gs_dBC;
+    if (g.dbias) g.dbias += z * g.gs_db;
+    a.Dskip = nullptr;
+    g.dD = nullptr;
+}
+
 __device__ __forceinline__ float sigmoid_f32(float x) {
     return rcp_hw(1.0f + exp2_hw(-x * kLog2e));
 }
@@ -364,6 +398,7 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 template <class IO, bool EXT, bool ZOH, bool ACC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2))) void bwd_kernel(ScanArgs a, BwdArgs g) {
     using IT = typename IO::T;
+    select_group(a, g);
     // per (channel, token) values of the tile: [t][c], see pc()
     __shared__ __attribute__((aligned(16))) float s_dt[kQC * kT];
     __shared__ __attribute__((aligned(16))) float s_w[kQC * kT];
@@ -894,6 +929,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
 // ------------------------------------------------------------ pass 4
 // One thread per output element; every sum runs in a fixed order.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) {
+    select_group(a, g);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nbc = a.Bsz * a.N * a.L;            // dB and dC elements
     const int64_t nA = a.D * a.N;
@@ -973,13 +1009,16 @@ static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t
         else
             hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, false>), ag, dim3(64), 0, s, a, g);
     }
-    const dim3 grid(gx, static_cast<unsigned>(a.J));
+    // groups side by side run one chunk each, without packed sequences
+    const unsigned gz = g.gz > 1 ? static_cast<unsigned>(g.gz) : 1u;
+    if (gz > 1 && (a.J != 1 || a.cu)) return hipErrorInvalidValue;
+    const dim3 grid(gx, static_cast<unsigned>(a.J), gz);
     if (g.accumulate && (ZOH || !EXT))
         hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, (ZOH || !EXT)>), grid, dim3(64), 0, s, a, g);
     else
         hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, false>), grid, dim3(64), 0, s, a, g);
     const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256), 1, gz),
                        dim3(256), 0, s, a, g);
     return hipGetLastError();
 }
@@ -1003,88 +1042,122 @@ hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
 namespace {
 
 template <class T>
+// blockIdx.y: the group of the call (groups n0, n0 + 16, ...), whose slice
+// lies blockIdx.y slots (of `slot` elements) into the gathered buffer
 __global__ __launch_bounds__(256) void gather_rows_kernel(T *dst, const T *src, int64_t R,
-                                                          int64_t N, int64_t n0, int64_t L) {
+                                                          int64_t N, int64_t n0, int64_t L,
+                                                          int64_t slot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= R * 16 * L) return;
     const int64_t t = i % L, k = (i / L) % 16, r = i / (16 * L);
-    const int64_t n = n0 + k;
-    dst[i] = n < N ? src[(r * N + n) * L + t] : T(0);
+    const int64_t n = n0 + 16 * static_cast<int64_t>(blockIdx.y) + k;
+    dst[blockIdx.y * slot + i] = n < N ? src[(r * N + n) * L + t] : T(0);
 }
 
 __global__ __launch_bounds__(256) void gather_cols_kernel(float *dst, const float *src, int64_t R,
-                                                          int64_t N, int64_t n0) {
+                                                          int64_t N, int64_t n0, int64_t slot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= R * 16) return;
-    const int64_t n = n0 + i % 16, r = i / 16;
-    dst[i] = n < N ? src[r * N + n] : 0.0f;
+    const int64_t n = n0 + 16 * static_cast<int64_t>(blockIdx.y) + i % 16, r = i / 16;
+    dst[blockIdx.y * slot + i] = n < N ? src[r * N + n] : 0.0f;
 }
 
 __global__ __launch_bounds__(256) void scatter_rows_kernel(float *dst, const float *src, int64_t R,
-                                                           int64_t N, int64_t n0, int64_t L) {
+                                                           int64_t N, int64_t n0, int64_t L,
+                                                           int64_t slot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= R * 16 * L) return;
     const int64_t t = i % L, k = (i / L) % 16, r = i / (16 * L);
-    const int64_t n = n0 + k;
-    if (n < N) dst[(r * N + n) * L + t] = src[i];
+    const int64_t n = n0 + 16 * static_cast<int64_t>(blockIdx.y) + k;
+    if (n < N) dst[(r * N + n) * L + t] = src[blockIdx.y * slot + i];
 }
 
 __global__ __launch_bounds__(256) void scatter_cols_kernel(float *dst, const float *src, int64_t R,
-                                                           int64_t N, int64_t n0) {
+                                                           int64_t N, int64_t n0, int64_t slot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= R * 16) return;
-    const int64_t n = n0 + i % 16, r = i / 16;
-    if (n < N) dst[r * N + n] = src[i];
+    const int64_t n = n0 + 16 * static_cast<int64_t>(blockIdx.y) + i % 16, r = i / 16;
+    if (n < N) dst[r * N + n] = src[blockIdx.y * slot + i];
 }
 
-__global__ __launch_bounds__(256) void accumulate_kernel(float *dst, const float *src, int64_t n) {
+// dst[i] += src[i], then += src[i + slot], ... (P terms, in that order)
+__global__ __launch_bounds__(256) void accumulate_kernel(float *dst, const float *src, int64_t n,
+                                                         int P, int64_t slot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i < n) dst[i] += src[i];
+    if (i >= n) return;
+    float v = dst[i];
+    for (int z = 0; z < P; ++z) v += src[i + z * slot];
+    dst[i] = v;
+}
+
+__global__ __launch_bounds__(256) void sum_slots_kernel(float *dst, const float *src, int P,
+                                                        int64_t stride, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = src[i];
+    for (int z = 1; z < P; ++z) v += src[i + z * stride];
+    dst[i] = v;
 }
 
 dim3 grid_of(int64_t n) { return dim3(static_cast<unsigned>((n + 255) / 256)); }
 
 }  // namespace
 
+static dim3 grid_of(int64_t n, int P) {
+    return dim3(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(P));
+}
+
 hipError_t launch_gather_rows(void *dst, const void *src, int64_t R, int64_t N, int64_t n0,
-                              int64_t L, int esz, hipStream_t s) {
+                              int64_t L, int esz, hipStream_t s, int P, int64_t slot) {
     const int64_t n = R * 16 * L;
-    if (n == 0) return hipSuccess;
+    if (n == 0 || P < 1) return hipSuccess;
     if (esz == 2)
-        hipLaunchKernelGGL(gather_rows_kernel<uint16_t>, grid_of(n), dim3(256), 0, s,
+        hipLaunchKernelGGL(gather_rows_kernel<uint16_t>, grid_of(n, P), dim3(256), 0, s,
                            static_cast<uint16_t *>(dst), static_cast<const uint16_t *>(src), R, N,
-                           n0, L);
+                           n0, L, slot);
     else
-        hipLaunchKernelGGL(gather_rows_kernel<float>, grid_of(n), dim3(256), 0, s,
-                           static_cast<float *>(dst), static_cast<const float *>(src), R, N, n0, L);
+        hipLaunchKernelGGL(gather_rows_kernel<float>, grid_of(n, P), dim3(256), 0, s,
+                           static_cast<float *>(dst), static_cast<const float *>(src), R, N, n0, L,
+                           slot);
     return hipGetLastError();
 }
 
 hipError_t launch_gather_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                              hipStream_t s) {
-    if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_cols_kernel, grid_of(R * 16), dim3(256), 0, s, dst, src, R, N, n0);
+                              hipStream_t s, int P, int64_t slot) {
+    if (R == 0 || P < 1) return hipSuccess;
+    hipLaunchKernelGGL(gather_cols_kernel, grid_of(R * 16, P), dim3(256), 0, s, dst, src, R, N,
+                       n0, slot);
     return hipGetLastError();
 }
 
 hipError_t launch_scatter_rows(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                               int64_t L, hipStream_t s) {
+                               int64_t L, hipStream_t s, int P, int64_t slot) {
     const int64_t n = R * 16 * L;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(scatter_rows_kernel, grid_of(n), dim3(256), 0, s, dst, src, R, N, n0, L);
+    if (n == 0 || P < 1) return hipSuccess;
+    hipLaunchKernelGGL(scatter_rows_kernel, grid_of(n, P), dim3(256), 0, s, dst, src, R, N, n0, L,
+                       slot);
     return hipGetLastError();
 }
 
 hipError_t launch_scatter_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                               hipStream_t s) {
-    if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(scatter_cols_kernel, grid_of(R * 16), dim3(256), 0, s, dst, src, R, N, n0);
+                               hipStream_t s, int P, int64_t slot) {
+    if (R == 0 || P < 1) return hipSuccess;
+    hipLaunchKernelGGL(scatter_cols_kernel, grid_of(R * 16, P), dim3(256), 0, s, dst, src, R, N,
+                       n0, slot);
     return hipGetLastError();
 }
 
-hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s) {
+hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s, int P,
+                             int64_t slot) {
+    if (n == 0 || P < 1) return hipSuccess;
+    hipLaunchKernelGGL(accumulate_kernel, grid_of(n), dim3(256), 0, s, dst, src, n, P, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_slots(float *dst, const float *src, int P, int64_t stride, int64_t n,
+                            hipStream_t s) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(accumulate_kernel, grid_of(n), dim3(256), 0, s, dst, src, n);
+    hipLaunchKernelGGL(sum_slots_kernel, grid_of(n), dim3(256), 0, s, dst, src, P, stride, n);
     return hipGetLastError();
 }
 

@@ -87,23 +87,42 @@ struct BwdArgs {
     float *dAp;                 // (batch, d_inner, J, 16)
     float *dDp, *dbp;           // (batch, d_inner, J)
     int accumulate;             // du, ddelta, dz: add to what they hold (lean and ZOH instances)
+    // Groups of 16 states side by side (d_state > 16): gz groups in one launch,
+    // group blockIdx.z; every pointer above is group 0's, and group z's lies
+    // z strides further (one chunk only: no chunk operators).  D's terms and
+    // dD belong to group 0 alone.
+    int gz;                     // 0 or 1: one group
+    int64_t gs_A;               // floats: A (d_inner, 16) and dA
+    int64_t gs_BC;              // bytes: B and C (batch, 16, L)
+    int64_t gs_S;               // floats: start state, dlast, dh0 (batch, d_inner, 16)
+    int64_t gs_out;             // floats: du, ddelta, dz (batch, d_inner, L)
+    int64_t gs_ws;              // bytes: the workspace views (ckpt, dBp, dCp, dAp, dDp, dbp)
+    int64_t gs_dBC;             // floats: dB and dC (batch, 16, L)
+    int64_t gs_db;              // floats: dbias (d_inner)
 };
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);
 
-// One group of 16 states (n0 .. n0 + 15) out of N, for the backward with
-// d_state > 16.  Rows: dst (R, 16, L) <-> src (R, N, L); columns: dst (R, 16)
-// <-> src (R, N).  Gathers zero-fill states n >= N; scatters skip them.
+// P groups of 16 states (n0 .. n0 + 15, then n0 + 16 .. n0 + 31, ...) out of
+// N, for the backward with d_state > 16; group p's slice lies p slots (of
+// `slot` elements) into the gathered buffer.  Rows: dst (R, 16, L) <-> src
+// (R, N, L); columns: dst (R, 16) <-> src (R, N).  Gathers zero-fill states
+// n >= N; scatters skip them.
 hipError_t launch_gather_rows(void *dst, const void *src, int64_t R, int64_t N, int64_t n0,
-                              int64_t L, int esz, hipStream_t s);
+                              int64_t L, int esz, hipStream_t s, int P = 1, int64_t slot = 0);
 hipError_t launch_gather_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                              hipStream_t s);
+                              hipStream_t s, int P = 1, int64_t slot = 0);
 hipError_t launch_scatter_rows(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                               int64_t L, hipStream_t s);
+                               int64_t L, hipStream_t s, int P = 1, int64_t slot = 0);
 hipError_t launch_scatter_cols(float *dst, const float *src, int64_t R, int64_t N, int64_t n0,
-                               hipStream_t s);
-// dst[i] += src[i], i < n
-hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s);
+                               hipStream_t s, int P = 1, int64_t slot = 0);
+// dst[i] += src[i], then += src[i + slot], ... (P terms, in that order), i < n
+hipError_t launch_accumulate(float *dst, const float *src, int64_t n, hipStream_t s, int P = 1,
+                             int64_t slot = 0);
+// dst[i] = src[i] + src[i + stride] + ... + src[i + (P - 1) stride], added in
+// that order, i < n
+hipError_t launch_sum_slots(float *dst, const float *src, int P, int64_t stride, int64_t n,
+                            hipStream_t s);
 
 struct UpdateArgs {
     int64_t Bsz, D, N;

@@ -253,6 +253,29 @@ def test_flags_validation(lib):
     assert lib.ssm_scan_chunk_size(ctypes.byref(d)) == 2048
 
 
+def test_backward_state_groups_side_by_side_plan(lib):
+    """d_state > 16: groups of 16 states run side by side (one chunk each, du,
+    ddelta and dz summed through P slots of the workspace) when one group's
+    16-channel blocks fill under half of the 2048 wavefront slots (1024 with
+    ZOH), P <= 4 groups fill at least three quarters and no chunk length is
+    given; otherwise one group per launch.  Seen through the workspace size."""
+    def need(**kw):
+        return lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(**kw)))
+    slots = lambda P, b, d, L: 3 * P * _al(b * d * L * 4)
+    # 512 blocks: four groups side by side (the N = 256 layer's shape)
+    assert need(batch=4, d_inner=2048, d_state=256, seqlen=4096) >= slots(4, 4, 2048, 4096)
+    assert need(batch=1, d_inner=8192, d_state=80, seqlen=96) >= slots(4, 1, 8192, 96)
+    # three groups: three side by side
+    assert need(batch=2, d_inner=4096, d_state=48, seqlen=64) >= slots(3, 2, 4096, 64)
+    # ZOH: 1024 slots, two groups of 512 blocks
+    assert need(batch=1, d_inner=8192, d_state=32, seqlen=64,
+                flags=ssm.SSM_FLAG_ZOH) >= slots(2, 1, 8192, 64)
+    # a chunk length given: one group per launch, no slots
+    one = need(batch=1, d_inner=8192, d_state=64, seqlen=128, chunk_size=64)
+    assert 0 < one < slots(4, 1, 8192, 128) <= need(batch=1, d_inner=8192, d_state=64,
+                                                    seqlen=128)
+
+
 def test_backward_plan_and_validation(lib):
     """ssm_scan_bwd: any d_state up to 256 (Euler or ZOH, same workspace;
     above 16 in groups of 16 states, without packed sequences or forward

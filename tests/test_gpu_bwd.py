@@ -7,6 +7,7 @@ tails), gate on and off, start state and upstream last-state gradient on and
 off, d_state 1..16, fp32 and bf16 inputs; exact-integer inputs bit for bit;
 run-to-run identity.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -365,6 +366,33 @@ def test_backward_state_groups(dev, io, N, zoh, K, gate, with_state):
     d_inner, L = (24, 200) if N > 64 else (40, 300)
     say(f"bwd state groups N={N} io={io} zoh={zoh} K={K} gate={gate} state={with_state}")
     _, errs = run_case(dev, 2, d_inner, N, L, io, gate, with_state, K, seed=N + K, zoh=zoh)
+    for k, e in errs.items():
+        assert e <= GRAD_TOL, (k, e)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,zoh,P", [
+    ((1, 8192, 64, 128), False, 4),   # four groups in one launch
+    ((1, 8192, 80, 96), False, 4),    # five groups: a launch of four, then one
+    ((2, 4096, 48, 64), False, 3),    # three groups side by side, two batch rows
+    ((1, 8192, 32, 64), True, 2),     # zero-order hold (one wavefront per SIMD): two
+])
+@pytest.mark.parametrize("gate,with_state", [(True, True), (False, False)])
+def test_backward_state_groups_side_by_side(dev, io, shape, zoh, P, gate, with_state):
+    """d_state above 16 with enough channel blocks that P groups of 16
+    states fill the GPU together: they run side by side in one launch, each
+    over the whole sequence, adding du, ddelta and dz into P slots that are
+    summed at the end.  Every gradient against the oracle's reverse walk."""
+    batch, d_inner, N, L = shape
+    d = ssm.make_desc(batch, d_inner, N, L, 1 if io == "bf16" else 0, 0,
+                      ssm.SSM_FLAG_ZOH if zoh else 0)
+    need = ssm.load_library().ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
+    # the P slots of du, ddelta and dz are part of the workspace
+    assert need >= 3 * P * batch * d_inner * L * 4
+    say(f"bwd state groups side by side shape={shape} io={io} zoh={zoh} P={P} gate={gate} "
+        f"state={with_state}")
+    _, errs = run_case(dev, batch, d_inner, N, L, io, gate, with_state, 0,
+                       seed=N + L + batch, zoh=zoh)
     for k, e in errs.items():
         assert e <= GRAD_TOL, (k, e)
 

@@ -360,11 +360,14 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
 // When one group's 16-channel blocks fill under half of the backward's
 // wavefront slots, P groups (up to 4) run side by side in one launch, each
 // as one chunk: no chunk operators to compute, where one group alone would
-// need its sequence cut into chunks to fill the chip.  Group z of a launch
-// adds its du, ddelta and dz to buffer slot z (groups z, z + P, ... in turn,
-// old + new), and the slots are summed in slot order at the end.  Otherwise
-// (P = 1) the groups run one launch each, group 0 writing du, ddelta and dz
-// and each later one adding to them in place.
+// need its sequence cut into chunks to fill the chip.  Each group writes its
+// du, ddelta and dz to a workspace slot of its own (no launch reads what
+// another wrote: adding in place costs a launch about a fifth more), and
+// the slots are summed in group order at the end; this path is taken while
+// the slots take at most kMaxGroupSlotBytes.  Otherwise (P = 1) the groups
+// run one launch each, group 0 writing du, ddelta and dz and each later one
+// adding to them in place.
+constexpr size_t kMaxGroupSlotBytes = size_t(8) << 30;
 struct BwdGroupPlan {
     ssm_desc sd{};   // the 16-state descriptor of one group
     BwdPlan sub;
@@ -389,7 +392,8 @@ ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
     p->sd.workspace = nullptr;
     p->sd.workspace_bytes = 0;
     p->sd.profile_begin = p->sd.profile_end = nullptr;
-    // groups side by side: P of them fill at least 3/4 of the slots
+    // groups side by side: P of them fill at least 3/4 of the wavefront
+    // slots, and the groups' du, ddelta and dz slots fit the bound
     const int64_t w = d->batch * ((d->d_inner + 15) / 16);
     const int64_t slots = (d->flags & SSM_FLAG_ZOH) ? kBwdSlots / 2 : kBwdSlots;
     p->P = 1;
@@ -397,7 +401,10 @@ ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
         int64_t P = slots / w;
         if (P > 4) P = 4;
         if (P > p->NG) P = p->NG;
-        if (P >= 2 && 4 * P * w >= 3 * slots) p->P = P;
+        const size_t out = align_up(B * D * L * sizeof(float));
+        if (P >= 2 && 4 * P * w >= 3 * slots &&
+            3 * static_cast<size_t>(p->NG) * out <= kMaxGroupSlotBytes)
+            p->P = P;
     }
     if (p->P > 1) p->sd.chunk_size = static_cast<int64_t>((L + 15) / 16 * 16);   // one chunk
     ssm_status s2 = make_bwd_plan(&p->sd, &p->sub);
@@ -415,6 +422,7 @@ ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
     p->s_dBC = align_up(B * 16 * L * sizeof(float));
     p->s_db = align_up(D * sizeof(float));
     p->s_out = P > 1 ? align_up(B * D * L * sizeof(float)) : 0;
+    const size_t S = P > 1 ? static_cast<size_t>(p->NG) : 0;   // a slot per group
     size_t off = 0;
     auto take = [&](size_t &o, size_t slot) { o = off; off += P * slot; };
     take(p->off_sub, p->s_sub);
@@ -428,9 +436,10 @@ ssm_status make_bwd_group_plan(const ssm_desc *d, BwdGroupPlan *p) {
     take(p->off_dC, p->s_dBC);
     take(p->off_db, p->s_db);
     take(p->off_dh0, p->s_S);
-    take(p->off_du, p->s_out);
-    take(p->off_dd, p->s_out);
-    take(p->off_dz, p->s_out);
+    auto take_s = [&](size_t &o, size_t slot) { o = off; off += S * slot; };
+    take_s(p->off_du, p->s_out);
+    take_s(p->off_dd, p->s_out);
+    take_s(p->off_dz, p->s_out);
     p->bytes = off;
     return SSM_OK;
 }
@@ -747,22 +756,23 @@ ssm_status bwd_groups(const ssm_desc *desc, const void *u, const void *delta, co
         if (e != hipSuccess) return SSM_ERR_HIP;
         x.gz = np;
         const bool first = g0 == 0;
+        const int64_t s0 = g0 * x.gs_out;   // groups g0 .. g0 + np - 1: their own slots
         const ssm_status sst = bwd_single(
             &sd, u, delta, Ag, Bg, Cg, first ? D : nullptr, z, delta_bias, softplus_flag, h0g,
-            nullptr, 0, nullptr, dy, dlg, du_s, dd_s, dAg, dBg, dCg, first ? dD : nullptr, dz_s,
-            db_s, dh0g, first ? 0 : 1, stream, &x);
+            nullptr, 0, nullptr, dy, dlg, du_s + s0, dd_s + s0, dAg, dBg, dCg,
+            first ? dD : nullptr, dz_s ? dz_s + s0 : nullptr, db_s, dh0g, 0, stream, &x);
         if (sst != SSM_OK) return sst;
         e = scatter(g0, np);
         if (e == hipSuccess && db_s)   // d(bias) in group order
             e = ssm::launch_accumulate(ddelta_bias, db_s, Dn, s, np, x.gs_db);
         if (e != hipSuccess) return SSM_ERR_HIP;
     }
-    // du, ddelta, dz: the slots summed in slot order
-    const int P = static_cast<int>(p.P);
+    // du, ddelta, dz: the groups' slots summed in group order
+    const int ng = static_cast<int>(p.NG);
     const int64_t n = Bn * Dn * L;
-    e = ssm::launch_sum_slots(du, du_s, P, x.gs_out, n, s);
-    if (e == hipSuccess) e = ssm::launch_sum_slots(ddelta, dd_s, P, x.gs_out, n, s);
-    if (e == hipSuccess && dz_s) e = ssm::launch_sum_slots(dz, dz_s, P, x.gs_out, n, s);
+    e = ssm::launch_sum_slots(du, du_s, ng, x.gs_out, n, s);
+    if (e == hipSuccess) e = ssm::launch_sum_slots(ddelta, dd_s, ng, x.gs_out, n, s);
+    if (e == hipSuccess && dz_s) e = ssm::launch_sum_slots(dz, dz_s, ng, x.gs_out, n, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

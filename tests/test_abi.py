@@ -255,10 +255,11 @@ def test_flags_validation(lib):
 
 def test_backward_state_groups_side_by_side_plan(lib):
     """d_state > 16: groups of 16 states run side by side (one chunk each, du,
-    ddelta and dz summed through P slots of the workspace) when one group's
-    16-channel blocks fill under half of the 2048 wavefront slots (1024 with
-    ZOH), P <= 4 groups fill at least three quarters and no chunk length is
-    given; otherwise one group per launch.  Seen through the workspace size."""
+    ddelta and dz written to a workspace slot per group and summed at the
+    end) when one group's 16-channel blocks fill under half of the 2048
+    wavefront slots (1024 with ZOH), P <= 4 groups fill at least three
+    quarters, no chunk length is given and the slots take at most 8 GiB;
+    otherwise one group per launch.  Seen through the workspace size."""
     def need(**kw):
         return lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(desc(**kw)))
     slots = lambda P, b, d, L: 3 * P * _al(b * d * L * 4)
@@ -270,10 +271,16 @@ def test_backward_state_groups_side_by_side_plan(lib):
     # ZOH: 1024 slots, two groups of 512 blocks
     assert need(batch=1, d_inner=8192, d_state=32, seqlen=64,
                 flags=ssm.SSM_FLAG_ZOH) >= slots(2, 1, 8192, 64)
+    # a slot per group: five groups, five slots
+    assert need(batch=1, d_inner=8192, d_state=80, seqlen=96) >= slots(5, 1, 8192, 96)
     # a chunk length given: one group per launch, no slots
     one = need(batch=1, d_inner=8192, d_state=64, seqlen=128, chunk_size=64)
     assert 0 < one < slots(4, 1, 8192, 128) <= need(batch=1, d_inner=8192, d_state=64,
                                                     seqlen=128)
+    # slots beyond 8 GiB (16 groups x 3 x 2 GiB): one group per launch
+    big = need(batch=1, d_inner=8192, d_state=256, seqlen=65536)
+    assert 0 < big < slots(16, 1, 8192, 65536)
+    assert need(batch=1, d_inner=8192, d_state=256, seqlen=1024) >= slots(16, 1, 8192, 1024)
 
 
 def test_backward_plan_and_validation(lib):

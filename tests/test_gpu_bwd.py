@@ -381,14 +381,15 @@ def test_backward_state_groups(dev, io, N, zoh, K, gate, with_state):
 def test_backward_state_groups_side_by_side(dev, io, shape, zoh, P, gate, with_state):
     """d_state above 16 with enough channel blocks that P groups of 16
     states fill the GPU together: they run side by side in one launch, each
-    over the whole sequence, adding du, ddelta and dz into P slots that are
-    summed at the end.  Every gradient against the oracle's reverse walk."""
+    over the whole sequence, writing du, ddelta and dz to a workspace slot per
+    group; the slots are summed at the end.  Every gradient against the
+    oracle's reverse walk."""
     batch, d_inner, N, L = shape
     d = ssm.make_desc(batch, d_inner, N, L, 1 if io == "bf16" else 0, 0,
                       ssm.SSM_FLAG_ZOH if zoh else 0)
     need = ssm.load_library().ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
-    # the P slots of du, ddelta and dz are part of the workspace
-    assert need >= 3 * P * batch * d_inner * L * 4
+    # the groups' slots of du, ddelta and dz are part of the workspace
+    assert need >= 3 * ((N + 15) // 16) * batch * d_inner * L * 4
     say(f"bwd state groups side by side shape={shape} io={io} zoh={zoh} P={P} gate={gate} "
         f"state={with_state}")
     _, errs = run_case(dev, batch, d_inner, N, L, io, gate, with_state, 0,

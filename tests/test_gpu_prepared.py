@@ -6,7 +6,8 @@ inputs the buffers hold at that moment: inputs are overwritten in place
 between launches, and each result is compared with a plain call on the same
 inputs.  Covered: the forward pass (plain, with start states and packed
 sequences, with checkpoints), the fused convolution, the decode step (whose
-state is updated in place), and the backward pass.
+state is updated in place), and the backward pass (also with d_state above
+16, captured in a graph).
 """
 import sys
 
@@ -165,3 +166,43 @@ def test_training_step_in_a_graph(dev, K):
             if v is not None:
                 assert torch.equal(v, grads_e[k]), (r, k)
         say(f"graph training step K={K} replay {r}: equal to eager")
+
+
+@pytest.mark.parametrize("shape", [(1, 8192, 64, 128),   # four groups side by side
+                                   (2, 40, 48, 300)])   # one group per launch
+def test_backward_state_groups_in_a_graph(dev, shape):
+    """The backward with d_state above 16 (start state, dlast, gate, delta
+    bias) captured as a graph: gathers, the backward launches, the reduces,
+    the scatters, the d(bias) additions and (side by side) the slot sums.
+    Three replays with new inputs written in place, host work and
+    synchronisation in between: every replay gives the bits of an eager call."""
+    import torch
+    batch, d_inner, N, L = shape
+    say(f"bwd state groups in a graph shape={shape}")
+    t = fresh(dev, batch, d_inner, N, L, "f32", 50)
+    dy = torch.randn(batch, d_inner, L, device=dev)
+    h0 = torch.randn(batch, d_inner, N, device=dev)
+    dl = torch.randn(batch, d_inner, N, device=dev)
+    bwd = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                           t["delta_bias"], initial_state=h0, dlast=dl, prepare=True)
+    bwd()                             # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bwd(stream=torch.cuda.current_stream().cuda_stream)
+    for r in range(3):
+        refill(t, fresh(dev, batch, d_inner, N, L, "f32", 60 + r))
+        dy.copy_(torch.randn(batch, d_inner, L, device=dev))
+        h0.copy_(torch.randn(batch, d_inner, N, device=dev))
+        dl.copy_(torch.randn(batch, d_inner, N, device=dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        grads_g = {k: (None if v is None else v.clone()) for k, v in bwd.result.items()}
+        grads_e = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"],
+                                   t["z"], t["delta_bias"], initial_state=h0, dlast=dl)
+        torch.cuda.synchronize()
+        for k, v in grads_g.items():
+            if v is not None:
+                assert torch.equal(v, grads_e[k]), (r, k)
+        say(f"  replay {r}: equal to eager")

@@ -7,7 +7,7 @@ between launches, and each result is compared with a plain call on the same
 inputs.  Covered: the forward pass (plain, with start states and packed
 sequences, with checkpoints), the fused convolution, the decode step (whose
 state is updated in place), and the backward pass (also with d_state above
-16, captured in a graph).
+16, captured in a graph); the in-wave scan captured in a graph.
 """
 import sys
 
@@ -205,4 +205,40 @@ def test_backward_state_groups_in_a_graph(dev, shape):
         for k, v in grads_g.items():
             if v is not None:
                 assert torch.equal(v, grads_e[k]), (r, k)
+        say(f"  replay {r}: equal to eager")
+
+
+@pytest.mark.parametrize("shape,io,K,h0", [
+    ((1, 2048, 16, 4096), "bf16", 256, False),   # segments of 16: event-counter ordering
+    ((2, 1536, 16, 1024), "f32", 0, True),       # segments of 8 (the library's plan), start states
+])
+def test_in_wave_scan_in_a_graph(dev, shape, io, K, h0):
+    """The in-wave scan captured as a graph and replayed three times with new
+    inputs written in place, host work and synchronisation in between: every
+    replay gives the bits of an eager call on the same inputs."""
+    import torch
+    batch, d_inner, N, L = shape
+    plan = ssm.scan_plan(batch, d_inner, N, L, 1 if io == "bf16" else 0, K)
+    assert plan.startswith("in-wave"), plan
+    say(f"in-wave scan in a graph shape={shape} io={io} plan '{plan}'")
+    t = fresh(dev, batch, d_inner, N, L, io, 70)
+    extra = dict(initial_state=torch.randn(batch, d_inner, N, device=dev)) if h0 else {}
+    args = [t[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    call = ssm.ssm_scan_fwd(*args, chunk_size=K, prepare=True, **extra)
+    call()                            # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(stream=torch.cuda.current_stream().cuda_stream)
+    for r in range(3):
+        refill(t, fresh(dev, batch, d_inner, N, L, io, 80 + r))
+        if h0:
+            extra["initial_state"].copy_(torch.randn(batch, d_inner, N, device=dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_g, h_g = (x.clone() for x in call.result)
+        y_e, h_e = ssm.ssm_scan_fwd(*args, chunk_size=K, **extra)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e) and torch.equal(h_g, h_e), r
         say(f"  replay {r}: equal to eager")

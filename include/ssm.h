@@ -252,6 +252,14 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
  * 0 for an invalid or unsupported descriptor.  Host-only. */
 size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc);
 
+/* The schedule that ssm_scan_bwd (with_ckpt 0) or ssm_scan_bwd_ex given the
+ * forward pass's checkpoints (with_ckpt 1; no packed sequences) runs for this
+ * descriptor, as a short static string (for example "one chunk", or "the
+ * blocks of a whole round in one chunk, the rest in chunks"), for logs and
+ * measurements; "invalid" for an invalid or unsupported descriptor.
+ * Host-only. */
+const char *ssm_scan_bwd_plan(const ssm_desc *desc, int with_ckpt);
+
 /* Backward pass of the scan: the gradients of the loss
  *   sum(dy * y) + sum(dlast * last_state)
  * with respect to every input, for upstream gradients dy (of y) and dlast

@@ -73,6 +73,8 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ssm_scan_chunk_size.restype = ctypes.c_int64
     lib.ssm_scan_plan.argtypes = [dp]
     lib.ssm_scan_plan.restype = ctypes.c_char_p
+    lib.ssm_scan_bwd_plan.argtypes = [dp, ctypes.c_int]
+    lib.ssm_scan_bwd_plan.restype = ctypes.c_char_p
     lib.ssm_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
@@ -221,6 +223,15 @@ def scan_plan(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0) -> str:
     """The schedule ssm_scan_fwd runs for these shapes (ssm_scan_plan)."""
     d = make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size)
     return load_library().ssm_scan_plan(ctypes.byref(d)).decode()
+
+
+def scan_bwd_plan(batch, d_inner, d_state, seqlen, io_dtype, chunk_size=0, zoh=False,
+                  with_ckpt=False) -> str:
+    """The schedule ssm_scan_bwd runs for these shapes, with or without the
+    forward's checkpoints (ssm_scan_bwd_plan)."""
+    d = make_desc(batch, d_inner, d_state, seqlen, io_dtype, chunk_size,
+                  SSM_FLAG_ZOH if zoh else 0)
+    return load_library().ssm_scan_bwd_plan(ctypes.byref(d), 1 if with_ckpt else 0).decode()
 
 
 # ---------------------------------------------------------------- entry points

@@ -266,6 +266,9 @@ uint64_t next_epoch() {
 struct BwdPlan {
     Plan f;
     int64_t n_tiles = 0;
+    // with the forward's checkpoints (no packed sequences): blocks below
+    // `split` in every batch row as one chunk, the others in J_s chunks of K_s
+    int64_t split = 0, J_s = 0, K_s = 0;
     size_t off_gend = 0, off_bdtsum = 0, off_ckpt = 0, off_dBp = 0, off_dCp = 0, off_dAp = 0,
            off_dDp = 0, off_dbp = 0, bytes = 0;
 };
@@ -328,11 +331,43 @@ ssm_status make_bwd_plan(const ssm_desc *d, BwdPlan *p) {
         f.J = (L + f.K - 1) / f.K;
     }
     f.fold = 1;
+    // Split by chunk count, for calls given the forward's checkpoints (no
+    // forward chunk operators needed): when the blocks take more than one
+    // round of wavefront slots, a whole round of them (the first `split`
+    // blocks of every batch row) runs as one chunk and only the rest is cut
+    // into chunks, which fill one more round.  The wavefronts then scan as
+    // many tokens per SIMD as with every block in chunks, and the reverse
+    // chunk aggregates cover the rest alone.
+    if (d->chunk_size == 0) {
+        const int64_t slots = (d->flags & SSM_FLAG_ZOH) ? kBwdSlots / 2 : kBwdSlots;
+        const int64_t w = d->batch * f.n_cblk;
+        const int64_t split = slots / d->batch;
+        if (w > slots && split >= 1 && split < f.n_cblk) {
+            const int64_t rest = d->batch * (f.n_cblk - split);
+            int64_t Js = slots / rest;
+            if (Js > kFoldMaxChunks) Js = kFoldMaxChunks;
+            if (Js > L / kMinAutoChunk) Js = L / kMinAutoChunk;
+            if (Js < 1) Js = 1;
+            int64_t Ks = (L + Js - 1) / Js;
+            Ks = (Ks + 15) / 16 * 16;
+            if (Ks > L) Ks = L;
+            Js = (L + Ks - 1) / Ks;
+            auto cost = [&](int64_t J, int64_t K, int64_t waves) {
+                return static_cast<double>((waves + slots - 1) / slots) * K * (1.0 + 0.01 * (J - 1));
+            };
+            const double c_split = static_cast<double>(L) + cost(Js, Ks, rest * Js);
+            const double c_all = cost(f.J, f.K, w * f.J);
+            if (Js > 1 && Js <= kFoldMaxChunks && c_split <= c_all) {
+                p->split = split; p->J_s = Js; p->K_s = Ks;
+            }
+        }
+    }
     const size_t B = static_cast<size_t>(d->batch), D = static_cast<size_t>(d->d_inner);
-    const size_t J = static_cast<size_t>(f.J);
+    // per-chunk arrays sized for either schedule
+    const size_t J = static_cast<size_t>(f.J > p->J_s ? f.J : p->J_s);
     p->n_tiles = (L + ssm::kBwdTile - 1) / ssm::kBwdTile;
     size_t off = 0;
-    if (f.J > 1) {
+    if (J > 1) {
         f.off_hend = off; off += align_up(B * D * J * 16 * sizeof(float));
         f.off_dtsum = off; off += align_up(B * D * J * sizeof(float));
         f.off_keep = off; off += align_up(B * J * sizeof(float));
@@ -620,7 +655,7 @@ ssm_status bwd_single(const ssm_desc *desc, const void *u, const void *delta, co
     g.accumulate = accumulate;
     g.dy = dy; g.dlast = dlast; g.du = du; g.ddelta = ddelta; g.dz = dz; g.dA = dA; g.dB = dB;
     g.dC = dC; g.dD = dD; g.dbias = ddelta_bias; g.dh0 = dh0; g.n_tiles = p.n_tiles;
-    if (f.J > 1) {
+    if (f.J > 1 || p.J_s > 1) {
         a.hend = reinterpret_cast<float *>(ws + f.off_hend);
         a.dtsum = reinterpret_cast<float *>(ws + f.off_dtsum);
         a.keep = reinterpret_cast<float *>(ws + f.off_keep);
@@ -635,6 +670,11 @@ ssm_status bwd_single(const ssm_desc *desc, const void *u, const void *delta, co
     g.dAp = reinterpret_cast<float *>(ws + p.off_dAp);
     g.dDp = reinterpret_cast<float *>(ws + p.off_dDp);
     g.dbp = reinterpret_cast<float *>(ws + p.off_dbp);
+    if (ckpt && !cu_seqlens && !side_by_side && p.split > 0) {
+        // the whole-round blocks in one chunk, the rest in J_s chunks
+        a.J = p.J_s; a.K = p.K_s;
+        g.split = p.split;
+    }
     if (side_by_side) {   // groups of states side by side: one chunk each
         if (f.J != 1 || cu_seqlens || ckpt) return SSM_ERR_UNSUPPORTED;
         const ssm::BwdArgs &x = *side_by_side;
@@ -944,6 +984,19 @@ ssm_status ssm_state_update(const ssm_desc *desc, float *state, const void *u, c
     a.state = state; a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.y = y;
     a.A = A; a.Dskip = D;
     return ssm::launch_update(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+const char *ssm_scan_bwd_plan(const ssm_desc *desc, int with_ckpt) {
+    if (desc && desc->d_state > 16) {
+        BwdGroupPlan p;
+        if (make_bwd_group_plan(desc, &p) != SSM_OK || with_ckpt) return "invalid";
+        return p.P > 1 ? "groups of 16 states side by side, one chunk each"
+                       : "groups of 16 states one per launch";
+    }
+    BwdPlan p;
+    if (make_bwd_plan(desc, &p) != SSM_OK) return "invalid";
+    if (with_ckpt && p.split > 0) return "the blocks of a whole round in one chunk, the rest in chunks";
+    return p.f.J <= 1 ? "one chunk" : "chunks joined by reverse chunk aggregates";
 }
 
 size_t ssm_scan_bwd_workspace_bytes(const ssm_desc *desc) {

@@ -257,9 +257,11 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
 
     const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
-    const int64_t b = blockIdx.x / a.n_cblk;
+    const int64_t nbr = g.ncb ? g.ncb : a.n_cblk;   // blocks of a row in this launch
+    const int64_t b = blockIdx.x / nbr;
     const int64_t j = static_cast<int64_t>(blockIdx.y) + 1;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x % a.n_cblk) * kQC;
+    const int64_t d0 = (g.cblk0 + static_cast<int64_t>(blockIdx.x % nbr)) * kQC;
+    const int64_t Jl = g.Jl ? g.Jl : a.J;
     const int64_t d = d0 + c;
     const bool lane_ok = d < a.D;
     const int64_t L = a.L;
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(ScanArgs a, BwdArgs g) {
         __syncthreads();
     }
     if (!lane_ok) return;
-    const size_t cd = (static_cast<size_t>(b) * a.D + d) * a.J + j;
+    const size_t cd = (static_cast<size_t>(b) * a.D + d) * Jl + j;
     *reinterpret_cast<float4 *>(g.gend + cd * 16 + 4 * q) = make_float4(G[0], G[1], G[2], G[3]);
     if (q == 0) g.bdtsum[cd] = dts;
 }
@@ -425,10 +427,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
 
     const int lane = threadIdx.x;
     const int c = lane & 15, q = lane >> 4;
-    const int64_t b = blockIdx.x / a.n_cblk;
-    const int64_t cblk = blockIdx.x % a.n_cblk;
+    const int64_t nbr = g.ncb ? g.ncb : a.n_cblk;   // blocks of a row in this launch
+    const int64_t b = blockIdx.x / nbr;
+    const int64_t cblk = g.cblk0 + blockIdx.x % nbr;
     const int64_t j = blockIdx.y;
     const int64_t d0 = cblk * kQC;
+    const int64_t Jl = g.Jl ? g.Jl : a.J;           // chunks per channel in the arrays
     const int64_t d = d0 + c;
     const bool lane_ok = d < a.D;
     const int64_t L = a.L;
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
         An[k] = (lane_ok && n < a.N) ? v : 0.0f;
         A2[k] = An[k] * kLog2e;
     }
-    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * a.J;
+    const size_t cd0 = (static_cast<size_t>(b) * a.D + dcl) * Jl;
     const size_t cd = cd0 + j;
 
     // ---- start state of the chunk (forward) and the gradient arriving at its
@@ -904,7 +908,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)
     db_acc = halves_sum(rows_pair_sum(db_acc));
     if (!lane_ok) return;
     if (q == 0) {
-        const size_t o = (static_cast<size_t>(b) * a.D + d) * a.J + j;
+        const size_t o = (static_cast<size_t>(b) * a.D + d) * Jl + j;
         g.dDp[o] = dD_acc;
         g.dbp[o] = db_acc;
     }
@@ -962,21 +966,26 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
         return;
     }
     const int64_t ia = i - nbc;
+    // chunks of a channel: one below the split, J above; Jl per channel in the arrays
+    const int64_t Jl = g.Jl ? g.Jl : a.J;
+    auto chunks_of = [&](int64_t dd) { return dd / 16 < g.split ? int64_t(1) : a.J; };
     if (ia < nA) {
         const int64_t dd = ia / a.N, n = ia % a.N;
+        const int64_t Jd = chunks_of(dd);
         float s = 0.0f;
         for (int64_t b = 0; b < a.Bsz; ++b)
-            for (int64_t j = 0; j < a.J; ++j)
-                s += g.dAp[((static_cast<size_t>(b) * a.D + dd) * a.J + j) * 16 + n];
+            for (int64_t j = 0; j < Jd; ++j)
+                s += g.dAp[((static_cast<size_t>(b) * a.D + dd) * Jl + j) * 16 + n];
         g.dA[ia] = s;
         return;
     }
     const int64_t id = ia - nA;
     if (id < a.D) {
+        const int64_t Jd = chunks_of(id);
         float sD = 0.0f, sb = 0.0f;
         for (int64_t b = 0; b < a.Bsz; ++b)
-            for (int64_t j = 0; j < a.J; ++j) {
-                const size_t o = (static_cast<size_t>(b) * a.D + id) * a.J + j;
+            for (int64_t j = 0; j < Jd; ++j) {
+                const size_t o = (static_cast<size_t>(b) * a.D + id) * Jl + j;
                 sD += g.dDp[o];
                 sb += g.dbp[o];
             }
@@ -991,32 +1000,58 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ScanArgs a, BwdArgs g) 
 // sequences never accumulate: the groups of states are not run for them).
 template <class IO, bool EXT, bool ZOH>
 static hipError_t launch_bwd_io(const ScanArgs &a, const BwdArgs &g, hipStream_t s) {
-    const unsigned gx = static_cast<unsigned>(a.n_cblk * a.Bsz);
-    if (a.J > 1) {
-        if (!g.ckpt_given) {   // the forward chunk operators, for the start states
-            const hipError_t e = launch_scan_agg(a, s);
-            if (e != hipSuccess) return e;
-        }
-        // 16-byte pieces of delta, dy, z and C need whole pieces per row and
-        // aligned rows
-        constexpr int VW = Seg<IO>::VW;
-        auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-        const bool vec = a.L % VW == 0 && al(a.delta) && al(g.dy) && (!a.z || al(a.z)) &&
-                         al(a.C);
-        const dim3 ag(gx, static_cast<unsigned>(a.J - 1));
-        if (vec)
-            hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, true>), ag, dim3(64), 0, s, a, g);
-        else
-            hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, false>), ag, dim3(64), 0, s, a, g);
-    }
-    // groups side by side run one chunk each, without packed sequences
+    // groups side by side run one chunk each, without packed sequences; a
+    // split by chunk count needs the forward's checkpoints and no packing
     const unsigned gz = g.gz > 1 ? static_cast<unsigned>(g.gz) : 1u;
     if (gz > 1 && (a.J != 1 || a.cu)) return hipErrorInvalidValue;
-    const dim3 grid(gx, static_cast<unsigned>(a.J), gz);
-    if (g.accumulate && (ZOH || !EXT))
-        hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, (ZOH || !EXT)>), grid, dim3(64), 0, s, a, g);
-    else
-        hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, false>), grid, dim3(64), 0, s, a, g);
+    if (g.split > 0 && (!g.ckpt_given || a.cu || gz > 1 || g.split >= a.n_cblk))
+        return hipErrorInvalidValue;
+    // the blocks of one launch: nbr per batch row (reverse chunk aggregates
+    // first when they run in several chunks)
+    auto run = [&](const ScanArgs &aa, const BwdArgs &gg, int64_t nbr) {
+        const unsigned gx = static_cast<unsigned>(nbr * aa.Bsz);
+        if (aa.J > 1) {
+            if (!gg.ckpt_given) {   // the forward chunk operators, for the start states
+                const hipError_t e = launch_scan_agg(aa, s);
+                if (e != hipSuccess) return e;
+            }
+            // 16-byte pieces of delta, dy, z and C need whole pieces per row and
+            // aligned rows
+            constexpr int VW = Seg<IO>::VW;
+            auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+            const bool vec = aa.L % VW == 0 && al(aa.delta) && al(gg.dy) && (!aa.z || al(aa.z)) &&
+                             al(aa.C);
+            const dim3 ag(gx, static_cast<unsigned>(aa.J - 1));
+            if (vec)
+                hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, true>), ag, dim3(64), 0, s, aa, gg);
+            else
+                hipLaunchKernelGGL((bwd_agg_kernel<IO, EXT, false>), ag, dim3(64), 0, s, aa, gg);
+        }
+        const dim3 grid(gx, static_cast<unsigned>(aa.J), gz);
+        if (gg.accumulate && (ZOH || !EXT))
+            hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, (ZOH || !EXT)>), grid, dim3(64), 0, s, aa,
+                               gg);
+        else
+            hipLaunchKernelGGL((bwd_kernel<IO, EXT, ZOH, false>), grid, dim3(64), 0, s, aa, gg);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    if (g.split > 0) {
+        // the blocks past the split in J chunks, then those below it as one
+        // chunk (a whole round of wavefronts); the arrays keep J chunks each
+        BwdArgs gr = g;
+        gr.cblk0 = g.split; gr.ncb = a.n_cblk - g.split; gr.Jl = a.J;
+        e = run(a, gr, gr.ncb);
+        if (e != hipSuccess) return e;
+        ScanArgs af = a;
+        af.J = 1; af.K = a.L;
+        BwdArgs gf = g;
+        gf.cblk0 = 0; gf.ncb = g.split; gf.Jl = a.J;
+        e = run(af, gf, gf.ncb);
+    } else {
+        e = run(a, g, a.n_cblk);
+    }
+    if (e != hipSuccess) return e;
     const int64_t total = a.Bsz * a.N * a.L + a.D * a.N + a.D;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256), 1, gz),
                        dim3(256), 0, s, a, g);

@@ -99,6 +99,12 @@ struct BwdArgs {
     int64_t gs_ws;              // bytes: the workspace views (ckpt, dBp, dCp, dAp, dDp, dbp)
     int64_t gs_dBC;             // floats: dB and dC (batch, 16, L)
     int64_t gs_db;              // floats: dbias (d_inner)
+    // Blocks split by chunk count (forward checkpoints given, no packed
+    // sequences): in every batch row, channel blocks below `split` run as one
+    // chunk, the others in J chunks.  A launch covers blocks cblk0 .. cblk0 +
+    // ncb - 1 of every row (ncb 0: all of them); the per-chunk arrays (gend,
+    // bdtsum, dAp, dDp, dbp) hold Jl chunks per channel (0: J).
+    int64_t split, cblk0, ncb, Jl;
 };
 
 hipError_t launch_bwd(const ScanArgs &a, const BwdArgs &g, hipStream_t s);

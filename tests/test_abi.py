@@ -29,7 +29,8 @@ def test_header_declares_expected_entry_points():
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_ex",
               "ssm_scan_fwd_ckpt", "ssm_scan_ckpt_bytes",
               "ssm_scan_bwd_workspace_bytes", "ssm_state_update", "ssm_scan_workspace_bytes",
-              "ssm_scan_chunk_size", "ssm_scan_plan", "ssm_status_string", "ssm_version"):
+              "ssm_scan_chunk_size", "ssm_scan_plan", "ssm_scan_bwd_plan", "ssm_status_string",
+              "ssm_version"):
         assert n in names
 
 
@@ -281,6 +282,30 @@ def test_backward_state_groups_side_by_side_plan(lib):
     big = need(batch=1, d_inner=8192, d_state=256, seqlen=65536)
     assert 0 < big < slots(16, 1, 8192, 65536)
     assert need(batch=1, d_inner=8192, d_state=256, seqlen=1024) >= slots(16, 1, 8192, 1024)
+
+
+def test_backward_plan_strings(lib):
+    """ssm_scan_bwd_plan: with the forward's checkpoints and more 16-channel
+    blocks than one round of wavefront slots (2048; 1024 with ZOH), a whole
+    round of blocks runs as one chunk and the rest in chunks; otherwise, as
+    without checkpoints."""
+    p = ssm.scan_bwd_plan
+    split = "the blocks of a whole round in one chunk, the rest in chunks"
+    chunks = "chunks joined by reverse chunk aggregates"
+    assert p(8, 5120, 16, 2048, 1, with_ckpt=True) == split          # the Mamba-2.8B layer
+    assert p(8, 5120, 16, 2048, 1) == chunks
+    assert p(3, 12288, 16, 256, 0, with_ckpt=True) == split
+    assert p(2, 24576, 16, 128, 0, with_ckpt=True) == split
+    assert p(3, 6144, 16, 128, 0, zoh=True, with_ckpt=True) == split
+    # a chunk length given; blocks within one round; a single chunk
+    assert p(8, 5120, 16, 2048, 1, chunk_size=512, with_ckpt=True) == chunks
+    assert p(2, 64, 16, 2048, 0, with_ckpt=True) == chunks
+    assert p(4, 8192, 16, 300, 0, with_ckpt=True) == "one chunk"
+    # d_state above 16 (never with checkpoints)
+    assert p(4, 2048, 256, 4096, 0) == "groups of 16 states side by side, one chunk each"
+    assert p(2, 40, 48, 300, 0) == "groups of 16 states one per launch"
+    assert p(4, 2048, 256, 4096, 0, with_ckpt=True) == "invalid"
+    assert p(2, 40, 257, 300, 0) == "invalid"
 
 
 def test_backward_plan_and_validation(lib):

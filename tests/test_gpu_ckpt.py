@@ -209,6 +209,27 @@ def test_backward_with_checkpoints(dev, io, shape, K_fwd, K_bwd, zoh):
         assert e_fast <= GRAD_TOL and e_pair <= GRAD_TOL, k
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,zoh", [((3, 12288, 16, 256), False), ((2, 24576, 16, 128), False),
+                                       ((3, 6144, 16, 128), True)])
+def test_backward_with_checkpoints_split(dev, io, shape, zoh):
+    """More 16-channel blocks than one round of wavefront slots: given the
+    checkpoints, the blocks of a whole round run as one chunk and the rest in
+    chunks (two launches, the per-chunk sums over each channel's own chunk
+    count).  Every gradient against the oracle and against the backward
+    without checkpoints (which cuts every block into chunks)."""
+    batch, d_inner, N, L = shape
+    plan = ssm.scan_bwd_plan(batch, d_inner, N, L, 1 if io == "bf16" else 0, zoh=zoh,
+                             with_ckpt=True)
+    assert plan.startswith("the blocks of a whole round"), plan
+    say(f"bwd with checkpoints, split: shape={shape} io={io} zoh={zoh}")
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=True,
+                                      seed=L + d_inner + zoh)
+    worst = backward_pair(dev, inp, io, N, L, 0, 0, zoh, True, seed=L + 1)
+    for k, (e_fast, e_pair, _) in worst.items():
+        assert e_fast <= GRAD_TOL and e_pair <= GRAD_TOL, k
+
+
 @pytest.mark.parametrize("K_fwd,K_bwd", [(0, 0), (32, 16)])
 @pytest.mark.parametrize("zoh", [False, True])
 def test_backward_with_checkpoints_packed(dev, K_fwd, K_bwd, zoh):

@@ -352,7 +352,9 @@ def bench_backward(args, torch, ssm, dev):
                                f"{' + gate' if gate else ''}"
                                f"{', forward checkpoints given' if ck is not None else ''}",
                    "batch": batch, "d_inner": d_inner, "d_state": N, "seqlen": L,
-                   "io_dtype": io, "gate": gate, "checkpoints": ck is not None},
+                   "io_dtype": io, "gate": gate, "checkpoints": ck is not None,
+                   "plan": ssm.scan_bwd_plan(batch, d_inner, N, L, 1 if io == "bf16" else 0,
+                                             args.chunk or 0, with_ckpt=ck is not None)},
         "roofline": {"bound": "alu", "achieved": tflops, "peak": VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / VALU_PEAK_TFLOPS, "traffic": None,
                      "peak_nonpacked": VALU_PEAK_NONPACKED_TFLOPS,

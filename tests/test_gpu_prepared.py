@@ -242,3 +242,44 @@ def test_in_wave_scan_in_a_graph(dev, shape, io, K, h0):
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_e) and torch.equal(h_g, h_e), r
         say(f"  replay {r}: equal to eager")
+
+
+def test_training_step_split_backward_in_a_graph(dev):
+    """A training step whose backward, given the checkpoints, runs the blocks
+    of a whole round as one chunk and the rest in chunks (two backward
+    launches, reverse aggregates for the second), captured as one graph and
+    replayed three times with new inputs: every replay gives the bits of an
+    eager step."""
+    import torch
+    batch, d_inner, N, L = 2, 24576, 16, 128
+    plan = ssm.scan_bwd_plan(batch, d_inner, N, L, 0, with_ckpt=True)
+    assert plan.startswith("the blocks of a whole round"), plan
+    say(f"graph training step, split backward: '{plan}'")
+    t = fresh(dev, batch, d_inner, N, L, "f32", 90)
+    dy = torch.randn(batch, d_inner, L, device=dev)
+    ck = torch.empty(ssm.ckpt_shape(batch, d_inner, L), device=dev)
+    args = [t[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+    fwd = ssm.ssm_scan_fwd(*args, ckpt=ck, prepare=True)
+    bwd = ssm.ssm_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["z"],
+                           t["delta_bias"], ckpt=ck, prepare=True)
+    fwd(); bwd()                      # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        fwd(stream=cap)
+        bwd(stream=cap)
+    for r in range(3):
+        refill(t, fresh(dev, batch, d_inner, N, L, "f32", 91 + r))
+        dy.copy_(torch.randn(batch, d_inner, L, device=dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        grads_g = {k: (None if v is None else v.clone()) for k, v in bwd.result.items()}
+        fwd()
+        grads_e = bwd()
+        torch.cuda.synchronize()
+        for k, v in grads_g.items():
+            if v is not None:
+                assert torch.equal(v, grads_e[k]), (r, k)
+        say(f"  replay {r}: equal to eager")

@@ -130,6 +130,32 @@ def test_forward_checkpoints_equal_oracle_states(dev, shape, io, zoh):
     assert np.all(ck[:, :, :, N:] == 0.0)   # states past d_state
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 24576, 16, 256), (2, 10240, 16, 512)])
+def test_forward_checkpoints_split_walks(dev, shape, io):
+    """Shapes that run the balanced serial walks (the blocks past the last
+    whole round in two chunks, the second starting from the first's end
+    state): checkpoints come from the same plan, those of the second chunk
+    from its start state on.  Against the oracle's tile states, with start
+    states; y and last_state bit-equal to the call without checkpoints."""
+    import torch
+    batch, d_inner, N, L = shape
+    plan = ssm.scan_plan(batch, d_inner, N, L, 1 if io == "bf16" else 0)
+    assert plan.startswith("one chunk, the blocks past"), plan
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=True,
+                                      seed=L + d_inner)
+    h0 = np.random.default_rng(8).standard_normal((batch, d_inner, N)).astype(np.float32)
+    t = {k: to_device(inp.get(k), dev) for k in KEYS}
+    ck = forward_with_ckpt(dev, t, N, L, 0, False, h0=torch.from_numpy(h0).to(dev))
+    ck = ck.cpu().numpy().astype(np.float64)
+    f = decoded(inp)
+    tiles = tiles_to_check(ck.shape[2], 0)
+    ref = oracle_tile_states(f, h0.astype(np.float64), tiles, False)
+    err = max(floored_err(ck[:, :, i, :N], r) for i, r in ref.items())
+    say(f"ckpt split walks {shape} io={io}: {len(ref)} tiles, err={err:.3e}")
+    assert err <= TOL[io]
+
+
 def test_forward_checkpoints_packed_sequences(dev):
     import torch
     lens = [37, 0, 1, 200, 16, 0, 64, 5, 129, 0, 300]

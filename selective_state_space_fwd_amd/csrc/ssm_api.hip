@@ -124,15 +124,11 @@ constexpr int64_t kTsMaxRows = 8192;
 constexpr int64_t kTsRows16 = 2048;
 
 // fwd: the plan of a forward scan, which may run the chunked quad path as
-// one launch (long chunks) and, for calls without packed sequences, the
-// fused convolution or checkpoints (lean), the in-wave scan.  The
-// backward, which reuses the chunk-aggregate pass on its own, passes false.
-// walks: the balanced serial walks may be planned (calls without packed
-// sequences or the fused convolution; their passes write checkpoints too);
-// by default, as lean.
-ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = true,
-                     int walks = -1) {
-    const bool walks_ok = walks < 0 ? lean : walks != 0;
+// one launch (long chunks) and, for calls without packed sequences or the
+// fused convolution (lean), the in-wave scan or the balanced serial walks
+// (both write checkpoints when asked).  The backward, which reuses the
+// chunk-aggregate pass on its own, passes false.
+ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = true) {
     const ssm_status st = check_desc(d);
     if (st != SSM_OK) return st;
     if (d->chunk_size < 0 || (d->chunk_size > 0 && d->chunk_size % 16 != 0))
@@ -175,7 +171,7 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = tr
     // grid, and rows take whole 16-byte pieces (the element path needs more
     // registers than three wavefronts per SIMD leave it).
     const int64_t vw = d->io_dtype == SSM_BF16 ? 8 : 4;
-    if (fwd && walks_ok && p->quad && (d->flags & SSM_FLAG_ZOH) == 0 && d->chunk_size == 0 &&
+    if (fwd && lean && p->quad && (d->flags & SSM_FLAG_ZOH) == 0 && d->chunk_size == 0 &&
         L >= 256 && L % vw == 0) {
         const int64_t W = d->batch * p->n_cblk;
         const int64_t rounds = W / kSimds, surplus = W - rounds * kSimds;
@@ -501,8 +497,8 @@ ssm_status scan_impl(const ssm_desc *desc, const void *u, const ConvSpec &cv, co
                      const int32_t *cu_seqlens, int64_t n_seqs, void *y, float *last_state,
                      float *ckpt, ssm_stream_t stream) {
     Plan p;
-    const bool lean = !cu_seqlens && cv.width == 0 && !ckpt;
-    ssm_status st = make_plan(desc, &p, true, lean, !cu_seqlens && cv.width == 0);
+    const bool lean = !cu_seqlens && cv.width == 0;
+    ssm_status st = make_plan(desc, &p, true, lean);
     if (st != SSM_OK) return st;
     const hipStream_t s = stream;
     if (cu_seqlens && (desc->batch != 1 || n_seqs < 1)) return SSM_ERR_BAD_SHAPE;
@@ -862,15 +858,13 @@ ssm_status scratch_address(hipStream_t stream, void **out) {
 extern "C" {
 
 size_t ssm_scan_workspace_bytes(const ssm_desc *desc) {
-    // enough for every forward entry point: calls with packed sequences, the
-    // fused convolution or checkpoints may plan chunks where a plain call
-    // runs the in-wave scan (none) or the balanced serial walks (their own)
-    Plan plain, other, ck;
+    // enough for every forward entry point: calls with packed sequences or
+    // the fused convolution may plan chunks where a plain call runs the
+    // in-wave scan (none) or the balanced serial walks (their own)
+    Plan plain, other;
     if (make_plan(desc, &plain, true, true) != SSM_OK) return 0;
     if (make_plan(desc, &other, true, false) != SSM_OK) return 0;
-    if (make_plan(desc, &ck, true, false, 1) != SSM_OK) return 0;   // checkpoints
-    size_t m = plain.bytes > other.bytes ? plain.bytes : other.bytes;
-    return m > ck.bytes ? m : ck.bytes;
+    return plain.bytes > other.bytes ? plain.bytes : other.bytes;
 }
 
 int64_t ssm_scan_chunk_size(const ssm_desc *desc) {

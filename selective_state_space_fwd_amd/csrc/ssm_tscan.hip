@@ -256,9 +256,11 @@ struct TsShape {
 // TS: tokens per segment (8 or 16); tiles of 16 TS tokens.
 // Occupancy: TS = 16 keeps 128 VGPRs of dA/dBu (two wavefronts per SIMD),
 // TS = 8 keeps 64 (three per SIMD).
-// GT: with the silu gate (z given); SPL: softplus on the step size.  Both are
-// template flags so that the tile loop holds no branch on them.
-template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL>
+// GT: with the silu gate (z given); SPL: softplus on the step size; CK: the
+// replay also writes the state entering every kBwdTile-token tile
+// (a.ckpt, for the backward pass).  All are template flags so that the tile
+// loop holds no branch on them.
+template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL, bool CK>
 __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_kernel(ScanArgs a) {
     using IT = typename IO::T;
     using SH = TsShape<IO, TS>;
@@ -275,6 +277,7 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     constexpr int BT = K / TPR;         // tokens of B (and C) per staging thread
     static_assert(TS % 4 == 0 && PT % 2 == 0 && PT * 4 == TS, "tile shape");
     static_assert(BT % 4 == 0 && TS % BT == 0, "staging pieces within a segment");
+    static_assert(TS % kBwdTile == 0, "checkpoint tiles start on segment tokens");
 
     __shared__ __attribute__((aligned(16))) float sB[NBUF * 16 * RS];
     __shared__ __attribute__((aligned(16))) float sC[NBUF * 16 * RS];
@@ -330,6 +333,10 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     float *sdt = sDT + wv * RS;
     float *sw = sW + wv * RS;
     float *sy = sY + wv * RS;
+    // CK: this lane's states 4q .. 4q+3 in the channel's checkpoint row
+    // (batch, d_inner, n_ck, 16); states past N hold zero, as h does there
+    float *const ckrow =
+        (CK && ch_ok) ? a.ckpt + (static_cast<size_t>(b) * a.D + d) * a.n_ck * 16 + 4 * q : nullptr;
 
     // a tile's inputs in registers (raw words), loaded PF tiles ahead
     struct Regs {
@@ -562,6 +569,14 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = g4 + j;
+                if constexpr (CK) {
+                    if (t % kBwdTile == 0) {   // h enters token t0 + s TS + t
+                        const int64_t tok = t0 + s * TS + t;
+                        if (ch_ok && (!MASK || tok < L))
+                            *reinterpret_cast<float4 *>(ckrow + (tok / kBwdTile) * 16) =
+                                make_float4(h[0], h[1], h[2], h[3]);
+                    }
+                }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) h[k] = __builtin_fmaf(eA[t][k], h[k], eB[t][k]);
                 acc[j] = __builtin_fmaf(C4[0][j], h[0], __builtin_fmaf(C4[1][j], h[1],
@@ -649,17 +664,23 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     }
 }
 
-template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL>
-static hipError_t launch_tscan_one(const ScanArgs &a, hipStream_t s) {
+template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL, bool CK>
+static hipError_t launch_tscan_ck(const ScanArgs &a, hipStream_t s) {
     constexpr int W = TsShape<IO, TS>::W;
     const dim3 grid(static_cast<unsigned>(a.n_cblk * a.Bsz));
     const dim3 block(64 * W);
     if (a.ev_begin && a.ev_end)
-        hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL>), grid, block, 0, s,
+        hipExtLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL, CK>), grid, block, 0, s,
                               a.ev_begin, a.ev_end, 0, a);
     else
-        hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((tscan_kernel<IO, TS, VEC, ZOH, GT, SPL, CK>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+
+template <class IO, int TS, bool VEC, bool ZOH, bool GT, bool SPL>
+static hipError_t launch_tscan_one(const ScanArgs &a, hipStream_t s) {
+    return a.ckpt ? launch_tscan_ck<IO, TS, VEC, ZOH, GT, SPL, true>(a, s)
+                  : launch_tscan_ck<IO, TS, VEC, ZOH, GT, SPL, false>(a, s);
 }
 
 template <class IO, int TS, bool VEC>

@@ -112,8 +112,8 @@ def test_workspace_and_chunk_plan(lib):
 def test_in_wave_plan_choice(lib):
     """Chunks of 128 or 256 tokens requested, or chosen by the library for
     1024 to 8192 channels, run as the in-wave scan (no workspace for a plain
-    call); the workspace query still covers the chunked plan that calls with
-    packed sequences, the convolution or checkpoints run."""
+    call, with or without checkpoints); the workspace query still covers the
+    chunked plan that calls with packed sequences or the convolution run."""
     def plan(**kw):
         d = desc(**kw)
         return (lib.ssm_scan_plan(ctypes.byref(d)).decode(),

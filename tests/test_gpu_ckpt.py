@@ -156,6 +156,35 @@ def test_forward_checkpoints_split_walks(dev, shape, io):
     assert err <= TOL[io]
 
 
+@pytest.mark.parametrize("zoh", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 40, 16, 300, 256), (1, 33, 5, 301, 128),
+                                   (1, 1024, 16, 512, 0)])
+def test_forward_checkpoints_in_wave_scan(dev, shape, io, zoh):
+    """Shapes that run the in-wave scan (chunks of 256 with a ragged token
+    tail, chunks of 128 with d_state 5, and the library's own choice on 16-byte
+    rows): its replay writes the checkpoints, two per segment of 16 tokens or
+    one per segment of 8.  Against the oracle's tile states, with start
+    states; y and last_state bit-equal to the call without checkpoints."""
+    import torch
+    batch, d_inner, N, L, K = shape
+    plan = ssm.scan_plan(batch, d_inner, N, L, 1 if io == "bf16" else 0, K)
+    assert plan.startswith("in-wave scan"), plan
+    inp = ssm_inputs.make_scan_inputs(batch, d_inner, N, L, io_dtype=io, gate=True,
+                                      seed=sum(shape) + zoh)
+    h0 = np.random.default_rng(9).standard_normal((batch, d_inner, N)).astype(np.float32)
+    t = {k: to_device(inp.get(k), dev) for k in KEYS}
+    ck = forward_with_ckpt(dev, t, N, L, K, zoh, h0=torch.from_numpy(h0).to(dev))
+    ck = ck.cpu().numpy().astype(np.float64)
+    f = decoded(inp)
+    tiles = tiles_to_check(ck.shape[2], K)
+    ref = oracle_tile_states(f, h0.astype(np.float64), tiles, zoh)
+    err = max(floored_err(ck[:, :, i, :N], r) for i, r in ref.items())
+    say(f"ckpt in-wave scan {shape} io={io} zoh={zoh}: {len(ref)} tiles, err={err:.3e}")
+    assert err <= TOL[io]
+    assert np.all(ck[:, :, :, N:] == 0.0)   # states past d_state
+
+
 def test_forward_checkpoints_packed_sequences(dev):
     import torch
     lens = [37, 0, 1, 200, 16, 0, 64, 5, 129, 0, 300]
@@ -224,7 +253,9 @@ GRAD_TOL = TOL["f32"]
 @pytest.mark.parametrize("shape,K_fwd,K_bwd", [((2, 40, 16, 300), 0, 0),
                                                ((2, 40, 16, 300), 16, 64),
                                                ((1, 33, 5, 301), 32, 16),
-                                               ((1, 24, 16, 3000), 1024, 0)])
+                                               ((1, 24, 16, 3000), 1024, 0),
+                                               ((2, 40, 16, 300), 256, 0),
+                                               ((1, 33, 5, 301), 128, 16)])
 @pytest.mark.parametrize("zoh", [False, True])
 def test_backward_with_checkpoints(dev, io, shape, K_fwd, K_bwd, zoh):
     batch, d_inner, N, L = shape

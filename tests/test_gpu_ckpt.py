@@ -8,9 +8,11 @@ sequence when sequences are packed).  A tile that starts a sequence is not
 compared: the backward restarts such a tile from the sequence's start state
 and never reads its checkpoint.
 
-The backward with checkpoints is held to the oracle's gradients at the same
-bar as the backward without them, for one chunk and many, the one-launch
-chunked forward, packed sequences and ZOH; the two backward results agree
+Every forward schedule writes them: the chunked passes, the one-launch
+chunked path, the balanced serial walks and the in-wave scan.  The backward
+with checkpoints is held to the oracle's gradients at the same bar as the
+backward without them, for one chunk and many, checkpoints from each of
+those schedules, packed sequences and ZOH; the two backward results agree
 with each other within that bar.
 """
 import sys

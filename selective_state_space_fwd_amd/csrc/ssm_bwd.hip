@@ -104,19 +104,8 @@ __device__ __forceinline__ float row_transpose_sum(float v0, float v1, float v2,
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Raw buffer views (a gfx9 buffer resource: base address, byte range, 32-bit
-// data format, no stride).  A load at or past the range returns 0 and a store
-// there is dropped: rows past d_inner or d_state read as zeros, and a lane
-// with nothing to store aims its store at kDrop.  Ranges are at most 2^31
-// bytes, so kDrop lies past every one of them.
-constexpr int kRsrcFormat = 0x00020000;
-constexpr uint32_t kDrop = 0x80000000u;
-using Rsrc = __amdgpu_buffer_rsrc_t;
-
-__device__ __forceinline__ Rsrc view(const void *p, uint64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
-                                             kRsrcFormat);
-}
+// Raw buffer views (view() in ssm_common.h): rows past d_inner or d_state
+// read as zeros, and a lane with nothing to store aims its store at kDrop.
 
 // B or C of state 4q + K at token T of a tile, taken from the lanes that
 // loaded the tile: lane 4n + T / 2 holds tokens T & ~1 (in v0) and T | 1 (in

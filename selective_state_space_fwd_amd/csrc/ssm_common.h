@@ -40,6 +40,20 @@ __device__ __forceinline__ cfloat *as_constant(const float *p) {
     return (cfloat *)(p);
 }
 
+// ---------------------------------------------------------------- buffer views
+// Raw buffer views (a gfx9 buffer resource: base address, byte range, 32-bit
+// data format, no stride).  A load at or past the range returns 0 and a store
+// there is dropped.  Ranges are below 2^31 bytes, so kDrop lies past every
+// one of them.
+constexpr int kRsrcFormat = 0x00020000;
+constexpr uint32_t kDrop = 0x80000000u;
+using Rsrc = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ Rsrc view(const void *p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes),
+                                             kRsrcFormat);
+}
+
 // ---------------------------------------------------------------- scheduling
 // Wavefronts that share a SIMD get its issue slots oldest first, so of two
 // wavefronts with equal work the younger runs its last tiles alone, at the

@@ -69,6 +69,8 @@ __device__ __forceinline__ float dpp_row(float old, float src) {
         __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, 0xF, false));
 }
 constexpr int kRowShr1 = 0x111;
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2, 3, 0, 1]
 constexpr int kRowNewBcast15 = 0x15F;
 
 // One step of the inclusive scan along a row, for the 4 states of a lane:
@@ -139,6 +141,48 @@ __device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ row,
                 if (i % 2 == 0) r.w[i / 2] = v; else r.w[i / 2] |= v << 16;
             }
         }
+    }
+}
+
+// NE elements at byte offset off of a buffer view, as raw words: one vector
+// access per 16 bytes, all in or all past the view's range (runs are aligned
+// to their size and ranges are whole rows); past it they read as zeros.
+template <class IO, int NE>
+__device__ __forceinline__ void load_view(Rsrc v, uint32_t off, Raw<IO, NE> &r) {
+    using R = Raw<IO, NE>;
+    if constexpr (R::NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < R::NW / 4; ++i) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(v, off + 16 * i, 0, 0);
+            r.w[4 * i] = x[0]; r.w[4 * i + 1] = x[1]; r.w[4 * i + 2] = x[2]; r.w[4 * i + 3] = x[3];
+        }
+    } else if constexpr (R::NW == 2) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(v, off, 0, 0);
+        r.w[0] = x[0]; r.w[1] = x[1];
+    } else {
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(v, off, 0, 0);
+    }
+}
+
+// NE values to byte offset off of a buffer view, converted to the I/O type
+// (bf16: round to nearest even); a run past the range is dropped.
+template <class IO, int NE>
+__device__ __forceinline__ void store_view(Rsrc v, uint32_t off, const float (&x)[NE]) {
+    constexpr bool F = std::is_same<IO, F32>::value;
+    constexpr int NW = F ? NE : NE / 2;
+    uint32_t w[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+        w[i] = F ? __float_as_uint(x[i]) : Seg<BF16>::pk(x[2 * i], x[2 * i + 1]);
+    if constexpr (NW == 4) {
+        using V4 = __attribute__((ext_vector_type(4))) unsigned int;
+        __builtin_amdgcn_raw_buffer_store_b128(V4{w[0], w[1], w[2], w[3]}, v, off, 0, 0);
+    } else if constexpr (NW == 2) {
+        using V2 = __attribute__((ext_vector_type(2))) unsigned int;
+        __builtin_amdgcn_raw_buffer_store_b64(V2{w[0], w[1]}, v, off, 0, 0);
+    } else {
+        static_assert(NW == 1, "runs of 1, 2 or 4 words");
+        __builtin_amdgcn_raw_buffer_store_b32(w[0], v, off, 0, 0);
     }
 }
 
@@ -295,7 +339,9 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     IT *__restrict__ y = static_cast<IT *>(a.y);
 
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;                    // wavefront: channel of the block
+    // wavefront: channel of the block (uniform, so that the row views
+    // below live in scalar registers)
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int q = lane >> 4;                    // row: states 4q .. 4q+3
     const int s = lane & 15;                    // time segment
@@ -352,38 +398,66 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     const IT *b_row = Bm + sbase;
     const IT *c_row = Cm + sbase;
     const int Li = static_cast<int>(L);
+    // VEC: the tile loads and the y stores go through wave-uniform buffer
+    // views: the channel's rows of u, delta, z and y (L elements each) and
+    // the batch row's N rows of B and C, past which rows n >= N read as
+    // zeros.  A lane's byte offsets are fixed plus the tile's first token;
+    // tokens at or past L read as zeros and their y stores are dropped.
+    // (The launch takes this path only when N L elements of B span less
+    // than 2^31 bytes.)
+    constexpr uint32_t ESZ = sizeof(IT);
+    const uint64_t row_bytes = VEC ? static_cast<uint64_t>(L) * ESZ : 0;
+    const Rsrc v_u = view(u_row, row_bytes), v_d = view(d_row, row_bytes);
+    const Rsrc v_z = view(z_row, row_bytes), v_y = view(y + rbase, row_bytes);
+    const uint64_t bc_bytes = VEC ? static_cast<uint64_t>(a.N) * L * ESZ : 0;
+    const Rsrc v_b = view(Bm + static_cast<size_t>(b) * a.N * L, bc_bytes);
+    const Rsrc v_c = view(Cm + static_cast<size_t>(b) * a.N * L, bc_bytes);
+    const uint32_t o_tok = static_cast<uint32_t>(lane * PT) * ESZ;
+    const uint32_t o_bc = (static_cast<uint32_t>(bn) * static_cast<uint32_t>(Li) + bt0) * ESZ;
     auto load_tile = [&](Regs &r, int64_t t0) {
         const int tl = static_cast<int>(t0) + lane * PT;
         const int tb = static_cast<int>(t0) + bt0;
+        const uint32_t ot = static_cast<uint32_t>(t0) * ESZ;
         // AHEAD stages B and C a tile before the tile's own loads are needed:
         // issued first, they can be waited for while u, delta and z are
         // still in flight (loads complete in issue order).  z next: the
         // compiler copies its registers at the loop's back edge, which then
         // waits for it alone.  The scheduling barriers keep that order.
+        auto ld_bc = [&] {
+            if constexpr (VEC) {
+                load_view<IO, BT>(v_b, o_bc + ot, r.b);
+                load_view<IO, BT>(v_c, o_bc + ot, r.c);
+            } else {
+                load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
+                load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+            }
+        };
+        auto ld_tok = [&](Rsrc v, const IT *row, Raw<IO, PT> &x) {
+            if constexpr (VEC) load_view<IO, PT>(v, o_tok + ot, x);
+            else load_raw<IO, PT, VEC>(row, tl, Li, x);
+        };
         if constexpr (AHEAD) {
-            load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);
-            load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+            ld_bc();
             __builtin_amdgcn_sched_barrier(0);
-            load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
+            ld_tok(v_z, z_row, r.z);
             __builtin_amdgcn_sched_barrier(0);
         }
-        load_raw<IO, PT, VEC>(u_row, tl, Li, r.u);
-        load_raw<IO, PT, VEC>(d_row, tl, Li, r.d);
-        if constexpr (!AHEAD) load_raw<IO, PT, VEC>(z_row, tl, Li, r.z);
-        if constexpr (!AHEAD) {
-            load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
-            load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
-        }
+        ld_tok(v_u, u_row, r.u);
+        ld_tok(v_d, d_row, r.d);
+        if constexpr (!AHEAD) ld_tok(v_z, z_row, r.z);
+        if constexpr (!AHEAD) ld_bc();
     };
 
     // This thread's pieces of a tile's B and C rows into LDS buffer nb
     // (branch-free: a branch here would make the compiler wait for every load
-    // in flight); rows n >= N store B = 0.
+    // in flight); rows n >= N store B = 0 (VEC: read as zeros).
     auto stage_bc = [&](const Regs &r, const int nb) {
         float xb[BT], xc[BT];
         unpack_raw<IO, BT>(r.b, xb);
+        if constexpr (!VEC) {
 #pragma unroll
-        for (int i = 0; i < BT; ++i) xb[i] = bn_ok ? xb[i] : 0.0f;
+            for (int i = 0; i < BT; ++i) xb[i] = bn_ok ? xb[i] : 0.0f;
+        }
         lds_write<BT>(sB + nb * 16 * RS + boff, xb);
         unpack_raw<IO, BT>(r.c, xc);
         lds_write<BT>(sC + nb * 16 * RS + boff, xc);
@@ -482,6 +556,15 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             }
             lds_write<PT>(sdt + poff, xdt);
             lds_write<PT>(sw + poff, xw);
+            // the segment's sum of dt, for its decay in (c): the 4 lanes of
+            // a segment add their pieces (every lane gets the same sum) and
+            // store it in the padding after the segment's tokens
+            float ps = xdt[0];
+#pragma unroll
+            for (int i = 1; i < PT; ++i) ps += xdt[i];
+            ps += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ps), kQuadSwap1, 0xF, 0xF, true));
+            ps += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ps), kQuadSwap2, 0xF, 0xF, true));
+            sdt[pseg * SP + TS] = ps;
         }
         if constexpr (AHEAD) {
             // every wavefront has staged its pieces of this tile and is done
@@ -515,7 +598,7 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
         // in VGPRs for the replay
         float eA[TS][4], eB[TS][4];
         float bs[4];
-        float dtsum = 0.0f;
+        const float dtsum = sdt[s * SP + TS];
 #pragma unroll
         for (int g4 = 0; g4 < TS; g4 += 4) {
             float dt4[4], w4[4], B4[4][4];
@@ -526,7 +609,6 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = g4 + j;
-                dtsum += dt4[j];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float xa = dt4[j] * A2[k];
@@ -606,7 +688,10 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             }
 #pragma unroll
             for (int i = 0; i < PT; ++i) ys[i] = (ys[i] + du[i]) * g[i];
-            if (ch_ok) store_run<IO, PT, VEC>(y, rbase, t0 + lane * PT, L, ys);
+            if (ch_ok) {
+                if constexpr (VEC) store_view<IO, PT>(v_y, o_tok + static_cast<uint32_t>(t0) * ESZ, ys);
+                else store_run<IO, PT, VEC>(y, rbase, t0 + lane * PT, L, ys);
+            }
         }
         if constexpr (AHEAD) signal(2 * ti + 3);   // done reading buffer ti % 3
         if (NBUF == 1) __syncthreads();   // every wavefront is done with this tile's B and C
@@ -705,8 +790,12 @@ static hipError_t launch_tscan_zoh(const ScanArgs &a0, hipStream_t s) {
 template <class IO>
 static hipError_t launch_tscan_io(const ScanArgs &a, hipStream_t s) {
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    // The vector path reads B and C through one view per batch row, at byte
+    // offsets below (16 L + 3 K) elements (state rows up to 15, tiles loaded
+    // up to two ahead of the last): they must stay below 2^31.
     const bool vec = a.L % 16 == 0 && al(a.u) && al(a.delta) && al(a.y) && (!a.z || al(a.z)) &&
-                     al(a.B) && al(a.C);
+                     al(a.B) && al(a.C) &&
+                     (16 * static_cast<uint64_t>(a.L) + 1024) * sizeof(typename IO::T) < (1ull << 31);
     if (a.tile_ts == 16)
         return vec ? launch_tscan_zoh<IO, 16, true>(a, s) : launch_tscan_zoh<IO, 16, false>(a, s);
     if (a.tile_ts == 8)

@@ -297,15 +297,48 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
         }
         return S::pack(e);
     };
+    // VEC: the tile loads and the y and checkpoint stores go through
+    // wave-uniform buffer views: the block's rows of u, delta, z and y (up to
+    // 16 channels of L elements), the batch row's N rows of B and C (rows
+    // r >= N read as zeros) and the block's checkpoint rows.  A lane's piece
+    // of row r lies at r L elements plus its token.  Loads past a chunk's end
+    // read the next tokens (masked in the walk), past the view zeros; a store
+    // that must not happen aims past its view (kDrop) and is dropped, so the
+    // stores are the same instructions on every path and the compiler's
+    // count of memory operations in flight stays exact (a store under a
+    // branch makes the wait for the next tile's loads wait for it too).
+    constexpr uint32_t ESZ = sizeof(IT);
+    const int64_t d0v = d0 < a.D ? d0 : a.D - 1;
+    const int64_t nrows = a.D - d0v < QC ? a.D - d0v : QC;
+    const size_t blk0 = (static_cast<size_t>(b) * a.D + d0v) * L;
+    const uint64_t blk_bytes = VEC ? static_cast<uint64_t>(nrows) * L * ESZ : 0;
+    const Rsrc v_u = view(u + blk0, blk_bytes), v_d = view(dl + blk0, blk_bytes);
+    const Rsrc v_z = view((gate ? z : u) + blk0, blk_bytes);
+    const Rsrc v_y = view(y ? y + blk0 : u + blk0, FULL && y ? blk_bytes : 0);
+    const uint64_t bc_bytes = VEC ? static_cast<uint64_t>(a.N) * L * ESZ : 0;
+    const Rsrc v_b = view(Bm + static_cast<size_t>(b) * a.N * L, bc_bytes);
+    const Rsrc v_c = view(Cm + static_cast<size_t>(b) * a.N * L, bc_bytes);
+    const uint32_t o_row = static_cast<uint32_t>(r) * static_cast<uint32_t>(L) * ESZ;
+    auto load_view = [&](Rsrc v, uint32_t off) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, 0);
+        V o;
+        if constexpr (std::is_same<IO, F32>::value) {
+            o = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                            __uint_as_float(x[3]));
+        } else {
+            o = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+        return o;
+    };
     auto load_tile = [&](int64_t t0) {
         const int64_t t = t0 + sc;
         if (VEC) {
-            const int64_t tc = t < t_end ? t : t_end - VW;   // t_end >= VW here
-            vu = *reinterpret_cast<const V *>(u + rbase + tc);
-            vd = *reinterpret_cast<const V *>(dl + rbase + tc);
-            if (FULL && gate) vz = *reinterpret_cast<const V *>(z + rbase + tc);
-            vb = *reinterpret_cast<const V *>(Bm + sbase + tc);
-            if (FULL) vc = *reinterpret_cast<const V *>(Cm + sbase + tc);
+            const uint32_t off = o_row + static_cast<uint32_t>(t) * ESZ;
+            vu = load_view(v_u, off);
+            vd = load_view(v_d, off);
+            if (FULL && gate) vz = load_view(v_z, off);
+            vb = load_view(v_b, off);
+            if (FULL) vc = load_view(v_c, off);
         } else {
             vu = load_elems(u, rbase, t);
             vd = load_elems(dl, rbase, t);
@@ -370,10 +403,27 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
     float *ckp = (FULL && a.ckpt && lane_ok)
                      ? a.ckpt + (static_cast<size_t>(b) * a.D + d) * a.n_ck * 16 + 4 * q
                      : nullptr;
-    auto ckpt_at = [&](int64_t t) {   // h is the state entering token t
-        if (ckp) *reinterpret_cast<float4 *>(ckp + (t / kBwdTile) * 16) = make_float4(h[0], h[1], h[2], h[3]);
+    // VEC: the block's checkpoint rows as a view (empty without
+    // checkpoints, so that every store is dropped); lane (channel c, row q)
+    // writes floats 4q .. 4q+3 of entry c n_ck + t / kBwdTile (16 floats each)
+    const Rsrc v_ck = view(a.ckpt ? a.ckpt + (static_cast<size_t>(b) * a.D + d0v) * a.n_ck * 16 : a.A,
+                           (VEC && FULL && a.ckpt) ? static_cast<uint64_t>(nrows) * a.n_ck * 64 : 0);
+    const uint32_t o_ck = (static_cast<uint32_t>(lane & 15) * static_cast<uint32_t>(a.n_ck) * 16 +
+                           4 * q) * 4;
+    // h is the state entering token t; `when` (uniform): the store happens
+    auto ckpt_at = [&](int64_t t, bool when) {
+        if constexpr (VEC) {
+            using V4 = __attribute__((ext_vector_type(4))) unsigned int;
+            const uint32_t off = when ? o_ck + static_cast<uint32_t>(t / kBwdTile) * 64 : kDrop;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                V4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]),
+                   __float_as_uint(h[3])}, v_ck, off, 0, 0);
+        } else {
+            if (ckp && when)
+                *reinterpret_cast<float4 *>(ckp + (t / kBwdTile) * 16) = make_float4(h[0], h[1], h[2], h[3]);
+        }
     };
-    if (FULL) ckpt_at(t_begin);
+    if (FULL) ckpt_at(t_begin, true);
 
     // silu(z) (1 without a gate) of this lane's piece of the tile: the lane
     // that converts a piece is the one that stores its y, so the gate stays
@@ -484,13 +534,15 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
             const int o = r * TP + sc;
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
+                // (VEC: rows past N read as zeros)
+                const bool keep_bc = VEC || st_ok;
                 *reinterpret_cast<float4 *>(&s_B[o + i]) =
-                    st_ok ? make_float4(xb[i], xb[i + 1], xb[i + 2], xb[i + 3])
-                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    keep_bc ? make_float4(xb[i], xb[i + 1], xb[i + 2], xb[i + 3])
+                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 if (FULL)
                     *reinterpret_cast<float4 *>(&s_C[o + i]) =
-                        st_ok ? make_float4(xc[i], xc[i + 1], xc[i + 2], xc[i + 3])
-                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        keep_bc ? make_float4(xc[i], xc[i + 1], xc[i + 2], xc[i + 3])
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
         // Unconditional prefetch (addresses are clamped into range): the same
@@ -530,7 +582,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
                 } else {
                     dt_sum += dt;
                 }
-                if (FULL && ckp && (t + 1) % kBwdTile == 0 && t + 1 < t_end) ckpt_at(t + 1);
+                if (FULL && (t + 1) % kBwdTile == 0 && t + 1 < t_end) ckpt_at(t + 1, true);
             }
         } else {
 #pragma unroll
@@ -580,7 +632,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
                 const float ysum = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // token c4 + q
                 const int o = rowc + c4 + q;
                 s_du[o] = ysum + s_du[o];
-                if ((c4 + 4) % kBwdTile == 0 && ckp && t0 + c4 + 4 < t_end) ckpt_at(t0 + c4 + 4);
+                if ((c4 + 4) % kBwdTile == 0) ckpt_at(t0 + c4 + 4, t0 + c4 + 4 < t_end);
             }
         }
         }
@@ -600,8 +652,17 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
                 yo[i + 3] = v.w * gk[i + 3];
             }
             if (VEC) {
-                if (row_ok && t < t_end)
-                    *reinterpret_cast<typename S::V *>(y + rbase + t) = S::pack(yo);
+                const typename S::V pv = S::pack(yo);
+                using V4 = __attribute__((ext_vector_type(4))) unsigned int;
+                V4 w;
+                if constexpr (std::is_same<IO, F32>::value) {
+                    w = V4{__float_as_uint(pv.x), __float_as_uint(pv.y), __float_as_uint(pv.z),
+                           __float_as_uint(pv.w)};
+                } else {
+                    w = V4{pv.x, pv.y, pv.z, pv.w};
+                }
+                const uint32_t off = (row_ok && t < t_end) ? o_row + static_cast<uint32_t>(t) * ESZ : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b128(w, v_y, off, 0, 0);
             } else {
 #pragma unroll
                 for (int i = 0; i < VW; ++i)
@@ -1397,6 +1458,17 @@ struct Dispatch {
     }
 };
 
+// The vector path of the serial walks (quad_pass) reaches a block's 16 rows,
+// and a batch row's N rows of B and C, through buffer views of under 2^31
+// bytes: its offsets reach 16 L elements plus two tiles, and the checkpoint
+// view's 16 rows of n_ck 64-byte entries.
+template <class IO>
+static bool quad_views_fit(const ScanArgs &a) {
+    const uint64_t e = (16 * static_cast<uint64_t>(a.L) + 64) * sizeof(typename IO::T);
+    const uint64_t c = a.ckpt ? 16 * static_cast<uint64_t>(a.n_ck) * 64 : 0;
+    return e < (1ull << 31) && c < (1ull << 31);
+}
+
 template <class IO, bool VEC, bool EXT, bool ZOH>
 static hipError_t launch_quad(const ScanArgs &a, hipStream_t s) {
     Dispatch go(a, s);
@@ -1460,7 +1532,7 @@ static hipError_t launch_scan_io(const ScanArgs &a, hipStream_t s) {
         constexpr int VW = Seg<IO>::VW;
         auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
         const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.y) &&
-                         (!a.z || al(a.z)) && al(a.B) && al(a.C);
+                         (!a.z || al(a.z)) && al(a.B) && al(a.C) && quad_views_fit<IO>(a);
         if (a.zoh)
             return vec ? launch_quad<IO, true, true, true>(a, s)
                        : launch_quad<IO, false, true, true>(a, s);
@@ -1483,7 +1555,8 @@ template <class IO>
 static hipError_t launch_agg_io(const ScanArgs &a, hipStream_t s) {
     constexpr int VW = Seg<IO>::VW;
     auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.B) && al(a.C);
+    const bool vec = a.L % VW == 0 && al(a.u) && al(a.delta) && al(a.B) && al(a.C) &&
+                     quad_views_fit<IO>(a);
     const dim3 agrid(static_cast<unsigned>(a.n_cblk * a.Bsz), static_cast<unsigned>(a.J - 1));
     if (a.zoh) {   // zero-order hold: the extended ZOH instance
         if (vec)

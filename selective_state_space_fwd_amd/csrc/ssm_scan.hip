@@ -297,7 +297,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
         }
         return S::pack(e);
     };
-    // VEC: the tile loads and the y and checkpoint stores go through
+    // VIEWS: the tile loads and the y and checkpoint stores go through
     // wave-uniform buffer views: the block's rows of u, delta, z and y (up to
     // 16 channels of L elements), the batch row's N rows of B and C (rows
     // r >= N read as zeros) and the block's checkpoint rows.  A lane's piece
@@ -307,15 +307,21 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
     // stores are the same instructions on every path and the compiler's
     // count of memory operations in flight stays exact (a store under a
     // branch makes the wait for the next tile's loads wait for it too).
+    // The packed-sequence / convolution instance (EXT without ZOH) keeps
+    // plain pointers: there the views' scalar registers spilled (25 -> 59
+    // SGPRs) and it ran slower (Mamba-2.8B-shaped layer packed as 5
+    // sequences 698 -> 736 us, with the fused convolution 498 -> 509 us;
+    // with zero-order hold 865 -> 800 us, which keeps them).
+    constexpr bool VIEWS = VEC && (!EXT || ZOH);
     constexpr uint32_t ESZ = sizeof(IT);
     const int64_t d0v = d0 < a.D ? d0 : a.D - 1;
     const int64_t nrows = a.D - d0v < QC ? a.D - d0v : QC;
     const size_t blk0 = (static_cast<size_t>(b) * a.D + d0v) * L;
-    const uint64_t blk_bytes = VEC ? static_cast<uint64_t>(nrows) * L * ESZ : 0;
+    const uint64_t blk_bytes = VIEWS ? static_cast<uint64_t>(nrows) * L * ESZ : 0;
     const Rsrc v_u = view(u + blk0, blk_bytes), v_d = view(dl + blk0, blk_bytes);
     const Rsrc v_z = view((gate ? z : u) + blk0, blk_bytes);
     const Rsrc v_y = view(y ? y + blk0 : u + blk0, FULL && y ? blk_bytes : 0);
-    const uint64_t bc_bytes = VEC ? static_cast<uint64_t>(a.N) * L * ESZ : 0;
+    const uint64_t bc_bytes = VIEWS ? static_cast<uint64_t>(a.N) * L * ESZ : 0;
     const Rsrc v_b = view(Bm + static_cast<size_t>(b) * a.N * L, bc_bytes);
     const Rsrc v_c = view(Cm + static_cast<size_t>(b) * a.N * L, bc_bytes);
     const uint32_t o_row = static_cast<uint32_t>(r) * static_cast<uint32_t>(L) * ESZ;
@@ -332,13 +338,20 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
     };
     auto load_tile = [&](int64_t t0) {
         const int64_t t = t0 + sc;
-        if (VEC) {
+        if constexpr (VIEWS) {
             const uint32_t off = o_row + static_cast<uint32_t>(t) * ESZ;
             vu = load_view(v_u, off);
             vd = load_view(v_d, off);
             if (FULL && gate) vz = load_view(v_z, off);
             vb = load_view(v_b, off);
             if (FULL) vc = load_view(v_c, off);
+        } else if constexpr (VEC) {
+            const int64_t tc = t < t_end ? t : t_end - VW;   // t_end >= VW here
+            vu = *reinterpret_cast<const V *>(u + rbase + tc);
+            vd = *reinterpret_cast<const V *>(dl + rbase + tc);
+            if (FULL && gate) vz = *reinterpret_cast<const V *>(z + rbase + tc);
+            vb = *reinterpret_cast<const V *>(Bm + sbase + tc);
+            if (FULL) vc = *reinterpret_cast<const V *>(Cm + sbase + tc);
         } else {
             vu = load_elems(u, rbase, t);
             vd = load_elems(dl, rbase, t);
@@ -403,16 +416,16 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
     float *ckp = (FULL && a.ckpt && lane_ok)
                      ? a.ckpt + (static_cast<size_t>(b) * a.D + d) * a.n_ck * 16 + 4 * q
                      : nullptr;
-    // VEC: the block's checkpoint rows as a view (empty without
+    // VIEWS: the block's checkpoint rows as a view (empty without
     // checkpoints, so that every store is dropped); lane (channel c, row q)
     // writes floats 4q .. 4q+3 of entry c n_ck + t / kBwdTile (16 floats each)
     const Rsrc v_ck = view(a.ckpt ? a.ckpt + (static_cast<size_t>(b) * a.D + d0v) * a.n_ck * 16 : a.A,
-                           (VEC && FULL && a.ckpt) ? static_cast<uint64_t>(nrows) * a.n_ck * 64 : 0);
+                           (VIEWS && FULL && a.ckpt) ? static_cast<uint64_t>(nrows) * a.n_ck * 64 : 0);
     const uint32_t o_ck = (static_cast<uint32_t>(lane & 15) * static_cast<uint32_t>(a.n_ck) * 16 +
                            4 * q) * 4;
     // h is the state entering token t; `when` (uniform): the store happens
     auto ckpt_at = [&](int64_t t, bool when) {
-        if constexpr (VEC) {
+        if constexpr (VIEWS) {
             using V4 = __attribute__((ext_vector_type(4))) unsigned int;
             const uint32_t off = when ? o_ck + static_cast<uint32_t>(t / kBwdTile) * 64 : kDrop;
             __builtin_amdgcn_raw_buffer_store_b128(
@@ -534,8 +547,8 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
             const int o = r * TP + sc;
 #pragma unroll
             for (int i = 0; i < VW; i += 4) {
-                // (VEC: rows past N read as zeros)
-                const bool keep_bc = VEC || st_ok;
+                // (VIEWS: rows past N read as zeros)
+                const bool keep_bc = VIEWS || st_ok;
                 *reinterpret_cast<float4 *>(&s_B[o + i]) =
                     keep_bc ? make_float4(xb[i], xb[i + 1], xb[i + 2], xb[i + 3])
                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -651,7 +664,7 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
                 yo[i + 2] = v.z * gk[i + 2];
                 yo[i + 3] = v.w * gk[i + 3];
             }
-            if (VEC) {
+            if constexpr (VIEWS) {
                 const typename S::V pv = S::pack(yo);
                 using V4 = __attribute__((ext_vector_type(4))) unsigned int;
                 V4 w;
@@ -663,6 +676,9 @@ __device__ __forceinline__ void quad_pass(const ScanArgs &a, int64_t blk, int64_
                 }
                 const uint32_t off = (row_ok && t < t_end) ? o_row + static_cast<uint32_t>(t) * ESZ : kDrop;
                 __builtin_amdgcn_raw_buffer_store_b128(w, v_y, off, 0, 0);
+            } else if constexpr (VEC) {
+                if (row_ok && t < t_end)
+                    *reinterpret_cast<typename S::V *>(y + rbase + t) = S::pack(yo);
             } else {
 #pragma unroll
                 for (int i = 0; i < VW; ++i)

@@ -654,9 +654,18 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
                 if constexpr (CK) {
                     if (t % kBwdTile == 0) {   // h enters token t0 + s TS + t
                         const int64_t tok = t0 + s * TS + t;
-                        if (ch_ok && (!MASK || tok < L))
-                            *reinterpret_cast<float4 *>(ckrow + (tok / kBwdTile) * 16) =
-                                make_float4(h[0], h[1], h[2], h[3]);
+                        if (ch_ok && (!MASK || tok < L)) {
+                            // segments of 8 (many channels): non-temporal
+                            // stores (Mamba-130M-shaped layer with
+                            // checkpoints 50 -> 40 us); segments of 16
+                            // (long sequences): plain stores, faster there
+                            // (705 against 720 us)
+                            using F4 = __attribute__((ext_vector_type(4))) float;
+                            F4 *dst = reinterpret_cast<F4 *>(ckrow + (tok / kBwdTile) * 16);
+                            const F4 hv{h[0], h[1], h[2], h[3]};
+                            if constexpr (TS == 8) __builtin_nontemporal_store(hv, dst);
+                            else *dst = hv;
+                        }
                     }
                 }
 #pragma unroll

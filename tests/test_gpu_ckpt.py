@@ -105,9 +105,11 @@ def forward_with_ckpt(dev, t, N, L, K, zoh, h0=None, cu=None):
 
 # (batch, d_inner, N, L, K): one chunk, 16- and 32-token chunks (edges on and
 # between tiles of the backward), a ragged channel block and token tail, the
-# element path (L % 4 != 0), and the one-launch chunked path (K = 1024)
+# element path (L % 4 != 0), the one-launch chunked path (K = 1024), and the
+# vector path's buffer views with a ragged channel block and d_state 9 (the
+# checkpoint stores of channels past d_inner dropped)
 SHAPES = [(2, 40, 16, 300, 0), (2, 40, 16, 300, 16), (1, 33, 5, 301, 32),
-          (3, 16, 1, 97, 0), (1, 24, 16, 3000, 1024)]
+          (3, 16, 1, 97, 0), (1, 24, 16, 3000, 1024), (2, 40, 9, 512, 64)]
 
 
 @pytest.mark.parametrize("zoh", [False, True])

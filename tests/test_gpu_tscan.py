@@ -80,6 +80,8 @@ def run_and_check(dev, inp, K, zoh=False, h0=None, softplus=None, tol=None):
     ((2, 600, 16, 2048), 0),     # the library's choice: 1200 channels, chunks of 256
     ((1, 3072, 16, 512), 0),     # the library's choice: 3072 channels, chunks of 128
     ((1, 1024, 12, 777), 0),     # the library's choice, element path
+    ((1, 20, 9, 1024), 256),     # buffer views: partial workgroup, B/C rows past d_state 9 read as zeros
+    ((2, 22, 3, 2048), 128),     # buffer views, segments of 8: partial workgroup, d_state 3
 ])
 def test_tscan_shapes(dev, io, shape, K):
     batch, d_inner, N, L = shape

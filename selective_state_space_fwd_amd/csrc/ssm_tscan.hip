@@ -104,42 +104,21 @@ struct Raw {
     uint32_t w[NW];
 };
 
-// Load NE elements at token t of a row (row = the row's first element).
-// VEC: one vector access (16-byte pieces); the row length L is a multiple of
-// 16 and the pointer 16-byte aligned, so a run that would pass L is moved
-// back to end at L (min(t, L - NE): its values past L are never used).  The
-// same instructions run for every tile -- no branch, so that the register
-// sets of the tiles in flight are never merged (a merge copies registers,
-// which waits for every load in flight).  Otherwise element loads with the
-// token index clamped to L - 1.
-template <class IO, int NE, bool VEC>
+// Load NE elements at token t of a row (row = the row's first element) as
+// raw words, one element access each, the token index clamped to L - 1 (the
+// element path: rows not in 16-byte pieces; the vector path reads through
+// buffer views, below).
+template <class IO, int NE>
 __device__ __forceinline__ void load_raw(const typename IO::T *__restrict__ row, int t, int L,
                                          Raw<IO, NE> &r) {
-    using R = Raw<IO, NE>;
-    if (VEC) {
-        const typename IO::T *q = row + min(t, L - NE);
-        if constexpr (R::NW % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < R::NW / 4; ++i) {
-                const uint4 v = reinterpret_cast<const uint4 *>(q)[i];
-                r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
-            }
-        } else if constexpr (R::NW == 2) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(q);
-            r.w[0] = v.x; r.w[1] = v.y;
+    for (int i = 0; i < NE; ++i) {
+        const int tc = t + i < L ? t + i : L - 1;
+        if constexpr (std::is_same<IO, F32>::value) {
+            r.w[i] = __float_as_uint(row[tc]);
         } else {
-            r.w[0] = *reinterpret_cast<const uint32_t *>(q);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int tc = t + i < L ? t + i : L - 1;
-            if constexpr (std::is_same<IO, F32>::value) {
-                r.w[i] = __float_as_uint(row[tc]);
-            } else {
-                const uint32_t v = row[tc];
-                if (i % 2 == 0) r.w[i / 2] = v; else r.w[i / 2] |= v << 16;
-            }
+            const uint32_t v = row[tc];
+            if (i % 2 == 0) r.w[i / 2] = v; else r.w[i / 2] |= v << 16;
         }
     }
 }
@@ -199,39 +178,14 @@ __device__ __forceinline__ void unpack_raw(const Raw<IO, NE> &r, float (&o)[NE])
 }
 
 // Store NE values at token t of a row, converting to the I/O type (bf16:
-// round to nearest even); tokens at or past L are not written.  VEC: L is a
-// multiple of 16, so a run never straddles L and one predicated vector store
-// serves every lane (the same store instructions on every path keep the
-// compiler's count of memory operations in flight exact, so that a later
-// wait for a tile's loads does not also wait for these stores).
-template <class IO, int NE, bool VEC>
+// round to nearest even), one element store each; tokens at or past L are not
+// written (the element path; the vector path stores through a buffer view).
+template <class IO, int NE>
 __device__ __forceinline__ void store_run(typename IO::T *__restrict__ p, size_t base, int64_t t,
                                           int64_t L, const float (&v)[NE]) {
-    if (VEC) {
-        if (t >= L) return;
-        if constexpr (std::is_same<IO, F32>::value) {
-            if constexpr (NE == 4)
-                *reinterpret_cast<float4 *>(p + base + t) = make_float4(v[0], v[1], v[2], v[3]);
-            else if constexpr (NE == 2)
-                *reinterpret_cast<float2 *>(p + base + t) = make_float2(v[0], v[1]);
-            else
 #pragma unroll
-                for (int i = 0; i < NE; ++i) p[base + t + i] = v[i];
-        } else {
-            if constexpr (NE == 4)
-                *reinterpret_cast<uint2 *>(p + base + t) =
-                    make_uint2(Seg<BF16>::pk(v[0], v[1]), Seg<BF16>::pk(v[2], v[3]));
-            else if constexpr (NE == 2)
-                *reinterpret_cast<uint32_t *>(p + base + t) = Seg<BF16>::pk(v[0], v[1]);
-            else
-#pragma unroll
-                for (int i = 0; i < NE; ++i) IO::store(p, base + t + i, v[i]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NE; ++i)
-            if (t + i < L) IO::store(p, base + t + i, v[i]);
-    }
+    for (int i = 0; i < NE; ++i)
+        if (t + i < L) IO::store(p, base + t + i, v[i]);
 }
 
 template <int N>
@@ -403,8 +357,8 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
     // the batch row's N rows of B and C, past which rows n >= N read as
     // zeros.  A lane's byte offsets are fixed plus the tile's first token;
     // tokens at or past L read as zeros and their y stores are dropped.
-    // (The launch takes this path only when N L elements of B span less
-    // than 2^31 bytes.)
+    // (The launch takes this path only when the offsets, below 16 L + 3 K
+    // elements, stay under 2^31 bytes.)
     constexpr uint32_t ESZ = sizeof(IT);
     const uint64_t row_bytes = VEC ? static_cast<uint64_t>(L) * ESZ : 0;
     const Rsrc v_u = view(u_row, row_bytes), v_d = view(d_row, row_bytes);
@@ -428,13 +382,13 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
                 load_view<IO, BT>(v_b, o_bc + ot, r.b);
                 load_view<IO, BT>(v_c, o_bc + ot, r.c);
             } else {
-                load_raw<IO, BT, VEC>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
-                load_raw<IO, BT, VEC>(c_row, tb, Li, r.c);
+                load_raw<IO, BT>(b_row, tb, Li, r.b);   // rows n >= N read row N-1, unused
+                load_raw<IO, BT>(c_row, tb, Li, r.c);
             }
         };
         auto ld_tok = [&](Rsrc v, const IT *row, Raw<IO, PT> &x) {
             if constexpr (VEC) load_view<IO, PT>(v, o_tok + ot, x);
-            else load_raw<IO, PT, VEC>(row, tl, Li, x);
+            else load_raw<IO, PT>(row, tl, Li, x);
         };
         if constexpr (AHEAD) {
             ld_bc();
@@ -699,7 +653,7 @@ __global__ __launch_bounds__(64 * ts_waves<TS>(), TS == 8 ? 3 : 2) void tscan_ke
             for (int i = 0; i < PT; ++i) ys[i] = (ys[i] + du[i]) * g[i];
             if (ch_ok) {
                 if constexpr (VEC) store_view<IO, PT>(v_y, o_tok + static_cast<uint32_t>(t0) * ESZ, ys);
-                else store_run<IO, PT, VEC>(y, rbase, t0 + lane * PT, L, ys);
+                else store_run<IO, PT>(y, rbase, t0 + lane * PT, L, ys);
             }
         }
         if constexpr (AHEAD) signal(2 * ti + 3);   // done reading buffer ti % 3

@@ -122,6 +122,11 @@ int64_t quad_auto_chunk(int64_t L, int64_t waves) {
 constexpr int64_t kTsMinRows = 1024;
 constexpr int64_t kTsMaxRows = 8192;
 constexpr int64_t kTsRows16 = 2048;
+// Fewer channels and a short sequence (up to kTsShortL tokens): one launch of
+// the in-wave scan at segments of 8 also beats the two passes that the serial
+// mapping needs to fill the chip (measured for 64 to 1000 channels: 8-15 us
+// against 17-24 us up to 1024 tokens; about even at 2048, behind at 4096).
+constexpr int64_t kTsShortL = 1024;
 
 // fwd: the plan of a forward scan, which may run the chunked quad path as
 // one launch (long chunks) and, for calls without packed sequences or the
@@ -152,6 +157,8 @@ ssm_status make_plan(const ssm_desc *d, Plan *p, bool fwd = true, bool lean = tr
     } else if (ts_ok && d->chunk_size == 0 && d->batch * p->n_cblk < kEnoughWaves &&
                rows >= kTsMinRows && rows <= kTsMaxRows && L > 64) {
         p->tile_ts = rows <= kTsRows16 ? 16 : 8;
+    } else if (ts_ok && d->chunk_size == 0 && rows < kTsMinRows && L > 64 && L <= kTsShortL) {
+        p->tile_ts = 8;
     }
     if (p->tile_ts > 0) {
         p->K = 16 * p->tile_ts < L ? 16 * p->tile_ts : L;

@@ -111,7 +111,8 @@ def test_workspace_and_chunk_plan(lib):
 
 def test_in_wave_plan_choice(lib):
     """Chunks of 128 or 256 tokens requested, or chosen by the library for
-    1024 to 8192 channels, run as the in-wave scan (no workspace for a plain
+    1024 to 8192 channels (or fewer channels and at most 1024 tokens), run as
+    the in-wave scan (no workspace for a plain
     call, with or without checkpoints); the workspace query still covers the
     chunked plan that calls with packed sequences or the convolution run."""
     def plan(**kw):
@@ -127,8 +128,12 @@ def test_in_wave_plan_choice(lib):
     assert p.startswith("in-wave") and K == 256
     # enough channels for the serial mapping in one chunk
     assert plan(batch=8, d_inner=4096)[0] == "one chunk"
-    # few channels: chunks on separate workgroups
-    assert plan(batch=1, d_inner=64, seqlen=256)[0].startswith("two passes")
+    # few channels and a short sequence: the in-wave scan at chunks of 128
+    for d_inner, seqlen in ((64, 256), (1000, 1024), (1, 65)):
+        p, K, _ = plan(batch=1, d_inner=d_inner, seqlen=seqlen)
+        assert p.startswith("in-wave") and K == min(128, seqlen), (d_inner, seqlen, p)
+    # few channels, longer sequences: chunks on separate workgroups
+    assert plan(batch=1, d_inner=64, seqlen=1040)[0].startswith("two passes")
     assert plan(batch=1, d_inner=512, seqlen=65536)[0].startswith("two passes")
     # asked for explicitly, at any channel count, also with zero-order hold
     for k in (128, 256):
@@ -412,18 +417,20 @@ def test_forward_auto_chunking(lib):
     # a whole number of rounds: one chunk
     assert K(batch=8, d_inner=4096, seqlen=2048, io_dtype=1) == 2048
     assert K(batch=4, d_inner=2048, d_state=256, seqlen=4096) == 4096
-    assert K(batch=1, d_inner=64, seqlen=256) == 64
+    # few channels and at most 1024 tokens: the in-wave scan's chunks of 128
+    assert K(batch=1, d_inner=64, seqlen=256) == 128
+    assert K(batch=1, d_inner=16, seqlen=65) == 65
     # one wavefront per chunk: the minimum chunk length, or one chunk when the
     # sequence is no longer than it
     assert K(batch=1, d_inner=16, seqlen=16) == 16
     assert K(batch=1, d_inner=16, seqlen=64) == 64
-    assert K(batch=1, d_inner=16, seqlen=65) == 64
+    assert K(batch=1, d_inner=16, seqlen=1100) == 64
     assert K(batch=1, d_inner=16, seqlen=1) == 1
     # the choice is a minimum of the cost over the candidate chunk counts
     def cost(k, waves, L):
         nj = -(-L // k)
         return k * (5 * -(-waves * nj // 1024) + 4 * -(-waves * (nj - 1) // 1024))
-    for b, dI, L in ((1, 768, 4096), (1, 1000, 3000), (4, 2560, 2048), (1, 16, 300)):
+    for b, dI, L in ((1, 768, 4096), (1, 1000, 3000), (4, 2560, 2048), (1, 16, 3000)):
         waves = b * -(-dI // 16)
         got = K(batch=b, d_inner=dI, seqlen=L)
         J0 = -(-2048 // waves)
